@@ -1,0 +1,33 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line(
+        "markers", "slow: long-running CPU test (full-size oracle runs)")
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="session")
+def fb():
+    """The HIP library binding; GPU tests fail loudly when it is missing."""
+    if not gpu_available():
+        pytest.fail("GPU test selected but no GPU is visible")
+    import block_diffusion_attention_amd as fbmod
+    fbmod.load()          # raises if the built library is missing
+    return fbmod
