@@ -1,0 +1,106 @@
+"""MI355X (gfx950) FlashBlock block-diffusion attention step.
+
+The compute lives in ``libflashblock.so`` (hand-written HIP kernels behind a
+C ABI, ``include/flashblock.h``); this package is a thin ctypes binding with
+the same entry-point names plus ``Step``, a helper that allocates the device
+buffers one block's ``fb_step`` calls use. PyTorch supplies device memory and
+streams only.
+"""
+
+import torch
+
+from . import _abi
+from ._abi import (  # noqa: F401
+    ABI_VERSION, FB_BF16, FB_F32, FB_OK, FB_ERR_DEVICE, FB_ERR_INVALID_ARGUMENT,
+    FB_ERR_UNSUPPORTED, FB_ERR_WORKSPACE_TOO_SMALL, FB_REUSE_ACTIVE_MSE, FB_REUSE_COUNT,
+    FB_REUSE_HEAD_COS, FB_SEL_DENSE, FB_SEL_GATHER, FB_SEL_SPLIT, FB_STEP_SPARSE,
+    FB_STEP_TEXT, FB_STEP_VIDEO, LIB_PATH, SYMBOLS, FlashBlockError, dtype_code,
+    fb_abi_version, fb_attn_shape, fb_block_attn_merge, fb_block_attn_merge_workspace,
+    fb_page_meta, fb_page_sel, fb_page_select, fb_page_select_workspace, fb_prefix_attn,
+    fb_prefix_attn_workspace, fb_reuse_args, fb_reuse_decide, fb_reuse_decide_workspace,
+    fb_status_string, fb_step, fb_step_args, fb_step_state, fb_step_workspace, fb_tensor,
+    load, page_sel, ptr, shape_of, stream_of, tensor_of)
+
+
+class Step:
+    """One block's fb_step state and the caller-owned device buffers behind it.
+
+    mode: FB_STEP_TEXT / FB_STEP_VIDEO / FB_STEP_SPARSE. k_prefix, v_prefix:
+    [n_kv, Hkv, d] tensors (any token/head strides). ``new_block()`` restarts
+    the step counter (the next call recomputes the cached pair).
+    """
+
+    def __init__(self, mode, shape, n_q, k_prefix, v_prefix, tau=0, gamma=0.0,
+                 page_size=16, k_pages=0, pct=25, device=None):
+        load()
+        dev = device or k_prefix.device
+        hq, d = shape.n_q_heads, shape.head_dim
+        f32 = dict(device=dev, dtype=torch.float32)
+        self.shape = shape
+        self.n_q = n_q
+        self.k_prefix, self.v_prefix = k_prefix, v_prefix
+        self.a_out = torch.zeros(n_q, hq, d, **f32)
+        self.l_out = torch.zeros(n_q, hq, **f32)
+        self._masks = [torch.zeros(hq, device=dev, dtype=torch.uint8),
+                       torch.zeros(hq, device=dev, dtype=torch.uint8)]
+        self.m_count = torch.zeros(1, device=dev, dtype=torch.int32)
+        self.ids_prev = torch.zeros(n_q, device=dev, dtype=torch.int32)
+        st = fb_step_state()
+        st.shape = shape
+        st.mode = int(mode)
+        st.n_q = int(n_q)
+        st.k_prefix = tensor_of(k_prefix)
+        st.v_prefix = tensor_of(v_prefix)
+        st.tau = int(tau)
+        st.gamma = float(gamma)
+        st.page_size = int(page_size)
+        st.k_pages = int(k_pages)
+        st.pct = int(pct)
+        st.a_out, st.l_out = ptr(self.a_out), ptr(self.l_out)
+        st.mask, st.mask_next = ptr(self._masks[0]), ptr(self._masks[1])
+        st.m_count, st.ids_prev = ptr(self.m_count), ptr(self.ids_prev)
+        if mode == FB_STEP_VIDEO:
+            self.a_probe = torch.zeros(n_q, hq, d, **f32)
+            self.l_probe = torch.zeros(n_q, hq, **f32)
+            self.sim = torch.full((hq,), float("nan"), device=dev, dtype=torch.float64)
+            st.a_probe, st.l_probe, st.sim = ptr(self.a_probe), ptr(self.l_probe), ptr(self.sim)
+        if mode == FB_STEP_SPARSE:
+            hkv = shape.n_kv_heads
+            n_pages = (k_prefix.shape[0] + page_size - 1) // page_size
+            kdt = k_prefix.dtype
+            self.a_res = torch.zeros(n_q, hq, d, **f32)
+            self.l_res = torch.zeros(n_q, hq, **f32)
+            self.pages = torch.zeros(n_q, hkv, max(k_pages, 1), device=dev, dtype=torch.int32)
+            self.kmin = torch.empty(hkv, max(n_pages, 1), d, device=dev, dtype=kdt)
+            self.kmax = torch.empty(hkv, max(n_pages, 1), d, device=dev, dtype=kdt)
+            self.q_prev = torch.zeros(n_q, hq, d, device=dev, dtype=kdt)
+            self.mse = torch.zeros(n_q, device=dev, dtype=torch.float64)
+            self.active = torch.zeros(n_q, device=dev, dtype=torch.uint8)
+            for name in ("a_res", "l_res", "pages", "kmin", "kmax", "q_prev", "mse", "active"):
+                setattr(st, name, ptr(getattr(self, name)))
+        self.state = st
+        nbytes = fb_step_workspace(st)
+        self.ws = torch.empty(max(nbytes, 16), device=dev, dtype=torch.uint8)
+        st.ws, st.ws_bytes = ptr(self.ws), self.ws.numel()
+
+    @property
+    def mask(self):
+        """The [Hq] reuse flags used by the latest step (1 = reused)."""
+        cur = self.state.mask
+        return self._masks[0] if self._masks[0].data_ptr() == cur else self._masks[1]
+
+    @property
+    def mask_next(self):
+        cur = self.state.mask
+        return self._masks[1] if self._masks[0].data_ptr() == cur else self._masks[0]
+
+    def new_block(self):
+        self.state.step = 0
+
+    def step(self, q, k, v, a_full, l_full=None, ids=None, decision=-1, stream=None):
+        args = fb_step_args()
+        args.q_blk, args.k_blk, args.v_blk = tensor_of(q), tensor_of(k), tensor_of(v)
+        args.ids_cur = ptr(ids)
+        args.decision = int(decision)
+        args.a_full, args.l_full = ptr(a_full), ptr(l_full)
+        fb_step(self.state, args, stream)

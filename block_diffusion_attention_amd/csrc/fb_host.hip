@@ -1,0 +1,552 @@
+// fb_host.hip -- the C ABI (include/flashblock.h): argument validation,
+// split-K planning and workspace sizing, and the launch order of one
+// FlashBlock denoising step on the caller's stream.
+//
+// Nothing here allocates, synchronises or keeps global state; every
+// decision the method takes per step (FlashBlock technical summary, s2
+// "adaptive reuse strategies") is taken on the device and consumed there.
+#include <math.h>
+#include <string.h>
+
+#include "fb_internal.h"
+
+namespace fb {
+hipError_t launch_fill_u8(uint8_t* p, int n, uint8_t v, hipStream_t s);
+hipError_t launch_copy_rows(const void* src, int64_t st, int64_t sh, void* dst, int n_q, int hq,
+                            int d, fb_dtype dt, hipStream_t s);
+}  // namespace fb
+
+using namespace fb;
+
+namespace {
+
+// Split-K planning. A launch should put several workgroups on each of the
+// 256 CUs (8 XCDs x 32); chunks are at least a few tiles per wave long so the
+// partials stay a small fraction of the K/V bytes.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int64_t kMinTilesMfma = 16;     // 32-token tiles per chunk (4 waves)
+constexpr int64_t kMinTilesGeneric = 4;   // 64-token tiles per chunk
+constexpr size_t kAlign = 256;
+
+enum Path { PATH_GENERIC = 0, PATH_MFMA = 1 };
+
+struct PrefixPlan {
+  int path = PATH_GENERIC;
+  int row_blocks = 1;
+  int n_chunks = 0;
+  int64_t tiles_per_chunk = 0;
+  bool direct = false;         // one chunk, written straight to the outputs
+  int64_t rows = 0;            // n_q * Hq
+  size_t off_l = 0, off_ra = 0, off_rl = 0, ws_bytes = 0;
+};
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fb_status check_shape(const fb_attn_shape* s) {
+  if (!s) return FB_ERR_INVALID_ARGUMENT;
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
+    return FB_ERR_INVALID_ARGUMENT;
+  if (s->dtype != FB_BF16 && s->dtype != FB_F32) return FB_ERR_INVALID_ARGUMENT;
+  if (!(s->scale > 0.f) || !isfinite(s->scale)) return FB_ERR_INVALID_ARGUMENT;
+  if (s->head_dim < 1) return FB_ERR_INVALID_ARGUMENT;
+  if (s->head_dim != 64 && s->head_dim != 128) return FB_ERR_UNSUPPORTED;
+  return FB_OK;
+}
+
+// n_tok must equal `want` when want >= 0. Token/head grid must not overlap:
+// either token-major (stride_head >= d, stride_tok >= heads*stride_head) or
+// head-major (stride_tok >= d, stride_head >= n_tok*stride_tok).
+fb_status check_tensor(const fb_tensor& t, int64_t want, int heads, int d) {
+  if (t.n_tok < 0) return FB_ERR_INVALID_ARGUMENT;
+  if (want >= 0 && t.n_tok != want) return FB_ERR_INVALID_ARGUMENT;
+  if (t.n_tok == 0) return FB_OK;
+  if (!t.ptr || !aligned16(t.ptr)) return FB_ERR_INVALID_ARGUMENT;
+  if (t.stride_tok < 0 || t.stride_head < 0) return FB_ERR_INVALID_ARGUMENT;
+  if (t.stride_tok % 8 != 0 || t.stride_head % 8 != 0) return FB_ERR_INVALID_ARGUMENT;
+  const bool one_head = heads == 1, one_tok = t.n_tok == 1;
+  const bool tok_major = (one_head || t.stride_head >= d) &&
+                         (one_tok || t.stride_tok >= (one_head ? d : heads * t.stride_head));
+  const bool head_major = (one_tok || t.stride_tok >= d) &&
+                          (one_head || t.stride_head >= t.n_tok * t.stride_tok);
+  if (!tok_major && !head_major) return FB_ERR_INVALID_ARGUMENT;
+  return FB_OK;
+}
+
+fb_status check_sel(const fb_page_sel* sel, const fb_attn_shape& s, int64_t n_q, int64_t n_kv) {
+  if (!sel || sel->mode == FB_SEL_DENSE) return FB_OK;
+  if (sel->mode != FB_SEL_SPLIT && sel->mode != FB_SEL_GATHER) return FB_ERR_INVALID_ARGUMENT;
+  if (sel->page_size < 1 || sel->k_pages < 0) return FB_ERR_INVALID_ARGUMENT;
+  const int64_t n_pages = (n_kv + sel->page_size - 1) / sel->page_size;
+  if (sel->k_pages > n_pages) return FB_ERR_INVALID_ARGUMENT;
+  if (sel->k_pages > 0 && !sel->pages) return FB_ERR_INVALID_ARGUMENT;
+  (void)s;
+  (void)n_q;
+  return FB_OK;
+}
+
+PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const fb_page_sel* sel) {
+  PrefixPlan pl;
+  const int mode = sel ? sel->mode : FB_SEL_DENSE;
+  const int G = s.n_q_heads / s.n_kv_heads;
+  const int64_t group_rows = n_q * G;
+  pl.rows = n_q * s.n_q_heads;
+  pl.path = (s.dtype == FB_BF16 && s.head_dim == 128 && mode == FB_SEL_DENSE) ? PATH_MFMA
+                                                                             : PATH_GENERIC;
+  const int tile = prefix_tile_tokens(pl.path);
+  const int64_t n_virt = mode == FB_SEL_GATHER ? static_cast<int64_t>(sel->k_pages) * sel->page_size
+                                               : n_kv;
+  const int64_t n_tiles = (n_virt + tile - 1) / tile;
+  int64_t wg_per_chunk;
+  int64_t min_tiles;
+  if (pl.path == PATH_MFMA) {
+    pl.row_blocks = group_rows <= 32 ? 1 : 2;
+    wg_per_chunk = s.n_kv_heads * ((group_rows + 63) / 64);
+    min_tiles = kMinTilesMfma;
+  } else {
+    wg_per_chunk = pl.rows;
+    min_tiles = kMinTilesGeneric;
+  }
+  if (n_tiles > 0) {
+    int64_t want = kTargetWorkgroups / wg_per_chunk;
+    if (want < 1) want = 1;
+    int64_t cap = n_tiles / min_tiles;
+    if (cap < 1) cap = 1;
+    const int64_t chunks = want < cap ? want : cap;
+    pl.tiles_per_chunk = (n_tiles + chunks - 1) / chunks;
+    pl.n_chunks = static_cast<int>((n_tiles + pl.tiles_per_chunk - 1) / pl.tiles_per_chunk);
+  }
+  pl.direct = pl.n_chunks == 1 && mode == FB_SEL_DENSE;
+  if (!pl.direct && pl.n_chunks > 0) {
+    const size_t nc = static_cast<size_t>(pl.n_chunks);
+    const size_t a_bytes = align_up(nc * pl.rows * s.head_dim * sizeof(float));
+    const size_t l_bytes = align_up(nc * pl.rows * sizeof(float));
+    pl.off_l = a_bytes;
+    pl.ws_bytes = a_bytes + l_bytes;
+    if (mode == FB_SEL_SPLIT) {
+      pl.off_ra = pl.ws_bytes;
+      pl.off_rl = pl.off_ra + a_bytes;
+      pl.ws_bytes = pl.off_rl + l_bytes;
+    }
+  }
+  return pl;
+}
+
+fb_status dev(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_DEVICE; }
+
+fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor& k,
+                     const fb_tensor& v, const uint8_t* mask, const fb_page_sel* sel, float* a_out,
+                     float* l_out, float* a_res, float* l_res, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  const int64_t n_q = q.n_tok, n_kv = k.n_tok;
+  const int mode = sel ? sel->mode : FB_SEL_DENSE;
+  const PrefixPlan pl = plan_prefix(s, n_q, n_kv, sel);
+  if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;
+  if (pl.ws_bytes > 0 && !aligned16(ws)) return FB_ERR_INVALID_ARGUMENT;
+
+  char* w = static_cast<char*>(ws);
+  PrefixParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q = q.ptr;
+  pp.q_st = q.stride_tok;
+  pp.q_sh = q.stride_head;
+  pp.k = k.ptr;
+  pp.v = v.ptr;
+  pp.kv_st = k.stride_tok;
+  pp.kv_sh = k.stride_head;
+  pp.n_kv = n_kv;
+  pp.n_q = static_cast<int>(n_q);
+  pp.hq = s.n_q_heads;
+  pp.hkv = s.n_kv_heads;
+  pp.group = s.n_q_heads / s.n_kv_heads;
+  pp.scale_log2 = s.scale * kLog2e;
+  pp.mask = mask;
+  pp.tiles_per_chunk = pl.tiles_per_chunk;
+  pp.n_chunks = pl.n_chunks;
+  pp.sel_mode = mode;
+  if (mode != FB_SEL_DENSE) {
+    pp.page_size = sel->page_size;
+    pp.k_pages = sel->k_pages;
+    pp.pages = sel->pages;
+    pp.active = mode == FB_SEL_GATHER ? sel->active : nullptr;
+  }
+  if (pl.direct) {
+    pp.out = RowOut{a_out, l_out, 0};
+  } else {
+    pp.out = RowOut{reinterpret_cast<float*>(w), reinterpret_cast<float*>(w + pl.off_l), pl.rows};
+    if (mode == FB_SEL_SPLIT)
+      pp.out_res = RowOut{reinterpret_cast<float*>(w + pl.off_ra),
+                          reinterpret_cast<float*>(w + pl.off_rl), pl.rows};
+  }
+  // K and V share strides in the kernels
+  if (v.stride_tok != k.stride_tok || v.stride_head != k.stride_head) return FB_ERR_UNSUPPORTED;
+
+  if (pl.n_chunks > 0) {
+    hipError_t e = pl.path == PATH_MFMA ? launch_prefix_mfma(pp, pl.row_blocks, stream)
+                                        : launch_prefix_generic(pp, s.dtype, s.head_dim, stream);
+    if (e != hipSuccess) return FB_ERR_DEVICE;
+  }
+  if (pl.direct) return FB_OK;
+  ReduceParams rp;
+  memset(&rp, 0, sizeof(rp));
+  rp.part_a = pp.out.a;
+  rp.part_l = pp.out.l;
+  rp.n_chunks = pl.n_chunks;
+  rp.rows = pl.rows;
+  rp.hq = s.n_q_heads;
+  rp.d = s.head_dim;
+  rp.mask = mask;
+  rp.a_out = a_out;
+  rp.l_out = l_out;
+  if (mode == FB_SEL_SPLIT) {
+    rp.part_ra = pp.out_res.a;
+    rp.part_rl = pp.out_res.l;
+    rp.a_res = a_res;
+    rp.l_res = l_res;
+  } else if (mode == FB_SEL_GATHER) {
+    rp.active = sel->active;
+    rp.res_a = a_res;
+    rp.res_l = l_res;
+  }
+  return dev(launch_prefix_reduce(rp, stream));
+}
+
+fb_status validate_prefix(const fb_attn_shape* shape, const fb_tensor& q, const fb_tensor& k,
+                          const fb_tensor& v, const fb_page_sel* sel, const float* a_out,
+                          const float* l_out, const float* a_res, const float* l_res) {
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  const int d = shape->head_dim;
+  if (q.n_tok < 1) return FB_ERR_INVALID_ARGUMENT;
+  if ((st = check_tensor(q, -1, shape->n_q_heads, d)) != FB_OK) return st;
+  if ((st = check_tensor(k, -1, shape->n_kv_heads, d)) != FB_OK) return st;
+  if ((st = check_tensor(v, k.n_tok, shape->n_kv_heads, d)) != FB_OK) return st;
+  if (!a_out || !l_out || !aligned16(a_out)) return FB_ERR_INVALID_ARGUMENT;
+  if (q.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
+  if ((st = check_sel(sel, *shape, q.n_tok, k.n_tok)) != FB_OK) return st;
+  const int mode = sel ? sel->mode : FB_SEL_DENSE;
+  if (mode == FB_SEL_DENSE && (a_res || l_res)) return FB_ERR_INVALID_ARGUMENT;
+  if (mode != FB_SEL_DENSE && (!a_res || !l_res)) return FB_ERR_INVALID_ARGUMENT;
+  return FB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fb_status_string(fb_status s) {
+  switch (s) {
+    case FB_OK: return "ok";
+    case FB_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FB_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FB_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FB_ERR_DEVICE: return "device (HIP) error";
+  }
+  return "unknown status";
+}
+
+int fb_abi_version(void) { return FB_ABI_VERSION; }
+
+size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t n_kv,
+                                const fb_page_sel* sel) {
+  if (check_shape(shape) != FB_OK || n_q < 1 || n_kv < 0) return 0;
+  if (check_sel(sel, *shape, n_q, n_kv) != FB_OK) return 0;
+  return plan_prefix(*shape, n_q, n_kv, sel).ws_bytes;
+}
+
+fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k, fb_tensor v,
+                         const uint8_t* head_reuse_mask, const fb_page_sel* sel, float* a_out,
+                         float* l_out, float* a_res, float* l_res, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  fb_status st = validate_prefix(shape, q, k, v, sel, a_out, l_out, a_res, l_res);
+  if (st != FB_OK) return st;
+  return run_prefix(*shape, q, k, v, head_reuse_mask, sel, a_out, l_out, a_res, l_res, ws,
+                    ws_bytes, stream);
+}
+
+size_t fb_block_attn_merge_workspace(const fb_attn_shape* shape, int64_t n_q) {
+  (void)shape;
+  (void)n_q;
+  return 0;
+}
+
+fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk, fb_tensor k_blk,
+                              fb_tensor v_blk, const float* a_out, const float* l_out,
+                              float* a_full, float* l_full, float* a_in, float* l_in, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  const int d = shape->head_dim;
+  if (q_blk.n_tok < 1) return FB_ERR_INVALID_ARGUMENT;
+  if ((st = check_tensor(q_blk, -1, shape->n_q_heads, d)) != FB_OK) return st;
+  if ((st = check_tensor(k_blk, q_blk.n_tok, shape->n_kv_heads, d)) != FB_OK) return st;
+  if ((st = check_tensor(v_blk, q_blk.n_tok, shape->n_kv_heads, d)) != FB_OK) return st;
+  if (!a_out || !l_out || !a_full) return FB_ERR_INVALID_ARGUMENT;
+  if (q_blk.n_tok > 65535) return FB_ERR_UNSUPPORTED;
+  BlockParams bp;
+  memset(&bp, 0, sizeof(bp));
+  bp.q = q_blk.ptr;
+  bp.q_st = q_blk.stride_tok;
+  bp.q_sh = q_blk.stride_head;
+  bp.k = k_blk.ptr;
+  bp.v = v_blk.ptr;
+  bp.k_st = k_blk.stride_tok;
+  bp.k_sh = k_blk.stride_head;
+  bp.v_st = v_blk.stride_tok;
+  bp.v_sh = v_blk.stride_head;
+  bp.n_q = static_cast<int>(q_blk.n_tok);
+  bp.hq = shape->n_q_heads;
+  bp.hkv = shape->n_kv_heads;
+  bp.group = shape->n_q_heads / shape->n_kv_heads;
+  bp.d = d;
+  bp.scale_log2 = shape->scale * kLog2e;
+  bp.a_out = a_out;
+  bp.l_out = l_out;
+  bp.a_full = a_full;
+  bp.l_full = l_full;
+  bp.a_in = a_in;
+  bp.l_in = l_in;
+  return dev(launch_block_small(bp, shape->dtype, stream));
+}
+
+size_t fb_reuse_decide_workspace(const fb_reuse_args* a) {
+  if (!a || a->n_q < 0 || a->n_heads < 1) return 0;
+  switch (a->mode) {
+    case FB_REUSE_COUNT: return 0;
+    case FB_REUSE_HEAD_COS:
+      return align_up(static_cast<size_t>(head_cos_chunks(a->n_q)) * a->n_heads * 3 * sizeof(double));
+    case FB_REUSE_ACTIVE_MSE: return align_up(static_cast<size_t>(a->n_q) * sizeof(double));
+  }
+  return 0;
+}
+
+fb_status fb_reuse_decide(const fb_reuse_args* a, hipStream_t stream) {
+  if (!a || a->n_heads < 1 || a->n_q < 0) return FB_ERR_INVALID_ARGUMENT;
+  switch (a->mode) {
+    case FB_REUSE_COUNT:
+      if (!a->mask || (a->n_q > 0 && !a->ids_cur)) return FB_ERR_INVALID_ARGUMENT;
+      if (a->force < -1 || a->force > 1) return FB_ERR_INVALID_ARGUMENT;
+      return dev(launch_count(a->ids_prev, a->ids_cur, a->n_q, a->tau, a->force, a->n_heads,
+                              a->mask, a->m_count, a->ids_store, stream));
+    case FB_REUSE_HEAD_COS: {
+      if (a->n_q < 1 || !a->a_cached || !a->a_probe || !a->sim || !a->mask)
+        return FB_ERR_INVALID_ARGUMENT;
+      if (a->head_dim < 1) return FB_ERR_INVALID_ARGUMENT;
+      if (!isfinite(a->gamma)) return FB_ERR_INVALID_ARGUMENT;
+      const size_t need = fb_reuse_decide_workspace(a);
+      if (a->ws_bytes < need || !a->ws) return FB_ERR_WORKSPACE_TOO_SMALL;
+      return dev(launch_head_cos(a->a_cached, a->a_probe, a->n_q, a->n_heads, a->head_dim,
+                                 a->mask_in, a->gamma, a->sim, a->mask,
+                                 static_cast<double*>(a->ws), head_cos_chunks(a->n_q), stream));
+    }
+    case FB_REUSE_ACTIVE_MSE: {
+      if (a->n_q < 1 || !a->q_prev || !a->q_cur || !a->active) return FB_ERR_INVALID_ARGUMENT;
+      if (a->head_dim < 1 || a->pct < 1 || a->pct > 100) return FB_ERR_INVALID_ARGUMENT;
+      if (a->dtype != FB_BF16 && a->dtype != FB_F32) return FB_ERR_INVALID_ARGUMENT;
+      const size_t need = fb_reuse_decide_workspace(a);
+      if (a->ws_bytes < need || !a->ws) return FB_ERR_WORKSPACE_TOO_SMALL;
+      return dev(launch_active_mse(a->q_prev, a->q_cur, a->dtype, a->n_q, a->n_heads, a->head_dim,
+                                   a->pct, a->mse, a->active, static_cast<double*>(a->ws),
+                                   stream));
+    }
+  }
+  return FB_ERR_INVALID_ARGUMENT;
+}
+
+fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k, int32_t page_size, void* kmin,
+                       void* kmax, hipStream_t stream) {
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  if ((st = check_tensor(k, -1, shape->n_kv_heads, shape->head_dim)) != FB_OK) return st;
+  if (page_size < 1) return FB_ERR_INVALID_ARGUMENT;
+  if (k.n_tok > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
+  const int64_t n_pages = (k.n_tok + page_size - 1) / page_size;
+  if (n_pages > INT32_MAX) return FB_ERR_UNSUPPORTED;
+  return dev(launch_page_meta(k.ptr, k.stride_tok, k.stride_head, k.n_tok, shape->n_kv_heads,
+                              shape->head_dim, page_size, shape->dtype, kmin, kmax, stream));
+}
+
+size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t n_pages) {
+  if (check_shape(shape) != FB_OK || n_q < 1 || n_pages < 0) return 0;
+  return align_up(static_cast<size_t>(n_q) * shape->n_kv_heads * n_pages * sizeof(double));
+}
+
+fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* kmin,
+                         const void* kmax, int64_t n_pages, int32_t k_pages, int32_t* pages,
+                         double* bound, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  if (q.n_tok < 1) return FB_ERR_INVALID_ARGUMENT;
+  if ((st = check_tensor(q, -1, shape->n_q_heads, shape->head_dim)) != FB_OK) return st;
+  if (n_pages < 0 || k_pages < 0 || k_pages > n_pages) return FB_ERR_INVALID_ARGUMENT;
+  if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
+  if (k_pages > 0 && !pages) return FB_ERR_INVALID_ARGUMENT;
+  const int G = shape->n_q_heads / shape->n_kv_heads;
+  const size_t smem = (static_cast<size_t>(q.n_tok) * G * shape->head_dim + 2 * 32 * shape->head_dim) *
+                      sizeof(float);
+  if (smem > 160 * 1024) return FB_ERR_UNSUPPORTED;
+  if (!bound) {
+    const size_t need = fb_page_select_workspace(shape, q.n_tok, n_pages);
+    if (ws_bytes < need || (need > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;
+    bound = static_cast<double*>(ws);
+  }
+  return dev(launch_page_select(q.ptr, q.stride_tok, q.stride_head, kmin, kmax,
+                                static_cast<int>(q.n_tok), shape->n_q_heads, shape->n_kv_heads,
+                                shape->head_dim, n_pages, k_pages, shape->dtype, bound, pages,
+                                stream));
+}
+
+// ---------------------------------------------------------------------------
+// fb_step
+// ---------------------------------------------------------------------------
+size_t fb_step_workspace(const fb_step_state* st) {
+  if (!st || check_shape(&st->shape) != FB_OK || st->n_q < 1) return 0;
+  size_t ws = 0;
+  fb_page_sel sel;
+  memset(&sel, 0, sizeof(sel));
+  const fb_page_sel* psel = nullptr;
+  if (st->mode == FB_STEP_SPARSE) {
+    sel.mode = FB_SEL_SPLIT;
+    sel.page_size = st->page_size > 0 ? st->page_size : 1;
+    sel.k_pages = st->k_pages;
+    psel = &sel;
+  }
+  const size_t p1 = plan_prefix(st->shape, st->n_q, st->k_prefix.n_tok, psel).ws_bytes;
+  ws = p1;
+  if (st->mode == FB_STEP_SPARSE) {
+    sel.mode = FB_SEL_GATHER;
+    const size_t p2 = plan_prefix(st->shape, st->n_q, st->k_prefix.n_tok, &sel).ws_bytes;
+    const int64_t n_pages = (st->k_prefix.n_tok + sel.page_size - 1) / sel.page_size;
+    const size_t p3 = fb_page_select_workspace(&st->shape, st->n_q, n_pages);
+    const size_t p4 = align_up(static_cast<size_t>(st->n_q) * sizeof(double));
+    ws = ws > p2 ? ws : p2;
+    ws = ws > p3 ? ws : p3;
+    ws = ws > p4 ? ws : p4;
+  }
+  if (st->mode == FB_STEP_VIDEO) {
+    const size_t pc = align_up(static_cast<size_t>(head_cos_chunks(st->n_q)) * st->shape.n_q_heads *
+                               3 * sizeof(double));
+    ws = ws > pc ? ws : pc;
+  }
+  return ws;
+}
+
+fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) {
+  if (!st || !a) return FB_ERR_INVALID_ARGUMENT;
+  fb_status rc = check_shape(&st->shape);
+  if (rc != FB_OK) return rc;
+  const fb_attn_shape& s = st->shape;
+  const int n_q = st->n_q, hq = s.n_q_heads, d = s.head_dim;
+  if (n_q < 1 || a->q_blk.n_tok != n_q) return FB_ERR_INVALID_ARGUMENT;
+  if (a->decision < -1 || a->decision > 1) return FB_ERR_INVALID_ARGUMENT;
+  if (!st->a_out || !st->l_out || !st->mask || !a->a_full) return FB_ERR_INVALID_ARGUMENT;
+  if ((rc = check_tensor(st->k_prefix, -1, s.n_kv_heads, d)) != FB_OK) return rc;
+  if ((rc = check_tensor(st->v_prefix, st->k_prefix.n_tok, s.n_kv_heads, d)) != FB_OK) return rc;
+  if (fb_step_workspace(st) > st->ws_bytes) return FB_ERR_WORKSPACE_TOO_SMALL;
+  const bool first = st->step == 0;
+
+  switch (st->mode) {
+    case FB_STEP_TEXT: {
+      if (!a->ids_cur || !st->ids_prev) return FB_ERR_INVALID_ARGUMENT;
+      const int force = first ? 0 : a->decision;
+      rc = dev(launch_count(first ? nullptr : st->ids_prev, a->ids_cur, n_q, st->tau, force, hq,
+                            st->mask, st->m_count, st->ids_prev, stream));
+      if (rc != FB_OK) return rc;
+      if (force != 1) {
+        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, st->mask, nullptr, st->a_out,
+                            st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream);
+        if (rc != FB_OK) return rc;
+      }
+      break;
+    }
+    case FB_STEP_VIDEO: {
+      if (!st->a_probe || !st->l_probe || !st->mask_next || !st->sim) return FB_ERR_INVALID_ARGUMENT;
+      if (first) {
+        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, nullptr, st->a_out,
+                            st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream);
+        if (rc != FB_OK) return rc;
+        rc = dev(launch_fill_u8(st->mask, hq, 0, stream));
+        if (rc != FB_OK) return rc;
+      } else if (a->decision != 1) {
+        const uint8_t* used = a->decision == 0 ? nullptr : st->mask;
+        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, used, nullptr, st->a_probe,
+                            st->l_probe, nullptr, nullptr, st->ws, st->ws_bytes, stream);
+        if (rc != FB_OK) return rc;
+        rc = dev(launch_head_cos(st->a_out, st->a_probe, n_q, hq, d, used, st->gamma, st->sim,
+                                 st->mask_next, static_cast<double*>(st->ws), head_cos_chunks(n_q),
+                                 stream));
+        if (rc != FB_OK) return rc;
+        rc = dev(launch_copy_heads(st->a_probe, st->l_probe, st->a_out, st->l_out, n_q, hq, d, used,
+                                   stream));
+        if (rc != FB_OK) return rc;
+        uint8_t* tmp = st->mask;
+        st->mask = st->mask_next;
+        st->mask_next = tmp;
+      }
+      break;
+    }
+    case FB_STEP_SPARSE: {
+      if (!st->a_res || !st->l_res || !st->pages || !st->kmin || !st->kmax || !st->q_prev ||
+          !st->active)
+        return FB_ERR_INVALID_ARGUMENT;
+      if (st->page_size < 1 || st->pct < 1 || st->pct > 100) return FB_ERR_INVALID_ARGUMENT;
+      const int64_t n_pages = (st->k_prefix.n_tok + st->page_size - 1) / st->page_size;
+      if (st->k_pages < 0 || st->k_pages > n_pages) return FB_ERR_INVALID_ARGUMENT;
+      // the active-set kernel reads contiguous [n_q, Hq, d] queries
+      if (a->q_blk.stride_head != d || a->q_blk.stride_tok != static_cast<int64_t>(hq) * d)
+        return FB_ERR_UNSUPPORTED;
+      fb_page_sel sel;
+      memset(&sel, 0, sizeof(sel));
+      sel.page_size = st->page_size;
+      sel.k_pages = st->k_pages;
+      sel.pages = st->pages;
+      if (first) {
+        if (!st->meta_ready) {
+          rc = fb_page_meta(&s, st->k_prefix, st->page_size, st->kmin, st->kmax, stream);
+          if (rc != FB_OK) return rc;
+          st->meta_ready = 1;
+        }
+        rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, st->k_pages, st->pages,
+                            nullptr, st->ws, st->ws_bytes, stream);
+        if (rc != FB_OK) return rc;
+        sel.mode = FB_SEL_SPLIT;
+        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
+                            st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
+        if (rc != FB_OK) return rc;
+        rc = dev(launch_fill_u8(st->active, n_q, 1, stream));
+        if (rc != FB_OK) return rc;
+      } else if (a->decision != 1) {
+        if (a->decision == 0) {
+          rc = dev(launch_fill_u8(st->active, n_q, 1, stream));
+        } else {
+          rc = dev(launch_active_mse(st->q_prev, a->q_blk.ptr, s.dtype, n_q, hq, d, st->pct,
+                                     st->mse, st->active, static_cast<double*>(st->ws), stream));
+        }
+        if (rc != FB_OK) return rc;
+        sel.mode = FB_SEL_GATHER;
+        sel.active = st->active;
+        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
+                            st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
+        if (rc != FB_OK) return rc;
+      } else {
+        rc = dev(launch_fill_u8(st->active, n_q, 0, stream));
+        if (rc != FB_OK) return rc;
+      }
+      rc = dev(launch_copy_rows(a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head, st->q_prev,
+                                n_q, hq, d, s.dtype, stream));
+      if (rc != FB_OK) return rc;
+      break;
+    }
+    default:
+      return FB_ERR_INVALID_ARGUMENT;
+  }
+  rc = fb_block_attn_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full,
+                           a->l_full, nullptr, nullptr, nullptr, 0, stream);
+  if (rc != FB_OK) return rc;
+  st->step += 1;
+  return FB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// fb_internal.h -- types and launchers shared by the library's own sources
+// (host ABI layer and the gfx950 kernels). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "flashblock.h"
+
+namespace fb {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Where a prefix pass writes its per-row result: either the final outputs
+// (chunk_stride 0, one chunk) or split-K partials (chunk-major).
+struct RowOut {
+  float* a;            // [n_chunks][n_q * Hq][D]  (A normalised)
+  float* l;            // [n_chunks][n_q * Hq]     (natural-log normaliser)
+  int64_t chunk_stride_rows;  // rows between chunks (n_q * Hq), 0 if final
+};
+
+struct PrefixParams {
+  const void* q; int64_t q_st, q_sh;
+  const void* k; const void* v; int64_t kv_st, kv_sh;
+  int64_t n_kv;
+  int n_q, hq, hkv, group;      // group = Hq / Hkv
+  float scale_log2;             // scale * log2(e)
+  const uint8_t* mask;          // [Hq] nullable, 1 = skip
+  int64_t tiles_per_chunk;      // in units of the kernel's tile
+  int n_chunks;
+  RowOut out;
+  // sparse modes
+  int sel_mode;                 // FB_SEL_*
+  int page_size, k_pages;
+  const int32_t* pages;         // [n_q, Hkv, k_pages]
+  const uint8_t* active;        // [n_q] nullable
+  RowOut out_res;               // SPLIT: residual partials
+};
+
+struct ReduceParams {
+  const float* part_a; const float* part_l;   // [n_chunks][rows][D], [n_chunks][rows]
+  const float* part_ra; const float* part_rl; // SPLIT residual partials (nullable)
+  int n_chunks;
+  int64_t rows;                 // n_q * Hq
+  int hq, d;
+  const uint8_t* mask;          // [Hq] nullable
+  const uint8_t* active;        // [n_q] nullable (GATHER)
+  const float* res_a; const float* res_l;     // GATHER: cached residual input
+  float* a_out; float* l_out;   // merged (all partials [+ residual])
+  float* a_res; float* l_res;   // SPLIT: residual-only merge
+};
+
+// ---- launchers (return hipError_t of the launch) -----------------------
+// prefix pass
+int prefix_tile_tokens(int path);               // tokens per tile of a path
+hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipStream_t s);
+hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s);
+hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_prefix_empty(float* a_out, float* l_out, int n_q, int hq, int d,
+                               const uint8_t* mask, hipStream_t s);
+
+// in-block pass + merge
+struct BlockParams {
+  const void* q; int64_t q_st, q_sh;
+  const void* k; const void* v; int64_t k_st, k_sh, v_st, v_sh;
+  int n_q, hq, hkv, group, d;
+  float scale_log2;
+  const float* a_out; const float* l_out;
+  float* a_full; float* l_full; float* a_in; float* l_in;
+};
+hipError_t launch_block_small(const BlockParams& p, fb_dtype dt, hipStream_t s);
+
+// decisions
+hipError_t launch_count(const int32_t* ids_prev, const int32_t* ids_cur, int n_q,
+                        int tau, int force, int hq, uint8_t* mask, int32_t* m_count,
+                        int32_t* ids_store, hipStream_t s);
+hipError_t launch_head_cos(const float* a_cached, const float* a_probe, int n_q, int hq,
+                           int d, const uint8_t* mask_in, double gamma, double* sim,
+                           uint8_t* mask, double* ws, int n_chunks, hipStream_t s);
+int head_cos_chunks(int n_q);
+hipError_t launch_active_mse(const void* q_prev, const void* q_cur, fb_dtype dt, int n_q,
+                             int hq, int d, int pct, double* mse, uint8_t* active,
+                             double* ws, hipStream_t s);
+hipError_t launch_copy_heads(const float* a_src, const float* l_src, float* a_dst,
+                             float* l_dst, int n_q, int hq, int d, const uint8_t* mask,
+                             hipStream_t s);
+
+// pages
+hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t n_kv,
+                            int hkv, int d, int page_size, fb_dtype dt, void* kmin,
+                            void* kmax, hipStream_t s);
+hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const void* kmin,
+                              const void* kmax, int n_q, int hq, int hkv, int d,
+                              int64_t n_pages, int k_pages, fb_dtype dt, double* bound,
+                              int32_t* pages, hipStream_t s);
+
+}  // namespace fb

@@ -1,0 +1,547 @@
+// k1_prefix.hip -- the block-external pass over J_out (the static prefix KV
+// cache): A_out and its log-normaliser L_out = ln Z_out for every block query
+// row, as cached by FlashBlock (technical summary, s2 "core mechanism").
+//
+// The prefix is split over the key axis into chunks (split-K); every chunk
+// yields a normalised partial (A_c, L_c), and the partials are combined by
+// the same log-space composition the method uses for A_full (s2, the A_full
+// equation), in a fixed chunk order, so results are run-to-run identical.
+//
+// Kernels:
+//  * prefix_mfma_kernel   bf16, d = 128, few query rows per KV head (the
+//    decode regime of text block diffusion: rows = B * Hq/Hkv <= 64 per
+//    workgroup row-slab). Grouped-query heads share every K/V tile, which is
+//    read from HBM once per KV head. Scores and P.V run on gfx950 MFMA.
+//  * prefix_generic_kernel  any dtype / d in {64,128} / any row count; VALU.
+//    Also implements the sparse SPLIT and GATHER modes.
+//  * prefix_reduce_kernel   fixed-order merge of the chunk partials.
+#include "fb_internal.h"
+
+#include <math.h>
+
+namespace fb {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Page-selection helpers (sparse modes).
+// ---------------------------------------------------------------------------
+// Is `page` in the ascending list pages[0..k)?
+__device__ __forceinline__ bool page_selected(const int32_t* pages, int k, int32_t page) {
+  int lo = 0, hi = k;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int32_t v = pages[mid];
+    if (v == page) return true;
+    if (v < page) lo = mid + 1; else hi = mid;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// Generic VALU prefix kernel: one wave per (chunk, query row). Lane j scores
+// token base + j; the 64 weights are broadcast through LDS for the P.V sum.
+// Dense and SPLIT chunk the token axis; GATHER chunks the row's list of
+// selected pages (k_pages * page_size virtual tokens).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void prefix_generic_kernel(PrefixParams p) {
+  constexpr int NPL = D / 64;                 // dims per lane
+  const int chunk = blockIdx.x;
+  const int64_t row = blockIdx.y;             // t * Hq + h
+  const int t = static_cast<int>(row / p.hq);
+  const int h = static_cast<int>(row % p.hq);
+  if (p.mask && p.mask[h]) return;
+  const bool gather = p.sel_mode == FB_SEL_GATHER;
+  const bool split = p.sel_mode == FB_SEL_SPLIT;
+  if (gather && p.active && !p.active[t]) return;
+  const int g = h / p.group;
+  const int lane = threadIdx.x;
+
+  __shared__ float qs[D];
+  __shared__ float ps[64];
+  const T* qrow = static_cast<const T*>(p.q) + t * p.q_st + static_cast<int64_t>(h) * p.q_sh;
+  for (int c = lane; c < D; c += 64) qs[c] = to_f32<T>(qrow[c]);
+  __syncthreads();
+
+  const T* kbase = static_cast<const T*>(p.k) + static_cast<int64_t>(g) * p.kv_sh;
+  const T* vbase = static_cast<const T*>(p.v) + static_cast<int64_t>(g) * p.kv_sh;
+  const int32_t* rpages = (split || gather)
+      ? p.pages + (static_cast<int64_t>(t) * p.hkv + g) * p.k_pages : nullptr;
+
+  const int64_t n_virt = gather ? static_cast<int64_t>(p.k_pages) * p.page_size : p.n_kv;
+  const int64_t per = p.tiles_per_chunk * 64;
+  const int64_t lo = static_cast<int64_t>(chunk) * per;
+  const int64_t hi = lo + per < n_virt ? lo + per : n_virt;
+
+  auto token_of = [&](int64_t j) -> int64_t {   // virtual -> prefix token, -1 if none
+    if (!gather) return j;
+    const int64_t tok = static_cast<int64_t>(rpages[j / p.page_size]) * p.page_size + j % p.page_size;
+    return tok < p.n_kv ? tok : -1;
+  };
+
+  const int nsets = split ? 2 : 1;
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  float o[2][NPL];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) o[s][i] = 0.f;
+
+  for (int64_t base = lo; base < hi; base += 64) {
+    const int64_t j = base + lane;
+    int64_t tok = j < hi ? token_of(j) : -1;
+    float sc = kNegInf;
+    int set = 0;
+    if (tok >= 0) {
+      const T* kr = kbase + tok * p.kv_st;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) acc += qs[c] * to_f32<T>(kr[c]);
+      sc = acc * p.scale_log2;
+      if (split) set = page_selected(rpages, p.k_pages, static_cast<int32_t>(tok / p.page_size)) ? 0 : 1;
+    }
+    for (int s = 0; s < nsets; ++s) {
+      const float x = (set == s) ? sc : kNegInf;
+      const float mx = wave_max(x);
+      const float mnew = fmaxf(m[s], mx);
+      if (mnew == kNegInf) continue;             // wave-uniform
+      const float alpha = fast_exp2(m[s] - mnew);
+      const float pr = fast_exp2(x - mnew);
+      l[s] = l[s] * alpha + wave_sum(pr);
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) o[s][i] *= alpha;
+      m[s] = mnew;
+      ps[lane] = pr;
+      __syncthreads();
+      const int nb = static_cast<int>(hi - base < 64 ? hi - base : 64);
+      for (int jj = 0; jj < nb; ++jj) {
+        const float pj = ps[jj];
+        if (pj == 0.f) continue;                 // wave-uniform
+        const int64_t tj = token_of(base + jj);
+        const T* vr = vbase + tj * p.kv_st;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) o[s][i] += pj * to_f32<T>(vr[lane + 64 * i]);
+      }
+      __syncthreads();
+    }
+  }
+
+  for (int s = 0; s < nsets; ++s) {
+    const RowOut& out = s == 0 ? p.out : p.out_res;
+    const int64_t orow = static_cast<int64_t>(chunk) * out.chunk_stride_rows + row;
+    const bool any = l[s] > 0.f;
+    const float inv = any ? 1.f / l[s] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) out.a[orow * D + lane + 64 * i] = o[s][i] * inv;
+    if (lane == 0) out.l[orow] = any ? (m[s] + __log2f(l[s])) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA prefix kernel (bf16, d = 128).
+//
+// Workgroup = 4 waves = (chunk of the prefix, KV head g, row slab of 64 rows).
+// Rows are the (query token, query head) pairs of the group: r = t*G + j.
+// Each wave streams its own 32-token tiles of the chunk (tiles w, w+4, ...),
+// keeps its own online-softmax state, and the four states are merged through
+// LDS at the end. Per tile:
+//   global -> VGPR (coalesced 16 B/lane: 4 token rows x 256 B per load)
+//   VGPR -> wave-private LDS, XOR-swizzled per 16-byte piece
+//   S^T[32 tok x 32 rows] = K . Q^T  (v_mfma_f32_32x32x16_bf16, 8 k-steps)
+//       -> each lane owns one row and 16 of its scores: the row max needs
+//          one exchange with the other lane half, the row sum none.
+//   O^T[128 dims x 32 rows] += V^T . P^T: P^T is the score accumulator
+//       itself (as bf16), V^T comes from LDS by ds_read_b64_tr_b16.
+// The next tile's global loads are in flight while a tile is computed.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 4;
+constexpr int kTile = 32;
+constexpr int kD = 128;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read (gfx950): within each 16-lane group, "row" s is the
+// concatenation of the 4-element loads of lanes 4s..4s+3, and lane j receives
+// element j of rows 0..3. The argument points into __shared__ memory.
+__device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
+  auto p = (const __attribute__((address_space(3))) char*)(lds_generic);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+template <int NRB>
+__global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
+  constexpr int RP = 32 * NRB;                     // padded rows per slab
+  constexpr int kStageBytes = kWaves * 16384;      // per wave: K 8 KB + V 8 KB
+  constexpr int kMergeStride = kD + 1;             // floats per merge row
+  constexpr int kMergeBytes = kWaves * RP * kMergeStride * 4;
+  constexpr int kLdsBytes = kMergeBytes > kStageBytes ? kMergeBytes : kStageBytes;
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ float ml_s[kWaves][RP][2];
+
+  const int chunk = blockIdx.x;
+  const int g = blockIdx.y;
+  const int slab = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int hl = lane >> 5, r32 = lane & 31;
+  const int G = p.group;
+  const int R = p.n_q * G;
+  const int row0 = slab * 64;
+
+  if (p.mask) {                                    // whole group reused?
+    bool all = true;
+    for (int j = 0; j < G; ++j) all = all && p.mask[g * G + j] != 0;
+    if (all) return;
+  }
+
+  // Q^T operands: lane holds row (row0 + 32 rb + r32), dims 16 kk + 8 hl .. +8.
+  bf16x8 qop[NRB][8];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = row0 + 32 * rb + r32;
+    const bool ok = r < R;
+    const int t = ok ? r / G : 0, jh = ok ? r % G : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(t) * p.q_st +
+                         static_cast<int64_t>(g * G + jh) * p.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if (ok) {
+        qop[rb][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl);
+      } else {
+        qop[rb][kk] = bf16x8{};
+      }
+    }
+  }
+
+  const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
+  const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
+  const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
+
+  char* kl = lds + w * 16384;
+  char* vl = kl + 8192;
+  const char* kg = static_cast<const char*>(p.k) + static_cast<int64_t>(g) * p.kv_sh * 2;
+  const char* vg = static_cast<const char*>(p.v) + static_cast<int64_t>(g) * p.kv_sh * 2;
+  const int64_t kvst_b = p.kv_st * 2;
+  const int lrow = lane >> 4, lpiece = lane & 15;
+
+  f32x16 o[NRB][4];
+  float m_run[NRB], l_run[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[rb][db] = f32x16{};
+  }
+
+  uint4 rk[8], rv[8];
+  auto load_tile = [&](int64_t tile) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t tok = tile * kTile + 4 * i + lrow;
+      if (tok < p.n_kv) {
+        rk[i] = *reinterpret_cast<const uint4*>(kg + tok * kvst_b + lpiece * 16);
+        rv[i] = *reinterpret_cast<const uint4*>(vg + tok * kvst_b + lpiece * 16);
+      } else {
+        rk[i] = make_uint4(0, 0, 0, 0);
+        rv[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  int64_t tile = t_begin + w;
+  if (tile < t_end) load_tile(tile);
+  for (; tile < t_end; tile += kWaves) {
+    // stage the tile (swizzle: K piece p of row r at p ^ (r & 15);
+    //                          V piece p of row r at p ^ 4 (r & 3))
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + lrow;
+      *reinterpret_cast<uint4*>(kl + r * 256 + ((lpiece ^ (r & 15)) << 4)) = rk[i];
+      *reinterpret_cast<uint4*>(vl + r * 256 + ((lpiece ^ ((r & 3) << 2)) << 4)) = rv[i];
+    }
+    asm volatile("" ::: "memory");
+    if (tile + kWaves < t_end) load_tile(tile + kWaves);
+
+    // S^T = K . Q^T
+    f32x16 s[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + r32 * 256 + (((2 * kk + hl) ^ (r32 & 15)) << 4));
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) s[rb] = mfma32(ka, qop[rb][kk], s[rb]);
+    }
+
+    // online softmax, per row (= per lane pair l, l^32). The weights enter
+    // the P.V product as bf16 hi + lo parts (two MFMAs), so the product
+    // carries ~2^-17 relative error instead of bf16's 2^-9; the row sum l is
+    // accumulated from the fp32 weights.
+    const int64_t valid = p.n_kv - tile * kTile;   // >= 1
+    bf16x8 pbh[NRB][2], pbl[NRB][2];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float x[16];
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = s[rb][i] * p.scale_log2;
+        if (valid < kTile) {
+          const int tk = 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (tk >= valid) x[i] = kNegInf;
+        }
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m_run[rb], mx);
+      const float muse = mnew == kNegInf ? 0.f : mnew;
+      const float alpha = fast_exp2(m_run[rb] - muse);
+      m_run[rb] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int hj = 0; hj < 2; ++hj) {
+        f32x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pf[e] = fast_exp2(x[8 * hj + e] - muse);
+          psum += pf[e];
+        }
+        const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
+        const f32x8 rest = pf - __builtin_convertvector(hi, f32x8);
+        pbh[rb][hj] = hi;
+        pbl[rb][hj] = __builtin_convertvector(rest, bf16x8);
+      }
+      l_run[rb] = l_run[rb] * alpha + psum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
+      }
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x4 vh[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int grp = lane >> 4;
+          const int tr = 16 * j + 8 * u + 4 * (grp >> 1) + ((lane & 15) >> 2);
+          const int q4 = lane & 3;
+          const int piece = 4 * db + 2 * (grp & 1) + (q4 >> 1);
+          vh[u] = ds_read_tr(vl + tr * 256 + ((piece ^ ((tr & 3) << 2)) << 4) + ((q4 & 1) << 3));
+        }
+        // whole-vector concatenation (element-wise inserts of the transposed
+        // halves were mis-lowered by the compiler)
+        const bf16x8 va = __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          o[rb][db] = mfma32(va, pbh[rb][j], o[rb][db]);
+          o[rb][db] = mfma32(va, pbl[rb][j], o[rb][db]);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- merge the four waves' states through LDS, write the chunk partial --
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) l_run[rb] += __shfl_xor(l_run[rb], 32, 64);
+  __syncthreads();                                  // staging LDS no longer read
+  if (hl == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      ml_s[w][32 * rb + r32][0] = m_run[rb];
+      ml_s[w][32 * rb + r32][1] = l_run[rb];
+    }
+  }
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int r = 32 * rb + r32;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml_s[ww][r][0]);
+    float tot = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = ml_s[ww][r][0];
+      if (mw != kNegInf) tot += ml_s[ww][r][1] * fast_exp2(mw - M);
+    }
+    const float f = (m_run[rb] == kNegInf || tot == 0.f) ? 0.f : fast_exp2(m_run[rb] - M) / tot;
+    float* dst = mg + (w * RP + r) * kMergeStride;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[32 * db + 8 * (i >> 2) + 4 * hl + (i & 3)] = o[rb][db][i] * f;
+  }
+  __syncthreads();
+
+  const int rows_here = R - row0 < RP ? R - row0 : RP;
+  for (int e = tid; e < rows_here * kD; e += 256) {
+    const int r = e / kD, c = e % kD;
+    const int rr = row0 + r;
+    const int t = rr / G, jh = rr % G, h = g * G + jh;
+    if (p.mask && p.mask[h]) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) sum += mg[(ww * RP + r) * kMergeStride + c];
+    const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows +
+                         static_cast<int64_t>(t) * p.hq + h;
+    p.out.a[orow * kD + c] = sum;
+  }
+  for (int r = tid; r < rows_here; r += 256) {
+    const int rr = row0 + r;
+    const int t = rr / G, jh = rr % G, h = g * G + jh;
+    if (p.mask && p.mask[h]) continue;
+    float M = kNegInf;
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml_s[ww][r][0]);
+    float tot = 0.f;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = ml_s[ww][r][0];
+      if (mw != kNegInf) tot += ml_s[ww][r][1] * fast_exp2(mw - M);
+    }
+    const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows +
+                         static_cast<int64_t>(t) * p.hq + h;
+    p.out.l[orow] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduce: merge the chunk partials of every (query, head) row in chunk
+// order, with the A_full composition rule (weights e^{L_c - max L}).
+// SPLIT: a_out merges selected + residual partials, a_res the residual ones.
+// GATHER: a_out merges the selected partials with the cached residual input.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void prefix_reduce_kernel(ReduceParams p) {
+  const int64_t row = blockIdx.x;
+  const int h = static_cast<int>(row % p.hq);
+  const int t = static_cast<int>(row / p.hq);
+  if (p.mask && p.mask[h]) return;
+  if (p.active && !p.active[t]) return;
+  const int c = threadIdx.x;
+  const bool has_c = c < p.d;
+
+  float M = kNegInf, Mr = kNegInf;
+  for (int ch = 0; ch < p.n_chunks; ++ch) M = fmaxf(M, p.part_l[ch * p.rows + row]);
+  if (p.part_rl)
+    for (int ch = 0; ch < p.n_chunks; ++ch) Mr = fmaxf(Mr, p.part_rl[ch * p.rows + row]);
+  if (p.res_l) Mr = fmaxf(Mr, p.res_l[row]);
+  const float Mall = fmaxf(M, Mr);
+
+  float S = 0.f, acc = 0.f, Sr = 0.f, accr = 0.f;
+  if (Mall != kNegInf) {
+    for (int ch = 0; ch < p.n_chunks; ++ch) {
+      const float L = p.part_l[ch * p.rows + row];
+      if (L == kNegInf) continue;
+      const float wgt = expf(L - Mall);
+      S += wgt;
+      if (has_c) acc += wgt * p.part_a[(ch * p.rows + row) * p.d + c];
+    }
+    if (p.part_rl) {
+      for (int ch = 0; ch < p.n_chunks; ++ch) {
+        const float L = p.part_rl[ch * p.rows + row];
+        if (L == kNegInf) continue;
+        const float wgt = expf(L - Mr);
+        Sr += wgt;
+        if (has_c) accr += wgt * p.part_ra[(ch * p.rows + row) * p.d + c];
+      }
+    }
+    if (p.res_l) {
+      const float L = p.res_l[row];
+      if (L != kNegInf) {
+        const float wgt = expf(L - Mr);
+        Sr += wgt;
+        if (has_c) accr += wgt * p.res_a[row * p.d + c];
+      }
+    }
+  }
+  // residual-only pair, then fold it into the full pair (same composition)
+  if (p.a_res) {
+    if (has_c) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
+    if (c == 0) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+  }
+  if (Mr != kNegInf) {
+    const float wr = expf(Mr - Mall);
+    S += Sr * wr;
+    acc += accr * wr;
+  }
+  if (has_c) p.a_out[row * p.d + c] = Mall != kNegInf ? acc / S : 0.f;
+  if (c == 0) p.l_out[row] = Mall != kNegInf ? Mall + logf(S) : kNegInf;
+}
+
+__global__ __launch_bounds__(128) void prefix_empty_kernel(float* a, float* l, int hq, int d,
+                                                           const uint8_t* mask) {
+  const int64_t row = blockIdx.x;
+  const int h = static_cast<int>(row % hq);
+  if (mask && mask[h]) return;
+  if (threadIdx.x < d) a[row * d + threadIdx.x] = 0.f;
+  if (threadIdx.x == 0) l[row] = kNegInf;
+}
+
+}  // namespace
+
+int prefix_tile_tokens(int path) { return path == 1 ? kTile : 64; }
+
+hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipStream_t s) {
+  dim3 grid(p.n_chunks, static_cast<unsigned>(static_cast<int64_t>(p.n_q) * p.hq));
+  if (dt == FB_BF16) {
+    if (d == 128) hipLaunchKernelGGL((prefix_generic_kernel<uint16_t, 128>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((prefix_generic_kernel<uint16_t, 64>), grid, dim3(64), 0, s, p);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((prefix_generic_kernel<float, 128>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((prefix_generic_kernel<float, 64>), grid, dim3(64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s) {
+  const int rows = p.n_q * p.group;
+  dim3 grid(p.n_chunks, p.hkv, (rows + 63) / 64);
+  if (row_blocks == 1) hipLaunchKernelGGL((prefix_mfma_kernel<1>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((prefix_mfma_kernel<2>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(prefix_reduce_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(128), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_empty(float* a_out, float* l_out, int n_q, int hq, int d,
+                               const uint8_t* mask, hipStream_t s) {
+  hipLaunchKernelGGL(prefix_empty_kernel, dim3(n_q * hq), dim3(128), 0, s, a_out, l_out, hq, d, mask);
+  return hipGetLastError();
+}
+
+}  // namespace fb

@@ -1,0 +1,266 @@
+// k3_decide.hip -- the reuse controller, on the device, producing integer
+// masks that the prefix pass consumes without a host round trip.
+//
+//  * count     (FlashBlock technical summary, s2 threshold reuse): M = number
+//              of block positions whose token id changed; reuse iff M < tau.
+//  * head_cos  (same section, per-head selection): cosine of a head's fresh
+//              block-external output against its cached one, float64, fixed
+//              reduction order; reuse iff sim > gamma.
+//  * active_mse (LoSA s2, token classification): per-token mean squared
+//              query change in float64 with the operations in a fixed order
+//              and no fused multiply-add; active iff above the nearest-rank
+//              percentile cutoff.
+//  * copy_heads: the probe replaces the cache for recomputed heads.
+#include "fb_internal.h"
+
+#include <math.h>
+
+namespace fb {
+namespace {
+
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* prev, const int32_t* cur, int n,
+                                                    int tau, int force, int hq, uint8_t* mask,
+                                                    int32_t* m_count, int32_t* store) {
+  __shared__ int total;
+  const int tid = threadIdx.x;
+  if (tid == 0) total = 0;
+  __syncthreads();
+  int c = 0;
+  if (prev != nullptr)
+    for (int i = tid; i < n; i += blockDim.x) c += prev[i] != cur[i] ? 1 : 0;
+  atomicAdd(&total, c);
+  __syncthreads();                                 // every read of prev is done
+  // prev == NULL: first step of a block, every token is new to the cache.
+  // force: -1 decide, 0 recompute, 1 reuse.
+  const int M = prev != nullptr ? total : n;
+  const bool reuse = force == 1 ? true : (force == 0 ? false : (M < tau));
+  for (int h = tid; h < hq; h += blockDim.x) mask[h] = reuse ? 1 : 0;
+  if (tid == 0 && m_count) *m_count = M;
+  if (store)
+    for (int i = tid; i < n; i += blockDim.x) store[i] = cur[i];
+}
+
+// Partial sums of <a, b>, |a|^2, |b|^2 for head h over a chunk of rows.
+// Every product of two floats is exact in float64; the chunk sum uses a
+// fixed tree, the chunk partials are summed in order by the finaliser.
+__global__ __launch_bounds__(256) void head_cos_partial_kernel(const float* a_cached,
+                                                               const float* a_probe, int n_q,
+                                                               int hq, int d,
+                                                               const uint8_t* mask_in,
+                                                               int rows_per_chunk, double* ws) {
+  const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (mask_in && mask_in[h]) return;
+  const int lo = chunk * rows_per_chunk;
+  const int hi = lo + rows_per_chunk < n_q ? lo + rows_per_chunk : n_q;
+  double dot = 0.0, nx = 0.0, ny = 0.0;
+  const int64_t n_el = static_cast<int64_t>(hi - lo) * d;
+  for (int64_t e = tid; e < n_el; e += 256) {
+    const int64_t t = lo + e / d, c = e % d;
+    const int64_t idx = (t * hq + h) * d + c;
+    const double x = a_probe[idx], y = a_cached[idx];
+    dot += x * y;
+    nx += x * x;
+    ny += y * y;
+  }
+  __shared__ double red[3][256];
+  red[0][tid] = dot;
+  red[1][tid] = nx;
+  red[2][tid] = ny;
+  __syncthreads();
+  for (int s = 128; s >= 1; s >>= 1) {
+    if (tid < s) {
+      red[0][tid] += red[0][tid + s];
+      red[1][tid] += red[1][tid + s];
+      red[2][tid] += red[2][tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double* o = ws + (static_cast<int64_t>(chunk) * hq + h) * 3;
+    o[0] = red[0][0];
+    o[1] = red[1][0];
+    o[2] = red[2][0];
+  }
+}
+
+__global__ void head_cos_final_kernel(int hq, int n_chunks, const uint8_t* mask_in, double gamma,
+                                      const double* ws, double* sim, uint8_t* mask) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= hq) return;
+  if (mask_in && mask_in[h]) {
+    mask[h] = 1;
+    return;
+  }
+  double dot = 0.0, nx = 0.0, ny = 0.0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const double* o = ws + (static_cast<int64_t>(c) * hq + h) * 3;
+    dot += o[0];
+    nx += o[1];
+    ny += o[2];
+  }
+  const double ax = sqrt(nx), ay = sqrt(ny);
+  double s;
+  if (ax * ay == 0.0) {
+    s = (ax == 0.0 && ay == 0.0) ? 1.0 : 0.0;
+  } else {
+    s = dot / (ax * ay);
+    s = s > 1.0 ? 1.0 : (s < -1.0 ? -1.0 : s);
+  }
+  sim[h] = s;
+  mask[h] = s > gamma ? 1 : 0;
+}
+
+template <typename T> __device__ __forceinline__ double ldd(const T* p);
+template <> __device__ __forceinline__ double ldd<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ double ldd<uint16_t>(const uint16_t* p) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(*p) << 16));
+}
+
+// One thread per block token: the float64 sum runs sequentially over
+// (head, dim); contraction into fused multiply-add is disabled so the
+// rounding sequence is exactly diff, square, add.
+template <typename T>
+__global__ __launch_bounds__(256) void active_mse_kernel(const T* q_prev, const T* q_cur, int n_q,
+                                                         int hq, int d, int pct, double* mse_out,
+                                                         uint8_t* active, double* ws) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x;
+  const int64_t per = static_cast<int64_t>(hq) * d;
+  for (int t = tid; t < n_q; t += blockDim.x) {
+    const T* a = q_prev + t * per;
+    const T* b = q_cur + t * per;
+    double acc = 0.0;
+    for (int64_t e = 0; e < per; ++e) {
+      const double diff = ldd<T>(b + e) - ldd<T>(a + e);
+      const double sq = diff * diff;
+      acc = acc + sq;
+    }
+    const double v = acc / static_cast<double>(per);
+    ws[t] = v;
+    if (mse_out) mse_out[t] = v;
+  }
+  __syncthreads();
+  // nearest-rank cutoff: the rank-th smallest, rank = ceil(pct * n / 100)
+  __shared__ double cutoff;
+  int rank = (pct * n_q + 99) / 100;
+  if (rank < 1) rank = 1;
+  for (int t = tid; t < n_q; t += blockDim.x) {
+    const double v = ws[t];
+    int less = 0, leq = 0;
+    for (int u = 0; u < n_q; ++u) {
+      const double x = ws[u];
+      less += x < v ? 1 : 0;
+      leq += x <= v ? 1 : 0;
+    }
+    if (less < rank && rank <= leq) cutoff = v;    // every writer writes the same value
+  }
+  __syncthreads();
+  const double c = cutoff;
+  for (int t = tid; t < n_q; t += blockDim.x) active[t] = ws[t] > c ? 1 : 0;
+}
+
+__global__ __launch_bounds__(256) void copy_heads_kernel(const float* a_src, const float* l_src,
+                                                         float* a_dst, float* l_dst, int n_q,
+                                                         int hq, int d, const uint8_t* mask) {
+  const int h = blockIdx.y;
+  if (mask && mask[h]) return;
+  const int64_t n_el = static_cast<int64_t>(n_q) * d;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n_el;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = e / d, c = e % d;
+    const int64_t idx = (t * hq + h) * d + c;
+    a_dst[idx] = a_src[idx];
+    if (c == 0) l_dst[t * hq + h] = l_src[t * hq + h];
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u8_kernel(uint8_t* p, int n, uint8_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const T* src, int64_t st, int64_t sh, T* dst,
+                                                        int n_q, int hq, int d) {
+  const int64_t n_el = static_cast<int64_t>(n_q) * hq * d;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n_el;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = e / (static_cast<int64_t>(hq) * d), h = (e / d) % hq, c = e % d;
+    dst[e] = src[t * st + h * sh + c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fill_u8(uint8_t* p, int n, uint8_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u8_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* src, int64_t st, int64_t sh, void* dst, int n_q, int hq,
+                            int d, fb_dtype dt, hipStream_t s) {
+  const int64_t n_el = static_cast<int64_t>(n_q) * hq * d;
+  int nb = static_cast<int>((n_el + 255) / 256);
+  if (nb > 2048) nb = 2048;
+  if (dt == FB_BF16)
+    hipLaunchKernelGGL(copy_rows_kernel<uint16_t>, dim3(nb), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), st, sh, static_cast<uint16_t*>(dst), n_q,
+                       hq, d);
+  else
+    hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(nb), dim3(256), 0, s,
+                       static_cast<const float*>(src), st, sh, static_cast<float*>(dst), n_q, hq, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_count(const int32_t* ids_prev, const int32_t* ids_cur, int n_q, int tau,
+                        int force, int hq, uint8_t* mask, int32_t* m_count, int32_t* ids_store,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(count_kernel, dim3(1), dim3(256), 0, s, ids_prev, ids_cur, n_q, tau, force, hq,
+                     mask, m_count, ids_store);
+  return hipGetLastError();
+}
+
+int head_cos_chunks(int n_q) {
+  const int rows_per_chunk = 64;
+  return (n_q + rows_per_chunk - 1) / rows_per_chunk;
+}
+
+hipError_t launch_head_cos(const float* a_cached, const float* a_probe, int n_q, int hq, int d,
+                           const uint8_t* mask_in, double gamma, double* sim, uint8_t* mask,
+                           double* ws, int n_chunks, hipStream_t s) {
+  const int rows_per_chunk = 64;
+  hipLaunchKernelGGL(head_cos_partial_kernel, dim3(n_chunks, hq), dim3(256), 0, s, a_cached,
+                     a_probe, n_q, hq, d, mask_in, rows_per_chunk, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_cos_final_kernel, dim3((hq + 63) / 64), dim3(64), 0, s, hq, n_chunks,
+                     mask_in, gamma, ws, sim, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_active_mse(const void* q_prev, const void* q_cur, fb_dtype dt, int n_q, int hq,
+                             int d, int pct, double* mse, uint8_t* active, double* ws,
+                             hipStream_t s) {
+  if (dt == FB_BF16)
+    hipLaunchKernelGGL(active_mse_kernel<uint16_t>, dim3(1), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q_prev), static_cast<const uint16_t*>(q_cur),
+                       n_q, hq, d, pct, mse, active, ws);
+  else
+    hipLaunchKernelGGL(active_mse_kernel<float>, dim3(1), dim3(256), 0, s,
+                       static_cast<const float*>(q_prev), static_cast<const float*>(q_cur), n_q,
+                       hq, d, pct, mse, active, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_heads(const float* a_src, const float* l_src, float* a_dst, float* l_dst,
+                             int n_q, int hq, int d, const uint8_t* mask, hipStream_t s) {
+  const int64_t n_el = static_cast<int64_t>(n_q) * d;
+  int nb = static_cast<int>((n_el + 255) / 256);
+  if (nb > 1024) nb = 1024;
+  hipLaunchKernelGGL(copy_heads_kernel, dim3(nb, hq), dim3(256), 0, s, a_src, l_src, a_dst, l_dst,
+                     n_q, hq, d, mask);
+  return hipGetLastError();
+}
+
+}  // namespace fb

@@ -1,0 +1,225 @@
+// k4_pages.hip -- QUEST-style page selection for the sparse subsystem.
+//
+// LoSA (Locality Aware Sparse Attention for Block-Wise Diffusion Language
+// Models), s2: active block tokens attend only to the prefix pages a QUEST
+// selector picks; FlashBlock technical summary, s2 sparse compatibility: the
+// pages left out form the residual whose contribution is cached.
+//
+// The pages name QUEST without restating it; the selector here is the page
+// bound: per (KV head, page, dim) the min and max of the page's keys, and for
+// a query row the upper bound sum_d max(q_d kmin_d, q_d kmax_d) of q.k over
+// the page, maximised over the query heads of the KV group. Products of two
+// bf16 (or two fp32) values are exact in float64, and the sum runs
+// sequentially over d with contraction disabled, so the bound's bits do not
+// depend on the device. Top-k is exact: the k-th largest key is found by
+// bisection on an order-preserving 64-bit image of the bound, ties go to the
+// lower page id, and the chosen pages are emitted in ascending order.
+#include "fb_internal.h"
+
+#include <math.h>
+
+namespace fb {
+namespace {
+
+template <typename T> __device__ __forceinline__ float ldf(const T* p);
+template <> __device__ __forceinline__ float ldf<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+template <typename T> __device__ __forceinline__ T stf(float x);
+template <> __device__ __forceinline__ float stf<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t stf<uint16_t>(float x) {
+  return static_cast<uint16_t>(__float_as_uint(x) >> 16);   // exact: x is a bf16 value
+}
+
+// kmin/kmax[g][p][c] over the tokens of page p (the last page may be short).
+template <typename T>
+__global__ __launch_bounds__(128) void page_meta_kernel(const T* k, int64_t kv_st, int64_t kv_sh,
+                                                        int64_t n_kv, int d, int page_size,
+                                                        int64_t n_pages, T* kmin, T* kmax) {
+  const int64_t p = blockIdx.x;
+  const int g = blockIdx.y;
+  const int c = threadIdx.x;
+  if (c >= d) return;
+  const int64_t lo = p * page_size;
+  const int64_t hi = lo + page_size < n_kv ? lo + page_size : n_kv;
+  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+  for (int64_t t = lo; t < hi; ++t) {
+    const float x = ldf<T>(k + t * kv_st + g * kv_sh + c);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  const int64_t o = (static_cast<int64_t>(g) * n_pages + p) * d + c;
+  kmin[o] = stf<T>(mn);
+  kmax[o] = stf<T>(mx);
+}
+
+// bound[t][g][p]: one thread per (page, token). The group's query rows and the
+// page block's metadata sit in LDS as float (exact copies of the inputs).
+constexpr int kPagesPerBlock = 32;
+
+template <typename T>
+__global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_st, int64_t q_sh,
+                                                         const T* kmin, const T* kmax, int n_q,
+                                                         int hq, int hkv, int d, int64_t n_pages,
+                                                         double* bound) {
+#pragma clang fp contract(off)
+  extern __shared__ float sm[];
+  const int G = hq / hkv;
+  const int g = blockIdx.y;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPagesPerBlock;
+  const int np = n_pages - p0 < kPagesPerBlock ? static_cast<int>(n_pages - p0) : kPagesPerBlock;
+  float* qs = sm;                                    // [n_q][G][d]
+  float* mn = qs + n_q * G * d;                      // [kPagesPerBlock][d]
+  float* mx = mn + kPagesPerBlock * d;
+  for (int e = threadIdx.x; e < n_q * G * d; e += blockDim.x) {
+    const int t = e / (G * d), j = (e / d) % G, c = e % d;
+    qs[e] = ldf<T>(q + t * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
+  }
+  for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
+    const int64_t o = (static_cast<int64_t>(g) * n_pages + p0) * d + e;
+    mn[e] = ldf<T>(kmin + o);
+    mx[e] = ldf<T>(kmax + o);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < np * n_q; e += blockDim.x) {
+    const int pi = e % np, t = e / np;
+    double best = -__builtin_huge_val();
+    for (int j = 0; j < G; ++j) {
+      const float* qr = qs + (t * G + j) * d;
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) {
+        const double qv = qr[c];
+        const double lo = qv * static_cast<double>(mn[pi * d + c]);
+        const double hi = qv * static_cast<double>(mx[pi * d + c]);
+        acc = acc + (lo > hi ? lo : hi);
+      }
+      best = acc > best ? acc : best;
+    }
+    bound[(static_cast<int64_t>(t) * hkv + g) * n_pages + p0 + pi] = best;
+  }
+}
+
+// Order-preserving image of a double as an unsigned 64-bit key.
+__device__ __forceinline__ uint64_t okey(double x) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ int block_sum(int v, int* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s >= 1; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const int r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per (token, KV head): exact top-k of bound[t][g][:].
+__global__ __launch_bounds__(256) void page_topk_kernel(const double* bound, int hkv,
+                                                        int64_t n_pages, int k, int32_t* pages) {
+  __shared__ int red[256];
+  __shared__ int scan[256];
+  const int tid = threadIdx.x;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * hkv + blockIdx.y;
+  const double* b = bound + row * n_pages;
+  int32_t* out = pages + row * k;
+  if (k <= 0) return;
+  // T = the k-th largest key: the largest T with #{key >= T} >= k.
+  uint64_t T = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = T | (1ull << bit);
+    int c = 0;
+    for (int64_t p = tid; p < n_pages; p += 256) c += okey(b[p]) >= cand ? 1 : 0;
+    if (block_sum(c, red) >= k) T = cand;
+  }
+  int gt = 0;
+  for (int64_t p = tid; p < n_pages; p += 256) gt += okey(b[p]) > T ? 1 : 0;
+  const int n_gt = block_sum(gt, red);
+  const int need_eq = k - n_gt;                      // >= 1 ties at T, lowest ids first
+  // emit in ascending page order: tiles of 256 pages, block-wide prefix sums
+  int written = 0, eq_taken = 0;
+  for (int64_t base = 0; base < n_pages; base += 256) {
+    const int64_t p = base + tid;
+    int is_gt = 0, is_eq = 0;
+    if (p < n_pages) {
+      const uint64_t kk = okey(b[p]);
+      is_gt = kk > T;
+      is_eq = kk == T;
+    }
+    // inclusive scan of is_eq to rank the ties in this tile
+    scan[tid] = is_eq;
+    __syncthreads();
+    for (int s = 1; s < 256; s <<= 1) {
+      const int v = tid >= s ? scan[tid - s] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int eq_rank = eq_taken + scan[tid] - is_eq;    // ties before me
+    const int tile_eq = scan[255];
+    __syncthreads();
+    const int sel = is_gt || (is_eq && eq_rank < need_eq);
+    scan[tid] = sel;
+    __syncthreads();
+    for (int s = 1; s < 256; s <<= 1) {
+      const int v = tid >= s ? scan[tid - s] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    if (sel) out[written + scan[tid] - 1] = static_cast<int32_t>(p);
+    written += scan[255];
+    eq_taken += tile_eq;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t n_kv, int hkv,
+                            int d, int page_size, fb_dtype dt, void* kmin, void* kmax,
+                            hipStream_t s) {
+  const int64_t n_pages = (n_kv + page_size - 1) / page_size;
+  if (n_pages == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(n_pages), hkv);
+  if (dt == FB_BF16)
+    hipLaunchKernelGGL(page_meta_kernel<uint16_t>, grid, dim3(128), 0, s,
+                       static_cast<const uint16_t*>(k), kv_st, kv_sh, n_kv, d, page_size, n_pages,
+                       static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax));
+  else
+    hipLaunchKernelGGL(page_meta_kernel<float>, grid, dim3(128), 0, s,
+                       static_cast<const float*>(k), kv_st, kv_sh, n_kv, d, page_size, n_pages,
+                       static_cast<float*>(kmin), static_cast<float*>(kmax));
+  return hipGetLastError();
+}
+
+hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const void* kmin,
+                              const void* kmax, int n_q, int hq, int hkv, int d, int64_t n_pages,
+                              int k_pages, fb_dtype dt, double* bound, int32_t* pages,
+                              hipStream_t s) {
+  if (n_pages == 0) return hipSuccess;
+  const int G = hq / hkv;
+  const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * d) * sizeof(float);
+  dim3 grid(static_cast<unsigned>((n_pages + kPagesPerBlock - 1) / kPagesPerBlock), hkv);
+  if (dt == FB_BF16)
+    hipLaunchKernelGGL(page_bound_kernel<uint16_t>, grid, dim3(256), smem, s,
+                       static_cast<const uint16_t*>(q), q_st, q_sh,
+                       static_cast<const uint16_t*>(kmin), static_cast<const uint16_t*>(kmax), n_q,
+                       hq, hkv, d, n_pages, bound);
+  else
+    hipLaunchKernelGGL(page_bound_kernel<float>, grid, dim3(256), smem, s,
+                       static_cast<const float*>(q), q_st, q_sh, static_cast<const float*>(kmin),
+                       static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, bound);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || k_pages <= 0) return e;
+  hipLaunchKernelGGL(page_topk_kernel, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv, n_pages,
+                     k_pages, pages);
+  return hipGetLastError();
+}
+
+}  // namespace fb

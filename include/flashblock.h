@@ -1,0 +1,306 @@
+/*
+ * flashblock.h -- C ABI of the MI355X (gfx950) FlashBlock block-diffusion
+ * attention step.
+ *
+ * The method (FlashBlock: Attention Caching for Efficient Long-Context Block
+ * Diffusion, technical summary, s2 "core mechanism"): the B queries of the
+ * block being denoised attend over two key sets, J_out (every token outside
+ * the block: the long, static prefix KV cache) and J_in (the block's own
+ * tokens). The block-external output A_out and its log-normaliser
+ * L_out = ln Z_out are cached and reused on later denoising steps; only the
+ * block-internal pair (A_in, L_in) is recomputed, and the two are combined
+ * by the log-space composition
+ *     m = max(L_out, L_in)
+ *     A_full = (e^{L_out-m} A_out + e^{L_in-m} A_in) / (e^{L_out-m} + e^{L_in-m}).
+ * A reuse controller (same page, s2 "adaptive reuse strategies") recomputes
+ * the cached pair when the count of updated tokens M reaches tau (text), or
+ * per head when the head's similarity is not above gamma (video); unselected
+ * keys of a sparse attention can play the role of J_out (sparse
+ * compatibility), with the page selection of LoSA (Locality Aware Sparse
+ * Attention for Block-Wise Diffusion Language Models, s2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is device memory owned by the caller, unless it
+ *    is documented as host memory. The library allocates nothing, keeps no
+ *    global state and is reentrant: calls on different streams may overlap
+ *    as long as they do not share output buffers.
+ *  - Tensors of q, k, v are described by fb_tensor: element strides between
+ *    tokens and between heads; the head dimension is contiguous (stride 1).
+ *    Base pointers must be 16-byte aligned and token/head strides multiples
+ *    of 8 elements (16 bytes for bf16, 32 for fp32).
+ *  - Outputs are fp32, contiguous: A as [n_q, Hq, head_dim], L as [n_q, Hq].
+ *  - L is a natural logarithm of the softmax denominator over the *scaled*
+ *    scores s_j = scale * q . k_j. An empty key set yields A = 0, L = -inf.
+ *  - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ *  - Mask bytes: 1 = reuse (skip the recompute), 0 = recompute.
+ *  - Every entry point validates its arguments on the host before any
+ *    launch and returns a status; none throws or aborts. Launch failures map
+ *    to FB_ERR_DEVICE. Faults inside kernels surface, as with any HIP work,
+ *    at the caller's next synchronisation.
+ *  - All work is enqueued on the given stream with no host synchronisation;
+ *    decisions taken on the device (masks, counts) are consumed on the
+ *    device.
+ */
+#ifndef FLASHBLOCK_H
+#define FLASHBLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FB_ABI_VERSION 1
+
+typedef enum {
+  FB_OK = 0,
+  FB_ERR_INVALID_ARGUMENT = 1,   /* bad shape, stride, pointer or value       */
+  FB_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. head_dim) */
+  FB_ERR_WORKSPACE_TOO_SMALL = 3,
+  FB_ERR_DEVICE = 4              /* a HIP launch or runtime call failed       */
+} fb_status;
+
+typedef enum { FB_BF16 = 0, FB_F32 = 1 } fb_dtype;
+
+typedef struct {
+  int32_t n_q_heads;    /* Hq >= 1                                         */
+  int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0                         */
+  int32_t head_dim;     /* 64 or 128                                       */
+  float scale;          /* softmax scale on q . k (usually 1/sqrt(d)), > 0 */
+  fb_dtype dtype;       /* element type of q, k, v                         */
+} fb_attn_shape;
+
+typedef struct {
+  const void* ptr;      /* device, 16-byte aligned; may be NULL iff n_tok == 0 */
+  int64_t n_tok;        /* tokens                                              */
+  int64_t stride_tok;   /* elements between consecutive tokens                 */
+  int64_t stride_head;  /* elements between consecutive heads                  */
+} fb_tensor;
+
+/* ------------------------------------------------------------------------ *
+ * Sparse page selection (optional; FlashBlock s2 sparse compatibility,     *
+ * LoSA s2 QUEST-selected sparse attention for active tokens).               *
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  FB_SEL_DENSE = 0,   /* every prefix key                                     */
+  FB_SEL_SPLIT = 1,   /* one pass: selected pages and their complement        */
+  FB_SEL_GATHER = 2   /* selected pages of active rows only, merged with the
+                         cached residual                                       */
+} fb_sel_mode;
+
+typedef struct {
+  fb_sel_mode mode;
+  int32_t page_size;      /* tokens per page (16); page p = tokens [p*ps, p*ps+ps) */
+  int32_t k_pages;        /* selected pages per (query token, KV head), >= 0     */
+  const int32_t* pages;   /* [n_q, Hkv, k_pages] page ids, strictly ascending    */
+  const uint8_t* active;  /* GATHER: [n_q] 1 = the row recomputes; NULL = all    */
+} fb_page_sel;
+
+/* ------------------------------------------------------------------------ *
+ * fb_prefix_attn -- the block-external pass over J_out.                    *
+ * FlashBlock s2 "core mechanism": A_out and L_out = log Z_out over the      *
+ * tokens outside the block, computed when the controller asks for it.      *
+ *                                                                           *
+ * q [n_q, Hq, d]; k, v [n_kv, Hkv, d] (any token/head strides).             *
+ * head_reuse_mask: NULL, or device [Hq]; heads with byte 1 are skipped and  *
+ *   their rows of every output are left untouched.                          *
+ * sel: NULL or mode DENSE -> a_out, l_out over all n_kv keys; a_res, l_res  *
+ *   must be NULL.                                                            *
+ *   SPLIT  -> a_res, l_res (outputs) = the pair over the keys NOT in the    *
+ *   row's selected pages; a_out, l_out = the pair over all keys (the merge  *
+ *   of the selected part and the residual).                                  *
+ *   GATHER -> a_res, l_res are INPUTS (the cached residual); for rows whose  *
+ *   active byte is 1, a_out, l_out = merge(pair over the selected pages,     *
+ *   cached residual); other rows are left untouched.                         *
+ * ws: device workspace of at least fb_prefix_attn_workspace() bytes (split- *
+ *   K partials); may be NULL when that size is 0.                            *
+ * Errors: INVALID_ARGUMENT on bad shape/stride/alignment/NULL, n_q < 1,     *
+ *   n_kv < 0, k/v token counts that differ, a page id out of range is NOT   *
+ *   checked (ids are device data); UNSUPPORTED for head_dim not in {64,128} *
+ *   or a sparse mode with fp32 inputs; WORKSPACE_TOO_SMALL.                  *
+ * ------------------------------------------------------------------------ */
+size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q,
+                                int64_t n_kv, const fb_page_sel* sel);
+fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k,
+                         fb_tensor v, const uint8_t* head_reuse_mask,
+                         const fb_page_sel* sel, float* a_out, float* l_out,
+                         float* a_res, float* l_res, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * fb_block_attn_merge -- the block-internal pass and the log-space merge.  *
+ * FlashBlock s2 "core mechanism": A_in, L_in over J_in (the block's own     *
+ * B tokens; every block query sees every block key -- the pages state no    *
+ * in-block mask), then A_full = the log-space composition of the cached      *
+ * (A_out, L_out) with (A_in, L_in).                                          *
+ *                                                                            *
+ * q_blk [n_q, Hq, d]; k_blk, v_blk [n_q, Hkv, d]; a_out, l_out: the cached  *
+ * pair (inputs). a_full (required), l_full, a_in, l_in (nullable) outputs.  *
+ * ws: device workspace of fb_block_attn_merge_workspace() bytes (0 for      *
+ * small blocks).                                                             *
+ * Errors: as fb_prefix_attn.                                                 *
+ * ------------------------------------------------------------------------ */
+size_t fb_block_attn_merge_workspace(const fb_attn_shape* shape, int64_t n_q);
+fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk,
+                              fb_tensor k_blk, fb_tensor v_blk,
+                              const float* a_out, const float* l_out,
+                              float* a_full, float* l_full, float* a_in,
+                              float* l_in, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * fb_reuse_decide -- the reuse controller.                                  *
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  /* FlashBlock s2 threshold reuse: M = #{i : ids_cur[i] != ids_prev[i]};
+     mask[h] = (M < tau) for every head, unless force says otherwise.        */
+  FB_REUSE_COUNT = 0,
+  /* FlashBlock s2 per-head selection: sim[h] = cosine of head h's output in
+     a_probe vs a_cached, flattened over [n_q, d], float64, clamped to
+     [-1, 1] (both all-zero -> 1, one zero -> 0); for heads with
+     mask_in[h] == 0: sim[h] updated, mask[h] = (sim[h] > gamma); heads with
+     mask_in[h] == 1 keep sim[h] and get mask[h] = 1.                        */
+  FB_REUSE_HEAD_COS = 1,
+  /* LoSA s2 token classification: mse[t] = sum over (head, dim), in that
+     order, of (q_cur - q_prev)^2 in float64 without fused multiply-add, then
+     divided by Hq*d; cutoff = the ceil(pct/100 * n_q)-th smallest mse;
+     active[t] = mse[t] > cutoff.                                            */
+  FB_REUSE_ACTIVE_MSE = 2
+} fb_reuse_mode;
+
+typedef struct {
+  fb_reuse_mode mode;
+  int32_t n_q;              /* block tokens / queries                         */
+  int32_t n_heads;          /* Hq                                             */
+  int32_t head_dim;         /* d (HEAD_COS, ACTIVE_MSE)                       */
+  /* COUNT */
+  const int32_t* ids_prev;  /* [n_q]                                          */
+  const int32_t* ids_cur;   /* [n_q]                                          */
+  int32_t tau;              /* reuse iff M < tau                              */
+  int32_t force;            /* -1 decide; 0 force recompute; 1 force reuse    */
+  int32_t* m_count;         /* out [1], nullable                              */
+  int32_t* ids_store;       /* nullable out [n_q]: receives ids_cur after the
+                               count (may alias ids_prev)                      */
+  /* HEAD_COS */
+  const float* a_cached;    /* [n_q, Hq, d]                                   */
+  const float* a_probe;     /* [n_q, Hq, d]                                   */
+  const uint8_t* mask_in;   /* [Hq] nullable (= all zero)                     */
+  double gamma;
+  double* sim;              /* in/out [Hq]                                    */
+  /* ACTIVE_MSE */
+  const void* q_prev;       /* [n_q, Hq, d] contiguous, dtype below           */
+  const void* q_cur;        /* [n_q, Hq, d] contiguous                        */
+  fb_dtype dtype;
+  int32_t pct;              /* 1..100                                         */
+  double* mse;              /* out [n_q], nullable                            */
+  uint8_t* active;          /* out [n_q]                                      */
+  /* output of COUNT and HEAD_COS */
+  uint8_t* mask;            /* [Hq]                                           */
+  void* ws;                 /* device workspace >= fb_reuse_decide_workspace  */
+  size_t ws_bytes;
+} fb_reuse_args;
+
+size_t fb_reuse_decide_workspace(const fb_reuse_args* args);
+fb_status fb_reuse_decide(const fb_reuse_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Page metadata and selection (optional sparse subsystem).                  *
+ * fb_page_meta: kmin, kmax [Hkv, P, d] (dtype of k), P = ceil(n_kv / ps):   *
+ *   elementwise min / max of the page's keys (the last page may be short).  *
+ * fb_page_select: bound[t, g, p] = max over the query heads h of group g of *
+ *   sum_{j = 0..d-1, in order} max(q[t,h,j]*kmin[g,p,j], q[t,h,j]*kmax[g,p,j])*
+ *   in float64 without fused multiply-add; pages[t, g, :] = the k_pages     *
+ *   pages of largest bound (ties: lower page id first), listed ascending.    *
+ *   bound may be NULL (then it lives in ws).                                  *
+ * ------------------------------------------------------------------------ */
+fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k,
+                       int32_t page_size, void* kmin, void* kmax,
+                       hipStream_t stream);
+size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q,
+                                int64_t n_pages);
+fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
+                         const void* kmin, const void* kmax, int64_t n_pages,
+                         int32_t k_pages, int32_t* pages, double* bound,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * fb_step -- one denoising step of one block, all launches on `stream`.    *
+ *                                                                           *
+ * TEXT   (FlashBlock s2 threshold reuse): COUNT decision on the device ->  *
+ *        prefix pass for the heads that recompute (every head at step 0)   *
+ *        into the cache (a_out, l_out) -> in-block pass + merge.            *
+ * VIDEO  (FlashBlock s2 per-head selection, probe reading): step 0 fills   *
+ *        the cache; at later steps heads with mask 0 recompute into the     *
+ *        probe buffer, HEAD_COS compares probe and cache and writes         *
+ *        mask_next, the probe replaces the cache for those heads; the       *
+ *        in-block pass merges with the cache. mask and mask_next swap.      *
+ * SPARSE (FlashBlock s2 sparse compatibility + LoSA s2 workflow): step 0   *
+ *        builds page metadata (once per prefix), selects pages, runs the    *
+ *        SPLIT pass (cache + residual); later steps classify tokens by      *
+ *        query MSE and run the GATHER pass for active rows.                 *
+ *                                                                           *
+ * fb_step_state is a host struct owned by the caller; `step` counts the    *
+ * steps of the current block (set it to 0 at a new block). Buffers it       *
+ * points to are caller-owned device memory sized as documented per field.  *
+ * ------------------------------------------------------------------------ */
+typedef enum { FB_STEP_TEXT = 0, FB_STEP_VIDEO = 1, FB_STEP_SPARSE = 2 } fb_step_mode;
+
+typedef struct {
+  fb_attn_shape shape;
+  fb_step_mode mode;
+  int32_t n_q;             /* block queries per step                           */
+  fb_tensor k_prefix;      /* J_out keys   [n_kv, Hkv, d]                      */
+  fb_tensor v_prefix;      /* J_out values [n_kv, Hkv, d]                      */
+  int32_t tau;             /* TEXT                                             */
+  double gamma;            /* VIDEO                                            */
+  int32_t page_size;       /* SPARSE                                           */
+  int32_t k_pages;         /* SPARSE                                           */
+  int32_t pct;             /* SPARSE active cutoff percentile                  */
+  float* a_out;            /* cache [n_q, Hq, d]                               */
+  float* l_out;            /* cache [n_q, Hq]                                  */
+  float* a_probe;          /* VIDEO [n_q, Hq, d]                               */
+  float* l_probe;          /* VIDEO [n_q, Hq]                                  */
+  float* a_res;            /* SPARSE residual [n_q, Hq, d]                     */
+  float* l_res;            /* SPARSE residual [n_q, Hq]                        */
+  int32_t* ids_prev;       /* TEXT [n_q]                                       */
+  int32_t* m_count;        /* TEXT [1]                                         */
+  uint8_t* mask;           /* [Hq] reuse flags used by this step               */
+  uint8_t* mask_next;      /* VIDEO [Hq]                                       */
+  double* sim;             /* VIDEO [Hq]                                       */
+  int32_t* pages;          /* SPARSE [n_q, Hkv, k_pages]                       */
+  void* kmin;              /* SPARSE [Hkv, P, d] (dtype)                       */
+  void* kmax;              /* SPARSE [Hkv, P, d]                               */
+  void* q_prev;            /* SPARSE [n_q, Hq, d] contiguous (dtype)           */
+  double* mse;             /* SPARSE [n_q]                                     */
+  uint8_t* active;         /* SPARSE [n_q]                                     */
+  void* ws;                /* device workspace >= fb_step_workspace()          */
+  size_t ws_bytes;
+  int64_t step;            /* host counter; fb_step increments it              */
+  int32_t meta_ready;      /* SPARSE: host flag, page metadata built           */
+} fb_step_state;
+
+typedef struct {
+  fb_tensor q_blk;         /* [n_q, Hq, d]                                     */
+  fb_tensor k_blk;         /* [n_q, Hkv, d]                                    */
+  fb_tensor v_blk;         /* [n_q, Hkv, d]                                    */
+  const int32_t* ids_cur;  /* TEXT [n_q] token ids of the block at this step   */
+  int32_t decision;        /* -1: the device decides; 0: force recompute;
+                              1: force reuse (TEXT/VIDEO: no prefix launch)     */
+  float* a_full;           /* out [n_q, Hq, d]                                 */
+  float* l_full;           /* out [n_q, Hq], nullable                          */
+} fb_step_args;
+
+size_t fb_step_workspace(const fb_step_state* st);
+fb_status fb_step(fb_step_state* st, const fb_step_args* args,
+                  hipStream_t stream);
+
+const char* fb_status_string(fb_status s);
+int fb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHBLOCK_H */

@@ -101,13 +101,14 @@ def active_mse(q_prev, q_cur):
 
 
 def percentile_cutoff(mse, pct=25):
-    """Nearest-rank percentile: the ceil(pct/100 * B)-th smallest value.
+    """Nearest-rank percentile: the ceil(pct * B / 100)-th smallest value
+    (the ceiling taken exactly, in integers).
 
     Reading of the 25th-percentile cutoff in the sparse workload: nearest
     rank (for B = 8 and pct = 25 it is the 2nd smallest).
     """
     x = np.sort(np.asarray(mse, dtype=np.float64))
-    rank = max(1, math.ceil(pct / 100.0 * len(x)))
+    rank = max(1, -(-int(pct) * len(x) // 100))   # exact integer ceil
     return float(x[rank - 1])
 
 

@@ -1,0 +1,199 @@
+"""Host-side checks of the C ABI that need no GPU: the built library loads and
+exports every entry point the header declares, the ctypes structs match the
+C layout, and invalid arguments are rejected with the documented status
+before any HIP call."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import block_diffusion_attention_amd as fb
+from block_diffusion_attention_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashblock.h")
+
+FAKE = 0x7F0000100000          # aligned fake device address; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fb.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fb_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_abi.SYMBOLS) == names
+
+
+def test_status_strings_and_version(lib):
+    assert fb.fb_abi_version() == 1
+    assert fb.fb_status_string(0) == "ok"
+    assert fb.fb_status_string(3) == "workspace too small"
+    assert fb.fb_status_string(99) == "unknown status"
+
+
+STRUCTS = {
+    "fb_attn_shape": ["n_q_heads", "n_kv_heads", "head_dim", "scale", "dtype"],
+    "fb_tensor": ["ptr", "n_tok", "stride_tok", "stride_head"],
+    "fb_page_sel": ["mode", "page_size", "k_pages", "pages", "active"],
+    "fb_reuse_args": [f[0] for f in _abi.fb_reuse_args._fields_],
+    "fb_step_state": [f[0] for f in _abi.fb_step_state._fields_],
+    "fb_step_args": [f[0] for f in _abi.fb_step_args._fields_],
+}
+
+
+def test_struct_layouts_match_c():
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "flashblock.h"', "int main(){"]
+    for s, fields in STRUCTS.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (s, s))
+        for f in fields:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (s, f, s, f))
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+                        "-I/opt/rocm/include", c, "-o", exe], check=True, capture_output=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    got = dict(line.rsplit(" ", 1) for line in out.strip().splitlines())
+    for s, fields in STRUCTS.items():
+        cls = getattr(_abi, s)
+        assert int(got[s]) == C.sizeof(cls), s
+        for f in fields:
+            assert int(got[s + "." + f]) == getattr(cls, f).offset, (s, f)
+
+
+# ------------------------------------------------------- validation, no GPU
+
+def shape(hq=32, hkv=8, d=128, dt=0, scale=0.088):
+    return fb.fb_attn_shape(hq, hkv, d, scale, dt)
+
+
+def ten(n, heads, d=128, st=None, sh=None, p=FAKE):
+    st = heads * d if st is None else st
+    sh = d if sh is None else sh
+    return fb.fb_tensor(p, n, st, sh)
+
+
+def prefix(lib, sh, q, k, v, a=FAKE, l=FAKE, sel=None, ar=None, lr=None, ws=None, wsb=0):
+    return lib.fb_prefix_attn(C.byref(sh), q, k, v, None, C.byref(sel) if sel else None,
+                              a, l, ar, lr, ws, wsb, None)
+
+
+def test_prefix_rejects_bad_arguments(lib):
+    q, k = ten(4, 32), ten(1000, 8)
+    bad = fb.FB_ERR_INVALID_ARGUMENT
+    assert prefix(lib, shape(hq=30), q, k, k) == bad                       # Hq % Hkv
+    assert prefix(lib, shape(d=96), ten(4, 32, 96), ten(9, 8, 96), ten(9, 8, 96)) == fb.FB_ERR_UNSUPPORTED
+    assert prefix(lib, shape(d=0), q, k, k) == bad
+    assert prefix(lib, shape(scale=-1.0), q, k, k) == bad
+    assert prefix(lib, shape(dt=7), q, k, k) == bad
+    assert prefix(lib, shape(), ten(0, 32), k, k) == bad                   # n_q < 1
+    assert prefix(lib, shape(), ten(4, 32, p=None), k, k) == bad            # NULL q
+    assert prefix(lib, shape(), ten(4, 32, p=FAKE + 8), k, k) == bad        # misaligned
+    assert prefix(lib, shape(), q, ten(1000, 8, st=1028), k) == bad        # stride % 8
+    assert prefix(lib, shape(), q, ten(1000, 8, st=512, sh=128), k) == bad  # overlap
+    assert prefix(lib, shape(), q, k, ten(999, 8)) == bad                   # |K| != |V|
+    assert prefix(lib, shape(), q, k, k, a=None) == bad
+    assert prefix(lib, shape(), q, k, k, ar=FAKE, lr=FAKE) == bad          # residual in dense
+    sel = fb.fb_page_sel(fb.FB_SEL_SPLIT, 16, 10000, FAKE, None)
+    assert prefix(lib, shape(), q, k, k, sel=sel, ar=FAKE, lr=FAKE) == bad  # k > pages
+    sel = fb.fb_page_sel(fb.FB_SEL_SPLIT, 16, 8, FAKE, None)
+    assert prefix(lib, shape(), q, k, k, sel=sel) == bad                    # residual missing
+
+
+def test_prefix_workspace_rules(lib):
+    sh = shape()
+    q, k = ten(16, 32), ten(800000, 8)
+    need = lib.fb_prefix_attn_workspace(C.byref(sh), 16, 800000, None)
+    assert need > 0 and need % 256 == 0
+    assert prefix(lib, sh, q, k, k, ws=FAKE, wsb=need - 1) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    assert prefix(lib, sh, q, k, k, ws=None, wsb=need) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    # a short prefix is one chunk written straight to the outputs
+    assert lib.fb_prefix_attn_workspace(C.byref(sh), 4, 100, None) == 0
+    # head-major K/V is accepted by the validator (workspace check is reached)
+    kh = ten(800000, 8, st=128, sh=800000 * 128)
+    assert prefix(lib, sh, q, kh, kh, ws=FAKE, wsb=need - 1) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    split = fb.fb_page_sel(fb.FB_SEL_SPLIT, 16, 819, FAKE, None)
+    ns = lib.fb_prefix_attn_workspace(C.byref(sh), 8, 65536, C.byref(split))
+    dense = lib.fb_prefix_attn_workspace(C.byref(sh), 8, 65536, None)
+    assert ns > 0 and dense > 0
+
+
+def test_block_merge_rejects(lib):
+    sh = shape()
+    q, k = ten(4, 32), ten(4, 8)
+    f = lib.fb_block_attn_merge
+    assert f(C.byref(sh), q, ten(5, 8), k, FAKE, FAKE, FAKE, None, None, None, None, 0, None) == 1
+    assert f(C.byref(sh), q, k, k, None, FAKE, FAKE, None, None, None, None, 0, None) == 1
+    assert f(C.byref(sh), q, k, k, FAKE, FAKE, None, None, None, None, None, 0, None) == 1
+
+
+def test_reuse_decide_rejects(lib):
+    a = fb.fb_reuse_args()
+    a.mode, a.n_q, a.n_heads = fb.FB_REUSE_COUNT, 4, 32
+    a.ids_cur, a.mask, a.force = FAKE, FAKE, 2
+    assert lib.fb_reuse_decide(C.byref(a), None) == 1
+    a.mode, a.force = fb.FB_REUSE_HEAD_COS, -1
+    a.head_dim, a.a_cached, a.a_probe, a.sim = 128, FAKE, None, FAKE
+    assert lib.fb_reuse_decide(C.byref(a), None) == 1
+    a.a_probe = FAKE
+    assert lib.fb_reuse_decide(C.byref(a), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    a.mode, a.q_prev, a.q_cur, a.active, a.pct = fb.FB_REUSE_ACTIVE_MSE, FAKE, FAKE, FAKE, 0
+    assert lib.fb_reuse_decide(C.byref(a), None) == 1
+    a.pct = 25
+    assert lib.fb_reuse_decide_workspace(C.byref(a)) == 256
+    assert lib.fb_reuse_decide(C.byref(a), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    a.mode = 9
+    assert lib.fb_reuse_decide(C.byref(a), None) == 1
+
+
+def test_page_calls_reject(lib):
+    sh = shape()
+    assert lib.fb_page_meta(C.byref(sh), ten(100, 8), 0, FAKE, FAKE, None) == 1
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 11, FAKE, FAKE,
+                              None, 0, None) == 1
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 3, FAKE, None,
+                              None, 0, None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    assert lib.fb_page_select_workspace(C.byref(sh), 8, 4096) == 8 * 8 * 4096 * 8
+
+
+def test_step_rejects(lib):
+    st = fb.fb_step_state()
+    st.shape = shape()
+    st.mode, st.n_q = fb.FB_STEP_TEXT, 4
+    st.k_prefix = st.v_prefix = ten(1000, 8)
+    st.a_out = st.l_out = st.mask = FAKE
+    st.ws, st.ws_bytes = FAKE, 1 << 40
+    args = fb.fb_step_args()
+    args.q_blk, args.k_blk, args.v_blk = ten(4, 32), ten(4, 8), ten(4, 8)
+    args.a_full, args.decision = FAKE, 3
+    assert lib.fb_step(C.byref(st), C.byref(args), None) == 1            # bad decision
+    args.decision = -1
+    args.q_blk = ten(5, 32)
+    assert lib.fb_step(C.byref(st), C.byref(args), None) == 1            # n_q mismatch
+    args.q_blk = ten(4, 32)
+    assert lib.fb_step(C.byref(st), C.byref(args), None) == 1            # ids missing
+    st.mode = 7
+    assert lib.fb_step(C.byref(st), C.byref(args), None) == 1
+    st.mode = fb.FB_STEP_TEXT
+    st.k_prefix = st.v_prefix = ten(800000, 8)
+    st.ws_bytes = 10
+    assert lib.fb_step(C.byref(st), C.byref(args), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    assert lib.fb_step_workspace(C.byref(st)) > 0
+    assert st.step == 0
