@@ -110,6 +110,8 @@ def load(path=LIB_PATH):
     """Load libflashblock.so (raises if it has not been built)."""
     global _lib
     if _lib is not None:
+        if path != LIB_PATH and _lib._name != path:
+            raise RuntimeError("another libflashblock is already loaded")
         return _lib
     if not os.path.exists(path):
         raise RuntimeError("libflashblock.so is not built (%s); run "

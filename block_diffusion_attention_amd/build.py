@@ -35,22 +35,25 @@ def _run(cmd):
     return r
 
 
-def _compile(src):
-    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+def _compile(src, out_dir, extra):
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    _run([HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose=True, extra_flags=(), lib_path=LIB, out_dir=OUT_DIR):
+    """Compile every source and link lib_path. extra_flags (e.g. -D tuning
+    macros) and another lib_path/out_dir serve tuning builds."""
+    os.makedirs(out_dir, exist_ok=True)
+    extra = list(extra_flags)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, out_dir, extra), SOURCES))
+    tmp = lib_path + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -23,8 +23,14 @@ namespace {
 // Split-K planning. A launch should put several workgroups on each of the
 // 256 CUs (8 XCDs x 32); chunks are at least a few tiles per wave long so the
 // partials stay a small fraction of the K/V bytes.
-constexpr int64_t kTargetWorkgroups = 1024;
-constexpr int64_t kMinTilesMfma = 16;     // 32-token tiles per chunk (4 waves)
+#ifndef FB_PREFIX_TARGET_WGS
+#define FB_PREFIX_TARGET_WGS 256
+#endif
+#ifndef FB_PREFIX_MIN_TILES
+#define FB_PREFIX_MIN_TILES 16
+#endif
+constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;
+constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
 constexpr int64_t kMinTilesGeneric = 4;   // 64-token tiles per chunk
 constexpr size_t kAlign = 256;
 

@@ -164,28 +164,51 @@ __global__ __launch_bounds__(64) void prefix_generic_kernel(PrefixParams p) {
 // MFMA prefix kernel (bf16, d = 128).
 //
 // Workgroup = 4 waves = (chunk of the prefix, KV head g, row slab of 64 rows).
-// Rows are the (query token, query head) pairs of the group: r = t*G + j.
+// Rows are the (query token, query head) pairs of the group: r = t*G + j, so
+// every K/V byte of the group is read from HBM once for all its query heads.
 // Each wave streams its own 32-token tiles of the chunk (tiles w, w+4, ...),
 // keeps its own online-softmax state, and the four states are merged through
 // LDS at the end. Per tile:
-//   global -> VGPR (coalesced 16 B/lane: 4 token rows x 256 B per load)
-//   VGPR -> wave-private LDS, XOR-swizzled per 16-byte piece
+//   global -> VGPR: coalesced 16 B per lane (4 token rows x 256 B per load),
+//       addressed as a wave-uniform SGPR base + one VGPR lane offset; DEPTH
+//       tiles are in flight per wave (DEPTH x 16 KB of VGPR staging);
+//   VGPR -> wave-private LDS with padded rows (K: 272 B, V: 320 B), chosen so
+//       the operand reads below hit distinct LDS banks;
 //   S^T[32 tok x 32 rows] = K . Q^T  (v_mfma_f32_32x32x16_bf16, 8 k-steps)
 //       -> each lane owns one row and 16 of its scores: the row max needs
-//          one exchange with the other lane half, the row sum none.
-//   O^T[128 dims x 32 rows] += V^T . P^T: P^T is the score accumulator
-//       itself (as bf16), V^T comes from LDS by ds_read_b64_tr_b16.
-// The next tile's global loads are in flight while a tile is computed.
+//          one exchange with the other lane half, the row sum none;
+//   O^T[128 dims x 32 rows] += V^T . P^T: P^T is the score accumulator itself
+//       (as bf16 hi + lo), V^T comes from LDS by ds_read_b64_tr_b16.
+// The running row max is raised only when a tile's max exceeds it by more
+// than 2^8 (weights then stay <= 256), so most tiles skip the O rescale.
 // ---------------------------------------------------------------------------
+#ifndef FB_PREFIX_DEPTH_R1
+#define FB_PREFIX_DEPTH_R1 3      // tiles in flight per wave, 32-row slabs
+#endif
+#ifndef FB_PREFIX_DEPTH_R2
+#define FB_PREFIX_DEPTH_R2 1      // tiles in flight per wave, 64-row slabs
+#endif
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
 constexpr int kD = 128;
+constexpr int kKRow = 272;                   // 17 x 16 B: 16 rows, 16 bank groups
+constexpr int kVRow = 320;                   // 20 x 16 B: 4 rows, 4 x 64 B bank spans
+constexpr int kKBytes = kTile * kKRow;
+constexpr int kVBytes = kTile * kVRow;
+constexpr int kWaveLds = kKBytes + kVBytes;
+constexpr float kRescaleLog2 = 8.f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct KvTile {            // one 32-token K/V tile, 16 B per lane per row-load
+  u32x4 k[8], v[8];        // native vectors (plain loads, kept in VGPRs)
+};
 
 // Transposing LDS read (gfx950): within each 16-lane group, "row" s is the
 // concatenation of the 4-element loads of lanes 4s..4s+3, and lane j receives
@@ -195,10 +218,10 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
 
-template <int NRB>
+template <int NRB, int DEPTH>
 __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
   constexpr int RP = 32 * NRB;                     // padded rows per slab
-  constexpr int kStageBytes = kWaves * 16384;      // per wave: K 8 KB + V 8 KB
+  constexpr int kStageBytes = kWaves * kWaveLds;
   constexpr int kMergeStride = kD + 1;             // floats per merge row
   constexpr int kMergeBytes = kWaves * RP * kMergeStride * 4;
   constexpr int kLdsBytes = kMergeBytes > kStageBytes ? kMergeBytes : kStageBytes;
@@ -209,7 +232,8 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
   const int g = blockIdx.y;
   const int slab = blockIdx.z;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, r32 = lane & 31;
   const int G = p.group;
   const int R = p.n_q * G;
@@ -231,25 +255,30 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(t) * p.q_st +
                          static_cast<int64_t>(g * G + jh) * p.q_sh;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      if (ok) {
-        qop[rb][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl);
-      } else {
-        qop[rb][kk] = bf16x8{};
-      }
-    }
+    for (int kk = 0; kk < 8; ++kk)
+      qop[rb][kk] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl) : bf16x8{};
   }
 
   const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
   const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
   const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
+  if (t_begin >= t_end) return;                    // (every launched chunk has a tile)
 
-  char* kl = lds + w * 16384;
-  char* vl = kl + 8192;
+  // LDS addresses: one base per access kind, everything else immediates.
+  char* kl = lds + w * kWaveLds;
+  char* vl = kl + kKBytes;
+  const int lrow = lane >> 4, lpiece = lane & 15;
+  char* k_wr = kl + lrow * kKRow + lpiece * 16;
+  char* v_wr = vl + lrow * kVRow + lpiece * 16;
+  const char* k_rd = kl + r32 * kKRow + hl * 16;
+  const int grp = lane >> 4, s4 = (lane & 15) >> 2, q4 = lane & 3;
+  const char* v_rd = vl + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
+
+  // global addressing: wave-uniform tile base + one 32-bit lane offset
   const char* kg = static_cast<const char*>(p.k) + static_cast<int64_t>(g) * p.kv_sh * 2;
   const char* vg = static_cast<const char*>(p.v) + static_cast<int64_t>(g) * p.kv_sh * 2;
   const int64_t kvst_b = p.kv_st * 2;
-  const int lrow = lane >> 4, lpiece = lane & 15;
+  const uint32_t voff = static_cast<uint32_t>(lrow * kvst_b) + lpiece * 16;
 
   f32x16 o[NRB][4];
   float m_run[NRB], l_run[NRB];
@@ -261,50 +290,66 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
     for (int db = 0; db < 4; ++db) o[rb][db] = f32x16{};
   }
 
-  uint4 rk[8], rv[8];
-  auto load_tile = [&](int64_t tile) {
+  // Every stage is refilled unconditionally (the tile index is clamped to the
+  // chunk's last tile once past the end, a re-read that hits L2; rows past
+  // n_kv are clamped to the last token, and their scores are masked), so each
+  // path through the loop issues the same loads and the waits before staging
+  // only cover the stage being consumed.
+  const int64_t t_last = t_end - 1;
+  auto load_tile = [&](int64_t tile) -> KvTile {
+    KvTile r;
+    tile = tile < t_last ? tile : t_last;
+    const int64_t tok0 = tile * kTile;
+    const char* kb = kg + tok0 * kvst_b;
+    const char* vb = vg + tok0 * kvst_b;
+    if (tok0 + kTile <= p.n_kv) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t tok = tile * kTile + 4 * i + lrow;
-      if (tok < p.n_kv) {
-        rk[i] = *reinterpret_cast<const uint4*>(kg + tok * kvst_b + lpiece * 16);
-        rv[i] = *reinterpret_cast<const uint4*>(vg + tok * kvst_b + lpiece * 16);
-      } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        r.k[i] = *reinterpret_cast<const u32x4*>(kb + 4 * i * kvst_b + voff);
+        r.v[i] = *reinterpret_cast<const u32x4*>(vb + 4 * i * kvst_b + voff);
+      }
+    } else {
+      const int64_t last = p.n_kv - 1 - tok0;        // >= 0
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t rr = 4 * i + lrow < last ? 4 * i + lrow : last;
+        const int64_t off = rr * kvst_b + lpiece * 16;
+        r.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
+        r.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
       }
     }
+    return r;
   };
+  KvTile stage[DEPTH];
 
-  int64_t tile = t_begin + w;
-  if (tile < t_end) load_tile(tile);
-  for (; tile < t_end; tile += kWaves) {
-    // stage the tile (swizzle: K piece p of row r at p ^ (r & 15);
-    //                          V piece p of row r at p ^ 4 (r & 3))
+  const int64_t tile0 = t_begin + w;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) stage[d] = load_tile(tile0 + d * kWaves);
+
+  auto stage_to_lds = [&](const KvTile& st) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + lrow;
-      *reinterpret_cast<uint4*>(kl + r * 256 + ((lpiece ^ (r & 15)) << 4)) = rk[i];
-      *reinterpret_cast<uint4*>(vl + r * 256 + ((lpiece ^ ((r & 3) << 2)) << 4)) = rv[i];
+      *reinterpret_cast<u32x4*>(k_wr + 4 * i * kKRow) = st.k[i];
+      *reinterpret_cast<u32x4*>(v_wr + 4 * i * kVRow) = st.v[i];
     }
     asm volatile("" ::: "memory");
-    if (tile + kWaves < t_end) load_tile(tile + kWaves);
+  };
 
+  auto process = [&](int64_t tile) {
     // S^T = K . Q^T
     f32x16 s[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + r32 * 256 + (((2 * kk + hl) ^ (r32 & 15)) << 4));
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_rd + 32 * kk);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) s[rb] = mfma32(ka, qop[rb][kk], s[rb]);
     }
 
-    // online softmax, per row (= per lane pair l, l^32). The weights enter
-    // the P.V product as bf16 hi + lo parts (two MFMAs), so the product
-    // carries ~2^-17 relative error instead of bf16's 2^-9; the row sum l is
-    // accumulated from the fp32 weights.
+    // online softmax per row (= lane pair l, l^32); weights enter P.V as
+    // bf16 hi + lo parts (two MFMAs: ~2^-17 relative instead of bf16's
+    // 2^-9), the row sum l is accumulated from the fp32 weights.
     const int64_t valid = p.n_kv - tile * kTile;   // >= 1
     bf16x8 pbh[NRB][2], pbl[NRB][2];
 #pragma unroll
@@ -321,10 +366,13 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
         mx = fmaxf(mx, x[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m_run[rb], mx);
-      const float muse = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = fast_exp2(m_run[rb] - muse);
-      m_run[rb] = mnew;
+      const bool bump = mx > m_run[rb] + kRescaleLog2;
+      float alpha = 1.f;
+      if (bump) {
+        alpha = fast_exp2(m_run[rb] - mx);
+        m_run[rb] = mx;
+      }
+      const float muse = m_run[rb] == kNegInf ? 0.f : m_run[rb];
       float psum = 0.f;
 #pragma unroll
       for (int hj = 0; hj < 2; ++hj) {
@@ -335,12 +383,11 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
           psum += pf[e];
         }
         const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
-        const f32x8 rest = pf - __builtin_convertvector(hi, f32x8);
         pbh[rb][hj] = hi;
-        pbl[rb][hj] = __builtin_convertvector(rest, bf16x8);
+        pbl[rb][hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
       }
       l_run[rb] = l_run[rb] * alpha + psum;
-      if (__any(alpha != 1.f)) {
+      if (__any(bump)) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
       }
@@ -351,18 +398,11 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bf16x4 vh[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int grp = lane >> 4;
-          const int tr = 16 * j + 8 * u + 4 * (grp >> 1) + ((lane & 15) >> 2);
-          const int q4 = lane & 3;
-          const int piece = 4 * db + 2 * (grp & 1) + (q4 >> 1);
-          vh[u] = ds_read_tr(vl + tr * 256 + ((piece ^ ((tr & 3) << 2)) << 4) + ((q4 & 1) << 3));
-        }
-        // whole-vector concatenation (element-wise inserts of the transposed
-        // halves were mis-lowered by the compiler)
-        const bf16x8 va = __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x4 v0 = ds_read_tr(v_rd + (16 * j) * kVRow + 64 * db);
+        const bf16x4 v1 = ds_read_tr(v_rd + (16 * j + 8) * kVRow + 64 * db);
+        // whole-vector concatenation (element-wise inserts of the
+        // transposed halves were mis-lowered by the compiler)
+        const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           o[rb][db] = mfma32(va, pbh[rb][j], o[rb][db]);
@@ -370,7 +410,30 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
         }
       }
     }
+
     asm volatile("" ::: "memory");
+  };
+
+  // Steady state: whole iterations only, so every stage is consumed and
+  // refilled on every path and the wait before staging covers one stage.
+  int64_t base = tile0;
+  for (; base + (DEPTH - 1) * kWaves < t_end; base += DEPTH * kWaves) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t tile = base + d * kWaves;
+      stage_to_lds(stage[d]);
+      stage[d] = load_tile(tile + DEPTH * kWaves);
+      process(tile);
+    }
+  }
+  // Drain: the last (< DEPTH) tiles of this wave are already staged.
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) {
+    const int64_t tile = base + d * kWaves;
+    if (tile < t_end) {
+      stage_to_lds(stage[d]);
+      process(tile);
+    }
   }
 
   // ---- merge the four waves' states through LDS, write the chunk partial --
@@ -528,8 +591,10 @@ hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipS
 hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s) {
   const int rows = p.n_q * p.group;
   dim3 grid(p.n_chunks, p.hkv, (rows + 63) / 64);
-  if (row_blocks == 1) hipLaunchKernelGGL((prefix_mfma_kernel<1>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((prefix_mfma_kernel<2>), grid, dim3(256), 0, s, p);
+  if (row_blocks == 1)
+    hipLaunchKernelGGL((prefix_mfma_kernel<1, FB_PREFIX_DEPTH_R1>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefix_mfma_kernel<2, FB_PREFIX_DEPTH_R2>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
