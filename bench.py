@@ -43,7 +43,10 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time dense / FlashBlock / forced-reuse blocks over contexts")
+                    help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
+    ap.add_argument("--prefix-only", action="store_true",
+                    help="profiling mode: run the prefix pass --roofline-reps times, then "
+                         "a 1 GiB device copy (counter calibration); prints a short JSON")
     return ap.parse_args()
 
 
@@ -78,6 +81,10 @@ def main():
               for s in steps]
     shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
     stream = torch.cuda.current_stream()
+
+    if args.prefix_only:
+        prefix_only(args, fb, shape, inputs[0][0], k_dev, v_dev, B, N, hq, hkv, d, stream)
+        return
 
     step = fb.Step(fb.FB_STEP_TEXT, shape, B, k_dev, v_dev, tau=cfg.tau)
     a_full = torch.empty(B, hq, d, device=dev)
@@ -213,6 +220,34 @@ def main():
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
     out["extra"]["t_generate_inputs_s"] = round(t_gen, 1)
     print(json.dumps(out), flush=True)
+
+
+def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):
+    import torch
+    dev = q0.device
+    a_out = torch.empty(B, hq, d, device=dev)
+    l_out = torch.empty(B, hq, device=dev)
+    ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, B, N), 16), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(args.roofline_reps):
+        fb.fb_prefix_attn(shape, q0, k_dev, v_dev, a_out, l_out, ws=ws, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    t = r0.elapsed_time(r1) / args.roofline_reps * 1e-3
+    # calibration: a plain device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    alg = N * hkv * d * 4 + B * hq * d * 2 + B * hq * (d + 1) * 4
+    print(json.dumps({"prefix_pass_us": round(t * 1e6, 2), "alg_bytes": alg,
+                      "GB_s": round(alg / t / 1e9, 1), "reps": args.roofline_reps,
+                      "calibration_copy_bytes": 1 << 30}), flush=True)
 
 
 def cpu_baseline(cfg, kp, vp, steps, decisions):

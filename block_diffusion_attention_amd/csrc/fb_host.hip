@@ -29,7 +29,11 @@ namespace {
 #ifndef FB_PREFIX_MIN_TILES
 #define FB_PREFIX_MIN_TILES 16
 #endif
-constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;
+#ifndef FB_PREFIX_SLAB_ROWS
+#define FB_PREFIX_SLAB_ROWS 64    // 32: query rows in 32-row slabs (one MFMA row block each)
+#endif
+constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights in LDS
+constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
 constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
 constexpr int64_t kMinTilesGeneric = 4;   // 64-token tiles per chunk
 constexpr size_t kAlign = 256;
@@ -39,6 +43,7 @@ enum Path { PATH_GENERIC = 0, PATH_MFMA = 1 };
 struct PrefixPlan {
   int path = PATH_GENERIC;
   int row_blocks = 1;
+  int n_slabs = 1;
   int n_chunks = 0;
   int64_t tiles_per_chunk = 0;
   bool direct = false;         // one chunk, written straight to the outputs
@@ -106,16 +111,19 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   int64_t wg_per_chunk;
   int64_t min_tiles;
   if (pl.path == PATH_MFMA) {
-    pl.row_blocks = group_rows <= 32 ? 1 : 2;
-    wg_per_chunk = s.n_kv_heads * ((group_rows + 63) / 64);
+    pl.row_blocks = (group_rows <= 32 || FB_PREFIX_SLAB_ROWS == 32) ? 1 : 2;
+    pl.n_slabs = static_cast<int>((group_rows + 32 * pl.row_blocks - 1) / (32 * pl.row_blocks));
+    wg_per_chunk = s.n_kv_heads * pl.n_slabs;
     min_tiles = kMinTilesMfma;
   } else {
     wg_per_chunk = pl.rows;
     min_tiles = kMinTilesGeneric;
   }
   if (n_tiles > 0) {
-    int64_t want = kTargetWorkgroups / wg_per_chunk;
+    const int64_t occ = pl.path == PATH_MFMA ? prefix_mfma_occupancy(pl.row_blocks) : 1;
+    int64_t want = kTargetWorkgroups * occ / wg_per_chunk;
     if (want < 1) want = 1;
+    if (want > kMaxChunks) want = kMaxChunks;
     int64_t cap = n_tiles / min_tiles;
     if (cap < 1) cap = 1;
     const int64_t chunks = want < cap ? want : cap;
@@ -169,6 +177,7 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   pp.mask = mask;
   pp.tiles_per_chunk = pl.tiles_per_chunk;
   pp.n_chunks = pl.n_chunks;
+  pp.n_slabs = pl.n_slabs;
   pp.sel_mode = mode;
   if (mode != FB_SEL_DENSE) {
     pp.page_size = sel->page_size;

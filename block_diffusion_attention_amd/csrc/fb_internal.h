@@ -36,6 +36,7 @@ struct PrefixParams {
   const uint8_t* mask;          // [Hq] nullable, 1 = skip
   int64_t tiles_per_chunk;      // in units of the kernel's tile
   int n_chunks;
+  int n_slabs;                  // MFMA path: row slabs per (chunk, KV head)
   RowOut out;
   // sparse modes
   int sel_mode;                 // FB_SEL_*
@@ -63,6 +64,7 @@ struct ReduceParams {
 int prefix_tile_tokens(int path);               // tokens per tile of a path
 hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipStream_t s);
 hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s);
+int prefix_mfma_occupancy(int row_blocks);      // workgroups per CU of that kernel
 hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_prefix_empty(float* a_out, float* l_out, int n_q, int hq, int d,
                                const uint8_t* mask, hipStream_t s);

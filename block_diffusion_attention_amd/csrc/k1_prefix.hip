@@ -170,8 +170,8 @@ __global__ __launch_bounds__(64) void prefix_generic_kernel(PrefixParams p) {
 // keeps its own online-softmax state, and the four states are merged through
 // LDS at the end. Per tile:
 //   global -> VGPR: coalesced 16 B per lane (4 token rows x 256 B per load),
-//       addressed as a wave-uniform SGPR base + one VGPR lane offset; DEPTH
-//       tiles are in flight per wave (DEPTH x 16 KB of VGPR staging);
+//       non-temporal, addressed as a wave-uniform SGPR base + one VGPR lane
+//       offset; DEPTH tiles are in flight per wave (DEPTH x 16 KB of VGPRs);
 //   VGPR -> wave-private LDS with padded rows (K: 272 B, V: 320 B), chosen so
 //       the operand reads below hit distinct LDS banks;
 //   S^T[32 tok x 32 rows] = K . Q^T  (v_mfma_f32_32x32x16_bf16, 8 k-steps)
@@ -183,10 +183,13 @@ __global__ __launch_bounds__(64) void prefix_generic_kernel(PrefixParams p) {
 // than 2^8 (weights then stay <= 256), so most tiles skip the O rescale.
 // ---------------------------------------------------------------------------
 #ifndef FB_PREFIX_DEPTH_R1
-#define FB_PREFIX_DEPTH_R1 3      // tiles in flight per wave, 32-row slabs
+#define FB_PREFIX_DEPTH_R1 1      // tiles in flight per wave, 32-row slabs
 #endif
 #ifndef FB_PREFIX_DEPTH_R2
 #define FB_PREFIX_DEPTH_R2 1      // tiles in flight per wave, 64-row slabs
+#endif
+#ifndef FB_PREFIX_OCC_R1
+#define FB_PREFIX_OCC_R1 1        // workgroups per CU the 32-row kernel is built for
 #endif
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
@@ -206,6 +209,12 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// K/V are streamed once per pass: non-temporal loads (measured on MI355X:
+// ~10-15% more read bandwidth than plain loads for this access pattern).
+__device__ __forceinline__ u32x4 ldnt(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 struct KvTile {            // one 32-token K/V tile, 16 B per lane per row-load
   u32x4 k[8], v[8];        // native vectors (plain loads, kept in VGPRs)
 };
@@ -218,8 +227,8 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
 
-template <int NRB, int DEPTH>
-__global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
+template <int NRB, int DEPTH, int OCC>
+__global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
   constexpr int RP = 32 * NRB;                     // padded rows per slab
   constexpr int kStageBytes = kWaves * kWaveLds;
   constexpr int kMergeStride = kD + 1;             // floats per merge row
@@ -228,16 +237,26 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   __shared__ float ml_s[kWaves][RP][2];
 
-  const int chunk = blockIdx.x;
-  const int g = blockIdx.y;
-  const int slab = blockIdx.z;
+  // XCD-aware order: consecutive workgroup ids go to different XCDs (id mod 8),
+  // so the row slabs of one (chunk, KV head) get ids congruent mod 8 and run
+  // side by side on one XCD, where the second slab's K/V reads hit its L2.
+  int chunk, g, slab;
+  {
+    const int id = blockIdx.x;
+    const int tq = id >> 3;
+    slab = tq % p.n_slabs;
+    const int idx = (tq / p.n_slabs) * 8 + (id & 7);
+    if (idx >= p.n_chunks * p.hkv) return;
+    chunk = idx % p.n_chunks;
+    g = idx / p.n_chunks;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, r32 = lane & 31;
   const int G = p.group;
   const int R = p.n_q * G;
-  const int row0 = slab * 64;
+  const int row0 = slab * RP;
 
   if (p.mask) {                                    // whole group reused?
     bool all = true;
@@ -305,8 +324,8 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
     if (tok0 + kTile <= p.n_kv) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        r.k[i] = *reinterpret_cast<const u32x4*>(kb + 4 * i * kvst_b + voff);
-        r.v[i] = *reinterpret_cast<const u32x4*>(vb + 4 * i * kvst_b + voff);
+        r.k[i] = ldnt(kb + 4 * i * kvst_b + voff);
+        r.v[i] = ldnt(vb + 4 * i * kvst_b + voff);
       }
     } else {
       const int64_t last = p.n_kv - 1 - tok0;        // >= 0
@@ -314,8 +333,8 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
       for (int i = 0; i < 8; ++i) {
         const int64_t rr = 4 * i + lrow < last ? 4 * i + lrow : last;
         const int64_t off = rr * kvst_b + lpiece * 16;
-        r.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
-        r.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
+        r.k[i] = ldnt(kb + off);
+        r.v[i] = ldnt(vb + off);
       }
     }
     return r;
@@ -501,66 +520,94 @@ __global__ __launch_bounds__(256) void prefix_mfma_kernel(PrefixParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K reduce: merge the chunk partials of every (query, head) row in chunk
-// order, with the A_full composition rule (weights e^{L_c - max L}).
+// Split-K reduce: merge the chunk partials of every (query, head) row with the
+// A_full composition rule (weights e^{L_c - max L}). One workgroup per row:
+// the chunk weights are computed once into LDS, then every dim sums its
+// chunks with independent (unrolled) loads; all sums run in a fixed order.
 // SPLIT: a_out merges selected + residual partials, a_res the residual ones.
 // GATHER: a_out merges the selected partials with the cached residual input.
 // ---------------------------------------------------------------------------
+constexpr int kMaxChunks = 1024;
+
+__device__ __forceinline__ float block_max128(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return r;
+}
+
 __global__ __launch_bounds__(128) void prefix_reduce_kernel(ReduceParams p) {
+  __shared__ float wa[kMaxChunks];
+  __shared__ float wr[kMaxChunks + 1];
+  __shared__ float red[2];
   const int64_t row = blockIdx.x;
   const int h = static_cast<int>(row % p.hq);
   const int t = static_cast<int>(row / p.hq);
   if (p.mask && p.mask[h]) return;
   if (p.active && !p.active[t]) return;
-  const int c = threadIdx.x;
-  const bool has_c = c < p.d;
+  const int tid = threadIdx.x;
+  const int nc = p.n_chunks;
+  const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
+  const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
 
-  float M = kNegInf, Mr = kNegInf;
-  for (int ch = 0; ch < p.n_chunks; ++ch) M = fmaxf(M, p.part_l[ch * p.rows + row]);
-  if (p.part_rl)
-    for (int ch = 0; ch < p.n_chunks; ++ch) Mr = fmaxf(Mr, p.part_rl[ch * p.rows + row]);
-  if (p.res_l) Mr = fmaxf(Mr, p.res_l[row]);
+  float m = kNegInf, mr = kNegInf;
+  for (int ch = tid; ch < nc; ch += 128) m = fmaxf(m, p.part_l[ch * p.rows + row]);
+  for (int ch = tid; ch < nr; ch += 128) mr = fmaxf(mr, p.part_rl[ch * p.rows + row]);
+  if (cached && tid == 0) mr = fmaxf(mr, p.res_l[row]);
+  const float M = block_max128(m, red);
+  const float Mr = block_max128(mr, red);
   const float Mall = fmaxf(M, Mr);
 
-  float S = 0.f, acc = 0.f, Sr = 0.f, accr = 0.f;
-  if (Mall != kNegInf) {
-    for (int ch = 0; ch < p.n_chunks; ++ch) {
-      const float L = p.part_l[ch * p.rows + row];
-      if (L == kNegInf) continue;
-      const float wgt = expf(L - Mall);
-      S += wgt;
-      if (has_c) acc += wgt * p.part_a[(ch * p.rows + row) * p.d + c];
-    }
-    if (p.part_rl) {
-      for (int ch = 0; ch < p.n_chunks; ++ch) {
-        const float L = p.part_rl[ch * p.rows + row];
-        if (L == kNegInf) continue;
-        const float wgt = expf(L - Mr);
-        Sr += wgt;
-        if (has_c) accr += wgt * p.part_ra[(ch * p.rows + row) * p.d + c];
-      }
-    }
-    if (p.res_l) {
-      const float L = p.res_l[row];
-      if (L != kNegInf) {
-        const float wgt = expf(L - Mr);
-        Sr += wgt;
-        if (has_c) accr += wgt * p.res_a[row * p.d + c];
-      }
-    }
+  for (int ch = tid; ch < nc; ch += 128) {
+    const float L = p.part_l[ch * p.rows + row];
+    wa[ch] = L == kNegInf ? 0.f : expf(L - Mall);
   }
-  // residual-only pair, then fold it into the full pair (same composition)
-  if (p.a_res) {
-    if (has_c) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
-    if (c == 0) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+  for (int ch = tid; ch < nr; ch += 128) {
+    const float L = p.part_rl[ch * p.rows + row];
+    wr[ch] = L == kNegInf ? 0.f : expf(L - Mr);
   }
-  if (Mr != kNegInf) {
-    const float wr = expf(Mr - Mall);
-    S += Sr * wr;
-    acc += accr * wr;
+  if (cached && tid == 0) {
+    const float L = p.res_l[row];
+    wr[nr] = L == kNegInf ? 0.f : expf(L - Mr);
   }
-  if (has_c) p.a_out[row * p.d + c] = Mall != kNegInf ? acc / S : 0.f;
-  if (c == 0) p.l_out[row] = Mall != kNegInf ? Mall + logf(S) : kNegInf;
+  __syncthreads();
+  const int nrt = nr + (cached ? 1 : 0);
+  float S = 0.f, Sr = 0.f;                         // same order in every thread
+  for (int ch = 0; ch < nc; ++ch) S += wa[ch];
+  for (int ch = 0; ch < nrt; ++ch) Sr += wr[ch];
+
+  const int c = tid;
+  if (c < p.d) {
+    float acc = 0.f, accr = 0.f;
+    const float* pa = p.part_a + row * p.d + c;
+    const int64_t cs = p.rows * p.d;               // chunk stride
+    int ch = 0;
+    for (; ch + 8 <= nc; ch += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pa[(ch + u) * cs];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wa[ch + u] * v[u];
+    }
+    for (; ch < nc; ++ch) acc += wa[ch] * pa[ch * cs];
+    if (nr) {
+      const float* pr = p.part_ra + row * p.d + c;
+      for (ch = 0; ch < nr; ++ch) accr += wr[ch] * pr[ch * cs];
+    }
+    if (cached) accr += wr[nr] * p.res_a[row * p.d + c];
+    if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
+    // fold the residual pair into the full pair (same composition)
+    const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+    const float Stot = S + Sr * wrr;
+    p.a_out[row * p.d + c] = Mall != kNegInf ? (acc + accr * wrr) / Stot : 0.f;
+  }
+  if (tid == 0) {
+    if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+    const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+    p.l_out[row] = Mall != kNegInf ? Mall + logf(S + Sr * wrr) : kNegInf;
+  }
 }
 
 __global__ __launch_bounds__(128) void prefix_empty_kernel(float* a, float* l, int hq, int d,
@@ -588,13 +635,16 @@ hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipS
   return hipGetLastError();
 }
 
+int prefix_mfma_occupancy(int row_blocks) { return row_blocks == 1 ? FB_PREFIX_OCC_R1 : 1; }
+
 hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s) {
-  const int rows = p.n_q * p.group;
-  dim3 grid(p.n_chunks, p.hkv, (rows + 63) / 64);
+  const int n_cg = p.n_chunks * p.hkv;
+  dim3 grid(static_cast<unsigned>((n_cg + 7) / 8 * 8 * p.n_slabs));
   if (row_blocks == 1)
-    hipLaunchKernelGGL((prefix_mfma_kernel<1, FB_PREFIX_DEPTH_R1>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prefix_mfma_kernel<1, FB_PREFIX_DEPTH_R1, FB_PREFIX_OCC_R1>), grid,
+                       dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((prefix_mfma_kernel<2, FB_PREFIX_DEPTH_R2>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prefix_mfma_kernel<2, FB_PREFIX_DEPTH_R2, 1>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
