@@ -32,6 +32,9 @@ namespace {
 #ifndef FB_PREFIX_SLAB_ROWS
 #define FB_PREFIX_SLAB_ROWS 64    // 32: query rows in 32-row slabs (one MFMA row block each)
 #endif
+#ifndef FB_PREFIX_PAIR
+#define FB_PREFIX_PAIR 1          // 64-row slabs use the row-split (wave pair) kernel
+#endif
 constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights in LDS
 constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
 constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
@@ -113,6 +116,7 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   if (pl.path == PATH_MFMA) {
     pl.row_blocks = (group_rows <= 32 || FB_PREFIX_SLAB_ROWS == 32) ? 1 : 2;
     pl.n_slabs = static_cast<int>((group_rows + 32 * pl.row_blocks - 1) / (32 * pl.row_blocks));
+    if (pl.row_blocks == 2 && FB_PREFIX_PAIR) pl.row_blocks = 3;   // kernel selector
     wg_per_chunk = s.n_kv_heads * pl.n_slabs;
     min_tiles = kMinTilesMfma;
   } else {

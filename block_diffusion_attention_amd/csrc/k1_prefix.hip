@@ -227,6 +227,94 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
 
+// One 32-token tile for NRB 32-row blocks: S^T = K . Q^T on MFMA, the online
+// softmax per row (lane pair l, l^32), O^T += V^T . P^T with the weights as
+// bf16 hi + lo parts (two MFMAs: ~2^-17 relative instead of bf16's 2^-9; the
+// row sum l is accumulated from the fp32 weights). `valid` = tokens of the
+// tile that exist (scores of the others are masked). k_rd / v_rd are this
+// lane's LDS operand addresses (see the kernels for the layout).
+template <int NRB>
+__device__ __forceinline__ void tile_compute(f32x16 (&o)[NRB][4], float (&m_run)[NRB],
+                                             float (&l_run)[NRB], const bf16x8 (&qop)[NRB][8],
+                                             const char* k_rd, const char* v_rd, float scale_log2,
+                                             int64_t valid, int hl) {
+  // S^T = K . Q^T
+  f32x16 s[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_rd + 32 * kk);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) s[rb] = mfma32(ka, qop[rb][kk], s[rb]);
+  }
+
+  // online softmax per row (= lane pair l, l^32); weights enter P.V as
+  // bf16 hi + lo parts (two MFMAs: ~2^-17 relative instead of bf16's
+  // 2^-9), the row sum l is accumulated from the fp32 weights.
+  bf16x8 pbh[NRB][2], pbl[NRB][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    float x[16];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = s[rb][i] * scale_log2;
+      if (valid < kTile) {
+        const int tk = 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (tk >= valid) x[i] = kNegInf;
+      }
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool bump = mx > m_run[rb] + kRescaleLog2;
+    float alpha = 1.f;
+    if (bump) {
+      alpha = fast_exp2(m_run[rb] - mx);
+      m_run[rb] = mx;
+    }
+    const float muse = m_run[rb] == kNegInf ? 0.f : m_run[rb];
+    float psum = 0.f;
+#pragma unroll
+    for (int hj = 0; hj < 2; ++hj) {
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf[e] = fast_exp2(x[8 * hj + e] - muse);
+        psum += pf[e];
+      }
+      const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
+      pbh[rb][hj] = hi;
+      pbl[rb][hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
+    }
+    l_run[rb] = l_run[rb] * alpha + psum;
+    if (__any(bump)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
+    }
+  }
+
+  // O^T += V^T . P^T
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x4 v0 = ds_read_tr(v_rd + (16 * j) * kVRow + 64 * db);
+      const bf16x4 v1 = ds_read_tr(v_rd + (16 * j + 8) * kVRow + 64 * db);
+      // whole-vector concatenation (element-wise inserts of the
+      // transposed halves were mis-lowered by the compiler)
+      const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        o[rb][db] = mfma32(va, pbh[rb][j], o[rb][db]);
+        o[rb][db] = mfma32(va, pbl[rb][j], o[rb][db]);
+      }
+    }
+  }
+
+  asm volatile("" ::: "memory");
+}
+
 template <int NRB, int DEPTH, int OCC>
 __global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
   constexpr int RP = 32 * NRB;                     // padded rows per slab
@@ -355,82 +443,7 @@ __global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
   };
 
   auto process = [&](int64_t tile) {
-    // S^T = K . Q^T
-    f32x16 s[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) s[rb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_rd + 32 * kk);
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) s[rb] = mfma32(ka, qop[rb][kk], s[rb]);
-    }
-
-    // online softmax per row (= lane pair l, l^32); weights enter P.V as
-    // bf16 hi + lo parts (two MFMAs: ~2^-17 relative instead of bf16's
-    // 2^-9), the row sum l is accumulated from the fp32 weights.
-    const int64_t valid = p.n_kv - tile * kTile;   // >= 1
-    bf16x8 pbh[NRB][2], pbl[NRB][2];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      float x[16];
-      float mx = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = s[rb][i] * p.scale_log2;
-        if (valid < kTile) {
-          const int tk = 8 * (i >> 2) + 4 * hl + (i & 3);
-          if (tk >= valid) x[i] = kNegInf;
-        }
-        mx = fmaxf(mx, x[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool bump = mx > m_run[rb] + kRescaleLog2;
-      float alpha = 1.f;
-      if (bump) {
-        alpha = fast_exp2(m_run[rb] - mx);
-        m_run[rb] = mx;
-      }
-      const float muse = m_run[rb] == kNegInf ? 0.f : m_run[rb];
-      float psum = 0.f;
-#pragma unroll
-      for (int hj = 0; hj < 2; ++hj) {
-        f32x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pf[e] = fast_exp2(x[8 * hj + e] - muse);
-          psum += pf[e];
-        }
-        const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
-        pbh[rb][hj] = hi;
-        pbl[rb][hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
-      }
-      l_run[rb] = l_run[rb] * alpha + psum;
-      if (__any(bump)) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[rb][db] *= alpha;
-      }
-    }
-
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x4 v0 = ds_read_tr(v_rd + (16 * j) * kVRow + 64 * db);
-        const bf16x4 v1 = ds_read_tr(v_rd + (16 * j + 8) * kVRow + 64 * db);
-        // whole-vector concatenation (element-wise inserts of the
-        // transposed halves were mis-lowered by the compiler)
-        const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          o[rb][db] = mfma32(va, pbh[rb][j], o[rb][db]);
-          o[rb][db] = mfma32(va, pbl[rb][j], o[rb][db]);
-        }
-      }
-    }
-
-    asm volatile("" ::: "memory");
+    tile_compute<NRB>(o, m_run, l_run, qop, k_rd, v_rd, p.scale_log2, p.n_kv - tile * kTile, hl);
   };
 
   // Steady state: whole iterations only, so every stage is consumed and
@@ -513,6 +526,200 @@ __global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
       const float mw = ml_s[ww][r][0];
       if (mw != kNegInf) tot += ml_s[ww][r][1] * fast_exp2(mw - M);
     }
+    const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows +
+                         static_cast<int64_t>(t) * p.hq + h;
+    p.out.l[orow] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-split MFMA prefix kernel: 33..64 query rows per KV head (a 16-token block
+// of a 4:1 grouped-query model has 64). A 4-wave workgroup forms two pairs;
+// each pair streams alternate tiles of the chunk into its own double-buffered
+// LDS region -- one wave of the pair stages the tile's K, the other its V --
+// and each wave of the pair computes 32 of the 64 rows from the shared tile.
+// One barrier per tile orders the stores of tile k against the reads of tile
+// k-1 of the other buffer. Per-wave state is that of 32 rows, so two
+// workgroups fit per CU (8 waves), and every K/V byte still crosses HBM once.
+// ---------------------------------------------------------------------------
+#ifndef FB_PREFIX_DEPTH_PAIR
+#define FB_PREFIX_DEPTH_PAIR 1    // half-tiles in flight per wave
+#endif
+#ifndef FB_PREFIX_OCC_PAIR
+#define FB_PREFIX_OCC_PAIR 2      // workgroups per CU
+#endif
+constexpr int kPairBuf = kKBytes + kVBytes;       // one K+V tile in LDS
+
+struct HalfTile {          // the K (or V) half of a tile: 8 row-loads per lane
+  u32x4 r[8];
+};
+
+template <int DEPTH, int OCC>
+__global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
+  constexpr int kStageBytes = 4 * kPairBuf;        // 2 pairs x 2 buffers
+  constexpr int kMergeStride = kD + 1;
+  constexpr int kMergeBytes = 4 * 32 * kMergeStride * 4;
+  constexpr int kLdsBytes = kMergeBytes > kStageBytes ? kMergeBytes : kStageBytes;
+  constexpr int U = 2 * DEPTH;                     // unroll: static stage and buffer index
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  __shared__ float ml_s[4][32][2];
+
+  int chunk, g, slab;
+  {
+    const int id = blockIdx.x;
+    const int tq = id >> 3;
+    slab = tq % p.n_slabs;
+    const int idx = (tq / p.n_slabs) * 8 + (id & 7);
+    if (idx >= p.n_chunks * p.hkv) return;
+    chunk = idx % p.n_chunks;
+    g = idx / p.n_chunks;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w >> 1, hr = w & 1;             // tile stream, row block / K-or-V role
+  const int hl = lane >> 5, r32 = lane & 31;
+  const int G = p.group;
+  const int R = p.n_q * G;
+  const int row0 = slab * 64;
+
+  if (p.mask) {
+    bool all = true;
+    for (int j = 0; j < G; ++j) all = all && p.mask[g * G + j] != 0;
+    if (all) return;
+  }
+
+  bf16x8 qop[1][8];
+  {
+    const int r = row0 + 32 * hr + r32;
+    const bool ok = r < R;
+    const int t = ok ? r / G : 0, jh = ok ? r % G : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(t) * p.q_st +
+                         static_cast<int64_t>(g * G + jh) * p.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qop[0][kk] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl) : bf16x8{};
+  }
+
+  const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
+  const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
+  const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
+  if (t_begin >= t_end) return;
+  const int64_t t_last = t_end - 1;
+  const int64_t n_iter = (t_end - t_begin + 1) / 2;   // tiles per pair, rounded up
+
+  // LDS: pair region = 2 buffers x (K tile, V tile)
+  char* pbase = lds + pair * 2 * kPairBuf;
+  const int lrow = lane >> 4, lpiece = lane & 15;
+  const int grp = lane >> 4, s4 = (lane & 15) >> 2, q4 = lane & 3;
+  const int wrow_bytes = hr == 0 ? kKRow : kVRow;
+  char* wr = pbase + (hr == 0 ? 0 : kKBytes) + lrow * wrow_bytes + lpiece * 16;
+  const char* k_rd = pbase + r32 * kKRow + hl * 16;
+  const char* v_rd = pbase + kKBytes + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
+
+  const char* src = static_cast<const char*>(hr == 0 ? p.k : p.v) +
+                    static_cast<int64_t>(g) * p.kv_sh * 2;
+  const int64_t kvst_b = p.kv_st * 2;
+  const uint32_t voff = static_cast<uint32_t>(lrow * kvst_b) + lpiece * 16;
+
+  auto load_half = [&](int64_t it) -> HalfTile {   // this wave's half of pair tile `it`
+    HalfTile r;
+    int64_t tile = t_begin + 2 * it + pair;
+    tile = tile < t_last ? tile : t_last;
+    const int64_t tok0 = tile * kTile;
+    const char* b = src + tok0 * kvst_b;
+    if (tok0 + kTile <= p.n_kv) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r.r[i] = ldnt(b + 4 * i * kvst_b + voff);
+    } else {
+      const int64_t last = p.n_kv - 1 - tok0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t rr = 4 * i + lrow < last ? 4 * i + lrow : last;
+        r.r[i] = ldnt(b + rr * kvst_b + lpiece * 16);
+      }
+    }
+    return r;
+  };
+
+  f32x16 o[1][4];
+  float m_run[1] = {kNegInf}, l_run[1] = {0.f};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[0][db] = f32x16{};
+
+  HalfTile stage[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) stage[d] = load_half(d);
+
+  auto iteration = [&](int u, int64_t it) {      // u static: stage u % DEPTH, buffer u % 2
+    const int boff = (u & 1) * kPairBuf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(wr + boff + 4 * i * wrow_bytes) = stage[u % DEPTH].r[i];
+    stage[u % DEPTH] = load_half(it + DEPTH);
+    __syncthreads();
+    const int64_t tile = t_begin + 2 * it + pair;
+    if (tile < t_end)
+      tile_compute<1>(o, m_run, l_run, qop, k_rd + boff, v_rd + boff, p.scale_log2,
+                      p.n_kv - tile * kTile, hl);
+  };
+
+  int64_t it = 0;
+  for (; it + U <= n_iter; it += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) iteration(u, it + u);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (it + u < n_iter) iteration(u, it + u);      // workgroup-uniform
+
+  // ---- merge the two tile streams of each row block, write the partial ----
+  l_run[0] += __shfl_xor(l_run[0], 32, 64);
+  __syncthreads();
+  if (hl == 0) {
+    ml_s[w][r32][0] = m_run[0];
+    ml_s[w][r32][1] = l_run[0];
+  }
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(lds);
+  {
+    const int wo = w ^ 2;                            // the other stream, same rows
+    const float ma = ml_s[w][r32][0], mb = ml_s[wo][r32][0];
+    const float M = fmaxf(ma, mb);
+    float tot = 0.f;
+    if (ma != kNegInf) tot += ml_s[w][r32][1] * fast_exp2(ma - M);
+    if (mb != kNegInf) tot += ml_s[wo][r32][1] * fast_exp2(mb - M);
+    const float f = (m_run[0] == kNegInf || tot == 0.f) ? 0.f : fast_exp2(m_run[0] - M) / tot;
+    float* dst = mg + (w * 32 + r32) * kMergeStride;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[32 * db + 8 * (i >> 2) + 4 * hl + (i & 3)] = o[0][db][i] * f;
+  }
+  __syncthreads();
+
+  const int rows_here = R - row0 < 64 ? R - row0 : 64;
+  for (int e = tid; e < rows_here * kD; e += 256) {
+    const int r = e / kD, c = e % kD;
+    const int rr = row0 + r;
+    const int t = rr / G, jh = rr % G, h = g * G + jh;
+    if (p.mask && p.mask[h]) continue;
+    const int wa = r >> 5, rl = r & 31;            // waves wa and wa + 2 hold this row
+    const float sum = mg[(wa * 32 + rl) * kMergeStride + c] + mg[((wa + 2) * 32 + rl) * kMergeStride + c];
+    const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows +
+                         static_cast<int64_t>(t) * p.hq + h;
+    p.out.a[orow * kD + c] = sum;
+  }
+  for (int r = tid; r < rows_here; r += 256) {
+    const int rr = row0 + r;
+    const int t = rr / G, jh = rr % G, h = g * G + jh;
+    if (p.mask && p.mask[h]) continue;
+    const int wa = r >> 5, rl = r & 31;
+    const float ma = ml_s[wa][rl][0], mb = ml_s[wa + 2][rl][0];
+    const float M = fmaxf(ma, mb);
+    float tot = 0.f;
+    if (ma != kNegInf) tot += ml_s[wa][rl][1] * fast_exp2(ma - M);
+    if (mb != kNegInf) tot += ml_s[wa + 2][rl][1] * fast_exp2(mb - M);
     const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows +
                          static_cast<int64_t>(t) * p.hq + h;
     p.out.l[orow] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
@@ -635,13 +842,18 @@ hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipS
   return hipGetLastError();
 }
 
-int prefix_mfma_occupancy(int row_blocks) { return row_blocks == 1 ? FB_PREFIX_OCC_R1 : 1; }
+int prefix_mfma_occupancy(int row_blocks) {
+  return row_blocks == 1 ? FB_PREFIX_OCC_R1 : (row_blocks == 3 ? FB_PREFIX_OCC_PAIR : 1);
+}
 
 hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s) {
   const int n_cg = p.n_chunks * p.hkv;
   dim3 grid(static_cast<unsigned>((n_cg + 7) / 8 * 8 * p.n_slabs));
   if (row_blocks == 1)
     hipLaunchKernelGGL((prefix_mfma_kernel<1, FB_PREFIX_DEPTH_R1, FB_PREFIX_OCC_R1>), grid,
+                       dim3(256), 0, s, p);
+  else if (row_blocks == 3)        // 64-row slabs split over wave pairs
+    hipLaunchKernelGGL((prefix_pair_kernel<FB_PREFIX_DEPTH_PAIR, FB_PREFIX_OCC_PAIR>), grid,
                        dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((prefix_mfma_kernel<2, FB_PREFIX_DEPTH_R2, 1>), grid, dim3(256), 0, s, p);
