@@ -31,6 +31,32 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_pass_traffic.json")
+KERNEL_SOURCES = ("block_diffusion_attention_amd/csrc/k1_prefix.hip",
+                  "block_diffusion_attention_amd/csrc/fb_host.hip")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(n_prefix, block):
+    """HBM bytes per prefix pass from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources and this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (t.get("kernel_source_sha256") != kernel_source_hash()
+            or t.get("n_prefix") != n_prefix or t.get("block") != block):
+        return None
+    return t.get("traffic_bytes_per_pass")
 
 
 def parse():
@@ -46,7 +72,8 @@ def parse():
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
     ap.add_argument("--prefix-only", action="store_true",
                     help="profiling mode: run the prefix pass --roofline-reps times, then "
-                         "a 1 GiB device copy (counter calibration); prints a short JSON")
+                         "a 1 GiB read + 1 GiB write elementwise kernel (counter "
+                         "calibration); prints a short JSON")
     return ap.parse_args()
 
 
@@ -210,7 +237,7 @@ def main():
                    "recompute_steps": n_compute},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(N, B),
                      "kernel": "prefix pass (prefix_mfma_kernel + prefix_reduce_kernel)",
                      "alg_bytes_per_launch": alg_bytes},
         "extra": extra,
@@ -229,6 +256,8 @@ def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):
     l_out = torch.empty(B, hq, device=dev)
     ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, B, N), 16), dtype=torch.uint8,
                      device=dev)
+    for _ in range(3):
+        fb.fb_prefix_attn(shape, q0, k_dev, v_dev, a_out, l_out, ws=ws, stream=stream)
     torch.cuda.synchronize()
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     r0.record(stream)
@@ -237,12 +266,13 @@ def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):
     r1.record(stream)
     torch.cuda.synchronize()
     t = r0.elapsed_time(r1) / args.roofline_reps * 1e-3
-    # calibration: a plain device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)
+    # counter calibration: an elementwise kernel that reads exactly 1 GiB and
+    # writes exactly 1 GiB (torch.add on uint8; the fill writes 1 GiB)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1)
     for _ in range(3):
-        dst.copy_(src)
+        torch.add(src, 1, out=dst)
     torch.cuda.synchronize()
     alg = N * hkv * d * 4 + B * hq * d * 2 + B * hq * (d + 1) * 4
     print(json.dumps({"prefix_pass_us": round(t * 1e6, 2), "alg_bytes": alg,
