@@ -35,18 +35,25 @@ namespace {
 #ifndef FB_PREFIX_PAIR
 #define FB_PREFIX_PAIR 1          // 64-row slabs use the row-split (wave pair) kernel
 #endif
+#ifndef FB_ROWS_MIN_ROWS
+#define FB_ROWS_MIN_ROWS 128      // query rows per KV head from which the many-rows kernel runs
+#endif
+#ifndef FB_ROWS_MIN_TILES
+#define FB_ROWS_MIN_TILES 32      // 32-key tiles per chunk of the many-rows kernel
+#endif
 constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights in LDS
 constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
 constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
 constexpr int64_t kMinTilesGeneric = 4;   // 64-token tiles per chunk
 constexpr size_t kAlign = 256;
 
-enum Path { PATH_GENERIC = 0, PATH_MFMA = 1 };
+enum Path { PATH_GENERIC = 0, PATH_MFMA = 1, PATH_ROWS = 2 };
 
 struct PrefixPlan {
   int path = PATH_GENERIC;
   int row_blocks = 1;
   int n_slabs = 1;
+  int n_rtiles = 1;            // PATH_ROWS: row tiles per KV head
   int n_chunks = 0;
   int64_t tiles_per_chunk = 0;
   bool direct = false;         // one chunk, written straight to the outputs
@@ -56,6 +63,8 @@ struct PrefixPlan {
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// The MFMA kernels address 32 token rows of a tile as 32-bit byte offsets.
+bool offsets32(const fb_tensor& t) { return t.stride_tok < (int64_t(1) << 25); }
 
 fb_status check_shape(const fb_attn_shape* s) {
   if (!s) return FB_ERR_INVALID_ARGUMENT;
@@ -107,7 +116,8 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   pl.rows = n_q * s.n_q_heads;
   pl.path = (s.dtype == FB_BF16 && s.head_dim == 128 && mode == FB_SEL_DENSE) ? PATH_MFMA
                                                                              : PATH_GENERIC;
-  const int tile = prefix_tile_tokens(pl.path);
+  if (pl.path == PATH_MFMA && group_rows >= FB_ROWS_MIN_ROWS) pl.path = PATH_ROWS;
+  const int tile = pl.path == PATH_ROWS ? 32 : prefix_tile_tokens(pl.path);
   const int64_t n_virt = mode == FB_SEL_GATHER ? static_cast<int64_t>(sel->k_pages) * sel->page_size
                                                : n_kv;
   const int64_t n_tiles = (n_virt + tile - 1) / tile;
@@ -119,12 +129,18 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
     if (pl.row_blocks == 2 && FB_PREFIX_PAIR) pl.row_blocks = 3;   // kernel selector
     wg_per_chunk = s.n_kv_heads * pl.n_slabs;
     min_tiles = kMinTilesMfma;
+  } else if (pl.path == PATH_ROWS) {
+    pl.n_rtiles = static_cast<int>((group_rows + rows_tile_rows() - 1) / rows_tile_rows());
+    wg_per_chunk = s.n_kv_heads * static_cast<int64_t>(pl.n_rtiles);
+    min_tiles = FB_ROWS_MIN_TILES;
   } else {
     wg_per_chunk = pl.rows;
     min_tiles = kMinTilesGeneric;
   }
   if (n_tiles > 0) {
-    const int64_t occ = pl.path == PATH_MFMA ? prefix_mfma_occupancy(pl.row_blocks) : 1;
+    const int64_t occ = pl.path == PATH_MFMA   ? prefix_mfma_occupancy(pl.row_blocks)
+                        : pl.path == PATH_ROWS ? rows_occupancy()
+                                               : 1;
     int64_t want = kTargetWorkgroups * occ / wg_per_chunk;
     if (want < 1) want = 1;
     if (want > kMaxChunks) want = kMaxChunks;
@@ -199,10 +215,37 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   }
   // K and V share strides in the kernels
   if (v.stride_tok != k.stride_tok || v.stride_head != k.stride_head) return FB_ERR_UNSUPPORTED;
+  if (pl.path != PATH_GENERIC && !offsets32(k)) return FB_ERR_UNSUPPORTED;
 
   if (pl.n_chunks > 0) {
-    hipError_t e = pl.path == PATH_MFMA ? launch_prefix_mfma(pp, pl.row_blocks, stream)
-                                        : launch_prefix_generic(pp, s.dtype, s.head_dim, stream);
+    hipError_t e;
+    if (pl.path == PATH_ROWS) {
+      RowsParams rp;
+      memset(&rp, 0, sizeof(rp));
+      rp.q = q.ptr;
+      rp.q_st = q.stride_tok;
+      rp.q_sh = q.stride_head;
+      rp.k = k.ptr;
+      rp.v = v.ptr;
+      rp.k_st = rp.v_st = k.stride_tok;
+      rp.k_sh = rp.v_sh = k.stride_head;
+      rp.n_kv = n_kv;
+      rp.n_q = static_cast<int>(n_q);
+      rp.hq = s.n_q_heads;
+      rp.hkv = s.n_kv_heads;
+      rp.group = pp.group;
+      rp.scale_log2 = pp.scale_log2;
+      rp.mask = mask;
+      rp.n_rtiles = pl.n_rtiles;
+      rp.tiles_per_chunk = pl.tiles_per_chunk;
+      rp.n_chunks = pl.n_chunks;
+      rp.n_items = s.n_kv_heads * pl.n_chunks * pl.n_rtiles;
+      rp.out = pp.out;
+      e = launch_rows(rp, stream);
+    } else {
+      e = pl.path == PATH_MFMA ? launch_prefix_mfma(pp, pl.row_blocks, stream)
+                               : launch_prefix_generic(pp, s.dtype, s.head_dim, stream);
+    }
     if (e != hipSuccess) return FB_ERR_DEVICE;
   }
   if (pl.direct) return FB_OK;
@@ -303,6 +346,41 @@ fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk, fb_te
   if ((st = check_tensor(k_blk, q_blk.n_tok, shape->n_kv_heads, d)) != FB_OK) return st;
   if ((st = check_tensor(v_blk, q_blk.n_tok, shape->n_kv_heads, d)) != FB_OK) return st;
   if (!a_out || !l_out || !a_full) return FB_ERR_INVALID_ARGUMENT;
+  if (q_blk.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
+  const int G = shape->n_q_heads / shape->n_kv_heads;
+  if (shape->dtype == FB_BF16 && d == 128 && q_blk.n_tok * G >= FB_ROWS_MIN_ROWS) {
+    // many rows: MFMA pass with the merge in its epilogue (16-byte row access)
+    if (!aligned16(a_out) || !aligned16(a_full) || (a_in && !aligned16(a_in)))
+      return FB_ERR_INVALID_ARGUMENT;
+    if (!offsets32(k_blk) || !offsets32(v_blk)) return FB_ERR_UNSUPPORTED;
+    RowsParams rp;
+    memset(&rp, 0, sizeof(rp));
+    rp.q = q_blk.ptr;
+    rp.q_st = q_blk.stride_tok;
+    rp.q_sh = q_blk.stride_head;
+    rp.k = k_blk.ptr;
+    rp.v = v_blk.ptr;
+    rp.k_st = k_blk.stride_tok;
+    rp.k_sh = k_blk.stride_head;
+    rp.v_st = v_blk.stride_tok;
+    rp.v_sh = v_blk.stride_head;
+    rp.n_kv = q_blk.n_tok;
+    rp.n_q = static_cast<int>(q_blk.n_tok);
+    rp.hq = shape->n_q_heads;
+    rp.hkv = shape->n_kv_heads;
+    rp.group = G;
+    rp.scale_log2 = shape->scale * kLog2e;
+    rp.n_rtiles = static_cast<int>((q_blk.n_tok * G + rows_tile_rows() - 1) / rows_tile_rows());
+    rp.n_chunks = 1;
+    rp.tiles_per_chunk = (q_blk.n_tok + 31) / 32;
+    rp.n_items = shape->n_kv_heads * rp.n_rtiles;
+    rp.out = RowOut{a_full, l_full, 0};
+    rp.a_prev = a_out;
+    rp.l_prev = l_out;
+    rp.a_raw = a_in;
+    rp.l_raw = l_in;
+    return dev(launch_rows(rp, stream));
+  }
   if (q_blk.n_tok > 65535) return FB_ERR_UNSUPPORTED;
   BlockParams bp;
   memset(&bp, 0, sizeof(bp));

@@ -80,6 +80,26 @@ struct BlockParams {
 };
 hipError_t launch_block_small(const BlockParams& p, fb_dtype dt, hipStream_t s);
 
+// many query rows per KV head (prefill regime, bf16, d = 128): either pass
+struct RowsParams {
+  const void* q; int64_t q_st, q_sh;
+  const void* k; const void* v; int64_t k_st, k_sh, v_st, v_sh;
+  int64_t n_kv;                 // >= 1
+  int n_q, hq, hkv, group;
+  float scale_log2;             // scale * log2(e)
+  const uint8_t* mask;          // [Hq] nullable, 1 = skip (rows of that head not written)
+  int n_rtiles;                 // row tiles per (KV head, chunk)
+  int64_t tiles_per_chunk;      // 32-key tiles per chunk
+  int n_chunks;
+  int n_items;                  // hkv * n_chunks * n_rtiles
+  RowOut out;                   // plain: A, L (direct or partials); merge: A_full, L_full
+  const float* a_prev; const float* l_prev;   // merge epilogue: cached pair (null = plain)
+  float* a_raw; float* l_raw;   // merge epilogue: optional fresh (A_in, L_in)
+};
+int rows_tile_rows();           // query rows per workgroup
+int rows_occupancy();           // workgroups per CU the kernel is built for
+hipError_t launch_rows(const RowsParams& p, hipStream_t s);
+
 // decisions
 hipError_t launch_count(const int32_t* ids_prev, const int32_t* ids_cur, int n_q,
                         int tau, int force, int hq, uint8_t* mask, int32_t* m_count,

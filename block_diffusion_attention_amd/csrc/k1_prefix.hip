@@ -229,7 +229,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
 
 // One 32-token tile for NRB 32-row blocks: S^T = K . Q^T on MFMA, the online
 // softmax per row (lane pair l, l^32), O^T += V^T . P^T with the weights as
-// bf16 hi + lo parts (two MFMAs: ~2^-17 relative instead of bf16's 2^-9; the
+// bf16 hi + lo parts (two MFMAs: ~2^-16 relative instead of bf16's 2^-8; the
 // row sum l is accumulated from the fp32 weights). `valid` = tokens of the
 // tile that exist (scores of the others are masked). k_rd / v_rd are this
 // lane's LDS operand addresses (see the kernels for the layout).
@@ -250,8 +250,8 @@ __device__ __forceinline__ void tile_compute(f32x16 (&o)[NRB][4], float (&m_run)
   }
 
   // online softmax per row (= lane pair l, l^32); weights enter P.V as
-  // bf16 hi + lo parts (two MFMAs: ~2^-17 relative instead of bf16's
-  // 2^-9), the row sum l is accumulated from the fp32 weights.
+  // bf16 hi + lo parts (two MFMAs: ~2^-16 relative instead of bf16's
+  // 2^-8), the row sum l is accumulated from the fp32 weights.
   bf16x8 pbh[NRB][2], pbl[NRB][2];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {

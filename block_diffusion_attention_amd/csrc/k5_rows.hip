@@ -1,0 +1,397 @@
+// k5_rows.hip -- attention for many query rows per KV head on MFMA (bf16,
+// d = 128): the prefill regime of both passes of the step when a block holds
+// thousands of queries (video generation), so that every K/V tile is reused
+// by many rows and the work is bound by matrix throughput, not by HBM.
+//   * the block-external pass over J_out: A_out and L_out = ln Z_out per row,
+//     direct or as split-K partials for the fixed-order reduce (FlashBlock
+//     technical summary, s2 "core mechanism");
+//   * the block-internal pass over J_in with the log-space composition of the
+//     cached pair and the fresh one in its epilogue (s2, the A_full equation).
+//
+// Workgroup = NW waves = (KV head g, key chunk, row tile of 32 NW rows), one
+// 32-row block per wave. Rows are (query token, query head of the group)
+// pairs r = t*G + j, so grouped heads share every K/V tile. The waves share
+// each 32-key K/V tile, staged global -> VGPR -> LDS with one barrier per
+// tile; each wave keeps the online-softmax state of its rows over the whole
+// key range of its chunk, and runs a software pipeline over the tiles: the
+// softmax of tile t (VALU) is interleaved with S(t+1) = QK(t+1) and
+// O += P(t-1).V(t-1) (matrix core). Per tile and wave:
+//   S^T[32 keys x 32 rows] = K . Q^T     (v_mfma_f32_32x32x16_bf16, 8 k-steps;
+//       each lane owns one row and 16 of its scores)
+//   O^T[128 dims x 32 rows] += V^T . P^T (P^T = the weights as bf16 hi + lo
+//       parts, V^T from LDS by the transposing read ds_read_b64_tr_b16)
+// The row max is taken on raw scores (scale > 0) and folded into one FMA per
+// weight; it is raised only when a tile's max exceeds it by more than 2^8.
+#include "fb_internal.h"
+
+#include <math.h>
+
+namespace fb {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kTile = 32;                    // keys per tile
+constexpr int kD = 128;
+constexpr int kKRow = 272;                   // 17 x 16 B: 16 rows, 16 bank groups
+constexpr int kVRow = 320;                   // 20 x 16 B: 4 rows, 4 x 64 B bank spans
+constexpr int kKBytes = kTile * kKRow;
+constexpr int kVBytes = kTile * kVRow;
+constexpr int kStage = kKBytes + kVBytes;
+constexpr float kRescaleLog2 = 8.f;
+
+#ifndef FB_ROWS_VALU_PER
+#define FB_ROWS_VALU_PER 6        // VALU instructions issued after each MFMA of a tile
+#endif
+#ifndef FB_ROWS_WAVES
+#define FB_ROWS_WAVES 8           // waves (32 query rows each) per workgroup
+#endif
+#ifndef FB_ROWS_OCC
+#define FB_ROWS_OCC 1             // workgroups per CU the kernel is built for (register budget)
+#endif
+#ifndef FB_ROWS_PSPLIT
+#define FB_ROWS_PSPLIT 1          // weights as bf16 hi + lo in P.V (0: one bf16 part)
+#endif
+
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposing LDS read (gfx950): within each 16-lane group, "row" s is the
+// concatenation of the 4-element loads of lanes 4s..4s+3, and lane j receives
+// element j of rows 0..3.
+__device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
+  auto p = (const __attribute__((address_space(3))) char*)(lds_generic);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// S^T[32 keys x 32 rows] = K . Q^T for one tile; k_rd = this lane's K row.
+__device__ __forceinline__ f32x16 qk_tile(const char* k_rd, const bf16x8 (&qop)[8]) {
+  f32x16 s = {};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    s = mfma32(*reinterpret_cast<const bf16x8*>(k_rd + 32 * kk), qop[kk], s);
+  return s;
+}
+
+// O^T[128 x 32] += V^T . P^T for one tile; v_rd = this lane's transposing
+// read address. Consecutive MFMAs go to different accumulators.
+template <bool PSPLIT>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[4], const bf16x8 (&ph)[2],
+                                        const bf16x8 (&pl)[2], const char* v_rd) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bf16x8 va[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16x4 v0 = ds_read_tr(v_rd + (16 * j) * kVRow + 64 * db);
+      const bf16x4 v1 = ds_read_tr(v_rd + (16 * j + 8) * kVRow + 64 * db);
+      // whole-vector concatenation (element-wise inserts of the transposed
+      // halves were mis-lowered by the compiler)
+      va[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = mfma32(va[db], ph[j], o[db]);
+    if (PSPLIT) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma32(va[db], pl[j], o[db]);
+    }
+  }
+}
+
+// max over the lane pair (l, l ^ 32) that shares a row: one VALU lane swap
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Online softmax of one tile's scores (lane = row, 16 of its 32 keys):
+// weights p = 2^(c*s - m) with the running max m raised lazily (only when
+// the tile's max exceeds it by more than 2^8), the row sum l adds the fp32
+// weights, and P^T leaves as bf16 (PSPLIT: hi + lo parts, ~2^-16 relative,
+// instead of bf16's 2^-8). Rescales O when m moves. `valid` = keys of the
+// tile that exist; c = scale * log2(e).
+template <bool PSPLIT, bool MASKED>
+__device__ __forceinline__ void softmax_tile(f32x16 s, int valid, int hl, float c, float& m_run,
+                                             float& l_run, float& alpha, bool& bump,
+                                             bf16x8 (&ph)[2], bf16x8 (&pl)[2]) {
+  if (MASKED) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tk = 8 * (i >> 2) + 4 * hl + (i & 3);
+      s[i] = tk < valid ? s[i] : kNegInf;
+    }
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  mx = pair_max(mx) * c;
+  bump = mx > m_run + kRescaleLog2;
+  alpha = bump ? fast_exp2(m_run - mx) : 1.f;
+  m_run = bump ? mx : m_run;
+  const float nm = m_run == kNegInf ? 0.f : -m_run;
+  float psum = 0.f;
+#pragma unroll
+  for (int hj = 0; hj < 2; ++hj) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pf[e] = fast_exp2(__builtin_fmaf(s[8 * hj + e], c, nm));
+      psum += pf[e];
+    }
+    const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
+    ph[hj] = hi;
+    if (PSPLIT) pl[hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
+  }
+  l_run = l_run * alpha + psum;
+}
+
+// Issue order for one pipelined tile (one scheduling region): the operand
+// reads first, then every MFMA followed by a few VALU instructions of the
+// softmax, so the matrix core and the VALU work side by side in one wave.
+template <bool PSPLIT>
+__device__ __forceinline__ void tile_schedule() {
+  constexpr int kMfma = PSPLIT ? 24 : 16;
+  constexpr int kValuPer = FB_ROWS_VALU_PER;
+  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);        // K operands, V operands (j = 0)
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
+    if (i == 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // V operands (j = 1)
+  }
+}
+
+// Software pipeline over the key tiles of a chunk, per wave: while the
+// VALU runs the softmax of tile t, the matrix core runs S(t+1) = QK(t+1) and
+// O += P(t-1).V(t-1). LDS holds four tile stages: V(t-1) and K(t+1) being
+// read, tile t (its V is read next), and tile t+2 being written from the
+// registers that were loaded from global memory during the previous tile.
+template <int NW, int OCC, bool PSPLIT, bool MERGE>
+__global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
+  constexpr int RPT = 32 / (NW * 4);              // tile rows staged per thread
+  constexpr int kStages = 4;
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
+
+  // XCD-aware order: workgroup id i runs on XCD i mod 8, and XCD x takes the
+  // x-th contiguous range of work items, so the row tiles of one (KV head,
+  // chunk) run side by side on one XCD and share its L2 for the K/V tiles.
+  int rt, chunk, g;
+  {
+    const int id = blockIdx.x;
+    const int per = (p.n_items + 7) >> 3;
+    const int item = (id & 7) * per + (id >> 3);
+    if (item >= p.n_items) return;
+    rt = item % p.n_rtiles;
+    const int rest = item / p.n_rtiles;
+    chunk = rest % p.n_chunks;
+    g = rest / p.n_chunks;
+  }
+  const int G = p.group;
+  if (p.mask) {                                    // every head of the group reused?
+    bool all = true;
+    for (int j = 0; j < G; ++j) all = all && p.mask[g * G + j] != 0;
+    if (all) return;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, r32 = lane & 31;
+  const int R = p.n_q * G;
+  const int row = rt * (NW * 32) + w * 32 + r32;        // this lane's row
+
+  // Q^T operand: lane holds its row's dims 16 kk + 8 hl .. +8.
+  bf16x8 qop[8];
+  {
+    const bool ok = row < R;
+    const int t = ok ? row / G : 0, jh = ok ? row % G : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(t) * p.q_st +
+                         static_cast<int64_t>(g * G + jh) * p.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qop[kk] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl) : bf16x8{};
+  }
+
+  const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
+  const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
+  const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
+  const int64_t t_last = t_end - 1;                // every launched chunk has a tile
+
+  // staging: thread = (rows lr + 4 NW i of the tile, 16-byte piece lp)
+  const int lr = tid >> 4, lp = tid & 15;
+  const char* kg = static_cast<const char*>(p.k) + static_cast<int64_t>(g) * p.k_sh * 2;
+  const char* vg = static_cast<const char*>(p.v) + static_cast<int64_t>(g) * p.v_sh * 2;
+  const int64_t kst = p.k_st * 2, vst = p.v_st * 2;
+  const uint32_t koff = static_cast<uint32_t>(lr * kst) + lp * 16;
+  const uint32_t voff = static_cast<uint32_t>(lr * vst) + lp * 16;
+
+  // Every step refills the registers unconditionally (tiles past the chunk's
+  // last are clamped to it; keys past n_kv to the last key, masked in the
+  // scores), so each path through the loop issues the same loads.
+  u32x4 kr[RPT], vr[RPT];
+  auto load = [&](int64_t tile) {
+    tile = tile < t_last ? tile : t_last;
+    const int64_t tok0 = tile * kTile;
+    if (tok0 + kTile <= p.n_kv) {
+      const char* kb = kg + tok0 * kst;
+      const char* vb = vg + tok0 * vst;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        kr[i] = *reinterpret_cast<const u32x4*>(kb + (4 * NW * i) * kst + koff);
+        vr[i] = *reinterpret_cast<const u32x4*>(vb + (4 * NW * i) * vst + voff);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        int64_t tok = tok0 + lr + 4 * NW * i;
+        tok = tok < p.n_kv ? tok : p.n_kv - 1;
+        kr[i] = *reinterpret_cast<const u32x4*>(kg + tok * kst + lp * 16);
+        vr[i] = *reinterpret_cast<const u32x4*>(vg + tok * vst + lp * 16);
+      }
+    }
+  };
+  auto stage_of = [&](int64_t tile) -> char* {
+    return lds + (static_cast<int>(tile - t_begin) & (kStages - 1)) * kStage;
+  };
+  auto store = [&](int64_t tile) {
+    char* kl = stage_of(tile);
+    char* vl = kl + kKBytes;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      *reinterpret_cast<u32x4*>(kl + (lr + 4 * NW * i) * kKRow + lp * 16) = kr[i];
+      *reinterpret_cast<u32x4*>(vl + (lr + 4 * NW * i) * kVRow + lp * 16) = vr[i];
+    }
+  };
+  auto valid_of = [&](int64_t tile) -> int {
+    const int64_t rem = p.n_kv - tile * kTile;
+    return rem < kTile ? static_cast<int>(rem) : kTile;
+  };
+
+  // operand addresses within a stage
+  const int grp = lane >> 4, s4 = (lane & 15) >> 2, q4 = lane & 3;
+  const int k_rd = r32 * kKRow + hl * 16;
+  const int v_rd = kKBytes + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  bf16x8 ph[2] = {}, pl[2] = {};                   // P(t-1); zero before the first tile
+
+  // prologue: tiles t_begin, t_begin + 1 staged, t_begin + 2 in registers,
+  // the V part of stage (t_begin - 1) zeroed (the first PV adds P = 0 times it)
+  load(t_begin);
+  store(t_begin);
+  load(t_begin + 1);
+  store(t_begin + 1);
+  load(t_begin + 2);
+  {
+    char* vz = stage_of(t_begin - 1) + kKBytes;
+    for (int i = tid; i < kVBytes / 16; i += 64 * NW) *reinterpret_cast<u32x4*>(vz + 16 * i) = u32x4{};
+  }
+  __syncthreads();
+  f32x16 s_cur = qk_tile(stage_of(t_begin) + k_rd, qop);
+
+  // one pipelined tile; MASKED only for a partial last tile of the keys
+  auto iter = [&](int64_t t, auto masked) {
+    constexpr bool M = decltype(masked)::value;
+    const f32x16 s_nxt = qk_tile(stage_of(t + 1) + k_rd, qop);
+    pv_tile<PSPLIT>(o, ph, pl, stage_of(t - 1) + v_rd);
+    float alpha;
+    bool bump;
+    softmax_tile<PSPLIT, M>(s_cur, valid_of(t), hl, p.scale_log2, m_run, l_run, alpha, bump, ph, pl);
+    // keep the weights' computation in this region (else it sinks past the
+    // branch below, away from the MFMAs it should overlap)
+    asm volatile("" ::"v"(ph[0]), "v"(ph[1]), "v"(pl[0]), "v"(pl[1]), "v"(l_run));
+    tile_schedule<PSPLIT>();
+    if (__any(bump)) {                             // O (through tile t-1) to the new max
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    store(t + 2);
+    load(t + 3);
+    __syncthreads();
+    s_cur = s_nxt;
+  };
+  for (int64_t t = t_begin; t < t_last; ++t) iter(t, Flag<false>{});
+  if (valid_of(t_last) < kTile) iter(t_last, Flag<true>{});
+  else iter(t_last, Flag<false>{});
+  pv_tile<PSPLIT>(o, ph, pl, stage_of(t_end - 1) + v_rd);
+
+  // epilogue: lane (r32, hl) holds dims 32 db + 8 q + 4 hl + (0..3) of its row
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  if (row >= R) return;
+  const int t = row / G, h = g * G + row % G;
+  if (p.mask && p.mask[h]) return;
+  const int64_t orow_base = static_cast<int64_t>(t) * p.hq + h;
+  const bool any = l > 0.f;
+  const float inv = any ? 1.f / l : 0.f;
+  const float lz = any ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+  if (!MERGE) {
+    const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows + orow_base;
+    float* a = p.out.a + orow * kD + 4 * hl;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
+                         o[db][4 * q + 3] * inv};
+        *reinterpret_cast<f32x4*>(a + 32 * db + 8 * q) = v;
+      }
+    if (hl == 0) p.out.l[orow] = lz;
+  } else {
+    // A_full = (w_out A_out + w_in A_in) / (w_out + w_in), m = max(L_out, L_in)
+    const int64_t r = orow_base;
+    const float l_prev = p.l_prev[r];
+    const float mm = fmaxf(l_prev, lz);
+    const float w_out = l_prev == kNegInf ? 0.f : expf(l_prev - mm);
+    const float w_in = expf(lz - mm);
+    const float den = w_out + w_in;
+    const float* ap = p.a_prev + r * kD + 4 * hl;
+    float* a = p.out.a + r * kD + 4 * hl;
+    float* ai = p.a_raw ? p.a_raw + r * kD + 4 * hl : nullptr;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 vin = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
+                           o[db][4 * q + 3] * inv};
+        const f32x4 vp = *reinterpret_cast<const f32x4*>(ap + 32 * db + 8 * q);
+        f32x4 vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vf[e] = w_out == 0.f ? vin[e] : (w_out * vp[e] + w_in * vin[e]) / den;
+        *reinterpret_cast<f32x4*>(a + 32 * db + 8 * q) = vf;
+        if (ai) *reinterpret_cast<f32x4*>(ai + 32 * db + 8 * q) = vin;
+      }
+    if (hl == 0) {
+      if (p.out.l) p.out.l[r] = mm + logf(den);
+      if (p.l_raw) p.l_raw[r] = lz;
+    }
+  }
+}
+
+}  // namespace
+
+int rows_tile_rows() { return FB_ROWS_WAVES * 32; }
+int rows_occupancy() { return FB_ROWS_OCC; }
+
+hipError_t launch_rows(const RowsParams& p, hipStream_t s) {
+  const int per = (p.n_items + 7) / 8;
+  const dim3 grid(per * 8);
+  if (p.a_prev)
+    hipLaunchKernelGGL((rows_mfma_kernel<FB_ROWS_WAVES, FB_ROWS_OCC, FB_ROWS_PSPLIT != 0, true>),
+                       grid, dim3(64 * FB_ROWS_WAVES), 0, s, p);
+  else
+    hipLaunchKernelGGL((rows_mfma_kernel<FB_ROWS_WAVES, FB_ROWS_OCC, FB_ROWS_PSPLIT != 0, false>),
+                       grid, dim3(64 * FB_ROWS_WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fb

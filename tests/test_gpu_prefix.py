@@ -10,29 +10,9 @@ import pytest
 import torch
 
 import workloads as W
-from oracle.attention import attn_gqa
-from _helpers import check_a, check_l, cpu, dev_tensor, tols, vals
+from _helpers import check_a, check_l, cpu, dev_tensor, run_prefix, tols
 
 pytestmark = pytest.mark.gpu
-
-
-def run_prefix(fb, cfg, n_q, n_kv, layout="tok", mask=None, q_gain=1.0, seed_variant=0):
-    cfg = cfg.with_(n_prefix=n_kv, n_block=n_q, q_gain=q_gain)
-    kp, vp = W.prefix_kv(cfg, variant=seed_variant)
-    q = W.text_steps(cfg.with_(n_steps=1), variant=seed_variant)[0]["q"]
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    shape = fb.shape_of(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.scale, tdt)
-    qd = dev_tensor(q, cfg.dtype)
-    kd, vd = dev_tensor(kp, cfg.dtype, layout), dev_tensor(vp, cfg.dtype, layout)
-    a = torch.full((n_q, cfg.n_q_heads, cfg.head_dim), 7.0, device="cuda")
-    l = torch.full((n_q, cfg.n_q_heads), 7.0, device="cuda")
-    nbytes = fb.fb_prefix_attn_workspace(shape, n_q, n_kv)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
-    md = None if mask is None else torch.tensor(mask, dtype=torch.uint8, device="cuda")
-    fb.fb_prefix_attn(shape, qd, kd, vd, a, l, mask=md, ws=ws)
-    torch.cuda.synchronize()
-    ra, rl = attn_gqa(vals(q, cfg.dtype), vals(kp, cfg.dtype), vals(vp, cfg.dtype), cfg.scale)
-    return cpu(a), cpu(l), ra, rl, cfg
 
 
 CASES = [
