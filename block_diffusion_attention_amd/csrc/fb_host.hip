@@ -45,9 +45,11 @@ constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights 
 constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
 constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
 constexpr int64_t kMinTilesGeneric = 4;   // 64-token tiles per chunk
+constexpr int64_t kMinTilesSparse = 8;    // 32-key tiles per chunk of the sparse MFMA pass
+constexpr int kMaxBitmapWords = 16384;    // selection bitmap row built in 64 KB of LDS
 constexpr size_t kAlign = 256;
 
-enum Path { PATH_GENERIC = 0, PATH_MFMA = 1, PATH_ROWS = 2 };
+enum Path { PATH_GENERIC = 0, PATH_MFMA = 1, PATH_ROWS = 2, PATH_SPARSE = 3 };
 
 struct PrefixPlan {
   int path = PATH_GENERIC;
@@ -59,6 +61,9 @@ struct PrefixPlan {
   bool direct = false;         // one chunk, written straight to the outputs
   int64_t rows = 0;            // n_q * Hq
   size_t off_l = 0, off_ra = 0, off_rl = 0, ws_bytes = 0;
+  size_t off_bm = 0, off_ul = 0, off_uc = 0;   // PATH_SPARSE: bitmaps, union list, union sizes
+  int words = 0;
+  int64_t n_pages = 0;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -117,9 +122,17 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   pl.path = (s.dtype == FB_BF16 && s.head_dim == 128 && mode == FB_SEL_DENSE) ? PATH_MFMA
                                                                              : PATH_GENERIC;
   if (pl.path == PATH_MFMA && group_rows >= FB_ROWS_MIN_ROWS) pl.path = PATH_ROWS;
-  const int tile = pl.path == PATH_ROWS ? 32 : prefix_tile_tokens(pl.path);
-  const int64_t n_virt = mode == FB_SEL_GATHER ? static_cast<int64_t>(sel->k_pages) * sel->page_size
-                                               : n_kv;
+  if (mode != FB_SEL_DENSE) {
+    pl.n_pages = (n_kv + sel->page_size - 1) / sel->page_size;
+    pl.words = static_cast<int>((pl.n_pages + 31) / 32);
+    if (s.dtype == FB_BF16 && s.head_dim == 128 && sel->page_size % 16 == 0 &&
+        pl.words <= kMaxBitmapWords)
+      pl.path = PATH_SPARSE;
+  }
+  const int tile = (pl.path == PATH_ROWS || pl.path == PATH_SPARSE) ? 32 : prefix_tile_tokens(pl.path);
+  int64_t n_virt = mode == FB_SEL_GATHER ? static_cast<int64_t>(sel->k_pages) * sel->page_size : n_kv;
+  if (pl.path == PATH_SPARSE && mode == FB_SEL_GATHER)   // the union may reach every page
+    n_virt = pl.n_pages * sel->page_size;
   const int64_t n_tiles = (n_virt + tile - 1) / tile;
   int64_t wg_per_chunk;
   int64_t min_tiles;
@@ -129,6 +142,10 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
     if (pl.row_blocks == 2 && FB_PREFIX_PAIR) pl.row_blocks = 3;   // kernel selector
     wg_per_chunk = s.n_kv_heads * pl.n_slabs;
     min_tiles = kMinTilesMfma;
+  } else if (pl.path == PATH_SPARSE) {
+    pl.n_slabs = static_cast<int>((group_rows + 31) / 32);
+    wg_per_chunk = s.n_kv_heads * pl.n_slabs;
+    min_tiles = kMinTilesSparse;
   } else if (pl.path == PATH_ROWS) {
     pl.n_rtiles = static_cast<int>((group_rows + rows_tile_rows() - 1) / rows_tile_rows());
     wg_per_chunk = s.n_kv_heads * static_cast<int64_t>(pl.n_rtiles);
@@ -146,7 +163,11 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
     if (want > kMaxChunks) want = kMaxChunks;
     int64_t cap = n_tiles / min_tiles;
     if (cap < 1) cap = 1;
-    const int64_t chunks = want < cap ? want : cap;
+    int64_t chunks = want < cap ? want : cap;
+    if (pl.path == PATH_SPARSE) {                  // bounded union slice per chunk
+      const int64_t lo = (n_tiles + sparse_max_tiles_per_chunk() - 1) / sparse_max_tiles_per_chunk();
+      chunks = chunks > lo ? chunks : lo;
+    }
     pl.tiles_per_chunk = (n_tiles + chunks - 1) / chunks;
     pl.n_chunks = static_cast<int>((n_tiles + pl.tiles_per_chunk - 1) / pl.tiles_per_chunk);
   }
@@ -161,6 +182,16 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
       pl.off_ra = pl.ws_bytes;
       pl.off_rl = pl.off_ra + a_bytes;
       pl.ws_bytes = pl.off_rl + l_bytes;
+    }
+  }
+  if (pl.path == PATH_SPARSE) {
+    pl.off_bm = pl.ws_bytes;
+    pl.ws_bytes += align_up(static_cast<size_t>(n_q) * s.n_kv_heads * pl.words * sizeof(uint32_t));
+    if (mode == FB_SEL_GATHER) {
+      pl.off_ul = pl.ws_bytes;
+      pl.ws_bytes += align_up(static_cast<size_t>(s.n_kv_heads) * pl.n_pages * sizeof(int32_t));
+      pl.off_uc = pl.ws_bytes;
+      pl.ws_bytes += align_up(static_cast<size_t>(s.n_kv_heads) * sizeof(int32_t));
     }
   }
   return pl;
@@ -219,7 +250,26 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
 
   if (pl.n_chunks > 0) {
     hipError_t e;
-    if (pl.path == PATH_ROWS) {
+    if (pl.path == PATH_SPARSE) {
+      uint32_t* bm = reinterpret_cast<uint32_t*>(w + pl.off_bm);
+      // (k_pages = 0: the kernel writes all-zero rows and reads no list)
+      e = launch_sel_bitmap(sel->pages, static_cast<int>(n_q) * s.n_kv_heads, sel->k_pages, pl.words,
+                            static_cast<int>(pl.n_pages), bm, stream);
+      if (e != hipSuccess) return FB_ERR_DEVICE;
+      pp.bitmap = bm;
+      pp.words = pl.words;
+      pp.n_pages = pl.n_pages;
+      if (mode == FB_SEL_GATHER) {
+        int32_t* ul = reinterpret_cast<int32_t*>(w + pl.off_ul);
+        int32_t* uc = reinterpret_cast<int32_t*>(w + pl.off_uc);
+        e = launch_sel_union(bm, sel->active, static_cast<int>(n_q), s.n_kv_heads, pl.words, ul, uc,
+                             static_cast<int>(pl.n_pages), stream);
+        if (e != hipSuccess) return FB_ERR_DEVICE;
+        pp.ulist = ul;
+        pp.ucnt = uc;
+      }
+      e = launch_prefix_sparse(pp, stream);
+    } else if (pl.path == PATH_ROWS) {
       RowsParams rp;
       memset(&rp, 0, sizeof(rp));
       rp.q = q.ptr;

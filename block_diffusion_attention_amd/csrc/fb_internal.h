@@ -44,6 +44,12 @@ struct PrefixParams {
   const int32_t* pages;         // [n_q, Hkv, k_pages]
   const uint8_t* active;        // [n_q] nullable
   RowOut out_res;               // SPLIT: residual partials
+  // sparse MFMA path
+  const uint32_t* bitmap;       // [n_q, Hkv, words] selection bits per (t, g)
+  int words;                    // ceil(n_pages / 32)
+  int64_t n_pages;
+  const int32_t* ulist;         // GATHER: [Hkv, n_pages] union pages, ascending
+  const int32_t* ucnt;          // GATHER: [Hkv] union sizes
 };
 
 struct ReduceParams {
@@ -66,6 +72,13 @@ hipError_t launch_prefix_generic(const PrefixParams& p, fb_dtype dt, int d, hipS
 hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t s);
 int prefix_mfma_occupancy(int row_blocks);      // workgroups per CU of that kernel
 hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s);
+// sparse MFMA path (bf16, d = 128, page size a multiple of 16)
+hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int words, int n_pages,
+                             uint32_t* bitmap, hipStream_t s);
+hipError_t launch_sel_union(const uint32_t* bitmap, const uint8_t* active, int n_q, int hkv,
+                            int words, int32_t* ulist, int32_t* ucnt, int n_pages, hipStream_t s);
+hipError_t launch_prefix_sparse(const PrefixParams& p, hipStream_t s);
+int sparse_max_tiles_per_chunk();               // 32-key tiles a GATHER chunk may span
 hipError_t launch_prefix_empty(float* a_out, float* l_out, int n_q, int hq, int d,
                                const uint8_t* mask, hipStream_t s);
 

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64) void prefix_generic_kernel(PrefixParams p) {
   auto token_of = [&](int64_t j) -> int64_t {   // virtual -> prefix token, -1 if none
     if (!gather) return j;
     const int64_t tok = static_cast<int64_t>(rpages[j / p.page_size]) * p.page_size + j % p.page_size;
-    return tok < p.n_kv ? tok : -1;
+    return tok >= 0 && tok < p.n_kv ? tok : -1;
   };
 
   const int nsets = split ? 2 : 1;

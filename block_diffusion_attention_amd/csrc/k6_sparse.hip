@@ -1,0 +1,443 @@
+// k6_sparse.hip -- the block-external pass with a per-row page selection on
+// MFMA (bf16, d = 128, page size a multiple of 16): the sparse subsystem
+// FlashBlock pairs with its cache (technical summary, s2 "sparse
+// compatibility"), with QUEST-selected pages as in LoSA (s2).
+//
+// Every row (query token t, query head h of KV group g) has a set S_{t,g} of
+// selected pages (shared by the query heads of the group), given as ascending
+// page lists; they are turned into one bitmap per (t, g) here.
+//   SPLIT  (refresh step): one pass over the whole prefix keeps two online
+//          softmax states per row, the selected keys and the rest (the
+//          residual), each with its own running max.
+//   GATHER (later steps): only the union over the active tokens of their
+//          selected pages is read (compacted per KV group, ascending), and
+//          each row keeps the keys of its own pages; rows of inactive tokens
+//          are not computed. The cached residual is merged by the reduce.
+// Both write split-K partials (normalised A, natural-log L) that the
+// fixed-order reduce combines.
+//
+// Workgroup = 4 waves = (chunk of tiles, KV group g, slab of 32 rows); each
+// wave streams its own 32-key tiles (w, w+4, ...) through a wave-private LDS
+// tile, as two 16-key halves that may come from different pages (GATHER),
+// and the four states are merged through LDS at the end. Scores and P.V use
+// v_mfma_f32_32x32x16_bf16 exactly as the dense decode kernel does (S^T =
+// K.Q^T with lane = row; O^T += V^T.P^T with P as bf16 hi + lo parts).
+#include "fb_internal.h"
+
+#include <math.h>
+
+namespace fb {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kWaves = 4;
+constexpr int kTile = 32;
+constexpr int kD = 128;
+constexpr int kKRow = 272;                   // 17 x 16 B: 16 rows, 16 bank groups
+constexpr int kVRow = 320;                   // 20 x 16 B: 4 rows, 4 x 64 B bank spans
+constexpr int kKBytes = kTile * kKRow;
+constexpr int kVBytes = kTile * kVRow;
+constexpr int kWaveLds = kKBytes + kVBytes;
+constexpr int kMergeStride = kD + 1;
+constexpr float kRescaleLog2 = 8.f;
+constexpr int kMaxSlicePages = 512;          // union pages one GATHER chunk may span
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
+  auto p = (const __attribute__((address_space(3))) char*)(lds_generic);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// ---------------------------------------------------------------------------
+// Selection bitmaps: bit p of row (t, g) set iff page p is in S_{t,g}.
+// One workgroup per (t, g); the row is built in LDS (words = ceil(P / 32)).
+// ---------------------------------------------------------------------------
+// Page ids outside [0, n_pages) select nothing.
+__global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* pages, int k_pages,
+                                                         int words, int n_pages, uint32_t* bitmap) {
+  extern __shared__ uint32_t wl[];
+  const int64_t row = blockIdx.x;                  // t * Hkv + g
+  for (int i = threadIdx.x; i < words; i += 256) wl[i] = 0u;
+  __syncthreads();
+  const int32_t* pl = pages + row * k_pages;
+  for (int i = threadIdx.x; i < k_pages; i += 256) {
+    const uint32_t pg = static_cast<uint32_t>(pl[i]);
+    if (pg < static_cast<uint32_t>(n_pages)) atomicOr(&wl[pg >> 5], 1u << (pg & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < words; i += 256) bitmap[row * words + i] = wl[i];
+}
+
+// Union over the active tokens of their selected pages, per KV group g, as an
+// ascending page list and its length. One workgroup per g.
+__global__ __launch_bounds__(256) void sel_union_kernel(const uint32_t* bitmap, const uint8_t* active,
+                                                        int n_q, int hkv, int words,
+                                                        int32_t* ulist, int32_t* ucnt, int n_pages) {
+  __shared__ int scan[256];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int w = w0 + tid;
+    uint32_t u = 0u;
+    if (w < words)
+      for (int t = 0; t < n_q; ++t)
+        if (!active || active[t]) u |= bitmap[(static_cast<int64_t>(t) * hkv + g) * words + w];
+    const int c = __popc(u);
+    scan[tid] = c;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {            // inclusive scan
+      const int v = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    int pos = base + scan[tid] - c;
+    while (u) {
+      const int b = __builtin_ctz(u);
+      ulist[static_cast<int64_t>(g) * n_pages + pos++] = w * 32 + b;
+      u &= u - 1;
+    }
+    base += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) ucnt[g] = base;
+}
+
+// ---------------------------------------------------------------------------
+// The sparse MFMA pass.
+// ---------------------------------------------------------------------------
+struct SpTile {             // one tile in flight: K/V rows + where its halves are
+  u32x4 k[8], v[8];
+  int32_t page[2];          // page of each 16-key half
+  int32_t valid[2];         // keys of each half that exist (0..16)
+  uint32_t word[2];         // this lane's row bitmap word holding page[h]
+};
+
+__device__ __forceinline__ void softmax_set(const float (&x)[16], float c, float& m_run,
+                                            float& l_run, f32x16 (&o)[4], bf16x8 (&ph)[2],
+                                            bf16x8 (&pl)[2]) {
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+  const bool bump = mx > m_run + kRescaleLog2;
+  float alpha = 1.f;
+  if (bump) {
+    alpha = fast_exp2(m_run - mx);
+    m_run = mx;
+  }
+  const float nm = m_run == kNegInf ? 0.f : -m_run;
+  float psum = 0.f;
+#pragma unroll
+  for (int hj = 0; hj < 2; ++hj) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pf[e] = fast_exp2(__builtin_fmaf(x[8 * hj + e], c, nm));
+      psum += pf[e];
+    }
+    const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
+    ph[hj] = hi;
+    pl[hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
+  }
+  l_run = l_run * alpha + psum;
+  if (__any(bump)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+  }
+}
+
+// SPLIT keeps two O states (occupancy 1, the register file holds both).
+template <bool SPLIT>
+__global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixParams p) {
+  constexpr int NSET = SPLIT ? 2 : 1;
+  constexpr int kStage = kWaves * kWaveLds;
+  constexpr int kMerge = kWaves * 32 * kMergeStride * 4;
+  constexpr int kLds = kMerge > kStage ? kMerge : kStage;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  __shared__ float ml_s[kWaves][32][2];
+  __shared__ int32_t upage[kMaxSlicePages];        // GATHER: this chunk's union pages
+
+  int chunk, g, slab;
+  {
+    const int id = blockIdx.x;
+    const int tq = id >> 3;
+    slab = tq % p.n_slabs;
+    const int idx = (tq / p.n_slabs) * 8 + (id & 7);
+    if (idx >= p.n_chunks * p.hkv) return;
+    chunk = idx % p.n_chunks;
+    g = idx / p.n_chunks;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, r32 = lane & 31;
+  const int G = p.group;
+  const int R = p.n_q * G;
+  const int row = slab * 32 + r32;
+  const bool row_ok = row < R;
+  const int t_row = row_ok ? row / G : 0;
+  const bool row_on = row_ok && (SPLIT || !p.active || p.active[t_row] != 0);
+
+  // tiles of this group: all keys (SPLIT) or the union of selected pages
+  const int hpp = p.page_size >> 4;                // 16-key halves per page
+  int64_t n_vt;
+  const int32_t* ulist = nullptr;
+  int64_t n_half = 0;
+  if (SPLIT) {
+    n_vt = (p.n_kv + kTile - 1) / kTile;
+  } else {
+    n_half = static_cast<int64_t>(p.ucnt[g]) * hpp;
+    n_vt = (n_half + 1) / 2;
+    ulist = p.ulist + static_cast<int64_t>(g) * p.n_pages;
+  }
+  const int64_t vt_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
+  const int64_t vt_end = vt_begin + p.tiles_per_chunk < n_vt ? vt_begin + p.tiles_per_chunk : n_vt;
+
+  auto out_row = [&](int r, int set) -> int64_t {
+    const RowOut& out = set == 0 ? p.out : p.out_res;
+    const int t = r / G, h = g * G + r % G;
+    return static_cast<int64_t>(chunk) * out.chunk_stride_rows + static_cast<int64_t>(t) * p.hq + h;
+  };
+  auto row_written = [&](int r) -> bool {
+    if (r >= R) return false;
+    return SPLIT || !p.active || p.active[r / G] != 0;
+  };
+
+  if (vt_begin >= vt_end) {                        // (GATHER) nothing to read: identity partial
+    for (int e = tid; e < 32 * kD; e += 256) {
+      const int r = slab * 32 + e / kD;
+      if (row_written(r)) p.out.a[out_row(r, 0) * kD + e % kD] = 0.f;
+    }
+    for (int r0 = tid; r0 < 32; r0 += 256) {
+      const int r = slab * 32 + r0;
+      if (row_written(r)) p.out.l[out_row(r, 0)] = kNegInf;
+    }
+    return;
+  }
+
+  // GATHER: the chunk's slice of the union page list, staged in LDS
+  const int64_t slice0 = SPLIT ? 0 : (2 * vt_begin) / hpp;
+  if (!SPLIT) {
+    int64_t slice1 = (2 * vt_end - 1) / hpp;         // inclusive, within the union
+    slice1 = slice1 < (n_half - 1) / hpp ? slice1 : (n_half - 1) / hpp;
+    for (int64_t i = tid; i <= slice1 - slice0; i += 256) upage[i] = ulist[slice0 + i];
+    __syncthreads();
+  }
+
+  // Q^T operand of this lane's row (zero for rows past R)
+  bf16x8 qop[8];
+  {
+    const int jh = row_ok ? row % G : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(t_row) * p.q_st +
+                         static_cast<int64_t>(g * G + jh) * p.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qop[kk] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl) : bf16x8{};
+  }
+  const uint32_t* bm_row = p.bitmap + (static_cast<int64_t>(t_row) * p.hkv + g) * p.words;
+
+  const char* kg = static_cast<const char*>(p.k) + static_cast<int64_t>(g) * p.kv_sh * 2;
+  const char* vg = static_cast<const char*>(p.v) + static_cast<int64_t>(g) * p.kv_sh * 2;
+  const int64_t kvst_b = p.kv_st * 2;
+  const int lrow = lane >> 4, lpiece = lane & 15;
+  char* kl = lds + w * kWaveLds;
+  char* vl = kl + kKBytes;
+  char* k_wr = kl + lrow * kKRow + lpiece * 16;
+  char* v_wr = vl + lrow * kVRow + lpiece * 16;
+  const char* k_rd = kl + r32 * kKRow + hl * 16;
+  const int grp = lane >> 4, s4 = (lane & 15) >> 2, q4 = lane & 3;
+  const char* v_rd = vl + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
+
+  const int64_t vt_last = vt_end - 1;
+  auto load_tile = [&](int64_t vt) -> SpTile {
+    SpTile r;
+    vt = vt < vt_last ? vt : vt_last;
+    int64_t tok0[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int64_t tok;
+      int32_t page;
+      bool exists;
+      if (SPLIT) {
+        tok = vt * kTile + 16 * h;
+        const int64_t pg = tok / p.page_size;            // (past n_kv: no keys, any bit)
+        page = static_cast<int32_t>(pg < p.n_pages ? pg : p.n_pages - 1);
+        exists = true;
+      } else {
+        int64_t hx = 2 * vt + h;
+        exists = hx < n_half;
+        hx = exists ? hx : 2 * vt;
+        page = upage[hx / hpp - slice0];
+        tok = static_cast<int64_t>(page) * p.page_size + 16 * (hx % hpp);
+      }
+      const int64_t rem = p.n_kv - tok;
+      r.valid[h] = !exists || rem <= 0 ? 0 : (rem < 16 ? static_cast<int32_t>(rem) : 16);
+      r.page[h] = page;
+      tok0[h] = tok;
+      r.word[h] = row_on ? bm_row[page >> 5] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int64_t tok = tok0[i >> 2] + 4 * (i & 3) + lrow;
+      tok = tok < p.n_kv ? tok : p.n_kv - 1;
+      const int64_t off = tok * kvst_b + lpiece * 16;
+      r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+    }
+    return r;
+  };
+
+  f32x16 o[NSET][4];
+  float m_run[NSET], l_run[NSET];
+#pragma unroll
+  for (int s = 0; s < NSET; ++s) {
+    m_run[s] = kNegInf;
+    l_run[s] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[s][db] = f32x16{};
+  }
+
+  auto process = [&](const SpTile& tl) {
+    f32x16 sc = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      sc = mfma32(*reinterpret_cast<const bf16x8*>(k_rd + 32 * kk), qop[kk], sc);
+    const bool sel0 = (tl.word[0] >> (tl.page[0] & 31)) & 1u;
+    const bool sel1 = (tl.word[1] >> (tl.page[1] & 31)) & 1u;
+    float xs[16], xr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = i >> 3;                        // half of the tile
+      const int kh = 8 * ((i >> 2) & 1) + 4 * hl + (i & 3);   // key within the half
+      const bool val = row_on && kh < tl.valid[h];
+      const bool sel = h ? sel1 : sel0;
+      xs[i] = val && sel ? sc[i] : kNegInf;
+      if (SPLIT) xr[i] = val && !sel ? sc[i] : kNegInf;
+    }
+    bf16x8 ph[NSET][2], pl[NSET][2];
+    softmax_set(xs, p.scale_log2, m_run[0], l_run[0], o[0], ph[0], pl[0]);
+    if (SPLIT) softmax_set(xr, p.scale_log2, m_run[NSET - 1], l_run[NSET - 1], o[NSET - 1],
+                                 ph[NSET - 1], pl[NSET - 1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x4 v0 = ds_read_tr(v_rd + (16 * j) * kVRow + 64 * db);
+        const bf16x4 v1 = ds_read_tr(v_rd + (16 * j + 8) * kVRow + 64 * db);
+        va[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int s = 0; s < NSET; ++s) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[s][db] = mfma32(va[db], ph[s][j], o[s][db]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[s][db] = mfma32(va[db], pl[s][j], o[s][db]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  SpTile cur = load_tile(vt_begin + w);
+  for (int64_t vt = vt_begin + w; vt < vt_end; vt += kWaves) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(k_wr + 4 * i * kKRow) = cur.k[i];
+      *reinterpret_cast<u32x4*>(v_wr + 4 * i * kVRow) = cur.v[i];
+    }
+    asm volatile("" ::: "memory");
+    const SpTile nxt = load_tile(vt + kWaves);
+    process(cur);
+    cur = nxt;
+  }
+
+  // ---- merge the four waves' states through LDS, write the chunk partial --
+#pragma unroll
+  for (int s = 0; s < NSET; ++s) {
+    const float lsum = l_run[s] + __shfl_xor(l_run[s], 32, 64);
+    __syncthreads();                               // tile LDS (or the previous set) no longer read
+    if (hl == 0) {
+      ml_s[w][r32][0] = m_run[s];
+      ml_s[w][r32][1] = lsum;
+    }
+    __syncthreads();
+    float* mg = reinterpret_cast<float*>(lds);
+    {
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml_s[ww][r32][0]);
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float mw = ml_s[ww][r32][0];
+        if (mw != kNegInf) tot += ml_s[ww][r32][1] * fast_exp2(mw - M);
+      }
+      const float f = (m_run[s] == kNegInf || tot == 0.f) ? 0.f : fast_exp2(m_run[s] - M) / tot;
+      float* dst = mg + (w * 32 + r32) * kMergeStride;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[32 * db + 8 * (i >> 2) + 4 * hl + (i & 3)] = o[s][db][i] * f;
+    }
+    __syncthreads();
+    const RowOut& out = s == 0 ? p.out : p.out_res;
+    for (int e = tid; e < 32 * kD; e += 256) {
+      const int r = e / kD, c = e % kD;
+      if (!row_written(slab * 32 + r)) continue;
+      float sum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) sum += mg[(ww * 32 + r) * kMergeStride + c];
+      out.a[out_row(slab * 32 + r, s) * kD + c] = sum;
+    }
+    for (int r = tid; r < 32; r += 256) {
+      if (!row_written(slab * 32 + r)) continue;
+      float M = kNegInf;
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml_s[ww][r][0]);
+      float tot = 0.f;
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float mw = ml_s[ww][r][0];
+        if (mw != kNegInf) tot += ml_s[ww][r][1] * fast_exp2(mw - M);
+      }
+      out.l[out_row(slab * 32 + r, s)] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int words, int n_pages,
+                             uint32_t* bitmap, hipStream_t s) {
+  hipLaunchKernelGGL(sel_bitmap_kernel, dim3(n_rows), dim3(256), words * sizeof(uint32_t), s, pages,
+                     k_pages, words, n_pages, bitmap);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_union(const uint32_t* bitmap, const uint8_t* active, int n_q, int hkv,
+                            int words, int32_t* ulist, int32_t* ucnt, int n_pages, hipStream_t s) {
+  hipLaunchKernelGGL(sel_union_kernel, dim3(hkv), dim3(256), 0, s, bitmap, active, n_q, hkv, words,
+                     ulist, ucnt, n_pages);
+  return hipGetLastError();
+}
+
+// a chunk of n tiles spans at most 2n union pages (one per 16-key half)
+int sparse_max_tiles_per_chunk() { return (kMaxSlicePages - 2) / 2; }
+
+hipError_t launch_prefix_sparse(const PrefixParams& p, hipStream_t s) {
+  const int n_cg = p.n_chunks * p.hkv;
+  const dim3 grid(static_cast<unsigned>((n_cg + 7) / 8 * 8 * p.n_slabs));
+  if (p.sel_mode == FB_SEL_SPLIT)
+    hipLaunchKernelGGL(sparse_mfma_kernel<true>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(sparse_mfma_kernel<false>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fb

@@ -95,7 +95,9 @@ typedef struct {
   fb_sel_mode mode;
   int32_t page_size;      /* tokens per page (16); page p = tokens [p*ps, p*ps+ps) */
   int32_t k_pages;        /* selected pages per (query token, KV head), >= 0     */
-  const int32_t* pages;   /* [n_q, Hkv, k_pages] page ids, strictly ascending    */
+  const int32_t* pages;   /* [n_q, Hkv, k_pages] page ids, strictly ascending;
+                             ids outside [0, ceil(n_kv / page_size)) select
+                             nothing                                           */
   const uint8_t* active;  /* GATHER: [n_q] 1 = the row recomputes; NULL = all    */
 } fb_page_sel;
 
@@ -118,9 +120,9 @@ typedef struct {
  * ws: device workspace of at least fb_prefix_attn_workspace() bytes (split- *
  *   K partials); may be NULL when that size is 0.                            *
  * Errors: INVALID_ARGUMENT on bad shape/stride/alignment/NULL, n_q < 1,     *
- *   n_kv < 0, k/v token counts that differ, a page id out of range is NOT   *
- *   checked (ids are device data); UNSUPPORTED for head_dim not in {64,128} *
- *   or a sparse mode with fp32 inputs; WORKSPACE_TOO_SMALL.                  *
+ *   n_kv < 0, k/v token counts that differ; UNSUPPORTED for head_dim not   *
+ *   in {64,128}; WORKSPACE_TOO_SMALL. Page ids are device data and are not  *
+ *   validated (see fb_page_sel).                                             *
  * ------------------------------------------------------------------------ */
 size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q,
                                 int64_t n_kv, const fb_page_sel* sel);
