@@ -531,9 +531,11 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
   if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
   if (k_pages > 0 && !pages) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
-  const size_t smem = (static_cast<size_t>(q.n_tok) * G * shape->head_dim + 2 * 32 * shape->head_dim) *
+  // LDS of the generic bound kernel (group sizes other than 1, 2, 4, 8)
+  const bool g_kernel = G == 1 || G == 2 || G == 4 || G == 8;
+  const size_t smem = (static_cast<size_t>(q.n_tok) * G * shape->head_dim + 2 * 32 * (shape->head_dim + 1)) *
                       sizeof(float);
-  if (smem > 160 * 1024) return FB_ERR_UNSUPPORTED;
+  if (!g_kernel && smem > 64 * 1024) return FB_ERR_UNSUPPORTED;
   if (!bound) {
     const size_t need = fb_page_select_workspace(shape, q.n_tok, n_pages);
     if (ws_bytes < need || (need > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;

@@ -69,17 +69,21 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
   const int g = blockIdx.y;
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPagesPerBlock;
   const int np = n_pages - p0 < kPagesPerBlock ? static_cast<int>(n_pages - p0) : kPagesPerBlock;
+  // page rows padded to d + 1 floats: the 32 pages a wave reads at once fall
+  // in distinct LDS banks
+  const int ds = d + 1;
   float* qs = sm;                                    // [n_q][G][d]
-  float* mn = qs + n_q * G * d;                      // [kPagesPerBlock][d]
-  float* mx = mn + kPagesPerBlock * d;
+  float* mn = qs + n_q * G * d;                      // [kPagesPerBlock][d + 1]
+  float* mx = mn + kPagesPerBlock * ds;
   for (int e = threadIdx.x; e < n_q * G * d; e += blockDim.x) {
     const int t = e / (G * d), j = (e / d) % G, c = e % d;
     qs[e] = ldf<T>(q + t * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
   }
   for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
     const int64_t o = (static_cast<int64_t>(g) * n_pages + p0) * d + e;
-    mn[e] = ldf<T>(kmin + o);
-    mx[e] = ldf<T>(kmax + o);
+    const int ls = (e / d) * ds + e % d;
+    mn[ls] = ldf<T>(kmin + o);
+    mx[ls] = ldf<T>(kmax + o);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < np * n_q; e += blockDim.x) {
@@ -90,13 +94,69 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
       double acc = 0.0;
       for (int c = 0; c < d; ++c) {
         const double qv = qr[c];
-        const double lo = qv * static_cast<double>(mn[pi * d + c]);
-        const double hi = qv * static_cast<double>(mx[pi * d + c]);
+        const double lo = qv * static_cast<double>(mn[pi * ds + c]);
+        const double hi = qv * static_cast<double>(mx[pi * ds + c]);
         acc = acc + (lo > hi ? lo : hi);
       }
       best = acc > best ? acc : best;
     }
     bound[(static_cast<int64_t>(t) * hkv + g) * n_pages + p0 + pi] = best;
+  }
+}
+
+// Same bound, with the G query heads of the group as G independent chains
+// (the sum of each head still runs sequentially over d, so every bit equals
+// the one-head-at-a-time kernel's).
+// Workgroup = (32 pages, KV group g, TC tokens).
+template <typename T, int G, int TC>
+__global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q_st, int64_t q_sh,
+                                                           const T* kmin, const T* kmax, int n_q,
+                                                           int hkv, int d, int64_t n_pages,
+                                                           double* bound) {
+#pragma clang fp contract(off)
+  extern __shared__ float sm[];
+  const int g = blockIdx.y;
+  const int t0 = blockIdx.z * TC;
+  const int nt = n_q - t0 < TC ? n_q - t0 : TC;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPagesPerBlock;
+  const int np = n_pages - p0 < kPagesPerBlock ? static_cast<int>(n_pages - p0) : kPagesPerBlock;
+  const int ds = d + 1;
+  float* qs = sm;                                    // [TC][d][G] (heads innermost)
+  float* mn = qs + TC * G * d;                       // [kPagesPerBlock][d + 1]
+  float* mx = mn + kPagesPerBlock * ds;
+  for (int e = threadIdx.x; e < nt * G * d; e += blockDim.x) {
+    const int t = e / (G * d), c = (e / G) % d, j = e % G;
+    qs[e] = ldf<T>(q + (t0 + t) * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
+  }
+  for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
+    const int64_t o = (static_cast<int64_t>(g) * n_pages + p0) * d + e;
+    const int ls = (e / d) * ds + e % d;
+    mn[ls] = ldf<T>(kmin + o);
+    mx[ls] = ldf<T>(kmax + o);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < np * nt; e += blockDim.x) {
+    const int pi = e % np, t = e / np;
+    const float* qr = qs + t * G * d;
+    const float* mnr = mn + pi * ds;
+    const float* mxr = mx + pi * ds;
+    double acc[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) acc[j] = 0.0;
+    for (int c = 0; c < d; ++c) {
+      const double a = mnr[c], b = mxr[c];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const double qv = qr[c * G + j];
+        const double lo = qv * a;
+        const double hi = qv * b;
+        acc[j] = acc[j] + (lo > hi ? lo : hi);
+      }
+    }
+    double best = acc[0];
+#pragma unroll
+    for (int j = 1; j < G; ++j) best = acc[j] > best ? acc[j] : best;
+    bound[(static_cast<int64_t>(t0 + t) * hkv + g) * n_pages + p0 + pi] = best;
   }
 }
 
@@ -179,6 +239,109 @@ __global__ __launch_bounds__(256) void page_topk_kernel(const double* bound, int
   }
 }
 
+// Block-wide exclusive scan over 256 threads (4 waves).
+__device__ __forceinline__ int block_exscan4(int v, int* red, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;                                       // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += red[i];
+  total = red[0] + red[1] + red[2] + red[3];
+  return before + x - v;
+}
+
+// Top-k with every key in registers: thread tid owns the KPT consecutive
+// pages [tid * KPT, tid * KPT + KPT), so ascending emission needs one scan.
+// Same result as page_topk_kernel: T = the k-th largest key, found exactly
+// by an 8-pass radix select (8 bits per pass, most significant first: the
+// pass's histogram over the keys that share T's prefix fixes the next byte),
+// then every key > T and the lowest-id ties at T.
+__device__ __forceinline__ int block_inscan4(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) x += red[i];
+  return x;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound, int hkv,
+                                                            int64_t n_pages, int k, int32_t* pages) {
+  __shared__ int hist[256];
+  __shared__ int red[4];
+  __shared__ unsigned long long sh_prefix;
+  __shared__ int sh_kk;
+  const int tid = threadIdx.x;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * hkv + blockIdx.y;
+  const double* b = bound + row * n_pages;
+  int32_t* out = pages + row * k;
+  const int64_t p0 = static_cast<int64_t>(tid) * KPT;
+  uint64_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = p0 + i < n_pages ? okey(b[p0 + i]) : 0ull;
+  // (okey of any bound is > 0; padding 0 is never in T's group, see below)
+
+  uint64_t prefix = 0, pmask = 0;
+  int kk = k;                                      // rank of T within the current group
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (p0 + i < n_pages && (key[i] & pmask) == prefix)
+        atomicAdd(&hist[(key[i] >> shift) & 255], 1);
+    __syncthreads();
+    // thread tid takes byte value bv = 255 - tid: S = #group keys with byte >= bv
+    const int bv = 255 - tid;
+    const int h = hist[bv];
+    const int S = block_inscan4(h, red);
+    if (S >= kk && S - h < kk) {                   // exactly one byte value
+      sh_prefix = prefix | (static_cast<uint64_t>(bv) << shift);
+      sh_kk = kk - (S - h);
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    kk = sh_kk;
+    pmask |= 255ull << shift;
+  }
+  const uint64_t T = prefix;
+  const int need_eq = kk;                          // ties at T to take, lowest ids first
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    gt += key[i] > T ? 1 : 0;
+    eq += key[i] == T ? 1 : 0;
+  }
+  int tot;
+  const int eq_before = block_exscan4(eq, red, tot);
+  int take_eq = need_eq - eq_before;
+  take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+  int pos = block_exscan4(gt + take_eq, red, tot);
+  int eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const bool is_eq = key[i] == T;
+    const bool sel = key[i] > T || (is_eq && eq_seen < take_eq);
+    eq_seen += is_eq ? 1 : 0;
+    if (sel) out[pos++] = static_cast<int32_t>(p0 + i);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t n_kv, int hkv,
@@ -204,9 +367,24 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                               hipStream_t s) {
   if (n_pages == 0) return hipSuccess;
   const int G = hq / hkv;
-  const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * d) * sizeof(float);
+  const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * (d + 1)) * sizeof(float);
   dim3 grid(static_cast<unsigned>((n_pages + kPagesPerBlock - 1) / kPagesPerBlock), hkv);
-  if (dt == FB_BF16)
+  // G-chain kernel: 32 pages x TC tokens per workgroup, TC = 8 (G <= 4) or 4 (G = 8)
+#define FB_BOUND_G(TT, GG)                                                                      \
+  hipLaunchKernelGGL((page_bound_g_kernel<TT, GG, 8 / ((GG + 3) / 4)>),                         \
+                     dim3(grid.x, grid.y, (n_q + 8 / ((GG + 3) / 4) - 1) / (8 / ((GG + 3) / 4))), \
+                     dim3(256), (8 / ((GG + 3) / 4) * GG * d + 2 * kPagesPerBlock * (d + 1)) * 4, s, \
+                     static_cast<const TT*>(q), q_st, q_sh, static_cast<const TT*>(kmin),       \
+                     static_cast<const TT*>(kmax), n_q, hkv, d, n_pages, bound)
+  if (dt == FB_BF16 && G == 4) FB_BOUND_G(uint16_t, 4);
+  else if (dt == FB_BF16 && G == 1) FB_BOUND_G(uint16_t, 1);
+  else if (dt == FB_BF16 && G == 2) FB_BOUND_G(uint16_t, 2);
+  else if (dt == FB_BF16 && G == 8) FB_BOUND_G(uint16_t, 8);
+  else if (dt == FB_F32 && G == 1) FB_BOUND_G(float, 1);
+  else if (dt == FB_F32 && G == 2) FB_BOUND_G(float, 2);
+  else if (dt == FB_F32 && G == 4) FB_BOUND_G(float, 4);
+  else if (dt == FB_F32 && G == 8) FB_BOUND_G(float, 8);
+  else if (dt == FB_BF16)
     hipLaunchKernelGGL(page_bound_kernel<uint16_t>, grid, dim3(256), smem, s,
                        static_cast<const uint16_t*>(q), q_st, q_sh,
                        static_cast<const uint16_t*>(kmin), static_cast<const uint16_t*>(kmax), n_q,
@@ -215,10 +393,18 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
     hipLaunchKernelGGL(page_bound_kernel<float>, grid, dim3(256), smem, s,
                        static_cast<const float*>(q), q_st, q_sh, static_cast<const float*>(kmin),
                        static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, bound);
+#undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;
-  hipLaunchKernelGGL(page_topk_kernel, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv, n_pages,
-                     k_pages, pages);
+  if (n_pages <= 256 * 16)
+    hipLaunchKernelGGL(page_topk_reg_kernel<16>, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv,
+                       n_pages, k_pages, pages);
+  else if (n_pages <= 256 * 32)
+    hipLaunchKernelGGL(page_topk_reg_kernel<32>, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv,
+                       n_pages, k_pages, pages);
+  else
+    hipLaunchKernelGGL(page_topk_kernel, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv, n_pages,
+                       k_pages, pages);
   return hipGetLastError();
 }
 

@@ -151,7 +151,9 @@ def test_active_mse_bit_exact(fb, dtype):
         assert np.array_equal(cpu(act).astype(bool), OC.active_set(want, 25))
 
 
-@pytest.mark.parametrize("n_kv,page,k", [(65536, 16, 819), (1000, 16, 7), (4096, 16, 0), (333, 8, 42)])
+@pytest.mark.parametrize("n_kv,page,k", [(65536, 16, 819), (1000, 16, 7), (4096, 16, 0), (333, 8, 42),
+                                          (100000, 16, 1875), (140000, 16, 3000)],
+                         ids=["64k_d02", "ragged", "k0", "page8", "6250_pages", "8750_pages"])
 def test_page_meta_and_select_bit_exact(fb, n_kv, page, k):
     cfg = W.SPARSE.with_(n_prefix=n_kv, page=page)
     kp, _ = W.prefix_kv(cfg)
@@ -171,3 +173,34 @@ def test_page_meta_and_select_bit_exact(fb, n_kv, page, k):
     assert np.array_equal(cpu(bound), rb)
     if k:
         assert np.array_equal(cpu(pages), OQ.topk_pages(rb, k))
+
+
+def test_page_select_ties_take_lower_ids(fb):
+    # pages 10..40 are copies of page 5: their bounds tie exactly, and k puts
+    # the selection boundary inside the tied group
+    n_kv, page = 4096, 16
+    cfg = W.SPARSE.with_(n_prefix=n_kv, page=page)
+    kp, _ = W.prefix_kv(cfg)
+    kp = kp.copy()
+    for pg in range(10, 41):
+        kp[pg * page:(pg + 1) * page] = kp[5 * page:6 * page]
+    q = W.sparse_steps(cfg.with_(n_steps=1))[0]["q"]
+    rmin, rmax = OQ.page_meta(vals(kp, "bf16"), page)
+    rb = OQ.page_bound(vals(q, "bf16"), rmin, rmax)
+    t, g = 3, 2
+    row = rb[t, g]
+    above = int(np.sum(row > row[5]))
+    k = above + 7                                   # 7 of the 32 tied pages
+    ref = OQ.topk_pages(rb, k)
+    tied = set(range(10, 41)) | {5}
+    assert len(tied & set(ref[t, g].tolist())) == 7
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    n_pages = n_kv // page
+    kmin = torch.empty(8, n_pages, 128, dtype=torch.bfloat16, device="cuda")
+    kmax = torch.empty_like(kmin)
+    fb.fb_page_meta(shape, dev_tensor(kp, "bf16"), page, kmin, kmax)
+    pages = torch.full((8, 8, k), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(fb.fb_page_select_workspace(shape, 8, n_pages), dtype=torch.uint8, device="cuda")
+    fb.fb_page_select(shape, dev_tensor(q, "bf16"), kmin, kmax, n_pages, k, pages, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(cpu(pages), ref)
