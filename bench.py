@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--block", type=int, default=16)
     ap.add_argument("--roofline-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the video and sparse workload measurements")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
     ap.add_argument("--prefix-only", action="store_true",
@@ -238,15 +240,171 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(N, B),
-                     "kernel": "prefix pass (prefix_mfma_kernel + prefix_reduce_kernel)",
+                     "kernel": "prefix pass (%s + prefix_reduce_kernel)" % (
+                         "prefix_pair_kernel" if 32 < B * hq // hkv <= 64 else "prefix_mfma_kernel"),
                      "alg_bytes_per_launch": alg_bytes},
         "extra": extra,
     }
+
+    extra["reuse_step_check"] = reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N,
+                                                 hq, hkv, d, stream)
+    if not args.no_extras:
+        extra["video"] = video_extra(fb, W, dev, stream)
+        extra["sparse"] = sparse_extra(fb, W, dev, stream)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
     out["extra"]["t_generate_inputs_s"] = round(t_gen, 1)
     print(json.dumps(out), flush=True)
+
+
+def _timed(fn, stream, reps):
+    """Average ms of `reps` calls of fn, HIP events on `stream` (after 2 warm-up calls)."""
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N, hq, hkv, d, stream):
+    """One denoising step on its own: forced reuse vs forced recompute, against
+    the KV-traffic ratio and the launch floor (two launches of the empty-prefix
+    kernel: a reuse step is two kernels, the count and the in-block pass)."""
+    import torch
+    q, k, v, ids = inputs[1]
+    step.new_block()
+    step.step(*inputs[0][:3], a_full, l_full, ids=inputs[0][3])
+
+    def one(dec):
+        step.state.step = 1
+        step.step(q, k, v, a_full, l_full, ids=ids, decision=dec)
+    ms_reuse = _timed(lambda: one(1), stream, 200)
+    ms_dense = _timed(lambda: one(0), stream, 20)
+    q1 = q[:1]
+    k0 = torch.empty(0, hkv, d, dtype=torch.bfloat16, device=q.device)
+    ao = torch.empty(1, hq, d, device=q.device)
+    lo = torch.empty(1, hq, device=q.device)
+
+    def floor():
+        fb.fb_prefix_attn(shape, q1, k0, k0, ao, lo, stream=stream)
+        fb.fb_prefix_attn(shape, q1, k0, k0, ao, lo, stream=stream)
+    ms_floor = _timed(floor, stream, 200)
+    bytes_dense = N * hkv * d * 4 + B * (hq + 2 * hkv) * d * 2 + B * hq * (d + 1) * 4 * 2
+    bytes_reuse = B * (hq + 2 * hkv) * d * 2 + B * hq * (d + 1) * 4 * 2
+    need = min(bytes_dense / bytes_reuse, ms_dense / ms_floor)
+    return {"ms_reuse_step": round(ms_reuse, 5), "ms_recompute_step": round(ms_dense, 5),
+            "ms_launch_floor_2_kernels": round(ms_floor, 5),
+            "speedup": round(ms_dense / ms_reuse, 2),
+            "kv_traffic_ratio": round(bytes_dense / bytes_reuse, 1),
+            "required_min(traffic_ratio, t_dense/t_floor)": round(need, 2),
+            "met": bool(ms_dense / ms_reuse >= need)}
+
+
+def video_extra(fb, W, dev, stream):
+    """Video block diffusion (12 MHA heads, d=128, 4680 block queries, 12480-token
+    prefix, 4 steps, gamma = 0.95): the block through fb_step, and the two
+    MFMA-bound passes alone against the bf16 MFMA peak."""
+    import torch
+    cfg = W.VIDEO
+    H, d, NQ, NK = cfg.n_q_heads, cfg.head_dim, cfg.n_block, cfg.n_prefix
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kp, vp = W.prefix_kv(cfg)
+    sig = W.video_sigmas(cfg, 0)
+    steps = [tuple(bf(s[n]) for n in ("q", "k", "v")) for s in W.video_steps(cfg, sig)]
+    kd, vd = bf(kp), bf(vp)
+    shape = fb.shape_of(H, H, d, cfg.scale, torch.bfloat16)
+    st = fb.Step(fb.FB_STEP_VIDEO, shape, NQ, kd, vd, gamma=cfg.gamma)
+    af = torch.empty(NQ, H, d, device=dev)
+    lf = torch.empty(NQ, H, device=dev)
+
+    def block(dec=-1):
+        st.new_block()
+        for i, (q, k, v) in enumerate(steps):
+            st.step(q, k, v, af, lf, decision=-1 if i == 0 else dec)
+    block()
+    torch.cuda.synchronize()
+    reused = [int(x) for x in st.mask.cpu()]
+    ms_block = _timed(block, stream, 5)
+    ms_dense = _timed(lambda: block(0), stream, 5)
+    q0 = steps[0][0]
+    a = torch.empty(NQ, H, d, device=dev)
+    l = torch.empty(NQ, H, device=dev)
+    ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, NQ, NK), 16), dtype=torch.uint8, device=dev)
+    ms_pre = _timed(lambda: fb.fb_prefix_attn(shape, q0, kd, vd, a, l, ws=ws, stream=stream), stream, 20)
+    ms_in = _timed(lambda: fb.fb_block_attn_merge(shape, q0, steps[0][1], steps[0][2], a, l, af, lf,
+                                                  stream=stream), stream, 20)
+    f_pre = 4.0 * NQ * H * NK * d
+    f_in = 4.0 * NQ * H * NQ * d
+    return {"workload": "video: 12 MHA heads, d=128, 4680 block queries, prefix 12480, 4 steps, "
+                        "gamma=0.95, sigma_h ~ LogU(1e-3, 1)",
+            "ms_block": round(ms_block, 3), "ms_block_all_heads_recompute": round(ms_dense, 3),
+            "query_tok_per_s": round(4 * NQ / (ms_block * 1e-3), 1),
+            "heads_reused_last_step": reused,
+            "prefix_pass": {"us": round(ms_pre * 1e3, 1), "TFLOP_s": round(f_pre / ms_pre / 1e9, 1),
+                            "frac_of_bf16_mfma_peak": round(f_pre / ms_pre / 1e9 / 2500.0, 4)},
+            "in_block_merge_pass": {"us": round(ms_in * 1e3, 1), "TFLOP_s": round(f_in / ms_in / 1e9, 1),
+                                    "frac_of_bf16_mfma_peak": round(f_in / ms_in / 1e9 / 2500.0, 4)}}
+
+
+def sparse_extra(fb, W, dev, stream):
+    """Sparse + residual reuse (32q/8kv, d=128, 65536-token prefix in 16-token
+    pages, B=8, 8 steps): per density, the block through fb_step and the gather
+    pass's HBM rate over the union of the active tokens' selected pages."""
+    import torch
+    res = []
+    base = W.SPARSE
+    kp, vp = W.prefix_kv(base)
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kd, vd = bf(kp), bf(vp)
+    H, G, d, B, N, PS = base.n_q_heads, base.n_kv_heads, base.head_dim, base.n_block, base.n_prefix, base.page
+    shape = fb.shape_of(H, G, d, base.scale, torch.bfloat16)
+    for dens in W.SPARSE_DENSITIES:
+        cfg = base.with_(density=dens)
+        steps = [tuple(bf(s[n]) for n in ("q", "k", "v")) for s in W.sparse_steps(cfg)]
+        st = fb.Step(fb.FB_STEP_SPARSE, shape, B, kd, vd, page_size=PS, k_pages=cfg.k_pages,
+                     pct=cfg.pct)
+        af = torch.empty(B, H, d, device=dev)
+        lf = torch.empty(B, H, device=dev)
+
+        def block():
+            st.new_block()
+            for q, k, v in steps:
+                st.step(q, k, v, af, lf)
+        block()
+        torch.cuda.synchronize()
+        ms_block = _timed(block, stream, 5)
+        # the gather pass alone, on the block's last selection and active set
+        act = st.active.clone()
+        sel = fb.page_sel(fb.FB_SEL_GATHER, PS, st.pages, act)
+        ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, B, N, sel), 16), dtype=torch.uint8,
+                         device=dev)
+        a = st.a_out.clone()
+        l = st.l_out.clone()
+        ms_g = _timed(lambda: fb.fb_prefix_attn(shape, steps[-1][0], kd, vd, a, l, sel=sel,
+                                                a_res=st.a_res, l_res=st.l_res, ws=ws,
+                                                stream=stream), stream, 20)
+        pg, on = st.pages.cpu().numpy(), act.cpu().numpy().astype(bool)
+        u = np.array([np.unique(pg[on, g]).size for g in range(G)])   # pages the gather reads
+        g_bytes = int(u.sum()) * PS * d * 2 * 2
+        res.append({"density": dens, "k_pages": cfg.k_pages, "ms_block": round(ms_block, 4),
+                    "query_tok_per_s": round(len(steps) * B / (ms_block * 1e-3), 1),
+                    "gather_pass_us": round(ms_g * 1e3, 1),
+                    "union_pages_per_kv_head": [int(x) for x in u],
+                    "gather_GB_s": round(g_bytes / (ms_g * 1e-3) / 1e9, 1),
+                    "gather_frac_of_hbm_peak": round(g_bytes / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "active_tokens_last_step": int(act.sum().item())})
+    return res
 
 
 def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):

@@ -41,6 +41,9 @@ namespace {
 #ifndef FB_ROWS_MIN_TILES
 #define FB_ROWS_MIN_TILES 32      // 32-key tiles per chunk of the many-rows kernel
 #endif
+#ifndef FB_ROWS_MAX_DYN
+#define FB_ROWS_MAX_DYN 8         // key chunks a masked many-rows pass may take
+#endif
 constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights in LDS
 constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
 constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
@@ -56,6 +59,8 @@ struct PrefixPlan {
   int row_blocks = 1;
   int n_slabs = 1;
   int n_rtiles = 1;            // PATH_ROWS: row tiles per KV head
+  int dyn_max = 0;             // PATH_ROWS: key chunks of a masked pass, at most
+  int64_t n_tiles = 0;
   int n_chunks = 0;
   int64_t tiles_per_chunk = 0;
   bool direct = false;         // one chunk, written straight to the outputs
@@ -170,10 +175,17 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
     }
     pl.tiles_per_chunk = (n_tiles + chunks - 1) / chunks;
     pl.n_chunks = static_cast<int>((n_tiles + pl.tiles_per_chunk - 1) / pl.tiles_per_chunk);
+    if (pl.path == PATH_ROWS) {
+      // a head mask leaves fewer groups: the pass then splits the keys further
+      int64_t dm = cap < FB_ROWS_MAX_DYN ? cap : FB_ROWS_MAX_DYN;
+      pl.dyn_max = static_cast<int>(dm > pl.n_chunks ? dm : pl.n_chunks);
+    }
   }
+  pl.n_tiles = n_tiles;
   pl.direct = pl.n_chunks == 1 && mode == FB_SEL_DENSE;
-  if (!pl.direct && pl.n_chunks > 0) {
-    const size_t nc = static_cast<size_t>(pl.n_chunks);
+  const int ws_chunks = pl.dyn_max > pl.n_chunks ? pl.dyn_max : pl.n_chunks;
+  if ((!pl.direct || ws_chunks > 1) && pl.n_chunks > 0) {
+    const size_t nc = static_cast<size_t>(ws_chunks);
     const size_t a_bytes = align_up(nc * pl.rows * s.head_dim * sizeof(float));
     const size_t l_bytes = align_up(nc * pl.rows * sizeof(float));
     pl.off_l = a_bytes;
@@ -236,7 +248,9 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
     pp.pages = sel->pages;
     pp.active = mode == FB_SEL_GATHER ? sel->active : nullptr;
   }
-  if (pl.direct) {
+  // many rows with a head mask: key chunks from the mask, partials + reduce
+  const bool dyn = pl.path == PATH_ROWS && mask && pl.dyn_max > 1;
+  if (pl.direct && !dyn) {
     pp.out = RowOut{a_out, l_out, 0};
   } else {
     pp.out = RowOut{reinterpret_cast<float*>(w), reinterpret_cast<float*>(w + pl.off_l), pl.rows};
@@ -289,7 +303,13 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
       rp.n_rtiles = pl.n_rtiles;
       rp.tiles_per_chunk = pl.tiles_per_chunk;
       rp.n_chunks = pl.n_chunks;
-      rp.n_items = s.n_kv_heads * pl.n_chunks * pl.n_rtiles;
+      if (dyn) {
+        rp.dyn = RowsDyn{1, pl.n_rtiles, s.n_kv_heads, pp.group, pl.dyn_max,
+                         static_cast<int>(kTargetWorkgroups) * rows_occupancy(), pl.n_tiles};
+        rp.n_chunks = pl.dyn_max;
+        rp.tiles_per_chunk = 0;                    // (from the mask, on the device)
+      }
+      rp.n_items = s.n_kv_heads * rp.n_chunks * pl.n_rtiles;
       rp.out = pp.out;
       e = launch_rows(rp, stream);
     } else {
@@ -298,12 +318,15 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
     }
     if (e != hipSuccess) return FB_ERR_DEVICE;
   }
-  if (pl.direct) return FB_OK;
+  if (pl.direct && !dyn) return FB_OK;
   ReduceParams rp;
   memset(&rp, 0, sizeof(rp));
   rp.part_a = pp.out.a;
   rp.part_l = pp.out.l;
   rp.n_chunks = pl.n_chunks;
+  if (dyn)
+    rp.dyn = RowsDyn{1, pl.n_rtiles, s.n_kv_heads, pp.group, pl.dyn_max,
+                     static_cast<int>(kTargetWorkgroups) * rows_occupancy(), pl.n_tiles};
   rp.rows = pl.rows;
   rp.hq = s.n_q_heads;
   rp.d = s.head_dim;

@@ -52,6 +52,45 @@ struct PrefixParams {
   const int32_t* ucnt;          // GATHER: [Hkv] union sizes
 };
 
+// Split-K of the many-rows pass sized on the device: when a head mask leaves
+// n_on KV groups to compute, the pass takes as many key chunks as keep about
+// `target` workgroups busy (at most c_max, every chunk non-empty). The pass
+// and the reduce that merges its partials both derive the split from the
+// same mask with this function.
+struct RowsDyn {
+  int on;                       // 1: chunks from the mask (partials + reduce)
+  int n_rtiles, hkv, group, c_max, target;
+  int64_t n_tiles;              // 32-key tiles of the prefix
+};
+struct RowsSplit {
+  int chunks;
+  int64_t tiles_per_chunk;
+};
+__host__ __device__ inline RowsSplit rows_dyn_split(int n_on, const RowsDyn& d) {
+  const int64_t base = static_cast<int64_t>(n_on > 0 ? n_on : 1) * d.n_rtiles;
+  int64_t c = (d.target + base / 2) / base;
+  if (c < 1) c = 1;
+  if (c > d.c_max) c = d.c_max;
+  if (c > d.n_tiles) c = d.n_tiles;
+  if (c < 1) c = 1;
+  const int64_t tpc = (d.n_tiles + c - 1) / c;
+  RowsSplit r;
+  r.chunks = static_cast<int>((d.n_tiles + tpc - 1) / tpc);
+  r.tiles_per_chunk = tpc;
+  return r;
+}
+// KV groups with at least one head the mask does not skip
+__host__ __device__ inline int groups_on(const uint8_t* mask, int hkv, int group) {
+  if (!mask) return hkv;
+  int n = 0;
+  for (int g = 0; g < hkv; ++g) {
+    bool on = false;
+    for (int j = 0; j < group; ++j) on = on || mask[g * group + j] == 0;
+    n += on ? 1 : 0;
+  }
+  return n;
+}
+
 struct ReduceParams {
   const float* part_a; const float* part_l;   // [n_chunks][rows][D], [n_chunks][rows]
   const float* part_ra; const float* part_rl; // SPLIT residual partials (nullable)
@@ -63,6 +102,7 @@ struct ReduceParams {
   const float* res_a; const float* res_l;     // GATHER: cached residual input
   float* a_out; float* l_out;   // merged (all partials [+ residual])
   float* a_res; float* l_res;   // SPLIT: residual-only merge
+  RowsDyn dyn;                  // dyn.on: n_chunks = the many-rows pass's split from the mask
 };
 
 // ---- launchers (return hipError_t of the launch) -----------------------
@@ -106,6 +146,7 @@ struct RowsParams {
   int n_chunks;
   int n_items;                  // hkv * n_chunks * n_rtiles
   RowOut out;                   // plain: A, L (direct or partials); merge: A_full, L_full
+  RowsDyn dyn;                  // dyn.on: split from the mask, n_chunks = its maximum
   const float* a_prev; const float* l_prev;   // merge epilogue: cached pair (null = plain)
   float* a_raw; float* l_raw;   // merge epilogue: optional fresh (A_in, L_in)
 };

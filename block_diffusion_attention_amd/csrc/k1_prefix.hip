@@ -755,7 +755,8 @@ __global__ __launch_bounds__(128) void prefix_reduce_kernel(ReduceParams p) {
   if (p.mask && p.mask[h]) return;
   if (p.active && !p.active[t]) return;
   const int tid = threadIdx.x;
-  const int nc = p.n_chunks;
+  const int nc = p.dyn.on ? rows_dyn_split(groups_on(p.mask, p.dyn.hkv, p.dyn.group), p.dyn).chunks
+                          : p.n_chunks;
   const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
   const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
 

@@ -116,32 +116,57 @@ template <> __device__ __forceinline__ double ldd<uint16_t>(const uint16_t* p) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(*p) << 16));
 }
 
-// One thread per block token: the float64 sum runs sequentially over
-// (head, dim); contraction into fused multiply-add is disabled so the
-// rounding sequence is exactly diff, square, add.
+// One workgroup per block token: the squared differences (diff and square in
+// float64, each one rounding as in a scalar loop) are formed in parallel into
+// LDS, and one thread adds them sequentially in (head, dim) order;
+// contraction into fused multiply-add is disabled, so the rounding sequence
+// is exactly diff, square, add.
+constexpr int kMseSlab = 4096;                     // squares staged per pass (32 KB)
+
 template <typename T>
-__global__ __launch_bounds__(256) void active_mse_kernel(const T* q_prev, const T* q_cur, int n_q,
-                                                         int hq, int d, int pct, double* mse_out,
-                                                         uint8_t* active, double* ws) {
+__global__ __launch_bounds__(256) void active_mse_kernel(const T* q_prev, const T* q_cur, int hq,
+                                                         int d, double* mse_out, double* ws) {
 #pragma clang fp contract(off)
+  __shared__ double sq[kMseSlab];
+  const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t per = static_cast<int64_t>(hq) * d;
-  for (int t = tid; t < n_q; t += blockDim.x) {
-    const T* a = q_prev + t * per;
-    const T* b = q_cur + t * per;
-    double acc = 0.0;
-    for (int64_t e = 0; e < per; ++e) {
-      const double diff = ldd<T>(b + e) - ldd<T>(a + e);
-      const double sq = diff * diff;
-      acc = acc + sq;
+  const T* a = q_prev + t * per;
+  const T* b = q_cur + t * per;
+  double acc = 0.0;
+  for (int64_t base = 0; base < per; base += kMseSlab) {
+    const int n = per - base < kMseSlab ? static_cast<int>(per - base) : kMseSlab;
+    for (int e = tid; e < n; e += 256) {
+      const double diff = ldd<T>(b + base + e) - ldd<T>(a + base + e);
+      sq[e] = diff * diff;
     }
+    __syncthreads();
+    if (tid == 0) {
+      int e = 0;
+      for (; e + 8 <= n; e += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = sq[e + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = acc + v[u];
+      }
+      for (; e < n; ++e) acc = acc + sq[e];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
     const double v = acc / static_cast<double>(per);
     ws[t] = v;
     if (mse_out) mse_out[t] = v;
   }
-  __syncthreads();
-  // nearest-rank cutoff: the rank-th smallest, rank = ceil(pct * n / 100)
+}
+
+// Nearest-rank cutoff over the block's MSE values (the rank-th smallest,
+// rank = ceil(pct * n / 100)) and the active flags MSE > cutoff.
+__global__ __launch_bounds__(256) void active_cut_kernel(int n_q, int pct, const double* ws,
+                                                         uint8_t* active) {
   __shared__ double cutoff;
+  const int tid = threadIdx.x;
   int rank = (pct * n_q + 99) / 100;
   if (rank < 1) rank = 1;
   for (int t = tid; t < n_q; t += blockDim.x) {
@@ -242,14 +267,18 @@ hipError_t launch_head_cos(const float* a_cached, const float* a_probe, int n_q,
 hipError_t launch_active_mse(const void* q_prev, const void* q_cur, fb_dtype dt, int n_q, int hq,
                              int d, int pct, double* mse, uint8_t* active, double* ws,
                              hipStream_t s) {
+  if (n_q < 1) return hipSuccess;
   if (dt == FB_BF16)
-    hipLaunchKernelGGL(active_mse_kernel<uint16_t>, dim3(1), dim3(256), 0, s,
+    hipLaunchKernelGGL(active_mse_kernel<uint16_t>, dim3(n_q), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q_prev), static_cast<const uint16_t*>(q_cur),
-                       n_q, hq, d, pct, mse, active, ws);
+                       hq, d, mse, ws);
   else
-    hipLaunchKernelGGL(active_mse_kernel<float>, dim3(1), dim3(256), 0, s,
-                       static_cast<const float*>(q_prev), static_cast<const float*>(q_cur), n_q,
-                       hq, d, pct, mse, active, ws);
+    hipLaunchKernelGGL(active_mse_kernel<float>, dim3(n_q), dim3(256), 0, s,
+                       static_cast<const float*>(q_prev), static_cast<const float*>(q_cur), hq, d,
+                       mse, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(active_cut_kernel, dim3(1), dim3(256), 0, s, n_q, pct, ws, active);
   return hipGetLastError();
 }
 

@@ -180,25 +180,47 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   constexpr int kStages = 4;
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
 
+  // Work items are (KV group with an unmasked head, chunk, row tile), the
+  // groups compacted so that heads a mask skips take no share of the grid.
   // XCD-aware order: workgroup id i runs on XCD i mod 8, and XCD x takes the
-  // x-th contiguous range of work items, so the row tiles of one (KV head,
-  // chunk) run side by side on one XCD and share its L2 for the K/V tiles.
+  // x-th contiguous range of items, so the row tiles of one (group, chunk)
+  // run side by side on one XCD and share its L2 for the K/V tiles.
+  const int G = p.group;
+  auto group_on = [&](int gg) -> bool {
+    if (!p.mask) return true;
+    for (int j = 0; j < G; ++j)
+      if (p.mask[gg * G + j] == 0) return true;
+    return false;
+  };
+  const int n_on = groups_on(p.mask, p.hkv, G);
+  int n_chunks = p.n_chunks;
+  int64_t tiles_per_chunk = p.tiles_per_chunk;
+  if (p.dyn.on) {
+    const RowsSplit sp = rows_dyn_split(n_on, p.dyn);
+    n_chunks = sp.chunks;
+    tiles_per_chunk = sp.tiles_per_chunk;
+  }
   int rt, chunk, g;
   {
+    const int n_items = n_on * n_chunks * p.n_rtiles;
     const int id = blockIdx.x;
-    const int per = (p.n_items + 7) >> 3;
+    const int per = (n_items + 7) >> 3;
     const int item = (id & 7) * per + (id >> 3);
-    if (item >= p.n_items) return;
+    if ((id >> 3) >= per || item >= n_items) return;
     rt = item % p.n_rtiles;
     const int rest = item / p.n_rtiles;
-    chunk = rest % p.n_chunks;
-    g = rest / p.n_chunks;
-  }
-  const int G = p.group;
-  if (p.mask) {                                    // every head of the group reused?
-    bool all = true;
-    for (int j = 0; j < G; ++j) all = all && p.mask[g * G + j] != 0;
-    if (all) return;
+    chunk = rest % n_chunks;
+    int gi = rest / n_chunks;                      // gi-th group that is on
+    g = 0;
+    for (int gg = 0; gg < p.hkv; ++gg) {
+      if (group_on(gg)) {
+        if (gi == 0) {
+          g = gg;
+          break;
+        }
+        --gi;
+      }
+    }
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,8 +242,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   }
 
   const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
-  const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
-  const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
+  const int64_t t_begin = static_cast<int64_t>(chunk) * tiles_per_chunk;
+  const int64_t t_end = t_begin + tiles_per_chunk < n_tiles ? t_begin + tiles_per_chunk : n_tiles;
   const int64_t t_last = t_end - 1;                // every launched chunk has a tile
 
   // staging: thread = (rows lr + 4 NW i of the tile, 16-byte piece lp)

@@ -122,3 +122,17 @@ def test_rows_block_merge_optional_outputs(fb):
                            torch.from_numpy(lo).cuda(), a)
     torch.cuda.synchronize()
     check_a("A_full only", cpu(a), af, 2e-3)
+
+
+@pytest.mark.parametrize("n_on", [1, 4, 11])
+def test_rows_prefix_mask_sized_split(fb, n_on):
+    # with a head mask the pass splits the keys by the number of heads left
+    # (partials + reduce); skipped heads stay untouched
+    rng = np.random.default_rng(n_on)
+    on = rng.choice(12, size=n_on, replace=False)
+    mask = [0 if h in on else 1 for h in range(12)]
+    a, l, ra, rl, cfg = run_prefix(fb, W.VIDEO, 300, 9000, mask=mask)
+    m = np.array(mask, bool)
+    assert np.all(a[:, m] == 7.0) and np.all(l[:, m] == 7.0)
+    check_a("A_out of computed heads", a[:, ~m], ra[:, ~m], 2e-3)
+    check_l("L_out of computed heads", l[:, ~m], rl[:, ~m], 1e-3)
