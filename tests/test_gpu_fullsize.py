@@ -1,0 +1,213 @@
+"""GPU parity at the full sizes the benchmark times, on sampled outputs.
+
+* long-context text: 32q/8kv heads, d = 128, B = 16 block queries over an
+  800,000-token prefix: the prefix pass in the launch configuration bench.py
+  times, and a whole 8-step block through fb_step (decisions recounted from
+  the token ids);
+* video: 12 MHA heads, 4,680 block queries, 12,480 prefix tokens: the prefix
+  pass (plain and with a head mask), the in-block pass with the merge, and
+  the per-head cosine decision on synthetic [4680, 12, 128] outputs.
+
+The oracle computes the sampled rows one by one (float64 dense softmax over
+every key of the row's KV head); properties that hold at any size (finite
+outputs, untouched skipped heads, bit-identical reruns) are checked on all
+rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import controller as OC
+from oracle.attention import attn, merge
+from _helpers import check_a, check_l, cpu, dev_tensor, vals
+
+pytestmark = pytest.mark.gpu
+
+N_TEXT, B_TEXT = 800000, 16
+
+
+@pytest.fixture(scope="module")
+def text_800k():
+    cfg = W.LONG.with_(n_prefix=N_TEXT, n_block=B_TEXT)
+    kp, vp = W.prefix_kv(cfg)
+    steps = W.text_steps(cfg)
+    return cfg, kp, vp, steps
+
+
+def _rows_ref(q, kp, vp, scale, rows, hq, hkv):
+    """Oracle A, L for sampled (t, h) rows; one KV head in float64 at a time."""
+    G = hq // hkv
+    out_a, out_l = {}, {}
+    for g in sorted({h // G for _, h in rows}):
+        kg = vals(kp[:, g, :], "bf16")
+        vg = vals(vp[:, g, :], "bf16")
+        for t, h in rows:
+            if h // G != g:
+                continue
+            a, l = attn(vals(q[t:t + 1, h, :], "bf16"), kg, vg, scale)
+            out_a[(t, h)], out_l[(t, h)] = a[0], l[0]
+    return out_a, out_l
+
+
+def _sample_rows(n_q, hq, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({(int(rng.integers(n_q)), int(rng.integers(hq))) for _ in range(n)})
+
+
+def test_text_800k_prefix_pass_sampled(fb, text_800k):
+    cfg, kp, vp, steps = text_800k
+    hq, hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    q = steps[0]["q"]
+    shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
+    kd, vd = dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16")
+    a = torch.empty(B_TEXT, hq, d, device="cuda")
+    l = torch.empty(B_TEXT, hq, device="cuda")
+    ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, B_TEXT, N_TEXT), 16), dtype=torch.uint8,
+                     device="cuda")
+    fb.fb_prefix_attn(shape, dev_tensor(q, "bf16"), kd, vd, a, l, ws=ws)
+    torch.cuda.synchronize()
+    a1, l1 = cpu(a), cpu(l)
+    fb.fb_prefix_attn(shape, dev_tensor(q, "bf16"), kd, vd, a, l, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(a1, cpu(a)) and np.array_equal(l1, cpu(l))   # fixed-order split-K
+    assert np.all(np.isfinite(a1)) and np.all(np.isfinite(l1))
+    rows = _sample_rows(B_TEXT, hq, 24, seed=1) + [(0, 0), (B_TEXT - 1, hq - 1)]
+    ra, rl = _rows_ref(q, kp, vp, cfg.scale, rows, hq, hkv)
+    got_a = np.stack([a1[t, h] for t, h in rows])
+    got_l = np.array([l1[t, h] for t, h in rows])
+    check_a("800k A_out rows", got_a, np.stack([ra[r] for r in rows]), 2e-3)
+    check_l("800k L_out rows", got_l, np.array([rl[r] for r in rows]), 1e-3)
+
+
+def test_text_800k_block_sampled(fb, text_800k):
+    cfg, kp, vp, steps = text_800k
+    hq, hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
+    step = fb.Step(fb.FB_STEP_TEXT, shape, B_TEXT, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
+                   tau=cfg.tau)
+    G = hq // hkv
+    # rows of two KV groups (their float64 K/V are held for the whole block)
+    rows = [(t, h) for t, h in _sample_rows(B_TEXT, hq, 40, seed=2) if h // G in (0, 5)][:12]
+    kg = {g: (vals(kp[:, g, :], "bf16"), vals(vp[:, g, :], "bf16")) for g in {h // G for _, h in rows}}
+    cached = {}
+    prev_ids = None
+    for s, st in enumerate(steps):
+        a = torch.empty(B_TEXT, hq, d, device="cuda")
+        l = torch.empty(B_TEXT, hq, device="cuda")
+        step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                  dev_tensor(st["v"], "bf16"), a, l, ids=torch.from_numpy(st["ids"]).cuda())
+        torch.cuda.synchronize()
+        if s == 0:
+            reuse = False
+        else:
+            m = OC.count_updated(prev_ids, st["ids"])
+            reuse = bool(OC.text_reuse(m, cfg.tau))
+            assert int(step.m_count.item()) == m
+            assert np.all(cpu(step.mask) == (1 if reuse else 0))
+        prev_ids = st["ids"]
+        a_np, l_np = cpu(a), cpu(l)
+        for t, h in rows:
+            g = h // G
+            qr = vals(st["q"][t:t + 1, h, :], "bf16")
+            if not reuse:
+                cached[(t, h)] = attn(qr, kg[g][0], kg[g][1], cfg.scale)
+            ao, lo = cached[(t, h)]
+            ai, li = attn(qr, vals(st["k"][:, g, :], "bf16"), vals(st["v"][:, g, :], "bf16"),
+                          cfg.scale)
+            af, lf = merge(ao, lo, ai, li)
+            check_a("step %d row %s A_full" % (s, (t, h)), a_np[t, h], af[0], 2e-3)
+            check_l("step %d row %s L_full" % (s, (t, h)), l_np[t, h:h + 1], lf, 1e-3)
+
+
+@pytest.fixture(scope="module")
+def video_full():
+    cfg = W.VIDEO
+    kp, vp = W.prefix_kv(cfg)
+    st = W.video_steps(cfg.with_(n_steps=1), W.video_sigmas(cfg, 0))[0]
+    return cfg, kp, vp, st
+
+
+def test_video_full_prefix_and_block_sampled(fb, video_full):
+    cfg, kp, vp, st = video_full
+    H, d, NQ, NK = cfg.n_q_heads, cfg.head_dim, cfg.n_block, cfg.n_prefix
+    shape = fb.shape_of(H, H, d, cfg.scale, torch.bfloat16)
+    q, kb, vb = (dev_tensor(st[x], "bf16") for x in ("q", "k", "v"))
+    kd, vd = dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16")
+    a = torch.empty(NQ, H, d, device="cuda")
+    l = torch.empty(NQ, H, device="cuda")
+    ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, NQ, NK), 16), dtype=torch.uint8,
+                     device="cuda")
+    fb.fb_prefix_attn(shape, q, kd, vd, a, l, ws=ws)
+    af = torch.empty(NQ, H, d, device="cuda")
+    lf = torch.empty(NQ, H, device="cuda")
+    ai = torch.empty(NQ, H, d, device="cuda")
+    li = torch.empty(NQ, H, device="cuda")
+    fb.fb_block_attn_merge(shape, q, kb, vb, a, l, af, lf, ai, li)
+    torch.cuda.synchronize()
+    A, L, AF, LF, AI, LI = (cpu(x) for x in (a, l, af, lf, ai, li))
+    for x in (A, L, AF, LF):
+        assert np.all(np.isfinite(x))
+    rows = _sample_rows(NQ, H, 40, seed=3) + [(0, 0), (NQ - 1, H - 1)]
+    for t, h in rows:
+        qr = vals(st["q"][t:t + 1, h, :], "bf16")
+        ao, lo = attn(qr, vals(kp[:, h, :], "bf16"), vals(vp[:, h, :], "bf16"), cfg.scale)
+        ain, lin = attn(qr, vals(st["k"][:, h, :], "bf16"), vals(st["v"][:, h, :], "bf16"), cfg.scale)
+        afr, lfr = merge(ao, lo, ain, lin)
+        check_a("video row %s A_out" % ((t, h),), A[t, h], ao[0], 2e-3)
+        check_l("video row %s L_out" % ((t, h),), L[t, h:h + 1], lo, 1e-3)
+        check_a("video row %s A_in" % ((t, h),), AI[t, h], ain[0], 2e-3)
+        check_l("video row %s L_in" % ((t, h),), LI[t, h:h + 1], lin, 1e-3)
+        check_a("video row %s A_full" % ((t, h),), AF[t, h], afr[0], 2e-3)
+        check_l("video row %s L_full" % ((t, h),), LF[t, h:h + 1], lfr, 1e-3)
+
+
+def test_video_full_masked_prefix_sampled(fb, video_full):
+    # 4 of 12 heads recompute: the pass splits its keys by the heads left
+    cfg, kp, vp, st = video_full
+    H, d, NQ, NK = cfg.n_q_heads, cfg.head_dim, cfg.n_block, cfg.n_prefix
+    mask = np.ones(H, np.uint8)
+    mask[[1, 4, 7, 11]] = 0
+    shape = fb.shape_of(H, H, d, cfg.scale, torch.bfloat16)
+    a = torch.full((NQ, H, d), 7.0, device="cuda")
+    l = torch.full((NQ, H), 7.0, device="cuda")
+    ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, NQ, NK), 16), dtype=torch.uint8,
+                     device="cuda")
+    fb.fb_prefix_attn(shape, dev_tensor(st["q"], "bf16"), dev_tensor(kp, "bf16"),
+                      dev_tensor(vp, "bf16"), a, l, mask=torch.from_numpy(mask).cuda(), ws=ws)
+    torch.cuda.synchronize()
+    A, L = cpu(a), cpu(l)
+    m = mask.astype(bool)
+    assert np.all(A[:, m] == 7.0) and np.all(L[:, m] == 7.0)
+    rows = [(t, h) for t, h in _sample_rows(NQ, H, 60, seed=4) if not m[h]]
+    for t, h in rows:
+        qr = vals(st["q"][t:t + 1, h, :], "bf16")
+        ao, lo = attn(qr, vals(kp[:, h, :], "bf16"), vals(vp[:, h, :], "bf16"), cfg.scale)
+        check_a("masked video row %s A_out" % ((t, h),), A[t, h], ao[0], 2e-3)
+        check_l("masked video row %s L_out" % ((t, h),), L[t, h:h + 1], lo, 1e-3)
+
+
+def test_video_full_head_cosine(fb):
+    # the per-head decision at the video output size, on synthetic fp32 outputs
+    rng = np.random.default_rng(21)
+    nq, hq, d = 4680, 12, 128
+    a_c = (0.05 * rng.standard_normal((nq, hq, d))).astype(np.float32)
+    noise = np.array([0.0, 1e-3, 0.02, 0.1, 0.3, 0.5, 1.0, 2.0, 0.25, 0.33, 0.05, 0.8])
+    a_p = (a_c + 0.05 * noise[None, :, None] * rng.standard_normal((nq, hq, d))).astype(np.float32)
+    gamma = 0.95
+    want = OC.head_cosine(a_p, a_c)
+    assert np.all(np.abs(want - gamma) > 1e-6)          # no decision within rounding of gamma
+    args = fb.fb_reuse_args()
+    args.mode, args.n_q, args.n_heads, args.head_dim = fb.FB_REUSE_HEAD_COS, nq, hq, d
+    dc, dp = torch.from_numpy(a_c).cuda(), torch.from_numpy(a_p).cuda()
+    sim = torch.full((hq,), -7.0, dtype=torch.float64, device="cuda")
+    mask = torch.zeros(hq, dtype=torch.uint8, device="cuda")
+    args.a_cached, args.a_probe = dc.data_ptr(), dp.data_ptr()
+    args.gamma, args.sim, args.mask = gamma, sim.data_ptr(), mask.data_ptr()
+    ws = torch.empty(fb.fb_reuse_decide_workspace(args), dtype=torch.uint8, device="cuda")
+    args.ws, args.ws_bytes = ws.data_ptr(), ws.numel()
+    fb.fb_reuse_decide(args)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(cpu(sim) - want)) < 1e-12
+    assert np.array_equal(cpu(mask).astype(bool), OC.head_reuse(want, gamma))
