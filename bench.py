@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
+    ap.add_argument("--only", choices=("video", "sparse"),
+                    help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
     ap.add_argument("--prefix-only", action="store_true",
@@ -94,6 +96,10 @@ def main():
     fb.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        fn = video_extra if args.only == "video" else sparse_extra
+        print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream())}), flush=True)
+        return
     cfg = W.LONG.with_(n_prefix=args.n_prefix, n_block=args.block)
     hq, hkv, d, B, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_block, cfg.n_prefix
 

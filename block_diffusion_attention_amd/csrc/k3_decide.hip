@@ -116,46 +116,43 @@ template <> __device__ __forceinline__ double ldd<uint16_t>(const uint16_t* p) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(*p) << 16));
 }
 
-// One workgroup per block token: the squared differences (diff and square in
-// float64, each one rounding as in a scalar loop) are formed in parallel into
-// LDS, and one thread adds them sequentially in (head, dim) order;
-// contraction into fused multiply-add is disabled, so the rounding sequence
-// is exactly diff, square, add.
-constexpr int kMseSlab = 4096;                     // squares staged per pass (32 KB)
-
+// One workgroup per block token. Thread h adds the squared differences of
+// head h in dim order (diff, square, add in float64; contraction into fused
+// multiply-add is disabled), and thread 0 adds the per-head sums in head
+// order: the same rounding sequence as a scalar loop in that order.
 template <typename T>
 __global__ __launch_bounds__(256) void active_mse_kernel(const T* q_prev, const T* q_cur, int hq,
                                                          int d, double* mse_out, double* ws) {
 #pragma clang fp contract(off)
-  __shared__ double sq[kMseSlab];
+  __shared__ double part[256];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t per = static_cast<int64_t>(hq) * d;
   const T* a = q_prev + t * per;
   const T* b = q_cur + t * per;
-  double acc = 0.0;
-  for (int64_t base = 0; base < per; base += kMseSlab) {
-    const int n = per - base < kMseSlab ? static_cast<int>(per - base) : kMseSlab;
-    for (int e = tid; e < n; e += 256) {
-      const double diff = ldd<T>(b + base + e) - ldd<T>(a + base + e);
-      sq[e] = diff * diff;
+  double total = 0.0;
+  for (int h0 = 0; h0 < hq; h0 += 256) {           // 256 heads per pass
+    const int h = h0 + tid;
+    if (h < hq) {
+      const T* ah = a + static_cast<int64_t>(h) * d;
+      const T* bh = b + static_cast<int64_t>(h) * d;
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j) {
+        const double diff = ldd<T>(bh + j) - ldd<T>(ah + j);
+        const double sq = diff * diff;
+        acc = acc + sq;
+      }
+      part[tid] = acc;
     }
     __syncthreads();
     if (tid == 0) {
-      int e = 0;
-      for (; e + 8 <= n; e += 8) {
-        double v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = sq[e + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc = acc + v[u];
-      }
-      for (; e < n; ++e) acc = acc + sq[e];
+      const int n = hq - h0 < 256 ? hq - h0 : 256;
+      for (int i = 0; i < n; ++i) total = total + part[i];
     }
     __syncthreads();
   }
   if (tid == 0) {
-    const double v = acc / static_cast<double>(per);
+    const double v = total / static_cast<double>(per);
     ws[t] = v;
     if (mse_out) mse_out[t] = v;
   }

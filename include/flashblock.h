@@ -166,10 +166,10 @@ typedef enum {
      mask_in[h] == 0: sim[h] updated, mask[h] = (sim[h] > gamma); heads with
      mask_in[h] == 1 keep sim[h] and get mask[h] = 1.                        */
   FB_REUSE_HEAD_COS = 1,
-  /* LoSA s2 token classification: mse[t] = sum over (head, dim), in that
-     order, of (q_cur - q_prev)^2 in float64 without fused multiply-add, then
-     divided by Hq*d; cutoff = the ceil(pct/100 * n_q)-th smallest mse;
-     active[t] = mse[t] > cutoff.                                            */
+  /* LoSA s2 token classification: mse[t] = (sum over heads, in head order,
+     of the head's sum over dims, in dim order, of (q_cur - q_prev)^2) / (Hq*d),
+     in float64 without fused multiply-add; cutoff = the ceil(pct/100 * n_q)-th
+     smallest mse; active[t] = mse[t] > cutoff.                              */
   FB_REUSE_ACTIVE_MSE = 2
 } fb_reuse_mode;
 

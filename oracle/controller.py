@@ -83,21 +83,24 @@ def active_mse(q_prev, q_cur):
 
     [LoSA s2 "token classification", "workflow"]: the score is the MSE
     between a token's query at step t and at step t-1, over all query heads
-    and dims. Float64, sequential over (head, dim) for every token: diff,
-    square, add; then one division by Hq*d.
+    and dims. The pages fix no summation order; reading: float64, for each
+    head the squared differences are added in dim order (diff, square, add),
+    the per-head sums are added in head order, then one division by Hq*d.
 
     q_prev, q_cur [B, Hq, d]  ->  mse [B] float64.
     """
     a = np.asarray(q_prev, dtype=np.float64)
     b = np.asarray(q_cur, dtype=np.float64)
     n_tok, hq, d = a.shape
-    acc = np.zeros(n_tok)
+    total = np.zeros(n_tok)
     for h in range(hq):
+        acc = np.zeros(n_tok)
         for j in range(d):
             diff = b[:, h, j] - a[:, h, j]
             sq = diff * diff
             acc = acc + sq
-    return acc / float(hq * d)
+        total = total + acc
+    return total / float(hq * d)
 
 
 def percentile_cutoff(mse, pct=25):

@@ -273,3 +273,15 @@ def test_sparse_stable_rows_keep_their_output():
         for g in range(cfg.n_kv_heads):
             want = len(set(recs[0]["sel"][act, g].ravel().tolist())) if act.any() else 0
             assert u[g] == want
+
+
+def test_mse_sums_each_head_in_dim_order_then_heads():
+    # Worked by hand (float64, round to nearest even). One token, 2 heads,
+    # d = 2; squared differences: head 0 = [2^54, 1], head 1 = [2.25, 2.25].
+    # Per head: 2^54 + 1 -> 2^54 (ulp 4); 2.25 + 2.25 = 4.5. Over heads:
+    # 2^54 + 4.5 -> 2^54 + 4. (One flat sequential sum would give 2^54 + 8:
+    # 2^54 + 1 -> 2^54, + 2.25 -> 2^54 + 4, + 2.25 -> 2^54 + 8.)
+    q_prev = np.zeros((1, 2, 2))
+    q_cur = np.array([[[2.0 ** 27, 1.0], [1.5, 1.5]]])
+    mse = C.active_mse(q_prev, q_cur)
+    assert mse[0] == (2.0 ** 54 + 4.0) / 4.0
