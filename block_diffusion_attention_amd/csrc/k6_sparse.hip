@@ -198,8 +198,11 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
     n_vt = (n_half + 1) / 2;
     ulist = p.ulist + static_cast<int64_t>(g) * p.n_pages;
   }
-  const int64_t vt_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
-  const int64_t vt_end = vt_begin + p.tiles_per_chunk < n_vt ? vt_begin + p.tiles_per_chunk : n_vt;
+  // GATHER: the planned chunks share the actual union (no more tiles each
+  // than planned for a union of every page)
+  const int64_t tpc = SPLIT ? p.tiles_per_chunk : (n_vt + p.n_chunks - 1) / p.n_chunks;
+  const int64_t vt_begin = static_cast<int64_t>(chunk) * tpc;
+  const int64_t vt_end = vt_begin + tpc < n_vt ? vt_begin + tpc : n_vt;
 
   auto out_row = [&](int r, int set) -> int64_t {
     const RowOut& out = set == 0 ? p.out : p.out_res;
