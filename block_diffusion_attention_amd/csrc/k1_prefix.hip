@@ -736,19 +736,17 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kMaxChunks = 1024;
 
-__device__ __forceinline__ float block_max128(float v, float* red) {
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = fmaxf(red[0], red[1]);
-  __syncthreads();
-  return r;
-}
 
-__global__ __launch_bounds__(128) void prefix_reduce_kernel(ReduceParams p) {
+// One workgroup (256 threads) per output row. Thread (half, c) sums dim c
+// over its half of the chunks with every load of the half in flight at
+// once, and the two halves meet in LDS; the chunk weights come from one
+// wave's max. The chunk order of every sum is fixed, so results are
+// run-to-run identical.
+__global__ __launch_bounds__(256) void prefix_reduce_kernel(ReduceParams p) {
   __shared__ float wa[kMaxChunks];
   __shared__ float wr[kMaxChunks + 1];
-  __shared__ float red[2];
+  __shared__ float red[4];
+  __shared__ float half_acc[2][2][128];            // [half][set][dim]
   const int64_t row = blockIdx.x;
   const int h = static_cast<int>(row % p.hq);
   const int t = static_cast<int>(row / p.hq);
@@ -761,18 +759,27 @@ __global__ __launch_bounds__(128) void prefix_reduce_kernel(ReduceParams p) {
   const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
 
   float m = kNegInf, mr = kNegInf;
-  for (int ch = tid; ch < nc; ch += 128) m = fmaxf(m, p.part_l[ch * p.rows + row]);
-  for (int ch = tid; ch < nr; ch += 128) mr = fmaxf(mr, p.part_rl[ch * p.rows + row]);
+  for (int ch = tid; ch < nc; ch += 256) m = fmaxf(m, p.part_l[ch * p.rows + row]);
+  for (int ch = tid; ch < nr; ch += 256) mr = fmaxf(mr, p.part_rl[ch * p.rows + row]);
   if (cached && tid == 0) mr = fmaxf(mr, p.res_l[row]);
-  const float M = block_max128(m, red);
-  const float Mr = block_max128(mr, red);
+  m = wave_max(m);
+  mr = wave_max(mr);
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = m;
+  }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = mr;
+  __syncthreads();
+  const float Mr = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float Mall = fmaxf(M, Mr);
 
-  for (int ch = tid; ch < nc; ch += 128) {
+  for (int ch = tid; ch < nc; ch += 256) {
     const float L = p.part_l[ch * p.rows + row];
     wa[ch] = L == kNegInf ? 0.f : expf(L - Mall);
   }
-  for (int ch = tid; ch < nr; ch += 128) {
+  for (int ch = tid; ch < nr; ch += 256) {
     const float L = p.part_rl[ch * p.rows + row];
     wr[ch] = L == kNegInf ? 0.f : expf(L - Mr);
   }
@@ -786,24 +793,35 @@ __global__ __launch_bounds__(128) void prefix_reduce_kernel(ReduceParams p) {
   for (int ch = 0; ch < nc; ++ch) S += wa[ch];
   for (int ch = 0; ch < nrt; ++ch) Sr += wr[ch];
 
-  const int c = tid;
+  const int hf = tid >> 7, c = tid & 127;          // half of the chunks, dim
+  const int64_t cs = p.rows * p.d;                 // chunk stride
+  const int mid = (nc + 1) / 2, midr = (nr + 1) / 2;
   if (c < p.d) {
-    float acc = 0.f, accr = 0.f;
+    const int c0 = hf ? mid : 0, c1 = hf ? nc : mid;
+    float acc = 0.f;
     const float* pa = p.part_a + row * p.d + c;
-    const int64_t cs = p.rows * p.d;               // chunk stride
-    int ch = 0;
-    for (; ch + 8 <= nc; ch += 8) {
-      float v[8];
+    int ch = c0;
+    for (; ch + 16 <= c1; ch += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = pa[(ch + u) * cs];
+      for (int u = 0; u < 16; ++u) v[u] = pa[(ch + u) * cs];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += wa[ch + u] * v[u];
+      for (int u = 0; u < 16; ++u) acc += wa[ch + u] * v[u];
     }
-    for (; ch < nc; ++ch) acc += wa[ch] * pa[ch * cs];
+    for (; ch < c1; ++ch) acc += wa[ch] * pa[ch * cs];
+    half_acc[hf][0][c] = acc;
+    float accr = 0.f;
     if (nr) {
+      const int r0 = hf ? midr : 0, r1 = hf ? nr : midr;
       const float* pr = p.part_ra + row * p.d + c;
-      for (ch = 0; ch < nr; ++ch) accr += wr[ch] * pr[ch * cs];
+      for (ch = r0; ch < r1; ++ch) accr += wr[ch] * pr[ch * cs];
     }
+    half_acc[hf][1][c] = accr;
+  }
+  __syncthreads();
+  if (tid < p.d) {
+    const float acc = half_acc[0][0][c] + half_acc[1][0][c];
+    float accr = half_acc[0][1][c] + half_acc[1][1][c];
     if (cached) accr += wr[nr] * p.res_a[row * p.d + c];
     if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
     // fold the residual pair into the full pair (same composition)
@@ -862,7 +880,7 @@ hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t
 }
 
 hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(prefix_reduce_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(prefix_reduce_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
