@@ -548,9 +548,10 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
                          double* bound, void* ws, size_t ws_bytes, hipStream_t stream) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
-  if (q.n_tok < 1) return FB_ERR_INVALID_ARGUMENT;
+  if (q.n_tok < 1 || q.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
   if ((st = check_tensor(q, -1, shape->n_q_heads, shape->head_dim)) != FB_OK) return st;
-  if (n_pages < 0 || k_pages < 0 || k_pages > n_pages) return FB_ERR_INVALID_ARGUMENT;
+  if (n_pages < 0 || n_pages > INT32_MAX || k_pages < 0 || k_pages > n_pages)
+    return FB_ERR_INVALID_ARGUMENT;
   if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
   if (k_pages > 0 && !pages) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
