@@ -266,22 +266,27 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
     hipError_t e;
     if (pl.path == PATH_SPARSE) {
       uint32_t* bm = reinterpret_cast<uint32_t*>(w + pl.off_bm);
-      // (k_pages = 0: the kernel writes all-zero rows and reads no list)
-      e = launch_sel_bitmap(sel->pages, static_cast<int>(n_q) * s.n_kv_heads, sel->k_pages, pl.words,
-                            static_cast<int>(pl.n_pages), bm, stream);
+      const bool gather = mode == FB_SEL_GATHER;
+      int32_t* ul = gather ? reinterpret_cast<int32_t*>(w + pl.off_ul) : nullptr;
+      int32_t* uc = gather ? reinterpret_cast<int32_t*>(w + pl.off_uc) : nullptr;
+      // (k_pages = 0: all-zero bitmaps, no list is read)
+      if (sel_prep_fits(static_cast<int>(n_q), pl.words)) {
+        e = launch_sel_prep(sel->pages, static_cast<int>(n_q), s.n_kv_heads, sel->k_pages, pl.words,
+                            static_cast<int>(pl.n_pages), sel->active, gather ? 1 : 0, bm, ul, uc,
+                            stream);
+      } else {
+        e = launch_sel_bitmap(sel->pages, static_cast<int>(n_q) * s.n_kv_heads, sel->k_pages,
+                              pl.words, static_cast<int>(pl.n_pages), bm, stream);
+        if (e == hipSuccess && gather)
+          e = launch_sel_union(bm, sel->active, static_cast<int>(n_q), s.n_kv_heads, pl.words, ul,
+                               uc, static_cast<int>(pl.n_pages), stream);
+      }
       if (e != hipSuccess) return FB_ERR_DEVICE;
       pp.bitmap = bm;
       pp.words = pl.words;
       pp.n_pages = pl.n_pages;
-      if (mode == FB_SEL_GATHER) {
-        int32_t* ul = reinterpret_cast<int32_t*>(w + pl.off_ul);
-        int32_t* uc = reinterpret_cast<int32_t*>(w + pl.off_uc);
-        e = launch_sel_union(bm, sel->active, static_cast<int>(n_q), s.n_kv_heads, pl.words, ul, uc,
-                             static_cast<int>(pl.n_pages), stream);
-        if (e != hipSuccess) return FB_ERR_DEVICE;
-        pp.ulist = ul;
-        pp.ucnt = uc;
-      }
+      pp.ulist = ul;
+      pp.ucnt = uc;
       e = launch_prefix_sparse(pp, stream);
     } else if (pl.path == PATH_ROWS) {
       RowsParams rp;
@@ -667,14 +672,32 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       if (st->page_size < 1 || st->pct < 1 || st->pct > 100) return FB_ERR_INVALID_ARGUMENT;
       const int64_t n_pages = (st->k_prefix.n_tok + st->page_size - 1) / st->page_size;
       if (st->k_pages < 0 || st->k_pages > n_pages) return FB_ERR_INVALID_ARGUMENT;
-      // the active-set kernel reads contiguous [n_q, Hq, d] queries
-      if (a->q_blk.stride_head != d || a->q_blk.stride_tok != static_cast<int64_t>(hq) * d)
-        return FB_ERR_UNSUPPORTED;
       fb_page_sel sel;
       memset(&sel, 0, sizeof(sel));
       sel.page_size = st->page_size;
       sel.k_pages = st->k_pages;
       sel.pages = st->pages;
+      // the step's token bookkeeping: active flags (query MSE, mode 1, or a
+      // constant, mode 0), then q_prev <- q_cur; one kernel for text-sized
+      // blocks, else separate kernels (whose MSE reads contiguous queries)
+      auto token_step = [&](int mode, uint8_t fill) -> fb_status {
+        if (active_step_fits(n_q, hq))
+          return dev(launch_active_step(st->q_prev, a->q_blk.ptr, a->q_blk.stride_tok,
+                                        a->q_blk.stride_head, s.dtype, n_q, hq, d, mode, fill,
+                                        st->pct, st->mse, st->active, stream));
+        fb_status r;
+        if (mode == 1) {
+          if (a->q_blk.stride_head != d || a->q_blk.stride_tok != static_cast<int64_t>(hq) * d)
+            return FB_ERR_UNSUPPORTED;
+          r = dev(launch_active_mse(st->q_prev, a->q_blk.ptr, s.dtype, n_q, hq, d, st->pct,
+                                    st->mse, st->active, static_cast<double*>(st->ws), stream));
+        } else {
+          r = dev(launch_fill_u8(st->active, n_q, fill, stream));
+        }
+        if (r != FB_OK) return r;
+        return dev(launch_copy_rows(a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head,
+                                    st->q_prev, n_q, hq, d, s.dtype, stream));
+      };
       if (first) {
         if (!st->meta_ready) {
           rc = fb_page_meta(&s, st->k_prefix, st->page_size, st->kmin, st->kmax, stream);
@@ -688,15 +711,10 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
                             st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
         if (rc != FB_OK) return rc;
-        rc = dev(launch_fill_u8(st->active, n_q, 1, stream));
+        rc = token_step(0, 1);                     // every token active at the refresh step
         if (rc != FB_OK) return rc;
       } else if (a->decision != 1) {
-        if (a->decision == 0) {
-          rc = dev(launch_fill_u8(st->active, n_q, 1, stream));
-        } else {
-          rc = dev(launch_active_mse(st->q_prev, a->q_blk.ptr, s.dtype, n_q, hq, d, st->pct,
-                                     st->mse, st->active, static_cast<double*>(st->ws), stream));
-        }
+        rc = token_step(a->decision == 0 ? 0 : 1, 1);
         if (rc != FB_OK) return rc;
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
@@ -704,12 +722,9 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
                             st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
         if (rc != FB_OK) return rc;
       } else {
-        rc = dev(launch_fill_u8(st->active, n_q, 0, stream));
+        rc = token_step(0, 0);                     // forced reuse: no token active
         if (rc != FB_OK) return rc;
       }
-      rc = dev(launch_copy_rows(a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head, st->q_prev,
-                                n_q, hq, d, s.dtype, stream));
-      if (rc != FB_OK) return rc;
       break;
     }
     default:

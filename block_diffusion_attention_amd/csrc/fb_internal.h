@@ -117,6 +117,10 @@ hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int 
                              uint32_t* bitmap, hipStream_t s);
 hipError_t launch_sel_union(const uint32_t* bitmap, const uint8_t* active, int n_q, int hkv,
                             int words, int32_t* ulist, int32_t* ucnt, int n_pages, hipStream_t s);
+bool sel_prep_fits(int n_q, int words);         // bitmaps of one KV group fit in LDS
+hipError_t launch_sel_prep(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
+                           int n_pages, const uint8_t* active, int do_union, uint32_t* bitmap,
+                           int32_t* ulist, int32_t* ucnt, hipStream_t s);
 hipError_t launch_prefix_sparse(const PrefixParams& p, hipStream_t s);
 int sparse_max_tiles_per_chunk();               // 32-key tiles a GATHER chunk may span
 hipError_t launch_prefix_empty(float* a_out, float* l_out, int n_q, int hq, int d,
@@ -165,6 +169,11 @@ int head_cos_chunks(int n_q);
 hipError_t launch_active_mse(const void* q_prev, const void* q_cur, fb_dtype dt, int n_q,
                              int hq, int d, int pct, double* mse, uint8_t* active,
                              double* ws, hipStream_t s);
+// sparse step: active set (mode 1) or active = fill (mode 0), then q_prev <- q_cur
+bool active_step_fits(int n_q, int hq);
+hipError_t launch_active_step(void* q_prev, const void* q_cur, int64_t q_st, int64_t q_sh,
+                              fb_dtype dt, int n_q, int hq, int d, int mode, uint8_t fill, int pct,
+                              double* mse, uint8_t* active, hipStream_t s);
 hipError_t launch_copy_heads(const float* a_src, const float* l_src, float* a_dst,
                              float* l_dst, int n_q, int hq, int d, const uint8_t* mask,
                              hipStream_t s);

@@ -181,6 +181,102 @@ __global__ __launch_bounds__(256) void active_cut_kernel(int n_q, int pct, const
   for (int t = tid; t < n_q; t += blockDim.x) active[t] = ws[t] > c ? 1 : 0;
 }
 
+// One sparse denoising step's token bookkeeping in one workgroup (the block
+// sizes of text block diffusion): the active set by the same arithmetic as
+// active_mse_kernel + active_cut_kernel (mode 1) or a constant (mode 0),
+// then q_prev <- q_cur for the next step's comparison.
+constexpr int kStepChains = 4096;                  // (token, head) sums held in LDS
+
+template <typename T>
+__global__ __launch_bounds__(1024) void active_step_kernel(T* q_prev, const T* q_cur, int64_t q_st,
+                                                           int64_t q_sh, int n_q, int hq, int d,
+                                                           int mode, uint8_t fill, int pct,
+                                                           double* mse_out, uint8_t* active) {
+#pragma clang fp contract(off)
+  __shared__ double part[kStepChains];
+  __shared__ double mse_s[1024];
+  __shared__ double cutoff;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int chains = n_q * hq;
+  if (mode == 1) {
+    // each chain loads its rows 32 dims at a time as 16-byte vectors (rows are
+    // 16-byte aligned: d is a multiple of 32 and strides of 8 elements)
+    constexpr int kV = 16 / sizeof(T);             // elements per vector
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    for (int i = tid; i < chains; i += nt) {
+      const int t = i / hq, h = i % hq;
+      const T* a = q_prev + static_cast<int64_t>(i) * d;
+      const T* b = q_cur + t * q_st + h * q_sh;
+      double acc = 0.0;
+      for (int j0 = 0; j0 < d; j0 += 32) {
+        u32x4v va[32 / kV], vb[32 / kV];
+#pragma unroll
+        for (int u = 0; u < 32 / kV; ++u) {
+          va[u] = *reinterpret_cast<const u32x4v*>(a + j0 + u * kV);
+          vb[u] = *reinterpret_cast<const u32x4v*>(b + j0 + u * kV);
+        }
+        const T* ea = reinterpret_cast<const T*>(va);
+        const T* eb = reinterpret_cast<const T*>(vb);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const double diff = ldd<T>(eb + j) - ldd<T>(ea + j);
+          const double sq = diff * diff;
+          acc = acc + sq;
+        }
+      }
+      part[i] = acc;
+    }
+    __syncthreads();
+    for (int t = tid; t < n_q; t += nt) {
+      double total = 0.0;
+      for (int h = 0; h < hq; ++h) total = total + part[t * hq + h];
+      const double v = total / static_cast<double>(hq * d);
+      mse_s[t] = v;
+      if (mse_out) mse_out[t] = v;
+    }
+    __syncthreads();
+    int rank = (pct * n_q + 99) / 100;
+    if (rank < 1) rank = 1;
+    for (int t = tid; t < n_q; t += nt) {
+      const double v = mse_s[t];
+      int less = 0, leq = 0;
+      for (int u = 0; u < n_q; ++u) {
+        less += mse_s[u] < v ? 1 : 0;
+        leq += mse_s[u] <= v ? 1 : 0;
+      }
+      if (less < rank && rank <= leq) cutoff = v;  // every writer writes the same value
+    }
+    __syncthreads();
+    for (int t = tid; t < n_q; t += nt) active[t] = mse_s[t] > cutoff ? 1 : 0;
+  } else {
+    for (int t = tid; t < n_q; t += nt) active[t] = fill;
+  }
+  __syncthreads();                                 // every read of q_prev is done
+  // copy as 16-byte vectors, four loads in flight per thread before the stores
+  typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+  constexpr int kVc = 16 / sizeof(T);
+  const int vpr = d / kVc;                         // vectors per (token, head) row
+  const int n_vec = chains * vpr;
+  for (int v0 = 0; v0 < n_vec; v0 += 4 * nt) {
+    u32x4c x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * nt + tid;
+      if (v < n_vec) {
+        const int i = v / vpr, j = v % vpr;
+        const int t = i / hq, h = i % hq;
+        x[u] = *reinterpret_cast<const u32x4c*>(q_cur + t * q_st + h * q_sh + j * kVc);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * nt + tid;
+      if (v < n_vec) *reinterpret_cast<u32x4c*>(q_prev + static_cast<int64_t>(v) * kVc) = x[u];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_heads_kernel(const float* a_src, const float* l_src,
                                                          float* a_dst, float* l_dst, int n_q,
                                                          int hq, int d, const uint8_t* mask) {
@@ -276,6 +372,24 @@ hipError_t launch_active_mse(const void* q_prev, const void* q_cur, fb_dtype dt,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(active_cut_kernel, dim3(1), dim3(256), 0, s, n_q, pct, ws, active);
+  return hipGetLastError();
+}
+
+bool active_step_fits(int n_q, int hq) {
+  return n_q >= 1 && n_q <= 1024 && static_cast<int64_t>(n_q) * hq <= kStepChains;
+}
+
+hipError_t launch_active_step(void* q_prev, const void* q_cur, int64_t q_st, int64_t q_sh,
+                              fb_dtype dt, int n_q, int hq, int d, int mode, uint8_t fill, int pct,
+                              double* mse, uint8_t* active, hipStream_t s) {
+  if (dt == FB_BF16)
+    hipLaunchKernelGGL(active_step_kernel<uint16_t>, dim3(1), dim3(1024), 0, s,
+                       static_cast<uint16_t*>(q_prev), static_cast<const uint16_t*>(q_cur), q_st,
+                       q_sh, n_q, hq, d, mode, fill, pct, mse, active);
+  else
+    hipLaunchKernelGGL(active_step_kernel<float>, dim3(1), dim3(1024), 0, s,
+                       static_cast<float*>(q_prev), static_cast<const float*>(q_cur), q_st, q_sh,
+                       n_q, hq, d, mode, fill, pct, mse, active);
   return hipGetLastError();
 }
 

@@ -110,6 +110,79 @@ __global__ __launch_bounds__(256) void sel_union_kernel(const uint32_t* bitmap, 
   if (tid == 0) ucnt[g] = base;
 }
 
+// Both of the above in one launch when a KV group's bitmaps fit in LDS: one
+// workgroup per g builds the rows (t, g) for every t, writes them, and (for
+// GATHER) compacts their union over the active tokens.
+constexpr int kPrepLdsWords = 12288;               // 48 KB of bitmap rows
+
+__global__ __launch_bounds__(1024) void sel_prep_kernel(const int32_t* pages, int n_q, int hkv,
+                                                       int k_pages, int words, int n_pages,
+                                                       const uint8_t* active, int do_union,
+                                                       uint32_t* bitmap, int32_t* ulist,
+                                                       int32_t* ucnt) {
+  extern __shared__ uint32_t bm[];                 // [n_q][words]
+  __shared__ int scan[256];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
+  __syncthreads();
+  // page ids are loaded 8 at a time ahead of their LDS atomics
+  const int64_t n_ids = static_cast<int64_t>(n_q) * k_pages;
+  for (int64_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
+    int32_t pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + tid;
+      pv[u] = -1;
+      if (i < n_ids) {
+        const int t = static_cast<int>(i / k_pages);
+        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + i % k_pages];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t pg = static_cast<uint32_t>(pv[u]);
+      if (i < n_ids && pg < static_cast<uint32_t>(n_pages))
+        atomicOr(&bm[static_cast<int>(i / k_pages) * words + (pg >> 5)], 1u << (pg & 31));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_q * words; i += 1024) {
+    const int t = i / words, w = i % words;
+    bitmap[(static_cast<int64_t>(t) * hkv + g) * words + w] = bm[i];
+  }
+  if (!do_union) return;                           // (uniform)
+  // the union, 256 words per pass; threads past 256 only keep the barriers
+  const bool scanner = tid < 256;
+  int base = 0;
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int w = w0 + tid;
+    uint32_t u = 0u;
+    if (scanner && w < words)
+      for (int t = 0; t < n_q; ++t)
+        if (!active || active[t]) u |= bm[t * words + w];
+    const int c = __popc(u);
+    if (scanner) scan[tid] = c;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {            // inclusive scan
+      const int v = scanner && tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      if (scanner) scan[tid] += v;
+      __syncthreads();
+    }
+    int pos = base + (scanner ? scan[tid] : 0) - c;
+    while (u) {
+      const int b = __builtin_ctz(u);
+      ulist[static_cast<int64_t>(g) * n_pages + pos++] = w * 32 + b;
+      u &= u - 1;
+    }
+    base += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) ucnt[g] = base;
+}
+
 // ---------------------------------------------------------------------------
 // The sparse MFMA pass.
 // ---------------------------------------------------------------------------
@@ -420,6 +493,19 @@ hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int 
                              uint32_t* bitmap, hipStream_t s) {
   hipLaunchKernelGGL(sel_bitmap_kernel, dim3(n_rows), dim3(256), words * sizeof(uint32_t), s, pages,
                      k_pages, words, n_pages, bitmap);
+  return hipGetLastError();
+}
+
+bool sel_prep_fits(int n_q, int words) {
+  return static_cast<int64_t>(n_q) * words <= kPrepLdsWords;
+}
+
+hipError_t launch_sel_prep(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
+                           int n_pages, const uint8_t* active, int do_union, uint32_t* bitmap,
+                           int32_t* ulist, int32_t* ucnt, hipStream_t s) {
+  hipLaunchKernelGGL(sel_prep_kernel, dim3(hkv), dim3(1024), static_cast<size_t>(n_q) * words * 4, s,
+                     pages, n_q, hkv, k_pages, words, n_pages, active, do_union, bitmap, ulist,
+                     ucnt);
   return hipGetLastError();
 }
 
