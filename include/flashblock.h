@@ -140,10 +140,12 @@ fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k,
  * (A_out, L_out) with (A_in, L_in).                                          *
  *                                                                            *
  * q_blk [n_q, Hq, d]; k_blk, v_blk [n_q, Hkv, d]; a_out, l_out: the cached  *
- * pair (inputs). a_full (required), l_full, a_in, l_in (nullable) outputs.  *
- * ws: device workspace of fb_block_attn_merge_workspace() bytes (0 for      *
- * small blocks).                                                             *
- * Errors: as fb_prefix_attn.                                                 *
+ * pair (inputs); l_out may hold -inf (no cached side: A_full = A_in).       *
+ * a_full (required), l_full, a_in, l_in (nullable) outputs.                 *
+ * ws: unused (fb_block_attn_merge_workspace() returns 0); may be NULL.      *
+ * Errors: as fb_prefix_attn; when a KV head serves >= 128 query rows (bf16, *
+ * d = 128: the MFMA pass) a_out, a_full and a_in must be 16-byte aligned;   *
+ * UNSUPPORTED for more than 65535 block tokens on the small-block path.    *
  * ------------------------------------------------------------------------ */
 size_t fb_block_attn_merge_workspace(const fb_attn_shape* shape, int64_t n_q);
 fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk,
@@ -242,7 +244,9 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
  * SPARSE (FlashBlock s2 sparse compatibility + LoSA s2 workflow): step 0   *
  *        builds page metadata (once per prefix), selects pages, runs the    *
  *        SPLIT pass (cache + residual); later steps classify tokens by      *
- *        query MSE and run the GATHER pass for active rows.                 *
+ *        query MSE and run the GATHER pass for active rows. Blocks with     *
+ *        n_q > 1024 or n_q * Hq > 4096 need a contiguous q_blk              *
+ *        (UNSUPPORTED otherwise).                                           *
  *                                                                           *
  * fb_step_state is a host struct owned by the caller; `step` counts the    *
  * steps of the current block (set it to 0 at a new block). Buffers it       *

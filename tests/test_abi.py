@@ -197,3 +197,45 @@ def test_step_rejects(lib):
     assert lib.fb_step(C.byref(st), C.byref(args), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
     assert lib.fb_step_workspace(C.byref(st)) > 0
     assert st.step == 0
+
+
+def test_many_rows_merge_requires_aligned_outputs(lib):
+    # 300 block tokens of a 12-head MHA model: the MFMA merge path (16-byte rows)
+    sh = shape(hq=12, hkv=12)
+    q, k = ten(300, 12), ten(300, 12)
+    f = lib.fb_block_attn_merge
+    args = (None, None, None, None, 0, None)
+    assert f(C.byref(sh), q, k, k, FAKE + 4, FAKE, FAKE, *args) == 1            # a_out
+    assert f(C.byref(sh), q, k, k, FAKE, FAKE, FAKE + 4, *args) == 1            # a_full
+    assert f(C.byref(sh), q, k, k, FAKE, FAKE, FAKE, None, FAKE + 4, None, None, 0, None) == 1
+    assert lib.fb_block_attn_merge_workspace(C.byref(sh), 300) == 0
+
+
+def test_many_rows_prefix_workspace_covers_masked_split(lib):
+    # a video-sized pass needs no partials unmasked, but a head mask splits the
+    # keys into chunks, so the workspace holds their partials
+    sh = shape(hq=12, hkv=12)
+    need = lib.fb_prefix_attn_workspace(C.byref(sh), 4680, 12480, None)
+    assert need >= 8 * 4680 * 12 * 129 * 4
+    q, k = ten(4680, 12), ten(12480, 12)
+    assert prefix(lib, sh, q, k, k, ws=FAKE, wsb=need - 1) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    # a short prefix has a single chunk and no workspace at all
+    assert lib.fb_prefix_attn_workspace(C.byref(sh), 4680, 500, None) == 0
+
+
+def test_page_select_rejects_counts_beyond_int32(lib):
+    sh = shape()
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 1 << 31, 3, FAKE, FAKE,
+                              None, 0, None) == 1
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, -1, 0, FAKE, FAKE,
+                              None, 0, None) == 1
+
+
+def test_sparse_plan_workspace_includes_selection_buffers(lib):
+    sh = shape()
+    split = fb.fb_page_sel(fb.FB_SEL_SPLIT, 16, 819, FAKE, None)
+    gather = fb.fb_page_sel(fb.FB_SEL_GATHER, 16, 819, FAKE, None)
+    ns = lib.fb_prefix_attn_workspace(C.byref(sh), 8, 65536, C.byref(split))
+    ng = lib.fb_prefix_attn_workspace(C.byref(sh), 8, 65536, C.byref(gather))
+    bitmaps = 8 * 8 * (4096 // 32) * 4
+    assert ns > bitmaps and ng > bitmaps + 8 * 4096 * 4           # GATHER adds the union list
