@@ -549,6 +549,8 @@ __global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
 #define FB_PREFIX_OCC_PAIR 2      // workgroups per CU
 #endif
 constexpr int kPairBuf = kKBytes + kVBytes;       // one K+V tile in LDS
+constexpr int kBufDword3 = 0x00020000;            // buffer resource word 3 (gfx9 raw buffer)
+constexpr int kAuxNT = 2;                         // cache policy: non-temporal
 
 struct HalfTile {          // the K (or V) half of a tile: 8 row-loads per lane
   u32x4 r[8];
@@ -605,41 +607,54 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
   const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
   const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
   if (t_begin >= t_end) return;
-  const int64_t t_last = t_end - 1;
   const int64_t n_iter = (t_end - t_begin + 1) / 2;   // tiles per pair, rounded up
 
   // LDS: pair region = 2 buffers x (K tile, V tile)
   char* pbase = lds + pair * 2 * kPairBuf;
   const int lrow = lane >> 4, lpiece = lane & 15;
   const int grp = lane >> 4, s4 = (lane & 15) >> 2, q4 = lane & 3;
-  const int wrow_bytes = hr == 0 ? kKRow : kVRow;
-  char* wr = pbase + (hr == 0 ? 0 : kKBytes) + lrow * wrow_bytes + lpiece * 16;
+  char* wr = pbase + (hr == 0 ? lrow * kKRow : kKBytes + lrow * kVRow) + lpiece * 16;
   const char* k_rd = pbase + r32 * kKRow + hl * 16;
   const char* v_rd = pbase + kKBytes + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
 
+  // Global reads through a buffer resource rebuilt per tile (scalar work):
+  // its record count ends at the last token of the prefix, so the rows of a
+  // ragged last tile past n_kv read as zeros, and a prefetch past the chunk's
+  // last tile (record count 0) reads nothing at all. Each lane keeps one
+  // 32-bit offset per row-load.
   const char* src = static_cast<const char*>(hr == 0 ? p.k : p.v) +
                     static_cast<int64_t>(g) * p.kv_sh * 2;
   const int64_t kvst_b = p.kv_st * 2;
-  const uint32_t voff = static_cast<uint32_t>(lrow * kvst_b) + lpiece * 16;
+  uint32_t voffs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    voffs[i] = static_cast<uint32_t>((4 * i + lrow) * kvst_b) + lpiece * 16;
 
   auto load_half = [&](int64_t it) -> HalfTile {   // this wave's half of pair tile `it`
     HalfTile r;
-    int64_t tile = t_begin + 2 * it + pair;
-    tile = tile < t_last ? tile : t_last;
+    const int64_t tile = t_begin + 2 * it + pair;
     const int64_t tok0 = tile * kTile;
-    const char* b = src + tok0 * kvst_b;
-    if (tok0 + kTile <= p.n_kv) {
+    const int64_t rows = tile < t_end ? (p.n_kv - tok0 < kTile ? p.n_kv - tok0 : kTile) : 0;
+    const int nrec = rows > 0 ? static_cast<int>((rows - 1) * kvst_b) + kD * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(src + (tile < t_end ? tok0 : 0) * kvst_b), 0, nrec, kBufDword3);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) r.r[i] = ldnt(b + 4 * i * kvst_b + voff);
-    } else {
-      const int64_t last = p.n_kv - 1 - tok0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t rr = 4 * i + lrow < last ? 4 * i + lrow : last;
-        r.r[i] = ldnt(b + rr * kvst_b + lpiece * 16);
-      }
-    }
+    for (int i = 0; i < 8; ++i)
+      r.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(voffs[i]), 0, kAuxNT);
     return r;
+  };
+
+  // LDS row stride as an immediate: one store sequence per role (wave-uniform)
+  auto store_half = [&](const HalfTile& h, int boff) {
+    if (hr == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(wr + boff + 4 * i * kKRow) = h.r[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(wr + boff + 4 * i * kVRow) = h.r[i];
+    }
   };
 
   f32x16 o[1][4];
@@ -653,9 +668,7 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
 
   auto iteration = [&](int u, int64_t it) {      // u static: stage u % DEPTH, buffer u % 2
     const int boff = (u & 1) * kPairBuf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(wr + boff + 4 * i * wrow_bytes) = stage[u % DEPTH].r[i];
+    store_half(stage[u % DEPTH], boff);
     stage[u % DEPTH] = load_half(it + DEPTH);
     __syncthreads();
     const int64_t tile = t_begin + 2 * it + pair;
@@ -737,102 +750,128 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
 constexpr int kMaxChunks = 1024;
 
 
-// One workgroup (256 threads) per output row. Thread (half, c) sums dim c
-// over its half of the chunks with every load of the half in flight at
-// once, and the two halves meet in LDS; the chunk weights come from one
-// wave's max. The chunk order of every sum is fixed, so results are
-// run-to-run identical.
+// One workgroup (256 threads) per output row. Thread (grp, q) owns dims
+// 4q .. 4q+3 and the chunks grp, grp + 8, grp + 16, ...: it issues the loads
+// of up to 8 of its chunks (and of as many residual chunks) before the chunk
+// weights are known, so a row of up to 64 chunks costs one round trip to
+// memory. The eight groups meet in LDS in a fixed order and every other sum
+// has a fixed order too, so results are run-to-run identical.
+constexpr int kRedGroups = 8;                     // chunk groups (of 32 threads)
+constexpr int kRedBatch = 8;                      // chunks per group per round trip
+
 __global__ __launch_bounds__(256) void prefix_reduce_kernel(ReduceParams p) {
-  __shared__ float wa[kMaxChunks];
-  __shared__ float wr[kMaxChunks + 1];
-  __shared__ float red[4];
-  __shared__ float half_acc[2][2][128];            // [half][set][dim]
+  __shared__ float wa[kMaxChunks];                 // chunk L, then chunk weight
+  __shared__ float wr[kMaxChunks + 1];             // residual chunk L, then weight
+  __shared__ float red[2][4];
+  __shared__ float sums[2];
+  __shared__ __attribute__((aligned(16))) float gacc[2][kRedGroups][128];   // [set][group][dim]
   const int64_t row = blockIdx.x;
   const int h = static_cast<int>(row % p.hq);
   const int t = static_cast<int>(row / p.hq);
   if (p.mask && p.mask[h]) return;
   if (p.active && !p.active[t]) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nc = p.dyn.on ? rows_dyn_split(groups_on(p.mask, p.dyn.hkv, p.dyn.group), p.dyn).chunks
                           : p.n_chunks;
   const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
   const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
+  const int nrt = nr + (cached ? 1 : 0);
 
+  // ---- issue this thread's first batch of partial loads ----
+  const int q = tid & 31, grp = tid >> 5;
+  const bool dok = 4 * q < p.d;
+  const int64_t cs = p.rows * p.d;                 // chunk stride
+  const float* pa = p.part_a + row * p.d + 4 * q;
+  const float* pr = nr ? p.part_ra + row * p.d + 4 * q : p.part_a;
+  f32x4 va[kRedBatch], vr[kRedBatch];
+  auto load_batch = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < kRedBatch; ++j) {
+      const int ch = grp + kRedGroups * (kRedBatch * b + j);
+      va[j] = dok && ch < nc ? *reinterpret_cast<const f32x4*>(pa + ch * cs) : f32x4{};
+      vr[j] = dok && ch < nr ? *reinterpret_cast<const f32x4*>(pr + ch * cs) : f32x4{};
+    }
+  };
+  load_batch(0);
+
+  // ---- maxima of the chunk log-normalisers (L kept in LDS) ----
   float m = kNegInf, mr = kNegInf;
-  for (int ch = tid; ch < nc; ch += 256) m = fmaxf(m, p.part_l[ch * p.rows + row]);
-  for (int ch = tid; ch < nr; ch += 256) mr = fmaxf(mr, p.part_rl[ch * p.rows + row]);
-  if (cached && tid == 0) mr = fmaxf(mr, p.res_l[row]);
-  m = wave_max(m);
-  mr = wave_max(mr);
-  if ((tid & 63) == 0) {
-    red[tid >> 6] = m;
-  }
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = mr;
-  __syncthreads();
-  const float Mr = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float Mall = fmaxf(M, Mr);
-
   for (int ch = tid; ch < nc; ch += 256) {
     const float L = p.part_l[ch * p.rows + row];
-    wa[ch] = L == kNegInf ? 0.f : expf(L - Mall);
+    wa[ch] = L;
+    m = fmaxf(m, L);
   }
   for (int ch = tid; ch < nr; ch += 256) {
     const float L = p.part_rl[ch * p.rows + row];
-    wr[ch] = L == kNegInf ? 0.f : expf(L - Mr);
+    wr[ch] = L;
+    mr = fmaxf(mr, L);
   }
   if (cached && tid == 0) {
-    const float L = p.res_l[row];
-    wr[nr] = L == kNegInf ? 0.f : expf(L - Mr);
+    wr[nr] = p.res_l[row];
+    mr = fmaxf(mr, wr[nr]);
+  }
+  m = wave_max(m);
+  mr = wave_max(mr);
+  if (lane == 0) {
+    red[0][wv] = m;
+    red[1][wv] = mr;
   }
   __syncthreads();
-  const int nrt = nr + (cached ? 1 : 0);
-  float S = 0.f, Sr = 0.f;                         // same order in every thread
-  for (int ch = 0; ch < nc; ++ch) S += wa[ch];
-  for (int ch = 0; ch < nrt; ++ch) Sr += wr[ch];
+  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  const float Mr = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  const float Mall = fmaxf(M, Mr);
 
-  const int hf = tid >> 7, c = tid & 127;          // half of the chunks, dim
-  const int64_t cs = p.rows * p.d;                 // chunk stride
-  const int mid = (nc + 1) / 2, midr = (nr + 1) / 2;
-  if (c < p.d) {
-    const int c0 = hf ? mid : 0, c1 = hf ? nc : mid;
-    float acc = 0.f;
-    const float* pa = p.part_a + row * p.d + c;
-    int ch = c0;
-    for (; ch + 16 <= c1; ch += 16) {
-      float v[16];
+  // ---- chunk weights e^{L_c - max}, in place (each thread its own entries) ----
+  for (int ch = tid; ch < nc; ch += 256) wa[ch] = wa[ch] == kNegInf ? 0.f : expf(wa[ch] - Mall);
+  for (int ch = tid; ch < nr; ch += 256) wr[ch] = wr[ch] == kNegInf ? 0.f : expf(wr[ch] - Mr);
+  if (cached && tid == 0) wr[nr] = wr[nr] == kNegInf ? 0.f : expf(wr[nr] - Mr);
+  __syncthreads();
+  if (wv < 2) {                                    // weight totals, fixed order
+    const float* w = wv == 0 ? wa : wr;
+    const int n = wv == 0 ? nc : nrt;
+    float sacc = 0.f;
+    for (int ch = lane; ch < n; ch += 64) sacc += w[ch];
+    sacc = wave_sum(sacc);
+    if (lane == 0) sums[wv] = sacc;
+  }
+
+  // ---- weighted sums of this thread's chunks ----
+  f32x4 acc = {}, accr = {};
+  const int nmax = nc > nr ? nc : nr;
+  for (int b = 0;; ++b) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = pa[(ch + u) * cs];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) acc += wa[ch + u] * v[u];
+    for (int j = 0; j < kRedBatch; ++j) {
+      const int ch = grp + kRedGroups * (kRedBatch * b + j);
+      if (ch < nc) acc += wa[ch] * va[j];
+      if (ch < nr) accr += wr[ch] * vr[j];
     }
-    for (; ch < c1; ++ch) acc += wa[ch] * pa[ch * cs];
-    half_acc[hf][0][c] = acc;
-    float accr = 0.f;
-    if (nr) {
-      const int r0 = hf ? midr : 0, r1 = hf ? nr : midr;
-      const float* pr = p.part_ra + row * p.d + c;
-      for (ch = r0; ch < r1; ++ch) accr += wr[ch] * pr[ch * cs];
-    }
-    half_acc[hf][1][c] = accr;
+    if (kRedGroups * kRedBatch * (b + 1) >= nmax) break;
+    load_batch(b + 1);
+  }
+  if (dok) {
+    *reinterpret_cast<f32x4*>(&gacc[0][grp][4 * q]) = acc;
+    *reinterpret_cast<f32x4*>(&gacc[1][grp][4 * q]) = accr;
   }
   __syncthreads();
   if (tid < p.d) {
-    const float acc = half_acc[0][0][c] + half_acc[1][0][c];
-    float accr = half_acc[0][1][c] + half_acc[1][1][c];
-    if (cached) accr += wr[nr] * p.res_a[row * p.d + c];
-    if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
+    const int c = tid;
+    float a = 0.f, ar = 0.f;
+#pragma unroll
+    for (int g = 0; g < kRedGroups; ++g) {
+      a += gacc[0][g][c];
+      ar += gacc[1][g][c];
+    }
+    const float S = sums[0], Sr = sums[1];
+    if (cached) ar += wr[nr] * p.res_a[row * p.d + c];
+    if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? ar / Sr : 0.f;
     // fold the residual pair into the full pair (same composition)
     const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
     const float Stot = S + Sr * wrr;
-    p.a_out[row * p.d + c] = Mall != kNegInf ? (acc + accr * wrr) / Stot : 0.f;
-  }
-  if (tid == 0) {
-    if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
-    const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
-    p.l_out[row] = Mall != kNegInf ? Mall + logf(S + Sr * wrr) : kNegInf;
+    p.a_out[row * p.d + c] = Mall != kNegInf ? (a + ar * wrr) / Stot : 0.f;
+    if (c == 0) {
+      if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+      p.l_out[row] = Mall != kNegInf ? Mall + logf(Stot) : kNegInf;
+    }
   }
 }
 

@@ -24,6 +24,8 @@ CASES = [
     ("b8_ragged", W.LONG, 8, 20001, "tok"),
     ("b16_ragged", W.LONG, 16, 20001, "tok"),
     ("b16_headmajor", W.LONG, 16, 50000, "head"),
+    ("b16_two_tiles_ragged", W.LONG, 16, 33, "tok"),      # second tile holds one key
+    ("b12_rows48_headmajor", W.LONG, 12, 5003, "head"),
     ("b1_short", W.LONG, 1, 45, "tok"),
     ("b32_two_slabs", W.LONG, 32, 3000, "tok"),
     ("b5_rows20", W.LONG, 5, 4096, "tok"),
