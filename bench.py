@@ -2,7 +2,8 @@
 
 Workload (one bench step): one block of the long-context text workload,
 B = 16 block queries, 32 query / 8 KV heads, head_dim 128, bf16, a static
-prefix of 800,000 tokens (token-major [N, Hkv, d] K and V, 3.28 GB), eight
+prefix of 800,000 tokens (K and V 3.28 GB, stored head-major: each KV head's
+keys contiguous, [Hkv, N, d], passed as an [N, Hkv, d] view), eight
 denoising steps driven through fb_step: step 0 computes the block-external
 pair, later steps reuse it unless M >= tau = 4 updated tokens (M ~ Binomial(16,
 0.3) per step, seeded), and every step recomputes the in-block pass and the
@@ -45,7 +46,7 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(n_prefix, block):
+def measured_traffic(n_prefix, block, kv_layout):
     """HBM bytes per prefix pass from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources and this workload."""
     try:
@@ -54,7 +55,8 @@ def measured_traffic(n_prefix, block):
     except (OSError, ValueError):
         return None
     if (t.get("kernel_source_sha256") != kernel_source_hash()
-            or t.get("n_prefix") != n_prefix or t.get("block") != block):
+            or t.get("n_prefix") != n_prefix or t.get("block") != block
+            or t.get("kv_layout") != kv_layout):
         return None
     return t.get("traffic_bytes_per_pass")
 
@@ -67,6 +69,8 @@ def parse():
     ap.add_argument("--n-prefix", type=int, default=800000)
     ap.add_argument("--block", type=int, default=16)
     ap.add_argument("--roofline-reps", type=int, default=50)
+    ap.add_argument("--kv-layout", choices=("head", "token"), default="head",
+                    help="prefix K/V storage: head-major [Hkv, N, d] or token-major [N, Hkv, d]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
@@ -111,7 +115,15 @@ def main():
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    k_dev, v_dev = bf(kp), bf(vp)
+    def cache(x):                    # the prefix K or V in the chosen layout
+        t = bf(x)
+        if args.kv_layout == "head":    # [Hkv, N, d] storage, [N, Hkv, d] view
+            t = t.transpose(0, 1).contiguous().transpose(0, 1)
+        return t
+
+    k_dev = cache(kp)
+    v_dev = cache(vp)
+    torch.cuda.empty_cache()
     inputs = [(bf(s["q"]), bf(s["k"]), bf(s["v"]), torch.from_numpy(s["ids"]).to(dev))
               for s in steps]
     shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
@@ -241,11 +253,11 @@ def main():
                                "B=%d, prefix %d tokens, 8 denoising steps per block, tau=4; "
                                "one bench step = one block" % (B, N),
                    "n_prefix": N, "block": B, "n_q_heads": hq, "n_kv_heads": hkv,
-                   "head_dim": d, "denoising_steps": n_steps_block,
+                   "head_dim": d, "kv_layout": args.kv_layout, "denoising_steps": n_steps_block,
                    "recompute_steps": n_compute},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(N, B),
+                     "traffic": measured_traffic(N, B, args.kv_layout),
                      "kernel": "prefix pass (%s + prefix_reduce_kernel)" % (
                          "prefix_pair_kernel" if 32 < B * hq // hkv <= 64 else "prefix_mfma_kernel"),
                      "alg_bytes_per_launch": alg_bytes},

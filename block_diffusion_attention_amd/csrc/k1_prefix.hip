@@ -9,12 +9,15 @@
 //
 // Kernels:
 //  * prefix_mfma_kernel   bf16, d = 128, few query rows per KV head (the
-//    decode regime of text block diffusion: rows = B * Hq/Hkv <= 64 per
+//    decode regime of text block diffusion: rows = B * Hq/Hkv <= 32 per
 //    workgroup row-slab). Grouped-query heads share every K/V tile, which is
 //    read from HBM once per KV head. Scores and P.V run on gfx950 MFMA.
+//  * prefix_pair_kernel   the same for 33..64 rows per slab: wave pairs share
+//    each tile through LDS, each wave computing 32 of the rows.
 //  * prefix_generic_kernel  any dtype / d in {64,128} / any row count; VALU.
 //    Also implements the sparse SPLIT and GATHER modes.
-//  * prefix_reduce_kernel   fixed-order merge of the chunk partials.
+//  * prefix_reduce_kernel / prefix_reduce_lean_kernel   fixed-order merge of
+//    the chunk partials (few rows: 256 threads per row; many rows: 128).
 #include "fb_internal.h"
 
 #include <math.h>
@@ -255,18 +258,24 @@ __device__ __forceinline__ void tile_compute(f32x16 (&o)[NRB][4], float (&m_run)
   bf16x8 pbh[NRB][2], pbl[NRB][2];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
+    // raw scores: the scale c > 0 enters once per score as an fma in the
+    // exponent, and max(c s) = c max(s)
     float x[16];
     float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      x[i] = s[rb][i] * scale_log2;
-      if (valid < kTile) {
+    for (int i = 0; i < 16; ++i) x[i] = s[rb][i];
+    if (valid < kTile) {               // ragged last tile only
+      int vv = static_cast<int>(valid);
+      asm volatile("" : "+v"(vv));     // keeps the per-key compares inside the branch
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
         const int tk = 8 * (i >> 2) + 4 * hl + (i & 3);
-        if (tk >= valid) x[i] = kNegInf;
+        if (tk >= vv) x[i] = kNegInf;
       }
-      mx = fmaxf(mx, x[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     const bool bump = mx > m_run[rb] + kRescaleLog2;
     float alpha = 1.f;
     if (bump) {
@@ -280,7 +289,7 @@ __device__ __forceinline__ void tile_compute(f32x16 (&o)[NRB][4], float (&m_run)
       f32x8 pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pf[e] = fast_exp2(x[8 * hj + e] - muse);
+        pf[e] = fast_exp2(fmaf(x[8 * hj + e], scale_log2, -muse));
         psum += pf[e];
       }
       const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
@@ -748,130 +757,190 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
 // GATHER: a_out merges the selected partials with the cached residual input.
 // ---------------------------------------------------------------------------
 constexpr int kMaxChunks = 1024;
+constexpr int64_t kReduceLeanRows = 4096;    // rows from which the lean reduce runs
 
 
-// One workgroup (256 threads) per output row. Thread (grp, q) owns dims
-// 4q .. 4q+3 and the chunks grp, grp + 8, grp + 16, ...: it issues the loads
-// of up to 8 of its chunks (and of as many residual chunks) before the chunk
-// weights are known, so a row of up to 64 chunks costs one round trip to
-// memory. The eight groups meet in LDS in a fixed order and every other sum
-// has a fixed order too, so results are run-to-run identical.
-constexpr int kRedGroups = 8;                     // chunk groups (of 32 threads)
-constexpr int kRedBatch = 8;                      // chunks per group per round trip
-
+// One workgroup (256 threads) per output row. Thread (half, c) sums dim c
+// over its half of the chunks with every load of the half in flight at
+// once, and the two halves meet in LDS; the chunk weights come from one
+// wave's max. The chunk order of every sum is fixed, so results are
+// run-to-run identical.
 __global__ __launch_bounds__(256) void prefix_reduce_kernel(ReduceParams p) {
-  __shared__ float wa[kMaxChunks];                 // chunk L, then chunk weight
-  __shared__ float wr[kMaxChunks + 1];             // residual chunk L, then weight
-  __shared__ float red[2][4];
-  __shared__ float sums[2];
-  __shared__ __attribute__((aligned(16))) float gacc[2][kRedGroups][128];   // [set][group][dim]
+  __shared__ float wa[kMaxChunks];
+  __shared__ float wr[kMaxChunks + 1];
+  __shared__ float red[4];
+  __shared__ float half_acc[2][2][128];            // [half][set][dim]
   const int64_t row = blockIdx.x;
   const int h = static_cast<int>(row % p.hq);
   const int t = static_cast<int>(row / p.hq);
   if (p.mask && p.mask[h]) return;
   if (p.active && !p.active[t]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   const int nc = p.dyn.on ? rows_dyn_split(groups_on(p.mask, p.dyn.hkv, p.dyn.group), p.dyn).chunks
                           : p.n_chunks;
   const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
   const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
-  const int nrt = nr + (cached ? 1 : 0);
 
-  // ---- issue this thread's first batch of partial loads ----
-  const int q = tid & 31, grp = tid >> 5;
-  const bool dok = 4 * q < p.d;
-  const int64_t cs = p.rows * p.d;                 // chunk stride
-  const float* pa = p.part_a + row * p.d + 4 * q;
-  const float* pr = nr ? p.part_ra + row * p.d + 4 * q : p.part_a;
-  f32x4 va[kRedBatch], vr[kRedBatch];
-  auto load_batch = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < kRedBatch; ++j) {
-      const int ch = grp + kRedGroups * (kRedBatch * b + j);
-      va[j] = dok && ch < nc ? *reinterpret_cast<const f32x4*>(pa + ch * cs) : f32x4{};
-      vr[j] = dok && ch < nr ? *reinterpret_cast<const f32x4*>(pr + ch * cs) : f32x4{};
-    }
-  };
-  load_batch(0);
-
-  // ---- maxima of the chunk log-normalisers (L kept in LDS) ----
   float m = kNegInf, mr = kNegInf;
+  for (int ch = tid; ch < nc; ch += 256) m = fmaxf(m, p.part_l[ch * p.rows + row]);
+  for (int ch = tid; ch < nr; ch += 256) mr = fmaxf(mr, p.part_rl[ch * p.rows + row]);
+  if (cached && tid == 0) mr = fmaxf(mr, p.res_l[row]);
+  m = wave_max(m);
+  mr = wave_max(mr);
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = m;
+  }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = mr;
+  __syncthreads();
+  const float Mr = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float Mall = fmaxf(M, Mr);
+
   for (int ch = tid; ch < nc; ch += 256) {
     const float L = p.part_l[ch * p.rows + row];
-    wa[ch] = L;
-    m = fmaxf(m, L);
+    wa[ch] = L == kNegInf ? 0.f : expf(L - Mall);
   }
   for (int ch = tid; ch < nr; ch += 256) {
     const float L = p.part_rl[ch * p.rows + row];
-    wr[ch] = L;
-    mr = fmaxf(mr, L);
+    wr[ch] = L == kNegInf ? 0.f : expf(L - Mr);
   }
   if (cached && tid == 0) {
-    wr[nr] = p.res_l[row];
-    mr = fmaxf(mr, wr[nr]);
-  }
-  m = wave_max(m);
-  mr = wave_max(mr);
-  if (lane == 0) {
-    red[0][wv] = m;
-    red[1][wv] = mr;
+    const float L = p.res_l[row];
+    wr[nr] = L == kNegInf ? 0.f : expf(L - Mr);
   }
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  const float Mr = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-  const float Mall = fmaxf(M, Mr);
+  const int nrt = nr + (cached ? 1 : 0);
+  float S = 0.f, Sr = 0.f;                         // same order in every thread
+  for (int ch = 0; ch < nc; ++ch) S += wa[ch];
+  for (int ch = 0; ch < nrt; ++ch) Sr += wr[ch];
 
-  // ---- chunk weights e^{L_c - max}, in place (each thread its own entries) ----
-  for (int ch = tid; ch < nc; ch += 256) wa[ch] = wa[ch] == kNegInf ? 0.f : expf(wa[ch] - Mall);
-  for (int ch = tid; ch < nr; ch += 256) wr[ch] = wr[ch] == kNegInf ? 0.f : expf(wr[ch] - Mr);
-  if (cached && tid == 0) wr[nr] = wr[nr] == kNegInf ? 0.f : expf(wr[nr] - Mr);
-  __syncthreads();
-  if (wv < 2) {                                    // weight totals, fixed order
-    const float* w = wv == 0 ? wa : wr;
-    const int n = wv == 0 ? nc : nrt;
-    float sacc = 0.f;
-    for (int ch = lane; ch < n; ch += 64) sacc += w[ch];
-    sacc = wave_sum(sacc);
-    if (lane == 0) sums[wv] = sacc;
-  }
-
-  // ---- weighted sums of this thread's chunks ----
-  f32x4 acc = {}, accr = {};
-  const int nmax = nc > nr ? nc : nr;
-  for (int b = 0;; ++b) {
+  const int hf = tid >> 7, c = tid & 127;          // half of the chunks, dim
+  const int64_t cs = p.rows * p.d;                 // chunk stride
+  const int mid = (nc + 1) / 2, midr = (nr + 1) / 2;
+  if (c < p.d) {
+    const int c0 = hf ? mid : 0, c1 = hf ? nc : mid;
+    float acc = 0.f;
+    const float* pa = p.part_a + row * p.d + c;
+    int ch = c0;
+    for (; ch + 16 <= c1; ch += 16) {
+      float v[16];
 #pragma unroll
-    for (int j = 0; j < kRedBatch; ++j) {
-      const int ch = grp + kRedGroups * (kRedBatch * b + j);
-      if (ch < nc) acc += wa[ch] * va[j];
-      if (ch < nr) accr += wr[ch] * vr[j];
+      for (int u = 0; u < 16; ++u) v[u] = pa[(ch + u) * cs];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += wa[ch + u] * v[u];
     }
-    if (kRedGroups * kRedBatch * (b + 1) >= nmax) break;
-    load_batch(b + 1);
-  }
-  if (dok) {
-    *reinterpret_cast<f32x4*>(&gacc[0][grp][4 * q]) = acc;
-    *reinterpret_cast<f32x4*>(&gacc[1][grp][4 * q]) = accr;
+    for (; ch < c1; ++ch) acc += wa[ch] * pa[ch * cs];
+    half_acc[hf][0][c] = acc;
+    float accr = 0.f;
+    if (nr) {
+      const int r0 = hf ? midr : 0, r1 = hf ? nr : midr;
+      const float* pr = p.part_ra + row * p.d + c;
+      for (ch = r0; ch < r1; ++ch) accr += wr[ch] * pr[ch * cs];
+    }
+    half_acc[hf][1][c] = accr;
   }
   __syncthreads();
   if (tid < p.d) {
-    const int c = tid;
-    float a = 0.f, ar = 0.f;
-#pragma unroll
-    for (int g = 0; g < kRedGroups; ++g) {
-      a += gacc[0][g][c];
-      ar += gacc[1][g][c];
-    }
-    const float S = sums[0], Sr = sums[1];
-    if (cached) ar += wr[nr] * p.res_a[row * p.d + c];
-    if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? ar / Sr : 0.f;
+    const float acc = half_acc[0][0][c] + half_acc[1][0][c];
+    float accr = half_acc[0][1][c] + half_acc[1][1][c];
+    if (cached) accr += wr[nr] * p.res_a[row * p.d + c];
+    if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
     // fold the residual pair into the full pair (same composition)
     const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
     const float Stot = S + Sr * wrr;
-    p.a_out[row * p.d + c] = Mall != kNegInf ? (a + ar * wrr) / Stot : 0.f;
-    if (c == 0) {
-      if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
-      p.l_out[row] = Mall != kNegInf ? Mall + logf(Stot) : kNegInf;
+    p.a_out[row * p.d + c] = Mall != kNegInf ? (acc + accr * wrr) / Stot : 0.f;
+  }
+  if (tid == 0) {
+    if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+    const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+    p.l_out[row] = Mall != kNegInf ? Mall + logf(S + Sr * wrr) : kNegInf;
+  }
+}
+
+__device__ __forceinline__ float block_max128(float v, float* red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return r;
+}
+
+// Many-row variant (one 128-thread workgroup per row, thread c sums dim c
+// over all chunks, 8 loads in flight): with tens of thousands of rows the
+// occupancy of the lean workgroup matters more than one row's latency.
+__global__ __launch_bounds__(128) void prefix_reduce_lean_kernel(ReduceParams p) {
+  __shared__ float wa[kMaxChunks];
+  __shared__ float wr[kMaxChunks + 1];
+  __shared__ float red[2];
+  const int64_t row = blockIdx.x;
+  const int h = static_cast<int>(row % p.hq);
+  const int t = static_cast<int>(row / p.hq);
+  if (p.mask && p.mask[h]) return;
+  if (p.active && !p.active[t]) return;
+  const int tid = threadIdx.x;
+  const int nc = p.dyn.on ? rows_dyn_split(groups_on(p.mask, p.dyn.hkv, p.dyn.group), p.dyn).chunks
+                          : p.n_chunks;
+  const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
+  const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
+
+  float m = kNegInf, mr = kNegInf;
+  for (int ch = tid; ch < nc; ch += 128) m = fmaxf(m, p.part_l[ch * p.rows + row]);
+  for (int ch = tid; ch < nr; ch += 128) mr = fmaxf(mr, p.part_rl[ch * p.rows + row]);
+  if (cached && tid == 0) mr = fmaxf(mr, p.res_l[row]);
+  const float M = block_max128(m, red);
+  const float Mr = block_max128(mr, red);
+  const float Mall = fmaxf(M, Mr);
+
+  for (int ch = tid; ch < nc; ch += 128) {
+    const float L = p.part_l[ch * p.rows + row];
+    wa[ch] = L == kNegInf ? 0.f : expf(L - Mall);
+  }
+  for (int ch = tid; ch < nr; ch += 128) {
+    const float L = p.part_rl[ch * p.rows + row];
+    wr[ch] = L == kNegInf ? 0.f : expf(L - Mr);
+  }
+  if (cached && tid == 0) {
+    const float L = p.res_l[row];
+    wr[nr] = L == kNegInf ? 0.f : expf(L - Mr);
+  }
+  __syncthreads();
+  const int nrt = nr + (cached ? 1 : 0);
+  float S = 0.f, Sr = 0.f;                         // same order in every thread
+  for (int ch = 0; ch < nc; ++ch) S += wa[ch];
+  for (int ch = 0; ch < nrt; ++ch) Sr += wr[ch];
+
+  const int c = tid;
+  if (c < p.d) {
+    float acc = 0.f, accr = 0.f;
+    const float* pa = p.part_a + row * p.d + c;
+    const int64_t cs = p.rows * p.d;               // chunk stride
+    int ch = 0;
+    for (; ch + 8 <= nc; ch += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pa[(ch + u) * cs];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wa[ch + u] * v[u];
     }
+    for (; ch < nc; ++ch) acc += wa[ch] * pa[ch * cs];
+    if (nr) {
+      const float* pr = p.part_ra + row * p.d + c;
+      for (ch = 0; ch < nr; ++ch) accr += wr[ch] * pr[ch * cs];
+    }
+    if (cached) accr += wr[nr] * p.res_a[row * p.d + c];
+    if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
+    // fold the residual pair into the full pair (same composition)
+    const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+    const float Stot = S + Sr * wrr;
+    p.a_out[row * p.d + c] = Mall != kNegInf ? (acc + accr * wrr) / Stot : 0.f;
+  }
+  if (tid == 0) {
+    if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+    const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+    p.l_out[row] = Mall != kNegInf ? Mall + logf(S + Sr * wrr) : kNegInf;
   }
 }
 
@@ -919,7 +988,12 @@ hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t
 }
 
 hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(prefix_reduce_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(256), 0, s, p);
+  if (p.rows >= kReduceLeanRows)
+    hipLaunchKernelGGL(prefix_reduce_lean_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(128), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL(prefix_reduce_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(256), 0, s,
+                       p);
   return hipGetLastError();
 }
 

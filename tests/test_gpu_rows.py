@@ -21,6 +21,7 @@ PREFIX_CASES = [
     # name, cfg, n_q, n_kv, layout
     ("mha_300x1000", W.VIDEO, 300, 1000, "tok"),          # 3 row tiles, ragged keys, direct
     ("mha_300x9000_splitk", W.VIDEO, 300, 9000, "tok"),   # split-K partials + reduce
+    ("mha_350x9000_lean_reduce", W.VIDEO, 350, 9000, "tok"),  # 4200 rows: many-row reduce
     ("mha_200x2500_headmajor", W.VIDEO, 200, 2500, "head"),
     ("gqa_50x5000", W.LONG, 50, 5000, "tok"),             # 200 rows per KV head
     ("gqa_64x33", W.LONG, 64, 33, "tok"),                 # last key tile holds one key
@@ -43,6 +44,7 @@ def test_rows_prefix_matches_oracle(fb, name, cfg, n_q, n_kv, layout):
 
 def test_rows_split_plan_is_exercised(fb):
     assert _plan_is_split(fb, W.VIDEO, 300, 9000)
+    assert _plan_is_split(fb, W.VIDEO, 350, 9000)
     assert not _plan_is_split(fb, W.VIDEO, 300, 1000)
 
 
