@@ -78,6 +78,8 @@ def parse():
                     help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
+    ap.add_argument("--prefix-warmup-s", type=float, default=1.5,
+                    help="--prefix-only: seconds of untimed passes before the timed ones")
     ap.add_argument("--prefix-only", action="store_true",
                     help="profiling mode: run the prefix pass --roofline-reps times, then "
                          "a 1 GiB read + 1 GiB write elementwise kernel (counter "
@@ -432,9 +434,14 @@ def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):
     l_out = torch.empty(B, hq, device=dev)
     ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, B, N), 16), dtype=torch.uint8,
                      device=dev)
-    for _ in range(3):
-        fb.fb_prefix_attn(shape, q0, k_dev, v_dev, a_out, l_out, ws=ws, stream=stream)
-    torch.cuda.synchronize()
+    # warm-up: the clocks of an idle GPU take about a second of load to settle
+    t_warm = time.time() + args.prefix_warmup_s
+    n_warm = 0
+    while n_warm < 3 or time.time() < t_warm:
+        for _ in range(20):
+            fb.fb_prefix_attn(shape, q0, k_dev, v_dev, a_out, l_out, ws=ws, stream=stream)
+        n_warm += 20
+        torch.cuda.synchronize()
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     r0.record(stream)
     for _ in range(args.roofline_reps):
@@ -451,7 +458,7 @@ def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):
         torch.add(src, 1, out=dst)
     torch.cuda.synchronize()
     alg = N * hkv * d * 4 + B * hq * d * 2 + B * hq * (d + 1) * 4
-    print(json.dumps({"prefix_pass_us": round(t * 1e6, 2), "alg_bytes": alg,
+    print(json.dumps({"prefix_pass_us": round(t * 1e6, 2), "alg_bytes": alg, "warmup_calls": n_warm,
                       "GB_s": round(alg / t / 1e9, 1), "reps": args.roofline_reps,
                       "calibration_copy_bytes": 1 << 30}), flush=True)
 
