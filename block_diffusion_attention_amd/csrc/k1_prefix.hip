@@ -613,10 +613,17 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
   }
 
   const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
-  const int64_t t_begin = static_cast<int64_t>(chunk) * p.tiles_per_chunk;
-  const int64_t t_end = t_begin + p.tiles_per_chunk < n_tiles ? t_begin + p.tiles_per_chunk : n_tiles;
+  // Tile pairs are dealt round-robin over the chunks (pair-tile it of this
+  // workgroup is tile 2 (chunk + n_chunks it) + pair): the workgroups of a KV
+  // head walk the prefix side by side, one sequential stream per head and
+  // K/V instead of one per chunk (measured 1-4% faster on a head-major cache
+  // than contiguous chunks). The plan keeps n_chunks <= n_tiles / 2, so
+  // every chunk has a tile.
+  const int64_t t_begin = 2 * static_cast<int64_t>(chunk);
+  const int64_t t_step = 2 * static_cast<int64_t>(p.n_chunks);
+  const int64_t t_end = n_tiles;
   if (t_begin >= t_end) return;
-  const int64_t n_iter = (t_end - t_begin + 1) / 2;   // tiles per pair, rounded up
+  const int64_t n_iter = (t_end - t_begin + t_step - 1) / t_step;
 
   // LDS: pair region = 2 buffers x (K tile, V tile)
   char* pbase = lds + pair * 2 * kPairBuf;
@@ -641,7 +648,7 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
 
   auto load_half = [&](int64_t it) -> HalfTile {   // this wave's half of pair tile `it`
     HalfTile r;
-    const int64_t tile = t_begin + 2 * it + pair;
+    const int64_t tile = t_begin + t_step * it + pair;
     const int64_t tok0 = tile * kTile;
     const int64_t rows = tile < t_end ? (p.n_kv - tok0 < kTile ? p.n_kv - tok0 : kTile) : 0;
     const int nrec = rows > 0 ? static_cast<int>((rows - 1) * kvst_b) + kD * 2 : 0;
@@ -680,7 +687,7 @@ __global__ __launch_bounds__(256, OCC) void prefix_pair_kernel(PrefixParams p) {
     store_half(stage[u % DEPTH], boff);
     stage[u % DEPTH] = load_half(it + DEPTH);
     __syncthreads();
-    const int64_t tile = t_begin + 2 * it + pair;
+    const int64_t tile = t_begin + t_step * it + pair;
     if (tile < t_end)
       tile_compute<1>(o, m_run, l_run, qop, k_rd + boff, v_rd + boff, p.scale_log2,
                       p.n_kv - tile * kTile, hl);
