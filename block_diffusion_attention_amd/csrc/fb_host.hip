@@ -35,6 +35,9 @@ namespace {
 #ifndef FB_PREFIX_PAIR
 #define FB_PREFIX_PAIR 1          // 64-row slabs use the row-split (wave pair) kernel
 #endif
+#ifndef FB_PREFIX_PAIR_SMALL
+#define FB_PREFIX_PAIR_SMALL 1    // <= 32 rows per KV head on head-major K/V: pair kernel
+#endif
 #ifndef FB_ROWS_MIN_ROWS
 #define FB_ROWS_MIN_ROWS 128      // query rows per KV head from which the many-rows kernel runs
 #endif
@@ -118,7 +121,10 @@ fb_status check_sel(const fb_page_sel* sel, const fb_attn_shape& s, int64_t n_q,
   return FB_OK;
 }
 
-PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const fb_page_sel* sel) {
+// kv_head_major: each KV head's keys are contiguous (stride_head >= n_kv
+// stride_tok), which decides the decode kernel for <= 32 rows per KV head.
+PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const fb_page_sel* sel,
+                       bool kv_head_major) {
   PrefixPlan pl;
   const int mode = sel ? sel->mode : FB_SEL_DENSE;
   const int G = s.n_q_heads / s.n_kv_heads;
@@ -142,7 +148,11 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   int64_t wg_per_chunk;
   int64_t min_tiles;
   if (pl.path == PATH_MFMA) {
-    pl.row_blocks = (group_rows <= 32 || FB_PREFIX_SLAB_ROWS == 32) ? 1 : 2;
+    // <= 32 rows: the 32-row kernel on token-major K/V, the pair kernel (one
+    // row block of each pair idle) on head-major K/V -- each measured 1-2.5%
+    // ahead of the other on its layout
+    const bool small_pair = FB_PREFIX_PAIR_SMALL && kv_head_major;
+    pl.row_blocks = ((group_rows <= 32 && !small_pair) || FB_PREFIX_SLAB_ROWS == 32) ? 1 : 2;
     pl.n_slabs = static_cast<int>((group_rows + 32 * pl.row_blocks - 1) / (32 * pl.row_blocks));
     if (pl.row_blocks == 2 && FB_PREFIX_PAIR) pl.row_blocks = 3;   // kernel selector
     wg_per_chunk = s.n_kv_heads * pl.n_slabs;
@@ -209,6 +219,14 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   return pl;
 }
 
+// Workspace of a prefix pass whatever the K/V layout (the layout picks the
+// decode kernel, whose split may differ).
+size_t prefix_ws_bytes(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const fb_page_sel* sel) {
+  const size_t a = plan_prefix(s, n_q, n_kv, sel, false).ws_bytes;
+  const size_t b = plan_prefix(s, n_q, n_kv, sel, true).ws_bytes;
+  return a > b ? a : b;
+}
+
 fb_status dev(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_DEVICE; }
 
 fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor& k,
@@ -217,7 +235,10 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
                      hipStream_t stream) {
   const int64_t n_q = q.n_tok, n_kv = k.n_tok;
   const int mode = sel ? sel->mode : FB_SEL_DENSE;
-  const PrefixPlan pl = plan_prefix(s, n_q, n_kv, sel);
+  const bool head_major = s.n_kv_heads == 1 ||
+                          ((k.n_tok <= 1 || k.stride_head >= k.n_tok * k.stride_tok) &&
+                           (v.n_tok <= 1 || v.stride_head >= v.n_tok * v.stride_tok));
+  const PrefixPlan pl = plan_prefix(s, n_q, n_kv, sel, head_major);
   if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;
   if (pl.ws_bytes > 0 && !aligned16(ws)) return FB_ERR_INVALID_ARGUMENT;
 
@@ -391,7 +412,7 @@ size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t
                                 const fb_page_sel* sel) {
   if (check_shape(shape) != FB_OK || n_q < 1 || n_kv < 0) return 0;
   if (check_sel(sel, *shape, n_q, n_kv) != FB_OK) return 0;
-  return plan_prefix(*shape, n_q, n_kv, sel).ws_bytes;
+  return prefix_ws_bytes(*shape, n_q, n_kv, sel);
 }
 
 fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k, fb_tensor v,
@@ -591,11 +612,11 @@ size_t fb_step_workspace(const fb_step_state* st) {
     sel.k_pages = st->k_pages;
     psel = &sel;
   }
-  const size_t p1 = plan_prefix(st->shape, st->n_q, st->k_prefix.n_tok, psel).ws_bytes;
+  const size_t p1 = prefix_ws_bytes(st->shape, st->n_q, st->k_prefix.n_tok, psel);
   ws = p1;
   if (st->mode == FB_STEP_SPARSE) {
     sel.mode = FB_SEL_GATHER;
-    const size_t p2 = plan_prefix(st->shape, st->n_q, st->k_prefix.n_tok, &sel).ws_bytes;
+    const size_t p2 = prefix_ws_bytes(st->shape, st->n_q, st->k_prefix.n_tok, &sel);
     const int64_t n_pages = (st->k_prefix.n_tok + sel.page_size - 1) / sel.page_size;
     const size_t p3 = fb_page_select_workspace(&st->shape, st->n_q, n_pages);
     const size_t p4 = align_up(static_cast<size_t>(st->n_q) * sizeof(double));

@@ -599,6 +599,7 @@ __global__ __launch_bounds__(128 * NP, OCC) void prefix_pair_kernel(PrefixParams
   const int G = p.group;
   const int R = p.n_q * G;
   const int row0 = slab * 64;
+  const bool rows_live = row0 + 32 * hr < R;       // this wave's row block has rows
 
   if (p.mask) {
     bool all = true;
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(128 * NP, OCC) void prefix_pair_kernel(PrefixParams
     stage[u % DEPTH] = load_half(it + DEPTH);
     __syncthreads();
     const int64_t tile = t_begin + t_step * it + pair;
-    if (tile < t_end)
+    if (tile < t_end && rows_live)
       tile_compute<1>(o, m_run, l_run, qop, k_rd + boff, v_rd + boff, p.scale_log2,
                       p.n_kv - tile * kTile, hl);
   };

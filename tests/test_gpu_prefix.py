@@ -29,6 +29,8 @@ CASES = [
     ("b1_short", W.LONG, 1, 45, "tok"),
     ("b32_two_slabs", W.LONG, 32, 3000, "tok"),
     ("b5_rows20", W.LONG, 5, 4096, "tok"),
+    ("b5_rows20_headmajor", W.LONG, 5, 4099, "head"),  # pair kernel, one row block idle
+    ("b1_short_headmajor", W.LONG, 1, 45, "head"),
     ("mha_d128_video_like", W.VIDEO, 6, 1000, "tok"),
     ("d64_bf16_generic", W.LONG.with_(head_dim=64), 4, 2000, "tok"),
 ]
