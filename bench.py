@@ -46,6 +46,16 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def prefix_cache(x, dev, layout):
+    """A prefix K or V ([N, Hkv, d] bf16 bits in numpy) on the device: stored
+    head-major ([Hkv, N, d], returned as an [N, Hkv, d] view) or token-major."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    if layout == "head":
+        t = t.transpose(0, 1).contiguous().transpose(0, 1)
+    return t
+
+
 def measured_traffic(n_prefix, block, kv_layout):
     """HBM bytes per prefix pass from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources and this workload."""
@@ -104,7 +114,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.only:
         fn = video_extra if args.only == "video" else sparse_extra
-        print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream())}), flush=True)
+        print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream(), args.kv_layout)}),
+              flush=True)
         return
     cfg = W.LONG.with_(n_prefix=args.n_prefix, n_block=args.block)
     hq, hkv, d, B, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_block, cfg.n_prefix
@@ -117,14 +128,8 @@ def main():
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def cache(x):                    # the prefix K or V in the chosen layout
-        t = bf(x)
-        if args.kv_layout == "head":    # [Hkv, N, d] storage, [N, Hkv, d] view
-            t = t.transpose(0, 1).contiguous().transpose(0, 1)
-        return t
-
-    k_dev = cache(kp)
-    v_dev = cache(vp)
+    k_dev = prefix_cache(kp, dev, args.kv_layout)
+    v_dev = prefix_cache(vp, dev, args.kv_layout)
     torch.cuda.empty_cache()
     inputs = [(bf(s["q"]), bf(s["k"]), bf(s["v"]), torch.from_numpy(s["ids"]).to(dev))
               for s in steps]
@@ -269,8 +274,8 @@ def main():
     extra["reuse_step_check"] = reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N,
                                                  hq, hkv, d, stream)
     if not args.no_extras:
-        extra["video"] = video_extra(fb, W, dev, stream)
-        extra["sparse"] = sparse_extra(fb, W, dev, stream)
+        extra["video"] = video_extra(fb, W, dev, stream, args.kv_layout)
+        extra["sparse"] = sparse_extra(fb, W, dev, stream, args.kv_layout)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
@@ -327,7 +332,7 @@ def reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N, hq, hkv, d, 
             "met": bool(ms_dense / ms_reuse >= need)}
 
 
-def video_extra(fb, W, dev, stream):
+def video_extra(fb, W, dev, stream, layout):
     """Video block diffusion (12 MHA heads, d=128, 4680 block queries, 12480-token
     prefix, 4 steps, gamma = 0.95): the block through fb_step, and the two
     MFMA-bound passes alone against the bf16 MFMA peak."""
@@ -340,7 +345,7 @@ def video_extra(fb, W, dev, stream):
     kp, vp = W.prefix_kv(cfg)
     sig = W.video_sigmas(cfg, 0)
     steps = [tuple(bf(s[n]) for n in ("q", "k", "v")) for s in W.video_steps(cfg, sig)]
-    kd, vd = bf(kp), bf(vp)
+    kd, vd = prefix_cache(kp, dev, layout), prefix_cache(vp, dev, layout)
     shape = fb.shape_of(H, H, d, cfg.scale, torch.bfloat16)
     st = fb.Step(fb.FB_STEP_VIDEO, shape, NQ, kd, vd, gamma=cfg.gamma)
     af = torch.empty(NQ, H, d, device=dev)
@@ -375,7 +380,7 @@ def video_extra(fb, W, dev, stream):
                                     "frac_of_bf16_mfma_peak": round(f_in / ms_in / 1e9 / 2500.0, 4)}}
 
 
-def sparse_extra(fb, W, dev, stream):
+def sparse_extra(fb, W, dev, stream, layout):
     """Sparse + residual reuse (32q/8kv, d=128, 65536-token prefix in 16-token
     pages, B=8, 8 steps): per density, the block through fb_step and the gather
     pass's HBM rate over the union of the active tokens' selected pages."""
@@ -386,7 +391,7 @@ def sparse_extra(fb, W, dev, stream):
 
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-    kd, vd = bf(kp), bf(vp)
+    kd, vd = prefix_cache(kp, dev, layout), prefix_cache(vp, dev, layout)
     H, G, d, B, N, PS = base.n_q_heads, base.n_kv_heads, base.head_dim, base.n_block, base.n_prefix, base.page
     shape = fb.shape_of(H, G, d, base.scale, torch.bfloat16)
     for dens in W.SPARSE_DENSITIES:
