@@ -65,13 +65,18 @@ def cpu(t):
     return t.detach().cpu().numpy()
 
 
-def run_prefix(fb, cfg, n_q, n_kv, layout="tok", mask=None, q_gain=1.0, seed_variant=0):
+def run_prefix(fb, cfg, n_q, n_kv, layout="tok", mask=None, q_gain=1.0, seed_variant=0,
+               v_edit=None):
     """fb_prefix_attn on seeded inputs of `cfg` (n_q block rows over an n_kv
     prefix) and the oracle's A_out, L_out. Outputs start as 7.0 so rows the
-    pass must leave alone can be checked."""
+    pass must leave alone can be checked. v_edit(vp) may alter the prefix V
+    (stored values) before both sides see it."""
     from oracle.attention import attn_gqa
     cfg = cfg.with_(n_prefix=n_kv, n_block=n_q, q_gain=q_gain)
     kp, vp = W.prefix_kv(cfg, variant=seed_variant)
+    if v_edit is not None:
+        vp = vp.copy()
+        v_edit(vp)
     q = W.text_steps(cfg.with_(n_steps=1), variant=seed_variant)[0]["q"]
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     shape = fb.shape_of(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.scale, tdt)

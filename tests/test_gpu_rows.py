@@ -138,3 +138,29 @@ def test_rows_prefix_mask_sized_split(fb, n_on):
     assert np.all(a[:, m] == 7.0) and np.all(l[:, m] == 7.0)
     check_a("A_out of computed heads", a[:, ~m], ra[:, ~m], 2e-3)
     check_l("L_out of computed heads", l[:, ~m], rl[:, ~m], 1e-3)
+
+
+def test_rows_prefix_very_peaked(fb):
+    # Q x 8: a few keys carry almost all of each row's weight, where the
+    # rounding of the weights in P.V matters most
+    a, l, ra, rl, cfg = run_prefix(fb, W.VIDEO, 256, 3000, q_gain=8.0)
+    check_a("very peaked A_out", a, ra, 2e-3)
+    check_l("very peaked L_out", l, rl, 1e-3)
+
+
+
+def _bf16_bits(x):
+    return np.array([x], np.float32).view(np.uint32)[0] >> 16
+
+
+def test_rows_prefix_large_v_entries(fb):
+    # a few V entries of magnitude 1000 dominate some outputs (|A| ~ 11): the
+    # hi + lo weights keep the absolute error within the output bound (one
+    # bf16 or fp16 weight would not: 2^-9 or 2^-11 of ~11)
+    def edit(vp):
+        vp[1234, 3, 9] = _bf16_bits(1000.0)
+        vp[77, 8, 64] = _bf16_bits(-1000.0)
+    a, l, ra, rl, cfg = run_prefix(fb, W.VIDEO, 300, 2000, v_edit=edit)
+    assert np.abs(ra).max() > 5.0
+    check_a("A_out with large V entries", a, ra, 2e-3)
+    check_l("L_out with large V entries", l, rl, 1e-3)
