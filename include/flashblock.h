@@ -106,7 +106,10 @@ typedef struct {
  * FlashBlock s2 "core mechanism": A_out and L_out = log Z_out over the      *
  * tokens outside the block, computed when the controller asks for it.      *
  *                                                                           *
- * q [n_q, Hq, d]; k, v [n_kv, Hkv, d] (any token/head strides).             *
+ * q [n_q, Hq, d]; k, v [n_kv, Hkv, d] (any token/head strides). Head-major *
+ *   storage (each KV head's keys contiguous: stride_head >= n_kv *          *
+ *   stride_tok) streams fastest; the workspace size does not depend on the  *
+ *   layout (the kernel it selects may change results at rounding level).    *
  * head_reuse_mask: NULL, or device [Hq]; heads with byte 1 are skipped and  *
  *   their rows of every output are left untouched.                          *
  * sel: NULL or mode DENSE -> a_out, l_out over all n_kv keys; a_res, l_res  *
