@@ -16,6 +16,25 @@ typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// The lo part of a bf16 hi + lo split of eight fp32 weights w: bf16(w - hi).
+// hi's fp32 values come from its packed pairs themselves (one shift or mask
+// each) rather than from a second conversion.
+__device__ __forceinline__ bf16x8 bf16_lo_part(f32x8 w, bf16x8 hi) {
+  const u32x4v hb = __builtin_bit_cast(u32x4v, hi);
+  u32x4v lb;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float h0 = __uint_as_float(hb[c] << 16), h1 = __uint_as_float(hb[c] & 0xffff0000u);
+    lb[c] = __builtin_bit_cast(uint32_t,
+                               __builtin_convertvector((f32x2){w[2 * c] - h0, w[2 * c + 1] - h1}, bf16x2));
+  }
+  return __builtin_bit_cast(bf16x8, lb);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -294,7 +294,7 @@ __device__ __forceinline__ void tile_compute(f32x16 (&o)[NRB][4], float (&m_run)
       }
       const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
       pbh[rb][hj] = hi;
-      pbl[rb][hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
+      pbl[rb][hj] = bf16_lo_part(pf, hi);
     }
     l_run[rb] = l_run[rb] * alpha + psum;
     if (__any(bump)) {

@@ -148,7 +148,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int valid, int hl, float 
     }
     const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
     ph[hj] = hi;
-    if (PSPLIT) pl[hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
+    if (PSPLIT) pl[hj] = bf16_lo_part(pf, hi);
   }
   l_run = l_run * alpha + psum;
 }

@@ -218,7 +218,7 @@ __device__ __forceinline__ void softmax_set(const float (&x)[16], float c, float
     }
     const bf16x8 hi = __builtin_convertvector(pf, bf16x8);
     ph[hj] = hi;
-    pl[hj] = __builtin_convertvector(pf - __builtin_convertvector(hi, f32x8), bf16x8);
+    pl[hj] = bf16_lo_part(pf, hi);
   }
   l_run = l_run * alpha + psum;
   if (__any(bump)) {
