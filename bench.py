@@ -15,6 +15,11 @@ prefix kernel plus its split-K reduce) with HIP events on the stream it is
 launched on, and divides the algorithmic bytes (K + V + Q + A_out/L_out) by
 that duration; the peak is MI355X's 8 TB/s HBM3E.
 
+extra: p10 / p50 / p90 of single prefix passes, the bandwidth of a plain
+device copy (the practical ceiling), and with --sweep the prefix pass at
+100k-800k tokens for B in {8, 16} plus a 32,768-token prefix (B = 4) whose
+K/V fit the last-level cache, timed warm and with that cache flushed.
+
 cpu_baseline: the fp64 oracle on the host cores for a bounded sample of the
 same block (one recompute step and one reuse step, timed), scaled to the
 block's mix of recompute and reuse steps.
@@ -191,6 +196,10 @@ def main():
     t_prefix = r0.elapsed_time(r1) / args.roofline_reps * 1e-3
     alg_bytes = N * hkv * d * 2 * 2 + B * hq * d * 2 + B * hq * (d + 1) * 4
     achieved = alg_bytes / t_prefix / 1e9
+    # the spread of single launches (their own events, after the timed block)
+    pass_pct = percentiles_us(lambda: fb.fb_prefix_attn(shape, q0, k_dev, v_dev, a_out, l_out,
+                                                        ws=ws, stream=stream),
+                              stream, args.roofline_reps)
 
     extra = {}
     # reuse-step floor vs dense recompute step (same block, device-side decisions)
@@ -212,35 +221,25 @@ def main():
     extra["decisions"] = decisions
     extra["m_counts"] = m_counts
     extra["prefix_pass_us"] = round(t_prefix * 1e6, 2)
+    extra["prefix_pass_us_p10_p50_p90"] = pass_pct
+    extra["achievable_copy_GB_s"] = copy_bandwidth(dev, stream)
 
     if args.sweep:
         sweep = []
-        for n_ctx in (131072, 200000, 400000, 800000):
+        for n_ctx in (100000, 131072, 200000, 400000, 800000):
             if n_ctx > N:
                 continue
             for b in (8, 16):
-                sh = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
-                qq = inputs[0][0][:b].contiguous()
-                kk, vv = k_dev[:n_ctx], v_dev[:n_ctx]
-                ao = torch.empty(b, hq, d, device=dev)
-                lo = torch.empty(b, hq, device=dev)
-                w2 = torch.empty(max(fb.fb_prefix_attn_workspace(sh, b, n_ctx), 16),
-                                 dtype=torch.uint8, device=dev)
-                for _ in range(3):
-                    fb.fb_prefix_attn(sh, qq, kk, vv, ao, lo, ws=w2, stream=stream)
-                torch.cuda.synchronize()
-                x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                x0.record(stream)
-                for _ in range(20):
-                    fb.fb_prefix_attn(sh, qq, kk, vv, ao, lo, ws=w2, stream=stream)
-                x1.record(stream)
-                torch.cuda.synchronize()
-                t = x0.elapsed_time(x1) / 20 * 1e-3
-                by = n_ctx * hkv * d * 4 + b * hq * d * 2 + b * hq * (d + 1) * 4
-                sweep.append({"n_prefix": n_ctx, "B": b, "prefix_pass_us": round(t * 1e6, 2),
-                              "GB_s": round(by / t / 1e9, 1),
-                              "frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)})
+                sweep.append(sweep_point(fb, torch, hq, hkv, d, cfg.scale, inputs[0][0][:b],
+                                         k_dev[:n_ctx], v_dev[:n_ctx], stream, dev))
         extra["prefix_sweep"] = sweep
+        # a 32,768-token prefix (B = 4): its 128 MiB of K/V fit the 256 MB
+        # last-level cache, so it is timed warm and with that cache flushed
+        # (a 1 GiB write between launches)
+        if N >= 32768:
+            extra["prefix_32k_b4"] = sweep_point(fb, torch, hq, hkv, d, cfg.scale,
+                                                 inputs[0][0][:4], k_dev[:32768],
+                                                 v_dev[:32768], stream, dev, cold=True)
 
     out = {
         "metric": "block-step attention query-tok/s (+ prefix-pass HBM GB/s vs peak)",
@@ -330,6 +329,86 @@ def reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N, hq, hkv, d, 
             "kv_traffic_ratio": round(bytes_dense / bytes_reuse, 1),
             "required_min(traffic_ratio, t_dense/t_floor)": round(need, 2),
             "met": bool(ms_dense / ms_reuse >= need)}
+
+
+def percentiles_us(fn, stream, reps):
+    """p10 / p50 / p90 of single launches of fn, each between its own events."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return [round(float(x), 2) for x in np.percentile(ts, [10, 50, 90])]
+
+
+def copy_bandwidth(dev, stream):
+    """Achievable bandwidth of a plain device copy (torch, 2 GiB read + 2 GiB
+    written), the practical ceiling the roofline fraction is read against."""
+    import torch
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 5 * 1e-3
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * (1 << 31) / t / 1e9, 1)
+
+
+def sweep_point(fb, torch, hq, hkv, d, scale, q, k, v, stream, dev, cold=False, reps=20):
+    """One prefix pass over k, v: the mean of `reps` back-to-back launches and the
+    p10 / p50 / p90 of single launches; cold: also with the last-level cache
+    flushed (1 GiB written) before every launch."""
+    b, n_ctx = q.shape[0], k.shape[0]
+    sh = fb.shape_of(hq, hkv, d, scale, torch.bfloat16)
+    qq = q.contiguous()
+    ao = torch.empty(b, hq, d, device=dev)
+    lo = torch.empty(b, hq, device=dev)
+    w2 = torch.empty(max(fb.fb_prefix_attn_workspace(sh, b, n_ctx), 16), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: fb.fb_prefix_attn(sh, qq, k, v, ao, lo, ws=w2, stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x0.record(stream)
+    for _ in range(reps):
+        run()
+    x1.record(stream)
+    torch.cuda.synchronize()
+    t = x0.elapsed_time(x1) / reps * 1e-3
+    by = n_ctx * hkv * d * 4 + b * hq * d * 2 + b * hq * (d + 1) * 4
+    pt = {"n_prefix": n_ctx, "B": b, "prefix_pass_us": round(t * 1e6, 2),
+          "GB_s": round(by / t / 1e9, 1), "frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4),
+          "us_p10_p50_p90": percentiles_us(run, stream, reps)}
+    if cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        ts = []
+        for _ in range(reps):
+            flush.fill_(0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        p = np.percentile(ts, [10, 50, 90])
+        pt["cold_us_p10_p50_p90"] = [round(float(x), 2) for x in p]
+        pt["cold_frac_p50"] = round(by / (p[1] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        del flush
+    return pt
 
 
 def video_extra(fb, W, dev, stream, layout):
@@ -492,8 +571,14 @@ def cpu_baseline(cfg, kp, vp, steps, decisions):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(len(decisions) * cfg.n_block / t_block, 3), "unit": "query-tok/s",
-            "cores": cores, "kind": "oracle",
+            "cores": cores, "cpu_model": model, "kind": "oracle",
             "sample": "one recompute step (fp64 dense softmax over the %d-token prefix for %d "
                       "queries x 32 heads) and one reuse step, timed; block time = %d x %.2f s + "
                       "%d x %.4f s" % (cfg.n_prefix, cfg.n_block, n_comp, t_recompute,
