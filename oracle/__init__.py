@@ -31,6 +31,8 @@ Modules:
   sparse) that use them.
 * ``quest``      -- page min/max metadata, the QUEST-style page bound, top-k
   page selection, and the selected/residual split of the prefix.
+* ``growing``    -- the outer loop over blocks: each finished block's keys
+  and values join the prefix cache before the next block.
 
 All arithmetic is float64 on the exact upcast of the bf16 (or fp32) input
 bits. Every function is pinned by the ``-m "not gpu"`` tests against closed
@@ -38,4 +40,4 @@ forms, invariants, library routines or brute force on tiny inputs; none is
 "parity unpinned".
 """
 
-from . import attention, controller, quest  # noqa: F401
+from . import attention, controller, growing, quest  # noqa: F401

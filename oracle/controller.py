@@ -125,7 +125,8 @@ def active_set(mse, pct=25):
 # text: threshold reuse of the block-external pair
 # --------------------------------------------------------------------------
 
-def text_block(steps, k_p, v_p, scale, tau, with_dense=True, force=None):
+def text_block(steps, k_p, v_p, scale, tau, with_dense=True, force=None,
+               since_refresh=False):
     """FlashBlock over one block of denoising steps with the count controller.
 
     ``steps`` is a list of dicts with q, k, v [B, H*, d] and ids [B] for each
@@ -143,6 +144,11 @@ def text_block(steps, k_p, v_p, scale, tau, with_dense=True, force=None):
     ``force`` (optional list of decisions per step) overrides the controller
     for s >= 1 ("reuse" / "recompute"), for the forced-reuse curves.
 
+    ``since_refresh``: the variant reading of M that counts the positions
+    whose id differs from the id they held at the last compute step (the
+    drift of the cached pair) instead of one step ago. With a recompute at
+    every step the two readings coincide.
+
     Returns one record per step: decision, M, the cached pair in use, the
     in-block pair, the merged pair, the per-row stale flag (the row's id
     differs from the id it had at the last compute step), and, with
@@ -156,7 +162,8 @@ def text_block(steps, k_p, v_p, scale, tau, with_dense=True, force=None):
         if s == 0:
             m_count, decision = None, INIT
         else:
-            m_count = count_updated(steps[s - 1]["ids"], st["ids"])
+            ref = ids_at_refresh if since_refresh else steps[s - 1]["ids"]
+            m_count = count_updated(ref, st["ids"])
             if force is not None and force[s] is not None:
                 decision = force[s]
             else:
