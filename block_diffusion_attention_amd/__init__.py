@@ -16,23 +16,78 @@ from ._abi import (  # noqa: F401
     FB_REUSE_HEAD_COS, FB_SEL_DENSE, FB_SEL_GATHER, FB_SEL_SPLIT, FB_STEP_SPARSE,
     FB_STEP_TEXT, FB_STEP_VIDEO, LIB_PATH, SYMBOLS, FlashBlockError, dtype_code,
     fb_abi_version, fb_attn_shape, fb_block_attn_merge, fb_block_attn_merge_workspace,
-    fb_page_meta, fb_page_sel, fb_page_select, fb_page_select_workspace, fb_prefix_attn,
-    fb_prefix_attn_workspace, fb_reuse_args, fb_reuse_decide, fb_reuse_decide_workspace,
-    fb_status_string, fb_step, fb_step_args, fb_step_state, fb_step_workspace, fb_tensor,
-    load, page_sel, ptr, shape_of, stream_of, tensor_of)
+    fb_kv_append, fb_kv_cache, fb_page_meta, fb_page_meta_update, fb_page_sel, fb_page_select,
+    fb_page_select_workspace, fb_prefix_attn, fb_prefix_attn_workspace, fb_reuse_args,
+    fb_reuse_decide, fb_reuse_decide_workspace, fb_status_string, fb_step, fb_step_args,
+    fb_step_next_block, fb_step_state, fb_step_workspace, fb_tensor, load, page_sel, ptr,
+    shape_of, stream_of, tensor_of)
+
+
+class KVCache:
+    """Device storage for a prefix KV cache that grows by whole blocks.
+
+    capacity tokens of K and V, [capacity, Hkv, d] viewed; ``layout`` "head"
+    stores each KV head's tokens contiguously (Hkv x capacity x d), "token"
+    stores tokens contiguously (capacity x Hkv x d). ``k_prefix`` and
+    ``v_prefix`` view the n_tok tokens in use; ``append`` adds a finished
+    block (fb_kv_append).
+    """
+
+    def __init__(self, capacity, n_kv_heads, head_dim, dtype, device, layout="head"):
+        load()
+        if layout == "head":
+            self._k = torch.empty(n_kv_heads, capacity, head_dim, device=device, dtype=dtype)
+            self._v = torch.empty_like(self._k)
+            self.k_all, self.v_all = self._k.permute(1, 0, 2), self._v.permute(1, 0, 2)
+        elif layout == "token":
+            self._k = torch.empty(capacity, n_kv_heads, head_dim, device=device, dtype=dtype)
+            self._v = torch.empty_like(self._k)
+            self.k_all, self.v_all = self._k, self._v
+        else:
+            raise ValueError("layout must be 'head' or 'token'")
+        self.cache = fb_kv_cache(self._k.data_ptr(), self._v.data_ptr(), int(capacity), 0,
+                                 self.k_all.stride(0), self.k_all.stride(1))
+
+    @property
+    def n_tok(self):
+        return int(self.cache.n_tok)
+
+    @property
+    def capacity(self):
+        return int(self.cache.capacity)
+
+    @property
+    def k_prefix(self):
+        return self.k_all[:self.n_tok]
+
+    @property
+    def v_prefix(self):
+        return self.v_all[:self.n_tok]
+
+    def append(self, shape, k_blk, v_blk, stream=None):
+        fb_kv_append(shape, self.cache, k_blk, v_blk, stream)
 
 
 class Step:
     """One block's fb_step state and the caller-owned device buffers behind it.
 
     mode: FB_STEP_TEXT / FB_STEP_VIDEO / FB_STEP_SPARSE. k_prefix, v_prefix:
-    [n_kv, Hkv, d] tensors (any token/head strides). ``new_block()`` restarts
-    the step counter (the next call recomputes the cached pair).
+    [n_kv, Hkv, d] tensors (any token/head strides), or ``cache`` (a
+    KVCache): the prefix is then the cache's tokens in use, ``next_block``
+    appends a finished block to it and starts the next block, and SPARSE
+    page metadata is kept for the cache's capacity and updated
+    incrementally. ``new_block()`` restarts the step counter over the same
+    prefix (the next call recomputes the cached pair). ``since_refresh``:
+    TEXT counts the ids changed since the last recompute step.
     """
 
-    def __init__(self, mode, shape, n_q, k_prefix, v_prefix, tau=0, gamma=0.0,
-                 page_size=16, k_pages=0, pct=25, device=None):
+    def __init__(self, mode, shape, n_q, k_prefix=None, v_prefix=None, tau=0, gamma=0.0,
+                 page_size=16, k_pages=0, pct=25, device=None, cache=None,
+                 since_refresh=False):
         load()
+        self.cache = cache
+        if cache is not None:
+            k_prefix, v_prefix = cache.k_prefix, cache.v_prefix
         dev = device or k_prefix.device
         hq, d = shape.n_q_heads, shape.head_dim
         f32 = dict(device=dev, dtype=torch.float32)
@@ -49,8 +104,13 @@ class Step:
         st.shape = shape
         st.mode = int(mode)
         st.n_q = int(n_q)
-        st.k_prefix = tensor_of(k_prefix)
-        st.v_prefix = tensor_of(v_prefix)
+        if cache is not None:      # the cache's storage, also while it is empty
+            c = cache.cache
+            st.k_prefix = fb_tensor(c.k, c.n_tok, c.stride_tok, c.stride_head)
+            st.v_prefix = fb_tensor(c.v, c.n_tok, c.stride_tok, c.stride_head)
+        else:
+            st.k_prefix = tensor_of(k_prefix)
+            st.v_prefix = tensor_of(v_prefix)
         st.tau = int(tau)
         st.gamma = float(gamma)
         st.page_size = int(page_size)
@@ -66,7 +126,8 @@ class Step:
             st.a_probe, st.l_probe, st.sim = ptr(self.a_probe), ptr(self.l_probe), ptr(self.sim)
         if mode == FB_STEP_SPARSE:
             hkv = shape.n_kv_heads
-            n_pages = (k_prefix.shape[0] + page_size - 1) // page_size
+            n_tok = cache.capacity if cache is not None else k_prefix.shape[0]
+            n_pages = (n_tok + page_size - 1) // page_size
             kdt = k_prefix.dtype
             self.a_res = torch.zeros(n_q, hq, d, **f32)
             self.l_res = torch.zeros(n_q, hq, **f32)
@@ -78,10 +139,26 @@ class Step:
             self.active = torch.zeros(n_q, device=dev, dtype=torch.uint8)
             for name in ("a_res", "l_res", "pages", "kmin", "kmax", "q_prev", "mse", "active"):
                 setattr(st, name, ptr(getattr(self, name)))
+            st.page_cap = n_pages if cache is not None else 0
+        st.count_since_refresh = 1 if since_refresh else 0
         self.state = st
-        nbytes = fb_step_workspace(st)
-        self.ws = torch.empty(max(nbytes, 16), device=dev, dtype=torch.uint8)
-        st.ws, st.ws_bytes = ptr(self.ws), self.ws.numel()
+        self._dev = dev
+        self.ws = None
+        self._fit_workspace()
+
+    def _fit_workspace(self):
+        nbytes = max(fb_step_workspace(self.state), 16)
+        if self.ws is None or self.ws.numel() < nbytes:
+            self.ws = torch.empty(nbytes, device=self._dev, dtype=torch.uint8)
+            self.state.ws, self.state.ws_bytes = ptr(self.ws), self.ws.numel()
+
+    def next_block(self, k_blk, v_blk, stream=None):
+        """Append the finished block's K/V to the cache and start the next block."""
+        if self.cache is None:
+            raise RuntimeError("next_block needs a Step built on a KVCache")
+        fb_step_next_block(self.state, self.cache.cache, k_blk, v_blk, stream)
+        self.k_prefix, self.v_prefix = self.cache.k_prefix, self.cache.v_prefix
+        self._fit_workspace()
 
     @property
     def mask(self):

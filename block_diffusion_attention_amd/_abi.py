@@ -18,7 +18,7 @@ FB_BF16, FB_F32 = 0, 1
 FB_SEL_DENSE, FB_SEL_SPLIT, FB_SEL_GATHER = 0, 1, 2
 FB_REUSE_COUNT, FB_REUSE_HEAD_COS, FB_REUSE_ACTIVE_MSE = 0, 1, 2
 FB_STEP_TEXT, FB_STEP_VIDEO, FB_STEP_SPARSE = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class fb_attn_shape(C.Structure):
@@ -45,7 +45,13 @@ class fb_reuse_args(C.Structure):
                 ("gamma", C.c_double), ("sim", C.c_void_p),
                 ("q_prev", C.c_void_p), ("q_cur", C.c_void_p), ("dtype", C.c_int),
                 ("pct", C.c_int32), ("mse", C.c_void_p), ("active", C.c_void_p),
-                ("mask", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+                ("mask", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+                ("since_refresh", C.c_int32)]
+
+
+class fb_kv_cache(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("capacity", C.c_int64),
+                ("n_tok", C.c_int64), ("stride_tok", C.c_int64), ("stride_head", C.c_int64)]
 
 
 class fb_step_state(C.Structure):
@@ -61,7 +67,8 @@ class fb_step_state(C.Structure):
                 ("pages", C.c_void_p), ("kmin", C.c_void_p), ("kmax", C.c_void_p),
                 ("q_prev", C.c_void_p), ("mse", C.c_void_p), ("active", C.c_void_p),
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
-                ("step", C.c_int64), ("meta_ready", C.c_int32)]
+                ("step", C.c_int64), ("meta_ready", C.c_int32),
+                ("page_cap", C.c_int64), ("count_since_refresh", C.c_int32)]
 
 
 class fb_step_args(C.Structure):
@@ -86,12 +93,19 @@ _SIGS = [
     ("fb_reuse_decide", C.c_int, [C.POINTER(fb_reuse_args), C.c_void_p]),
     ("fb_page_meta", C.c_int,
      [C.POINTER(fb_attn_shape), fb_tensor, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    ("fb_page_meta_update", C.c_int,
+     [C.POINTER(fb_attn_shape), fb_tensor, C.c_int32, C.c_int64, C.c_int64, C.c_void_p,
+      C.c_void_p, C.c_void_p]),
     ("fb_page_select_workspace", C.c_size_t, [C.POINTER(fb_attn_shape), C.c_int64, C.c_int64]),
     ("fb_page_select", C.c_int,
-     [C.POINTER(fb_attn_shape), fb_tensor, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
-      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+     [C.POINTER(fb_attn_shape), fb_tensor, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+      C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("fb_kv_append", C.c_int,
+     [C.POINTER(fb_attn_shape), C.POINTER(fb_kv_cache), fb_tensor, fb_tensor, C.c_void_p]),
     ("fb_step_workspace", C.c_size_t, [C.POINTER(fb_step_state)]),
     ("fb_step", C.c_int, [C.POINTER(fb_step_state), C.POINTER(fb_step_args), C.c_void_p]),
+    ("fb_step_next_block", C.c_int,
+     [C.POINTER(fb_step_state), C.POINTER(fb_kv_cache), fb_tensor, fb_tensor, C.c_void_p]),
     ("fb_status_string", C.c_char_p, [C.c_int]),
     ("fb_abi_version", C.c_int, []),
 ]
@@ -223,13 +237,26 @@ def fb_page_select_workspace(shape, n_q, n_pages):
     return load().fb_page_select_workspace(C.byref(shape), int(n_q), int(n_pages))
 
 
+def fb_page_meta_update(shape, k, page_size, n_tok_old, page_cap, kmin, kmax, stream=None):
+    _check("fb_page_meta_update",
+           load().fb_page_meta_update(C.byref(shape), tensor_of(k), int(page_size),
+                                      int(n_tok_old), int(page_cap), ptr(kmin), ptr(kmax),
+                                      stream_of(stream)))
+
+
 def fb_page_select(shape, q, kmin, kmax, n_pages, k_pages, pages, bound=None, ws=None,
-                   stream=None):
+                   stream=None, page_cap=0):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = load().fb_page_select(C.byref(shape), tensor_of(q), ptr(kmin), ptr(kmax),
-                               int(n_pages), int(k_pages), ptr(pages), ptr(bound), ptr(ws),
-                               ws_bytes, stream_of(stream))
+                               int(n_pages), int(page_cap), int(k_pages), ptr(pages), ptr(bound),
+                               ptr(ws), ws_bytes, stream_of(stream))
     _check("fb_page_select", st)
+
+
+def fb_kv_append(shape, cache, k_blk, v_blk, stream=None):
+    """cache: an fb_kv_cache (host struct; n_tok grows on success)."""
+    _check("fb_kv_append", load().fb_kv_append(C.byref(shape), C.byref(cache), tensor_of(k_blk),
+                                               tensor_of(v_blk), stream_of(stream)))
 
 
 def fb_step_workspace(state):
@@ -238,6 +265,12 @@ def fb_step_workspace(state):
 
 def fb_step(state, args, stream=None):
     _check("fb_step", load().fb_step(C.byref(state), C.byref(args), stream_of(stream)))
+
+
+def fb_step_next_block(state, cache, k_blk, v_blk, stream=None):
+    _check("fb_step_next_block",
+           load().fb_step_next_block(C.byref(state), C.byref(cache), tensor_of(k_blk),
+                                     tensor_of(v_blk), stream_of(stream)))
 
 
 def fb_status_string(status):

@@ -524,8 +524,9 @@ fb_status fb_reuse_decide(const fb_reuse_args* a, hipStream_t stream) {
     case FB_REUSE_COUNT:
       if (!a->mask || (a->n_q > 0 && !a->ids_cur)) return FB_ERR_INVALID_ARGUMENT;
       if (a->force < -1 || a->force > 1) return FB_ERR_INVALID_ARGUMENT;
+      if (a->since_refresh != 0 && a->since_refresh != 1) return FB_ERR_INVALID_ARGUMENT;
       return dev(launch_count(a->ids_prev, a->ids_cur, a->n_q, a->tau, a->force, a->n_heads,
-                              a->mask, a->m_count, a->ids_store, stream));
+                              a->mask, a->m_count, a->ids_store, a->since_refresh, stream));
     case FB_REUSE_HEAD_COS: {
       if (a->n_q < 1 || !a->a_cached || !a->a_probe || !a->sim || !a->mask)
         return FB_ERR_INVALID_ARGUMENT;
@@ -561,7 +562,26 @@ fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k, int32_t page_siz
   const int64_t n_pages = (k.n_tok + page_size - 1) / page_size;
   if (n_pages > INT32_MAX) return FB_ERR_UNSUPPORTED;
   return dev(launch_page_meta(k.ptr, k.stride_tok, k.stride_head, k.n_tok, shape->n_kv_heads,
-                              shape->head_dim, page_size, shape->dtype, kmin, kmax, stream));
+                              shape->head_dim, page_size, shape->dtype, kmin, kmax, 0, n_pages,
+                              n_pages, stream));
+}
+
+fb_status fb_page_meta_update(const fb_attn_shape* shape, fb_tensor k, int32_t page_size,
+                              int64_t n_tok_old, int64_t page_cap, void* kmin, void* kmax,
+                              hipStream_t stream) {
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  if ((st = check_tensor(k, -1, shape->n_kv_heads, shape->head_dim)) != FB_OK) return st;
+  if (page_size < 1 || n_tok_old < 0 || n_tok_old > k.n_tok) return FB_ERR_INVALID_ARGUMENT;
+  const int64_t n_pages = (k.n_tok + page_size - 1) / page_size;
+  if (page_cap < n_pages) return FB_ERR_INVALID_ARGUMENT;
+  if (n_pages > INT32_MAX) return FB_ERR_UNSUPPORTED;
+  if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
+  // pages wholly below n_tok_old keep their metadata; the old partial page
+  // and every new page are recomputed
+  return dev(launch_page_meta(k.ptr, k.stride_tok, k.stride_head, k.n_tok, shape->n_kv_heads,
+                              shape->head_dim, page_size, shape->dtype, kmin, kmax,
+                              n_tok_old / page_size, n_pages, page_cap, stream));
 }
 
 size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t n_pages) {
@@ -570,8 +590,9 @@ size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t
 }
 
 fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* kmin,
-                         const void* kmax, int64_t n_pages, int32_t k_pages, int32_t* pages,
-                         double* bound, void* ws, size_t ws_bytes, hipStream_t stream) {
+                         const void* kmax, int64_t n_pages, int64_t page_cap, int32_t k_pages,
+                         int32_t* pages, double* bound, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   if (q.n_tok < 1 || q.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
@@ -580,6 +601,8 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
     return FB_ERR_INVALID_ARGUMENT;
   if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
   if (k_pages > 0 && !pages) return FB_ERR_INVALID_ARGUMENT;
+  if (page_cap == 0) page_cap = n_pages;
+  if (page_cap < n_pages) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
   // LDS of the generic bound kernel (group sizes other than 1, 2, 4, 8)
   const bool g_kernel = G == 1 || G == 2 || G == 4 || G == 8;
@@ -593,8 +616,44 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
   }
   return dev(launch_page_select(q.ptr, q.stride_tok, q.stride_head, kmin, kmax,
                                 static_cast<int>(q.n_tok), shape->n_q_heads, shape->n_kv_heads,
-                                shape->head_dim, n_pages, k_pages, shape->dtype, bound, pages,
-                                stream));
+                                shape->head_dim, n_pages, page_cap, k_pages, shape->dtype, bound,
+                                pages, stream));
+}
+
+fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* c, fb_tensor k_blk,
+                       fb_tensor v_blk, hipStream_t stream) {
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  if (!c || c->capacity < 0 || c->n_tok < 0 || c->n_tok > c->capacity)
+    return FB_ERR_INVALID_ARGUMENT;
+  const int hkv = shape->n_kv_heads, d = shape->head_dim;
+  if ((st = check_tensor(k_blk, -1, hkv, d)) != FB_OK) return st;
+  if ((st = check_tensor(v_blk, k_blk.n_tok, hkv, d)) != FB_OK) return st;
+  const int64_t b = k_blk.n_tok;
+  if (b > c->capacity - c->n_tok) return FB_ERR_INVALID_ARGUMENT;
+  if (b == 0) return FB_OK;
+  if (b > INT32_MAX / hkv) return FB_ERR_INVALID_ARGUMENT;
+  // the storage, as tensors over its whole capacity
+  const fb_tensor ks = {c->k, c->capacity, c->stride_tok, c->stride_head};
+  const fb_tensor vs = {c->v, c->capacity, c->stride_tok, c->stride_head};
+  if ((st = check_tensor(ks, -1, hkv, d)) != FB_OK) return st;
+  if ((st = check_tensor(vs, -1, hkv, d)) != FB_OK) return st;
+  const int64_t es = shape->dtype == FB_BF16 ? 2 : 4;
+  // a block already written at the cache's tail is not copied
+  auto in_place = [&](const fb_tensor& t, const void* base) {
+    return t.ptr == static_cast<const char*>(base) + c->n_tok * c->stride_tok * es &&
+           t.stride_tok == c->stride_tok && t.stride_head == c->stride_head;
+  };
+  const void* k_src = in_place(k_blk, c->k) ? nullptr : k_blk.ptr;
+  const void* v_src = in_place(v_blk, c->v) ? nullptr : v_blk.ptr;
+  const fb_status rc =
+      dev(launch_kv_append(k_src, k_blk.stride_tok * es, k_blk.stride_head * es, v_src,
+                           v_blk.stride_tok * es, v_blk.stride_head * es, c->k, c->v,
+                           c->stride_tok * es, c->stride_head * es, c->n_tok, static_cast<int>(b),
+                           hkv, static_cast<int>(d * es), stream));
+  if (rc != FB_OK) return rc;
+  c->n_tok += b;
+  return FB_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -650,8 +709,11 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
     case FB_STEP_TEXT: {
       if (!a->ids_cur || !st->ids_prev) return FB_ERR_INVALID_ARGUMENT;
       const int force = first ? 0 : a->decision;
+      if (st->count_since_refresh != 0 && st->count_since_refresh != 1)
+        return FB_ERR_INVALID_ARGUMENT;
       rc = dev(launch_count(first ? nullptr : st->ids_prev, a->ids_cur, n_q, st->tau, force, hq,
-                            st->mask, st->m_count, st->ids_prev, stream));
+                            st->mask, st->m_count, st->ids_prev, st->count_since_refresh,
+                            stream));
       if (rc != FB_OK) return rc;
       if (force != 1) {
         rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, st->mask, nullptr, st->a_out,
@@ -693,6 +755,9 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       if (st->page_size < 1 || st->pct < 1 || st->pct > 100) return FB_ERR_INVALID_ARGUMENT;
       const int64_t n_pages = (st->k_prefix.n_tok + st->page_size - 1) / st->page_size;
       if (st->k_pages < 0 || st->k_pages > n_pages) return FB_ERR_INVALID_ARGUMENT;
+      if (st->page_cap < 0 || (st->page_cap > 0 && st->page_cap < n_pages))
+        return FB_ERR_INVALID_ARGUMENT;
+      const int64_t page_cap = st->page_cap > 0 ? st->page_cap : n_pages;
       fb_page_sel sel;
       memset(&sel, 0, sizeof(sel));
       sel.page_size = st->page_size;
@@ -721,12 +786,13 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       };
       if (first) {
         if (!st->meta_ready) {
-          rc = fb_page_meta(&s, st->k_prefix, st->page_size, st->kmin, st->kmax, stream);
+          rc = fb_page_meta_update(&s, st->k_prefix, st->page_size, 0, page_cap, st->kmin,
+                                   st->kmax, stream);
           if (rc != FB_OK) return rc;
           st->meta_ready = 1;
         }
-        rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, st->k_pages, st->pages,
-                            nullptr, st->ws, st->ws_bytes, stream);
+        rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
+                            st->pages, nullptr, st->ws, st->ws_bytes, stream);
         if (rc != FB_OK) return rc;
         sel.mode = FB_SEL_SPLIT;
         rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
@@ -755,6 +821,48 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
                            a->l_full, nullptr, nullptr, nullptr, 0, stream);
   if (rc != FB_OK) return rc;
   st->step += 1;
+  return FB_OK;
+}
+
+fb_status fb_step_next_block(fb_step_state* st, fb_kv_cache* c, fb_tensor k_blk, fb_tensor v_blk,
+                             hipStream_t stream) {
+  if (!st || !c) return FB_ERR_INVALID_ARGUMENT;
+  fb_status rc = check_shape(&st->shape);
+  if (rc != FB_OK) return rc;
+  // the state's prefix is the cache's first n_tok tokens
+  const fb_tensor& kp = st->k_prefix;
+  const fb_tensor& vp = st->v_prefix;
+  if (kp.ptr != c->k || vp.ptr != c->v || kp.n_tok != c->n_tok || vp.n_tok != c->n_tok ||
+      kp.stride_tok != c->stride_tok || kp.stride_head != c->stride_head ||
+      vp.stride_tok != c->stride_tok || vp.stride_head != c->stride_head)
+    return FB_ERR_INVALID_ARGUMENT;
+  const int64_t n_old = c->n_tok;
+  const bool sparse = st->mode == FB_STEP_SPARSE;
+  const bool incremental = sparse && st->page_cap > 0 && st->meta_ready;
+  if (sparse) {
+    if (st->page_size < 1 || st->page_cap < 0) return FB_ERR_INVALID_ARGUMENT;
+    if (k_blk.n_tok < 0 || k_blk.n_tok > c->capacity - n_old) return FB_ERR_INVALID_ARGUMENT;
+    const int64_t n_pages = (n_old + k_blk.n_tok + st->page_size - 1) / st->page_size;
+    if (st->page_cap > 0 && n_pages > st->page_cap) return FB_ERR_INVALID_ARGUMENT;
+    if (incremental && (!st->kmin || !st->kmax)) return FB_ERR_INVALID_ARGUMENT;
+  }
+  rc = fb_kv_append(&st->shape, c, k_blk, v_blk, stream);
+  if (rc != FB_OK) return rc;
+  st->k_prefix.n_tok = c->n_tok;
+  st->v_prefix.n_tok = c->n_tok;
+  st->step = 0;
+  if (sparse) {
+    if (!incremental) {
+      st->meta_ready = 0;              // rebuilt at the next refresh step
+    } else {
+      rc = fb_page_meta_update(&st->shape, st->k_prefix, st->page_size, n_old, st->page_cap,
+                               st->kmin, st->kmax, stream);
+      if (rc != FB_OK) {
+        st->meta_ready = 0;
+        return rc;
+      }
+    }
+  }
   return FB_OK;
 }
 

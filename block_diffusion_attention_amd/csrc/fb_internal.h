@@ -178,9 +178,10 @@ int rows_occupancy();           // workgroups per CU the kernel is built for
 hipError_t launch_rows(const RowsParams& p, hipStream_t s);
 
 // decisions
+// ids_store receives ids_cur (on recompute decisions only when store_on_recompute)
 hipError_t launch_count(const int32_t* ids_prev, const int32_t* ids_cur, int n_q,
                         int tau, int force, int hq, uint8_t* mask, int32_t* m_count,
-                        int32_t* ids_store, hipStream_t s);
+                        int32_t* ids_store, int store_on_recompute, hipStream_t s);
 hipError_t launch_head_cos(const float* a_cached, const float* a_probe, int n_q, int hq,
                            int d, const uint8_t* mask_in, double gamma, double* sim,
                            uint8_t* mask, double* ws, int n_chunks, hipStream_t s);
@@ -198,12 +199,21 @@ hipError_t launch_copy_heads(const float* a_src, const float* l_src, float* a_ds
                              hipStream_t s);
 
 // pages
+// metadata of pages [p_begin, p_end) of the first n_kv tokens; storage holds
+// page_cap pages per KV head ([Hkv][page_cap][d])
 hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t n_kv,
                             int hkv, int d, int page_size, fb_dtype dt, void* kmin,
-                            void* kmax, hipStream_t s);
+                            void* kmax, int64_t p_begin, int64_t p_end, int64_t page_cap,
+                            hipStream_t s);
 hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const void* kmin,
                               const void* kmax, int n_q, int hq, int hkv, int d,
-                              int64_t n_pages, int k_pages, fb_dtype dt, double* bound,
-                              int32_t* pages, hipStream_t s);
+                              int64_t n_pages, int64_t page_cap, int k_pages, fb_dtype dt,
+                              double* bound, int32_t* pages, hipStream_t s);
+// the finished block's K/V rows into cache tokens [tok0, tok0 + n_blk); byte
+// strides; rows are (d * elem_bytes) bytes, a multiple of 16
+hipError_t launch_kv_append(const void* k_src, int64_t ks_t, int64_t ks_h, const void* v_src,
+                            int64_t vs_t, int64_t vs_h, void* k_dst, void* v_dst, int64_t d_t,
+                            int64_t d_h, int64_t tok0, int n_blk, int hkv, int row_bytes,
+                            hipStream_t s);
 
 }  // namespace fb

@@ -3,6 +3,8 @@
 //
 //  * count     (FlashBlock technical summary, s2 threshold reuse): M = number
 //              of block positions whose token id changed; reuse iff M < tau.
+//              Changed since the previous step, or (variant) since the ids
+//              of the last step that recomputed, which are the ones kept.
 //  * head_cos  (same section, per-head selection): cosine of a head's fresh
 //              block-external output against its cached one, float64, fixed
 //              reduction order; reuse iff sim > gamma.
@@ -20,7 +22,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* prev, const int32_t* cur, int n,
                                                     int tau, int force, int hq, uint8_t* mask,
-                                                    int32_t* m_count, int32_t* store) {
+                                                    int32_t* m_count, int32_t* store,
+                                                    int store_on_recompute) {
   __shared__ int total;
   const int tid = threadIdx.x;
   if (tid == 0) total = 0;
@@ -36,7 +39,8 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* prev, const i
   const bool reuse = force == 1 ? true : (force == 0 ? false : (M < tau));
   for (int h = tid; h < hq; h += blockDim.x) mask[h] = reuse ? 1 : 0;
   if (tid == 0 && m_count) *m_count = M;
-  if (store)
+  // since-refresh counting keeps the ids of the last compute step
+  if (store && !(store_on_recompute && reuse))
     for (int i = tid; i < n; i += blockDim.x) store[i] = cur[i];
 }
 
@@ -333,9 +337,9 @@ hipError_t launch_copy_rows(const void* src, int64_t st, int64_t sh, void* dst, 
 
 hipError_t launch_count(const int32_t* ids_prev, const int32_t* ids_cur, int n_q, int tau,
                         int force, int hq, uint8_t* mask, int32_t* m_count, int32_t* ids_store,
-                        hipStream_t s) {
+                        int store_on_recompute, hipStream_t s) {
   hipLaunchKernelGGL(count_kernel, dim3(1), dim3(256), 0, s, ids_prev, ids_cur, n_q, tau, force, hq,
-                     mask, m_count, ids_store);
+                     mask, m_count, ids_store, store_on_recompute);
   return hipGetLastError();
 }
 

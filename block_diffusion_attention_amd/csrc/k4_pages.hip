@@ -32,12 +32,14 @@ template <> __device__ __forceinline__ uint16_t stf<uint16_t>(float x) {
   return static_cast<uint16_t>(__float_as_uint(x) >> 16);   // exact: x is a bf16 value
 }
 
-// kmin/kmax[g][p][c] over the tokens of page p (the last page may be short).
+// kmin/kmax[g][p][c] over the tokens of page p (the last page may be short),
+// for pages p0 .. p0 + gridDim.x - 1; page_cap pages per KV head in storage.
 template <typename T>
 __global__ __launch_bounds__(128) void page_meta_kernel(const T* k, int64_t kv_st, int64_t kv_sh,
                                                         int64_t n_kv, int d, int page_size,
-                                                        int64_t n_pages, T* kmin, T* kmax) {
-  const int64_t p = blockIdx.x;
+                                                        int64_t p0, int64_t page_cap, T* kmin,
+                                                        T* kmax) {
+  const int64_t p = p0 + blockIdx.x;
   const int g = blockIdx.y;
   const int c = threadIdx.x;
   if (c >= d) return;
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(128) void page_meta_kernel(const T* k, int64_t kv_s
     mn = fminf(mn, x);
     mx = fmaxf(mx, x);
   }
-  const int64_t o = (static_cast<int64_t>(g) * n_pages + p) * d + c;
+  const int64_t o = (static_cast<int64_t>(g) * page_cap + p) * d + c;
   kmin[o] = stf<T>(mn);
   kmax[o] = stf<T>(mx);
 }
@@ -62,7 +64,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_st, int64_t q_sh,
                                                          const T* kmin, const T* kmax, int n_q,
                                                          int hq, int hkv, int d, int64_t n_pages,
-                                                         double* bound) {
+                                                         int64_t page_cap, double* bound) {
 #pragma clang fp contract(off)
   extern __shared__ float sm[];
   const int G = hq / hkv;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
     qs[e] = ldf<T>(q + t * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
   }
   for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
-    const int64_t o = (static_cast<int64_t>(g) * n_pages + p0) * d + e;
+    const int64_t o = (static_cast<int64_t>(g) * page_cap + p0) * d + e;
     const int ls = (e / d) * ds + e % d;
     mn[ls] = ldf<T>(kmin + o);
     mx[ls] = ldf<T>(kmax + o);
@@ -112,7 +114,7 @@ template <typename T, int G, int TC>
 __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q_st, int64_t q_sh,
                                                            const T* kmin, const T* kmax, int n_q,
                                                            int hkv, int d, int64_t n_pages,
-                                                           double* bound) {
+                                                           int64_t page_cap, double* bound) {
 #pragma clang fp contract(off)
   extern __shared__ float sm[];
   const int g = blockIdx.y;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q
     qs[e] = ldf<T>(q + (t0 + t) * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
   }
   for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
-    const int64_t o = (static_cast<int64_t>(g) * n_pages + p0) * d + e;
+    const int64_t o = (static_cast<int64_t>(g) * page_cap + p0) * d + e;
     const int ls = (e / d) * ds + e % d;
     mn[ls] = ldf<T>(kmin + o);
     mx[ls] = ldf<T>(kmax + o);
@@ -346,25 +348,24 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
 
 hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t n_kv, int hkv,
                             int d, int page_size, fb_dtype dt, void* kmin, void* kmax,
-                            hipStream_t s) {
-  const int64_t n_pages = (n_kv + page_size - 1) / page_size;
-  if (n_pages == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(n_pages), hkv);
+                            int64_t p_begin, int64_t p_end, int64_t page_cap, hipStream_t s) {
+  if (p_end <= p_begin) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(p_end - p_begin), hkv);
   if (dt == FB_BF16)
     hipLaunchKernelGGL(page_meta_kernel<uint16_t>, grid, dim3(128), 0, s,
-                       static_cast<const uint16_t*>(k), kv_st, kv_sh, n_kv, d, page_size, n_pages,
-                       static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax));
+                       static_cast<const uint16_t*>(k), kv_st, kv_sh, n_kv, d, page_size, p_begin,
+                       page_cap, static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax));
   else
     hipLaunchKernelGGL(page_meta_kernel<float>, grid, dim3(128), 0, s,
-                       static_cast<const float*>(k), kv_st, kv_sh, n_kv, d, page_size, n_pages,
-                       static_cast<float*>(kmin), static_cast<float*>(kmax));
+                       static_cast<const float*>(k), kv_st, kv_sh, n_kv, d, page_size, p_begin,
+                       page_cap, static_cast<float*>(kmin), static_cast<float*>(kmax));
   return hipGetLastError();
 }
 
 hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const void* kmin,
                               const void* kmax, int n_q, int hq, int hkv, int d, int64_t n_pages,
-                              int k_pages, fb_dtype dt, double* bound, int32_t* pages,
-                              hipStream_t s) {
+                              int64_t page_cap, int k_pages, fb_dtype dt, double* bound,
+                              int32_t* pages, hipStream_t s) {
   if (n_pages == 0) return hipSuccess;
   const int G = hq / hkv;
   const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * (d + 1)) * sizeof(float);
@@ -375,7 +376,7 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                      dim3(grid.x, grid.y, (n_q + 8 / ((GG + 3) / 4) - 1) / (8 / ((GG + 3) / 4))), \
                      dim3(256), (8 / ((GG + 3) / 4) * GG * d + 2 * kPagesPerBlock * (d + 1)) * 4, s, \
                      static_cast<const TT*>(q), q_st, q_sh, static_cast<const TT*>(kmin),       \
-                     static_cast<const TT*>(kmax), n_q, hkv, d, n_pages, bound)
+                     static_cast<const TT*>(kmax), n_q, hkv, d, n_pages, page_cap, bound)
   if (dt == FB_BF16 && G == 4) FB_BOUND_G(uint16_t, 4);
   else if (dt == FB_BF16 && G == 1) FB_BOUND_G(uint16_t, 1);
   else if (dt == FB_BF16 && G == 2) FB_BOUND_G(uint16_t, 2);
@@ -388,11 +389,11 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
     hipLaunchKernelGGL(page_bound_kernel<uint16_t>, grid, dim3(256), smem, s,
                        static_cast<const uint16_t*>(q), q_st, q_sh,
                        static_cast<const uint16_t*>(kmin), static_cast<const uint16_t*>(kmax), n_q,
-                       hq, hkv, d, n_pages, bound);
+                       hq, hkv, d, n_pages, page_cap, bound);
   else
     hipLaunchKernelGGL(page_bound_kernel<float>, grid, dim3(256), smem, s,
                        static_cast<const float*>(q), q_st, q_sh, static_cast<const float*>(kmin),
-                       static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, bound);
+                       static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, page_cap, bound);
 #undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FB_ABI_VERSION 1
+#define FB_ABI_VERSION 2
 
 typedef enum {
   FB_OK = 0,
@@ -163,7 +163,10 @@ fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk,
  * ------------------------------------------------------------------------ */
 typedef enum {
   /* FlashBlock s2 threshold reuse: M = #{i : ids_cur[i] != ids_prev[i]};
-     mask[h] = (M < tau) for every head, unless force says otherwise.        */
+     mask[h] = (M < tau) for every head, unless force says otherwise.
+     ids_prev holds the previous step's ids, or, to count the drift since the
+     last recompute (since_refresh = 1), the ids of that step: ids_store then
+     receives ids_cur only when the decision is to recompute.                */
   FB_REUSE_COUNT = 0,
   /* FlashBlock s2 per-head selection: sim[h] = cosine of head h's output in
      a_probe vs a_cached, flattened over [n_q, d], float64, clamped to
@@ -208,6 +211,7 @@ typedef struct {
   uint8_t* mask;            /* [Hq]                                           */
   void* ws;                 /* device workspace >= fb_reuse_decide_workspace  */
   size_t ws_bytes;
+  int32_t since_refresh;    /* COUNT: 1 = ids_store only on recompute         */
 } fb_reuse_args;
 
 size_t fb_reuse_decide_workspace(const fb_reuse_args* args);
@@ -217,21 +221,66 @@ fb_status fb_reuse_decide(const fb_reuse_args* args, hipStream_t stream);
  * Page metadata and selection (optional sparse subsystem).                  *
  * fb_page_meta: kmin, kmax [Hkv, P, d] (dtype of k), P = ceil(n_kv / ps):   *
  *   elementwise min / max of the page's keys (the last page may be short).  *
+ * fb_page_meta_update: the same metadata kept in storage of page_cap pages  *
+ *   per KV head ([Hkv, page_cap, d]) for a cache that grows: given storage  *
+ *   that describes the first n_tok_old tokens of k, recomputes the pages     *
+ *   that tokens [n_tok_old, k.n_tok) touch -- the old partial last page and  *
+ *   the new ones, pages floor(n_tok_old / ps) .. ceil(k.n_tok / ps) - 1 --    *
+ *   so the storage then equals fb_page_meta over all k.n_tok tokens. Pages   *
+ *   wholly inside the old prefix keep their min / max (it depends on their   *
+ *   own tokens only). n_tok_old = 0 builds the whole storage.                *
+ *   INVALID_ARGUMENT if n_tok_old > k.n_tok or ceil(k.n_tok / ps) > page_cap.*
  * fb_page_select: bound[t, g, p] = max over the query heads h of group g of *
  *   sum_{j = 0..d-1, in order} max(q[t,h,j]*kmin[g,p,j], q[t,h,j]*kmax[g,p,j])*
  *   in float64 without fused multiply-add; pages[t, g, :] = the k_pages     *
  *   pages of largest bound (ties: lower page id first), listed ascending.    *
+ *   kmin/kmax hold page_cap pages per KV head (0: n_pages, packed).          *
  *   bound may be NULL (then it lives in ws).                                  *
  * ------------------------------------------------------------------------ */
 fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k,
                        int32_t page_size, void* kmin, void* kmax,
                        hipStream_t stream);
+fb_status fb_page_meta_update(const fb_attn_shape* shape, fb_tensor k,
+                              int32_t page_size, int64_t n_tok_old,
+                              int64_t page_cap, void* kmin, void* kmax,
+                              hipStream_t stream);
 size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q,
                                 int64_t n_pages);
 fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
                          const void* kmin, const void* kmax, int64_t n_pages,
-                         int32_t k_pages, int32_t* pages, double* bound,
-                         void* ws, size_t ws_bytes, hipStream_t stream);
+                         int64_t page_cap, int32_t k_pages, int32_t* pages,
+                         double* bound, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Growing prefix cache (FlashBlock s1 problem statement: block-wise         *
+ * decoding attends over a KV cache that grows as blocks finish).            *
+ *                                                                           *
+ * fb_kv_cache is a host struct owned by the caller describing device        *
+ * storage for up to `capacity` tokens of K and V ([capacity, Hkv, d] under  *
+ * the strides, token-major or head-major, both tensors alike); the first    *
+ * n_tok tokens are the prefix J_out. The prefix as an fb_tensor is          *
+ * {k, n_tok, stride_tok, stride_head}.                                       *
+ *                                                                           *
+ * fb_kv_append: copies k_blk, v_blk [B, Hkv, d] (the finished block, any    *
+ *   strides) into tokens [n_tok, n_tok + B) of the storage and, once the    *
+ *   copy is enqueued, sets cache->n_tok += B (host). A block already written *
+ *   in place (k_blk.ptr at token n_tok of the storage, same strides) is not  *
+ *   copied. The block rows must not otherwise overlap the destination.       *
+ *   Errors: INVALID_ARGUMENT for bad shape/strides/alignment, NULL storage,  *
+ *   k/v token counts that differ, or n_tok + B > capacity.                   *
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  void* k;                 /* device storage                                   */
+  void* v;
+  int64_t capacity;        /* tokens the storage holds                         */
+  int64_t n_tok;           /* tokens in use (0 <= n_tok <= capacity)           */
+  int64_t stride_tok;      /* elements between tokens (k and v alike)          */
+  int64_t stride_head;     /* elements between heads                           */
+} fb_kv_cache;
+
+fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* cache,
+                       fb_tensor k_blk, fb_tensor v_blk, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * fb_step -- one denoising step of one block, all launches on `stream`.    *
@@ -254,6 +303,21 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
  * fb_step_state is a host struct owned by the caller; `step` counts the    *
  * steps of the current block (set it to 0 at a new block). Buffers it       *
  * points to are caller-owned device memory sized as documented per field.  *
+ *                                                                           *
+ * fb_step_next_block -- the outer loop (FlashBlock s1: the cache grows by   *
+ * each finished block). Appends the finished block's k_blk, v_blk to the    *
+ * prefix storage `cache` (fb_kv_append), sets k_prefix / v_prefix to the    *
+ * grown prefix, brings SPARSE page metadata up to date incrementally        *
+ * when page_cap > 0 (fb_page_meta_update; INVALID_ARGUMENT if the new page  *
+ * count exceeds page_cap) -- with page_cap = 0 the packed metadata is       *
+ * rebuilt at the next refresh step, into kmin / kmax that must then hold    *
+ * the new page count -- and sets step = 0, so the next fb_step starts the   *
+ * next block with a full compute. k_prefix and                              *
+ * v_prefix must view the first cache->n_tok tokens of cache->k, cache->v    *
+ * (same pointers and strides). The workspace the next block needs may grow  *
+ * with the prefix: query fb_step_workspace() again (fb_step returns         *
+ * WORKSPACE_TOO_SMALL otherwise). Errors: INVALID_ARGUMENT when the state   *
+ * does not view the cache, or as fb_kv_append; the state is unchanged then. *
  * ------------------------------------------------------------------------ */
 typedef enum { FB_STEP_TEXT = 0, FB_STEP_VIDEO = 1, FB_STEP_SPARSE = 2 } fb_step_mode;
 
@@ -280,8 +344,8 @@ typedef struct {
   uint8_t* mask_next;      /* VIDEO [Hq]                                       */
   double* sim;             /* VIDEO [Hq]                                       */
   int32_t* pages;          /* SPARSE [n_q, Hkv, k_pages]                       */
-  void* kmin;              /* SPARSE [Hkv, P, d] (dtype)                       */
-  void* kmax;              /* SPARSE [Hkv, P, d]                               */
+  void* kmin;              /* SPARSE [Hkv, page_cap or P, d] (dtype)           */
+  void* kmax;              /* SPARSE [Hkv, page_cap or P, d]                   */
   void* q_prev;            /* SPARSE [n_q, Hq, d] contiguous (dtype)           */
   double* mse;             /* SPARSE [n_q]                                     */
   uint8_t* active;         /* SPARSE [n_q]                                     */
@@ -289,6 +353,10 @@ typedef struct {
   size_t ws_bytes;
   int64_t step;            /* host counter; fb_step increments it              */
   int32_t meta_ready;      /* SPARSE: host flag, page metadata built           */
+  int64_t page_cap;        /* SPARSE: pages per KV head in kmin / kmax storage;
+                              0 = P = ceil(n_kv / page_size) (packed)          */
+  int32_t count_since_refresh; /* TEXT: 1 = M counts ids changed since the last
+                              recompute step instead of the previous step      */
 } fb_step_state;
 
 typedef struct {
@@ -305,6 +373,9 @@ typedef struct {
 size_t fb_step_workspace(const fb_step_state* st);
 fb_status fb_step(fb_step_state* st, const fb_step_args* args,
                   hipStream_t stream);
+fb_status fb_step_next_block(fb_step_state* st, fb_kv_cache* cache,
+                             fb_tensor k_blk, fb_tensor v_blk,
+                             hipStream_t stream);
 
 const char* fb_status_string(fb_status s);
 int fb_abi_version(void);

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert fb.fb_abi_version() == 1
+    assert fb.fb_abi_version() == 2
     assert fb.fb_status_string(0) == "ok"
     assert fb.fb_status_string(3) == "workspace too small"
     assert fb.fb_status_string(99) == "unknown status"
@@ -53,6 +53,7 @@ STRUCTS = {
     "fb_reuse_args": [f[0] for f in _abi.fb_reuse_args._fields_],
     "fb_step_state": [f[0] for f in _abi.fb_step_state._fields_],
     "fb_step_args": [f[0] for f in _abi.fb_step_args._fields_],
+    "fb_kv_cache": [f[0] for f in _abi.fb_kv_cache._fields_],
 }
 
 
@@ -166,10 +167,19 @@ def test_reuse_decide_rejects(lib):
 def test_page_calls_reject(lib):
     sh = shape()
     assert lib.fb_page_meta(C.byref(sh), ten(100, 8), 0, FAKE, FAKE, None) == 1
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 11, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 0, 11, FAKE, FAKE,
                               None, 0, None) == 1
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 3, FAKE, None,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 0, 3, FAKE, None,
                               None, 0, None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    # metadata storage smaller than the page count
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 9, 3, FAKE, FAKE,
+                              None, 0, None) == 1
+    up = lib.fb_page_meta_update
+    assert up(C.byref(sh), ten(100, 8), 16, 0, 6, FAKE, FAKE, None) == 1      # 7 pages > 6
+    assert up(C.byref(sh), ten(100, 8), 16, 101, 7, FAKE, FAKE, None) == 1    # old > new
+    assert up(C.byref(sh), ten(100, 8), 16, -1, 7, FAKE, FAKE, None) == 1
+    assert up(C.byref(sh), ten(100, 8), 0, 0, 7, FAKE, FAKE, None) == 1       # page size
+    assert up(C.byref(sh), ten(100, 8), 16, 0, 7, None, FAKE, None) == 1
     assert lib.fb_page_select_workspace(C.byref(sh), 8, 4096) == 8 * 8 * 4096 * 8
 
 
@@ -225,9 +235,9 @@ def test_many_rows_prefix_workspace_covers_masked_split(lib):
 
 def test_page_select_rejects_counts_beyond_int32(lib):
     sh = shape()
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 1 << 31, 3, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 1 << 31, 0, 3, FAKE, FAKE,
                               None, 0, None) == 1
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, -1, 0, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, -1, 0, 0, FAKE, FAKE,
                               None, 0, None) == 1
 
 
@@ -239,3 +249,53 @@ def test_sparse_plan_workspace_includes_selection_buffers(lib):
     ng = lib.fb_prefix_attn_workspace(C.byref(sh), 8, 65536, C.byref(gather))
     bitmaps = 8 * 8 * (4096 // 32) * 4
     assert ns > bitmaps and ng > bitmaps + 8 * 4096 * 4           # GATHER adds the union list
+
+
+# ------------------------------------------------------ growing cache, no GPU
+
+def cache(cap=64, n=60, st=8 * 128, sh=128, k=FAKE, v=FAKE + (1 << 24)):
+    return fb.fb_kv_cache(k, v, cap, n, st, sh)
+
+
+def test_kv_append_rejects_and_leaves_the_count(lib):
+    sh = shape()
+    ap = lib.fb_kv_append
+    c = cache()
+    blk = ten(4, 8)
+    assert ap(C.byref(sh), C.byref(c), blk, ten(5, 8), None) == 1        # |K| != |V|
+    assert ap(C.byref(sh), C.byref(c), ten(5, 8), ten(5, 8), None) == 1  # 60 + 5 > 64
+    assert ap(C.byref(sh), None, blk, blk, None) == 1
+    c.n_tok = 65
+    assert ap(C.byref(sh), C.byref(c), blk, blk, None) == 1              # n_tok > capacity
+    c = cache(st=8 * 128 + 4)
+    assert ap(C.byref(sh), C.byref(c), blk, blk, None) == 1              # stride % 8
+    c = cache(st=512)
+    assert ap(C.byref(sh), C.byref(c), blk, blk, None) == 1              # rows overlap
+    c = cache(k=None)
+    assert ap(C.byref(sh), C.byref(c), blk, blk, None) == 1              # NULL storage
+    assert c.n_tok == 60
+    c = cache()
+    assert ap(C.byref(sh), C.byref(c), ten(0, 8), ten(0, 8), None) == 0  # empty block: no launch
+    assert c.n_tok == 60
+
+
+def test_step_next_block_requires_the_state_to_view_the_cache(lib):
+    st = fb.fb_step_state()
+    st.shape = shape()
+    st.mode, st.n_q = fb.FB_STEP_TEXT, 4
+    c = cache(n=40)
+    st.k_prefix = fb.fb_tensor(c.k, 40, c.stride_tok, c.stride_head)
+    st.v_prefix = fb.fb_tensor(c.v, 40, c.stride_tok, c.stride_head)
+    st.step = 3
+    nb = lib.fb_step_next_block
+    blk = ten(4, 8)
+    st.k_prefix.n_tok = 39
+    assert nb(C.byref(st), C.byref(c), blk, blk, None) == 1              # counts differ
+    st.k_prefix.n_tok = 40
+    st.v_prefix = fb.fb_tensor(c.k, 40, c.stride_tok, c.stride_head)
+    assert nb(C.byref(st), C.byref(c), blk, blk, None) == 1              # v views k storage
+    st.v_prefix = fb.fb_tensor(c.v, 40, c.stride_tok, c.stride_head)
+    assert nb(C.byref(st), C.byref(c), ten(30, 8), ten(30, 8), None) == 1  # beyond capacity
+    st.mode, st.page_size, st.page_cap = fb.FB_STEP_SPARSE, 16, 2
+    assert nb(C.byref(st), C.byref(c), blk, blk, None) == 1              # 3 pages > page_cap 2
+    assert st.step == 3 and c.n_tok == 40 and st.k_prefix.n_tok == 40

@@ -2,8 +2,8 @@
 
 * long-context text: 32q/8kv heads, d = 128, B = 16 block queries over an
   800,000-token prefix: the prefix pass in the launch configuration bench.py
-  times, and a whole 8-step block through fb_step (decisions recounted from
-  the token ids);
+  times, a whole 8-step block through fb_step (decisions recounted from
+  the token ids), and the next block after the first one joined the cache;
 * video: 12 MHA heads, 4,680 block queries, 12,480 prefix tokens: the prefix
   pass (plain and with a head mask), the in-block pass with the merge, and
   the per-head cosine decision on synthetic [4680, 12, 128] outputs.
@@ -119,6 +119,46 @@ def test_text_800k_block_sampled(fb, text_800k):
             af, lf = merge(ao, lo, ai, li)
             check_a("step %d row %s A_full" % (s, (t, h)), a_np[t, h], af[0], 2e-3)
             check_l("step %d row %s L_full" % (s, (t, h)), l_np[t, h:h + 1], lf, 1e-3)
+
+
+def test_text_800k_growing_cache_sampled(fb, text_800k):
+    """The 800,000-token prefix in a head-major cache with room for two more
+    blocks: block 0's last-step K/V are appended (bit for bit), then block 1's
+    first step attends over all 800,016 cache tokens and its own 16."""
+    cfg, kp, vp, steps = text_800k
+    hq, hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
+    cache = fb.KVCache(N_TEXT + 2 * B_TEXT, hkv, d, torch.bfloat16, "cuda", "head")
+    cache.append(shape, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"))
+    step = fb.Step(fb.FB_STEP_TEXT, shape, B_TEXT, cache=cache, tau=cfg.tau)
+    a = torch.empty(B_TEXT, hq, d, device="cuda")
+    l = torch.empty(B_TEXT, hq, device="cuda")
+    st0, last = steps[0], steps[-1]
+    step.step(dev_tensor(st0["q"], "bf16"), dev_tensor(st0["k"], "bf16"),
+              dev_tensor(st0["v"], "bf16"), a, l, ids=torch.from_numpy(st0["ids"]).cuda())
+    step.next_block(dev_tensor(last["k"], "bf16"), dev_tensor(last["v"], "bf16"))
+    torch.cuda.synchronize()
+    assert cache.n_tok == N_TEXT + B_TEXT and step.state.step == 0
+    for got, want in ((cache.k_all, last["k"]), (cache.v_all, last["v"])):
+        tail = got[N_TEXT:N_TEXT + B_TEXT].cpu().contiguous().view(torch.int16).numpy()
+        assert np.array_equal(tail, np.ascontiguousarray(want).view(np.int16))
+    st1 = W.text_steps(cfg, block=1)[0]
+    step.step(dev_tensor(st1["q"], "bf16"), dev_tensor(st1["k"], "bf16"),
+              dev_tensor(st1["v"], "bf16"), a, l, ids=torch.from_numpy(st1["ids"]).cuda())
+    torch.cuda.synchronize()
+    a_np, l_np = cpu(a), cpu(l)
+    assert np.all(np.isfinite(a_np)) and np.all(np.isfinite(l_np))
+    G = hq // hkv
+    rows = [(t, h) for t, h in _sample_rows(B_TEXT, hq, 40, seed=4) if h // G in (1, 6)][:10]
+    for g in sorted({h // G for _, h in rows}):
+        keys = np.concatenate([vals(x[:, g, :], "bf16") for x in (kp, last["k"], st1["k"])])
+        vs = np.concatenate([vals(x[:, g, :], "bf16") for x in (vp, last["v"], st1["v"])])
+        for t, h in rows:
+            if h // G != g:
+                continue
+            ar, lr = attn(vals(st1["q"][t:t + 1, h, :], "bf16"), keys, vs, cfg.scale)
+            check_a("grown 800k row %s A_full" % ((t, h),), a_np[t, h], ar[0], 2e-3)
+            check_l("grown 800k row %s L_full" % ((t, h),), l_np[t, h:h + 1], lr, 1e-3)
 
 
 @pytest.fixture(scope="module")
