@@ -89,7 +89,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
-    ap.add_argument("--only", choices=("video", "sparse"),
+    ap.add_argument("--only", choices=("video", "sparse", "growing"),
                     help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
@@ -118,7 +118,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.only:
-        fn = video_extra if args.only == "video" else sparse_extra
+        fn = {"video": video_extra, "sparse": sparse_extra, "growing": growing_extra}[args.only]
         print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream(), args.kv_layout)}),
               flush=True)
         return
@@ -275,6 +275,7 @@ def main():
     if not args.no_extras:
         extra["video"] = video_extra(fb, W, dev, stream, args.kv_layout)
         extra["sparse"] = sparse_extra(fb, W, dev, stream, args.kv_layout)
+        extra["growing"] = growing_extra(fb, W, dev, stream, args.kv_layout)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
@@ -509,6 +510,77 @@ def sparse_extra(fb, W, dev, stream, layout):
                     "gather_frac_of_hbm_peak": round(g_bytes / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "active_tokens_last_step": int(act.sum().item())})
     return res
+
+
+def growing_extra(fb, W, dev, stream, layout):
+    """The outer loop over blocks: 8 text blocks (32q/8kv, d=128, B=16, 8 steps,
+    tau=4) on a cache that starts with 131,072 prefix tokens and takes every
+    finished block's K/V, timed against the same blocks over the static
+    prefix; and what adding a block costs: the append, and the incremental
+    page-metadata update against a full rebuild over a 65,536-token cache."""
+    import torch
+    cfg = W.LONG.with_(n_prefix=131072, n_block=16)
+    n0, B, hq, hkv, d, nb = cfg.n_prefix, cfg.n_block, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, 8
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kp, vp = W.prefix_kv(cfg)
+    shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
+    cache = fb.KVCache(n0 + nb * B, hkv, d, torch.bfloat16, dev, layout)
+    cache.append(shape, bf(kp), bf(vp))
+    blocks = [[(bf(s["q"]), bf(s["k"]), bf(s["v"]), torch.from_numpy(s["ids"]).to(dev))
+               for s in W.text_steps(cfg, block=j)] for j in range(nb)]
+    step = fb.Step(fb.FB_STEP_TEXT, shape, B, cache=cache, tau=cfg.tau)
+    af = torch.empty(B, hq, d, device=dev)
+    lf = torch.empty(B, hq, device=dev)
+
+    def rewind():                       # host-side: back to the initial prefix
+        cache.cache.n_tok = n0
+        step.state.k_prefix.n_tok = step.state.v_prefix.n_tok = n0
+        step.state.step = 0
+
+    def run(grow):
+        rewind()
+        for blk in blocks:
+            for q, k, v, ids in blk:
+                step.step(q, k, v, af, lf, ids=ids)
+            if grow:
+                step.next_block(blk[-1][1], blk[-1][2])
+            else:
+                step.new_block()
+    run(True)
+    torch.cuda.synchronize()
+    assert cache.n_tok == n0 + nb * B
+    ms_grow = _timed(lambda: run(True), stream, 5)
+    ms_static = _timed(lambda: run(False), stream, 5)
+    k16, v16 = blocks[0][-1][1], blocks[0][-1][2]
+
+    def append():
+        cache.cache.n_tok = n0
+        cache.append(shape, k16, v16, stream)
+    us_append = _timed(append, stream, 50) * 1e3
+    # page metadata over a 65,536-token cache after 8 more tokens
+    sc = W.SPARSE
+    skp, svp = W.prefix_kv(sc)
+    sshape = fb.shape_of(sc.n_q_heads, sc.n_kv_heads, sc.head_dim, sc.scale, torch.bfloat16)
+    scache = fb.KVCache(sc.n_prefix, sc.n_kv_heads, sc.head_dim, torch.bfloat16, dev, layout)
+    scache.append(sshape, bf(skp), bf(svp))
+    cap = sc.n_prefix // sc.page
+    kmin = torch.empty(sc.n_kv_heads, cap, sc.head_dim, device=dev, dtype=torch.bfloat16)
+    kmax = torch.empty_like(kmin)
+    kv = scache.k_prefix
+    us_full = _timed(lambda: fb.fb_page_meta_update(sshape, kv, sc.page, 0, cap, kmin, kmax,
+                                                    stream), stream, 20) * 1e3
+    us_incr = _timed(lambda: fb.fb_page_meta_update(sshape, kv, sc.page, sc.n_prefix - 8, cap,
+                                                    kmin, kmax, stream), stream, 50) * 1e3
+    n_steps = nb * len(blocks[0])
+    return {"workload": "%d text blocks (32q/8kv, d=128, B=16, 8 steps, tau=4), cache from "
+                        "131072 to %d tokens" % (nb, n0 + nb * B),
+            "ms_run_growing_cache": round(ms_grow, 3), "ms_run_static_prefix": round(ms_static, 3),
+            "query_tok_per_s_growing": round(n_steps * B / (ms_grow * 1e-3), 1),
+            "append_block_us": round(us_append, 2),
+            "page_meta_65536_full_us": round(us_full, 2),
+            "page_meta_after_8_tokens_us": round(us_incr, 2)}
 
 
 def prefix_only(args, fb, shape, q0, k_dev, v_dev, B, N, hq, hkv, d, stream):

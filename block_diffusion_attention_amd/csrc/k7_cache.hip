@@ -28,8 +28,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const char* k_src, int64
   const int64_t t = row / hkv;
   const char* src = is_v ? v_src + t * vs_t + h * vs_h : k_src + t * ks_t + h * ks_h;
   char* dst = (is_v ? v_dst : k_dst) + (tok0 + t) * d_t + h * d_h;
-  const uint4 x = reinterpret_cast<const uint4*>(src)[w];
-  reinterpret_cast<uint4*>(dst)[w] = x;
+  const u32x4v x = reinterpret_cast<const u32x4v*>(src)[w];
+  reinterpret_cast<u32x4v*>(dst)[w] = x;
 }
 
 }  // namespace
