@@ -311,8 +311,72 @@ def sparse_block(steps, k_p, v_p, scale, k_pages, page=16, pct=25,
     return recs
 
 
+# --------------------------------------------------------------------------
+# LoSA per step: re-selected pages for active tokens, no residual
+# --------------------------------------------------------------------------
+
+def losa_block(steps, k_p, v_p, scale, k_pages, page=16, pct=25, with_dense=False):
+    """LoSA's own step: sparse attention for active tokens, reuse for stable ones.
+
+    [LoSA s2 "token classification", "optimisation mechanism", "workflow"]:
+
+    * s = 0: dense attention over the prefix for every token (the dense
+      initialisation); every token is active.
+    * s >= 1: active tokens (``active_set`` of the query MSE against the
+      previous step) attend only to the pages the QUEST-style selector picks
+      with their current query -- the selection is made again at every step
+      and nothing stands in for the pages left out (no cached residual);
+      stable tokens reuse the prefix result of the previous step.
+    * every step: fresh in-block pair, A_full = merge.
+
+    The selection granularity is one page set per (token, KV head), bound
+    maximised over the group's query heads (as in ``sparse_block``). It is
+    made for every token (stable ones included) so that the KV inflation of
+    selecting for the whole block can be set against the active-only union
+    [LoSA s1, s2 "KV union reduction"].
+
+    Records: active, mse, sel [B, Hkv, k], union (active tokens), union_all
+    (all B tokens), and the outputs.
+    """
+    recs = []
+    kmin, kmax = quest.page_meta(k_p, page)
+    a_out = l_out = None
+    n_tok = steps[0]["q"].shape[0]
+    for s, st in enumerate(steps):
+        bound = quest.page_bound(st["q"], kmin, kmax)
+        sel = quest.topk_pages(bound, k_pages)
+        if s == 0:
+            a_out, l_out = attn_gqa(st["q"], k_p, v_p, scale)
+            active = np.ones(n_tok, dtype=bool)
+            mse = None
+        else:
+            mse = active_mse(steps[s - 1]["q"], st["q"])
+            active = active_set(mse, pct)
+            a_out = a_out.copy()
+            l_out = l_out.copy()
+            rows = np.nonzero(active)[0]
+            if rows.size:
+                (a_sel, l_sel), _ = quest.split_attn(
+                    st["q"][rows], k_p, v_p, sel[rows], page, scale, residual=False)
+                a_out[rows] = a_sel
+                l_out[rows] = l_sel
+        a_in, l_in = attn_gqa(st["q"], st["k"], st["v"], scale)
+        a_full, l_full = merge(a_out, l_out, a_in, l_in)
+        rec = dict(step=s, active=active, mse=mse, sel=sel,
+                   union=quest.union_size(sel, active),
+                   union_all=quest.union_size(sel, np.ones(n_tok, dtype=bool)),
+                   a_out=a_out, l_out=l_out, a_in=a_in, l_in=l_in,
+                   a_full=a_full, l_full=l_full)
+        if with_dense:
+            rec["a_dense"], rec["l_dense"] = dense_step(
+                st["q"], k_p, v_p, st["k"], st["v"], scale)
+        recs.append(rec)
+    return recs
+
+
 __all__ = [
     "INIT", "REUSE", "RECOMPUTE", "count_updated", "text_reuse",
     "head_cosine", "head_reuse", "active_mse", "percentile_cutoff",
-    "active_set", "text_block", "video_block", "sparse_block", "NEG_INF",
+    "active_set", "text_block", "video_block", "sparse_block", "losa_block",
+    "NEG_INF",
 ]

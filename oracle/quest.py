@@ -65,6 +65,27 @@ def page_bound(q, kmin, kmax):
     return out
 
 
+def page_bound_heads(q, kmin, kmax):
+    """The bound before the group maximum: one row per query head.
+
+    U[t, h, p] = sum_d max(q[t,h,d] * kmin[g,p,d], q[t,h,d] * kmax[g,p,d])
+    with g the KV head of h, summed sequentially over d in float64 -- the
+    selection granularity of one page set per (token, query head).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_tok, hq, d = q.shape
+    hkv, p, _ = kmin.shape
+    out = np.empty((n_tok, hq, p))
+    for h in range(hq):
+        g = kv_head_of(h, hq, hkv)
+        acc = np.zeros((n_tok, p))
+        for j in range(d):
+            qj = q[:, h, j][:, None]
+            acc = acc + np.maximum(qj * kmin[g, :, j][None, :], qj * kmax[g, :, j][None, :])
+        out[:, h, :] = acc
+    return out
+
+
 def topk_pages(bound, k):
     """Top-k pages per (token, KV head) under the order (bound desc, page asc).
 
@@ -121,6 +142,23 @@ def split_attn(q, k_p, v_p, sel, page, scale, residual=True):
                 a, l_ = attn(rows, kg[keep], vg[keep], scale)
                 a_res[t, heads], l_res[t, heads] = a, l_
     return (a_sel, l_sel), ((a_res, l_res) if residual else None)
+
+
+def union_size_heads(sel_heads, active, hkv):
+    """|union over active tokens t and query heads h of group g of S[t, h]|
+    per KV head g, for a selection made per (token, query head).
+
+    sel_heads [B, Hq, k] page ids (the granularity of ``page_bound_heads``).
+    """
+    sel_heads = np.asarray(sel_heads)
+    n_tok, hq, _ = sel_heads.shape
+    act = np.nonzero(np.asarray(active))[0]
+    out = np.zeros(hkv, dtype=np.int64)
+    for g in range(hkv):
+        heads = [h for h in range(hq) if kv_head_of(h, hq, hkv) == g]
+        if act.size:
+            out[g] = np.unique(sel_heads[np.ix_(act, heads)]).size
+    return out
 
 
 def union_size(sel, active):
