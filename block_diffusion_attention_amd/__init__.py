@@ -78,12 +78,14 @@ class Step:
     page metadata is kept for the cache's capacity and updated
     incrementally. ``new_block()`` restarts the step counter over the same
     prefix (the next call recomputes the cached pair). ``since_refresh``:
-    TEXT counts the ids changed since the last recompute step.
+    TEXT counts the ids changed since the last recompute step. ``reselect``:
+    SPARSE runs LoSA's own step (dense first step, pages chosen again at
+    every step, no residual).
     """
 
     def __init__(self, mode, shape, n_q, k_prefix=None, v_prefix=None, tau=0, gamma=0.0,
                  page_size=16, k_pages=0, pct=25, device=None, cache=None,
-                 since_refresh=False):
+                 since_refresh=False, reselect=False):
         load()
         self.cache = cache
         if cache is not None:
@@ -140,6 +142,7 @@ class Step:
             for name in ("a_res", "l_res", "pages", "kmin", "kmax", "q_prev", "mse", "active"):
                 setattr(st, name, ptr(getattr(self, name)))
             st.page_cap = n_pages if cache is not None else 0
+            st.sparse_reselect = 1 if reselect else 0
         st.count_since_refresh = 1 if since_refresh else 0
         self.state = st
         self._dev = dev

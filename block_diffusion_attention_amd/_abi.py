@@ -68,7 +68,8 @@ class fb_step_state(C.Structure):
                 ("q_prev", C.c_void_p), ("mse", C.c_void_p), ("active", C.c_void_p),
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
                 ("step", C.c_int64), ("meta_ready", C.c_int32),
-                ("page_cap", C.c_int64), ("count_since_refresh", C.c_int32)]
+                ("page_cap", C.c_int64), ("count_since_refresh", C.c_int32),
+                ("sparse_reselect", C.c_int32)]
 
 
 class fb_step_args(C.Structure):

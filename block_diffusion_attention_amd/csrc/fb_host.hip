@@ -387,7 +387,10 @@ fb_status validate_prefix(const fb_attn_shape* shape, const fb_tensor& q, const 
   if ((st = check_sel(sel, *shape, q.n_tok, k.n_tok)) != FB_OK) return st;
   const int mode = sel ? sel->mode : FB_SEL_DENSE;
   if (mode == FB_SEL_DENSE && (a_res || l_res)) return FB_ERR_INVALID_ARGUMENT;
-  if (mode != FB_SEL_DENSE && (!a_res || !l_res)) return FB_ERR_INVALID_ARGUMENT;
+  if (mode == FB_SEL_SPLIT && (!a_res || !l_res)) return FB_ERR_INVALID_ARGUMENT;
+  // GATHER: the cached residual, or none at all (both NULL)
+  if (mode == FB_SEL_GATHER && (a_res == nullptr) != (l_res == nullptr))
+    return FB_ERR_INVALID_ARGUMENT;
   return FB_OK;
 }
 
@@ -673,6 +676,10 @@ size_t fb_step_workspace(const fb_step_state* st) {
   }
   const size_t p1 = prefix_ws_bytes(st->shape, st->n_q, st->k_prefix.n_tok, psel);
   ws = p1;
+  if (st->mode == FB_STEP_SPARSE && st->sparse_reselect) {   // dense first step
+    const size_t p0 = prefix_ws_bytes(st->shape, st->n_q, st->k_prefix.n_tok, nullptr);
+    ws = ws > p0 ? ws : p0;
+  }
   if (st->mode == FB_STEP_SPARSE) {
     sel.mode = FB_SEL_GATHER;
     const size_t p2 = prefix_ws_bytes(st->shape, st->n_q, st->k_prefix.n_tok, &sel);
@@ -749,8 +756,10 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       break;
     }
     case FB_STEP_SPARSE: {
-      if (!st->a_res || !st->l_res || !st->pages || !st->kmin || !st->kmax || !st->q_prev ||
-          !st->active)
+      if (st->sparse_reselect != 0 && st->sparse_reselect != 1) return FB_ERR_INVALID_ARGUMENT;
+      const bool reselect = st->sparse_reselect == 1;
+      if ((!reselect && (!st->a_res || !st->l_res)) || !st->pages || !st->kmin || !st->kmax ||
+          !st->q_prev || !st->active)
         return FB_ERR_INVALID_ARGUMENT;
       if (st->page_size < 1 || st->pct < 1 || st->pct > 100) return FB_ERR_INVALID_ARGUMENT;
       const int64_t n_pages = (st->k_prefix.n_tok + st->page_size - 1) / st->page_size;
@@ -791,22 +800,35 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
           if (rc != FB_OK) return rc;
           st->meta_ready = 1;
         }
-        rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
-                            st->pages, nullptr, st->ws, st->ws_bytes, stream);
-        if (rc != FB_OK) return rc;
-        sel.mode = FB_SEL_SPLIT;
-        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
-                            st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
+        if (reselect) {
+          // LoSA: a dense first step; pages are chosen at every later step
+          rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, nullptr,
+                              st->a_out, st->l_out, nullptr, nullptr, st->ws, st->ws_bytes,
+                              stream);
+        } else {
+          rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
+                              st->pages, nullptr, st->ws, st->ws_bytes, stream);
+          if (rc != FB_OK) return rc;
+          sel.mode = FB_SEL_SPLIT;
+          rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
+                              st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
+        }
         if (rc != FB_OK) return rc;
         rc = token_step(0, 1);                     // every token active at the refresh step
         if (rc != FB_OK) return rc;
       } else if (a->decision != 1) {
         rc = token_step(a->decision == 0 ? 0 : 1, 1);
         if (rc != FB_OK) return rc;
+        if (reselect) {                            // the current queries choose the pages
+          rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
+                              st->pages, nullptr, st->ws, st->ws_bytes, stream);
+          if (rc != FB_OK) return rc;
+        }
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
         rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
-                            st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
+                            st->l_out, reselect ? nullptr : st->a_res,
+                            reselect ? nullptr : st->l_res, st->ws, st->ws_bytes, stream);
         if (rc != FB_OK) return rc;
       } else {
         rc = token_step(0, 0);                     // forced reuse: no token active

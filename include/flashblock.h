@@ -119,7 +119,9 @@ typedef struct {
  *   of the selected part and the residual).                                  *
  *   GATHER -> a_res, l_res are INPUTS (the cached residual); for rows whose  *
  *   active byte is 1, a_out, l_out = merge(pair over the selected pages,     *
- *   cached residual); other rows are left untouched.                         *
+ *   cached residual); other rows are left untouched. With a_res and l_res   *
+ *   both NULL there is no residual: a_out, l_out = the pair over the         *
+ *   selected pages alone (LoSA s2: sparse attention for active tokens).      *
  * ws: device workspace of at least fb_prefix_attn_workspace() bytes (split- *
  *   K partials); may be NULL when that size is 0.                            *
  * Errors: INVALID_ARGUMENT on bad shape/stride/alignment/NULL, n_q < 1,     *
@@ -296,7 +298,11 @@ fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* cache,
  * SPARSE (FlashBlock s2 sparse compatibility + LoSA s2 workflow): step 0   *
  *        builds page metadata (once per prefix), selects pages, runs the    *
  *        SPLIT pass (cache + residual); later steps classify tokens by      *
- *        query MSE and run the GATHER pass for active rows. Blocks with     *
+ *        query MSE and run the GATHER pass for active rows. With            *
+ *        sparse_reselect = 1 (LoSA s2 workflow as it stands): step 0 is a    *
+ *        dense pass; later steps select pages with the step's queries and   *
+ *        run GATHER for active rows with no residual (a_res, l_res unused).  *
+ *        Blocks with                                                        *
  *        n_q > 1024 or n_q * Hq > 4096 need a contiguous q_blk              *
  *        (UNSUPPORTED otherwise).                                           *
  *                                                                           *
@@ -357,6 +363,8 @@ typedef struct {
                               0 = P = ceil(n_kv / page_size) (packed)          */
   int32_t count_since_refresh; /* TEXT: 1 = M counts ids changed since the last
                               recompute step instead of the previous step      */
+  int32_t sparse_reselect; /* SPARSE: 1 = LoSA per step (dense first step, pages
+                              re-selected each step, no residual)              */
 } fb_step_state;
 
 typedef struct {
