@@ -89,7 +89,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
-    ap.add_argument("--only", choices=("video", "sparse", "growing"),
+    ap.add_argument("--only", choices=("video", "sparse", "growing", "losa"),
                     help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
@@ -118,7 +118,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.only:
-        fn = {"video": video_extra, "sparse": sparse_extra, "growing": growing_extra}[args.only]
+        fn = {"video": video_extra, "sparse": sparse_extra, "growing": growing_extra,
+              "losa": losa_extra}[args.only]
         print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream(), args.kv_layout)}),
               flush=True)
         return
@@ -276,6 +277,7 @@ def main():
         extra["video"] = video_extra(fb, W, dev, stream, args.kv_layout)
         extra["sparse"] = sparse_extra(fb, W, dev, stream, args.kv_layout)
         extra["growing"] = growing_extra(fb, W, dev, stream, args.kv_layout)
+        extra["losa"] = losa_extra(fb, W, dev, stream, args.kv_layout)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
@@ -509,6 +511,80 @@ def sparse_extra(fb, W, dev, stream, layout):
                     "gather_GB_s": round(g_bytes / (ms_g * 1e-3) / 1e9, 1),
                     "gather_frac_of_hbm_peak": round(g_bytes / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                     "active_tokens_last_step": int(act.sum().item())})
+    return res
+
+
+def losa_extra(fb, W, dev, stream, layout):
+    """LoSA's own step (32q/8kv, d=128, 65536-token prefix in 16-token pages,
+    B=8, 8 steps): pages re-selected with each step's queries for the active
+    tokens, no residual. Per density: the block through fb_step against the
+    FlashBlock residual block, and the KV inflation of steps 1-7 -- pages per
+    KV head in the union over the active tokens (one set per token and KV
+    group), over all B tokens, and with one set per query head -- next to
+    B*k and |A|*k."""
+    import torch
+    base = W.SPARSE
+    kp, vp = W.prefix_kv(base)
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kd, vd = prefix_cache(kp, dev, layout), prefix_cache(vp, dev, layout)
+    H, G, d, B, N, PS = base.n_q_heads, base.n_kv_heads, base.head_dim, base.n_block, base.n_prefix, base.page
+    P = N // PS
+    shape = fb.shape_of(H, G, d, base.scale, torch.bfloat16)
+    per_head = fb.shape_of(H, H, d, base.scale, torch.bfloat16)
+    res = []
+    for dens in W.SPARSE_DENSITIES:
+        cfg = base.with_(density=dens)
+        k = cfg.k_pages
+        steps = [tuple(bf(s[n]) for n in ("q", "k", "v")) for s in W.sparse_steps(cfg)]
+        af = torch.empty(B, H, d, device=dev)
+        lf = torch.empty(B, H, device=dev)
+        ms = {}
+        for name, reselect in (("losa", True), ("flashblock_residual", False)):
+            st = fb.Step(fb.FB_STEP_SPARSE, shape, B, kd, vd, page_size=PS, k_pages=k,
+                         pct=cfg.pct, reselect=reselect)
+
+            def block():
+                st.new_block()
+                for q, kb, vb in steps:
+                    st.step(q, kb, vb, af, lf)
+            block()
+            torch.cuda.synchronize()
+            ms[name] = _timed(block, stream, 5)
+            if reselect:
+                losa = st
+        # the unions, step by step (untimed)
+        kmin_h = losa.kmin.repeat_interleave(H // G, dim=0).contiguous()
+        kmax_h = losa.kmax.repeat_interleave(H // G, dim=0).contiguous()
+        pages_h = torch.empty(B, H, k, device=dev, dtype=torch.int32)
+        ws_h = torch.empty(max(fb.fb_page_select_workspace(per_head, B, P), 16), dtype=torch.uint8,
+                           device=dev)
+        u_act, u_all, u_head, n_act = [], [], [], []
+        losa.new_block()
+        for i, (q, kb, vb) in enumerate(steps):
+            losa.step(q, kb, vb, af, lf)
+            if i == 0:
+                continue
+            fb.fb_page_select(per_head, q, kmin_h, kmax_h, P, k, pages_h, ws=ws_h, stream=stream)
+            torch.cuda.synchronize()
+            pg, on, ph = losa.pages.cpu().numpy(), losa.active.cpu().numpy().astype(bool), pages_h.cpu().numpy()
+            grp = H // G
+            u_act.append(np.mean([np.unique(pg[on, g]).size for g in range(G)]))
+            u_all.append(np.mean([np.unique(pg[:, g]).size for g in range(G)]))
+            u_head.append(np.mean([np.unique(ph[on][:, g * grp:(g + 1) * grp]).size for g in range(G)]))
+            n_act.append(int(on.sum()))
+        res.append({"density": dens, "k_pages": k,
+                    "ms_block_losa": round(ms["losa"], 4),
+                    "ms_block_flashblock_residual": round(ms["flashblock_residual"], 4),
+                    "query_tok_per_s_losa": round(len(steps) * B / (ms["losa"] * 1e-3), 1),
+                    "mean_active_tokens": round(float(np.mean(n_act)), 2),
+                    "union_pages_per_kv_head": {
+                        "active_tokens_per_group": round(float(np.mean(u_act)), 1),
+                        "all_tokens_per_group": round(float(np.mean(u_all)), 1),
+                        "active_tokens_per_query_head": round(float(np.mean(u_head)), 1),
+                        "B_times_k": B * k, "active_times_k": round(float(np.mean(n_act)) * k, 1),
+                        "pages": P}})
     return res
 
 
