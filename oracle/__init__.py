@@ -16,6 +16,11 @@ of the papers):
   and the log-space composition equation for A_full), "adaptive reuse
   strategies" (threshold tau on the updated-token count M, per-head
   similarity against gamma, sparse-attention compatibility).
+* [SPA]  "Proxy singolari per la caching adattiva nei modelli linguistici
+  diffusivi" (SPA-Cache), technical summary (gist.science/it/paper/2602.02544):
+  methodology s1 identification by singular proxies (truncated SVD of the
+  value projection, cosine against the cached proxy, lowest similarity
+  recomputed).
 * [LoSA] "LoSA: Locality Aware Sparse Attention for Block-Wise Diffusion
   Language Models" (gist.science/it/paper/2604.12056): s1 KV inflation;
   s2 methodology -- token classification by query MSE, reuse for stable
@@ -33,6 +38,8 @@ Modules:
   page selection, and the selected/residual split of the prefix.
 * ``growing``    -- the outer loop over blocks: each finished block's keys
   and values join the prefix cache before the next block.
+* ``spa``        -- the singular-proxy identifier: rank-r proxies of the value
+  states, their cosine against the cached proxies, the least similar tokens.
 
 All arithmetic is float64 on the exact upcast of the bf16 (or fp32) input
 bits. Every function is pinned by the ``-m "not gpu"`` tests against closed
@@ -40,4 +47,4 @@ forms, invariants, library routines or brute force on tiny inputs; none is
 "parity unpinned".
 """
 
-from . import attention, controller, growing, quest  # noqa: F401
+from . import attention, controller, growing, quest, spa  # noqa: F401

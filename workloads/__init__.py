@@ -273,9 +273,84 @@ def sparse_steps(cfg, variant=0, block=0, m_override=None):
     return text_steps(cfg, variant, block, m_override)
 
 
+# --------------------------------------------------------------------------
+# singular-proxy identifier (SPA-Cache): hidden states and a value projection
+# --------------------------------------------------------------------------
+
+TAG_FACTOR_U, TAG_FACTOR_V, TAG_HIDDEN, TAG_DRIFT = 7, 8, 9, 10
+
+
+@dataclass(frozen=True)
+class SpaConfig:
+    """N hidden states of model width D per denoising step, a rank-r factor of
+    the value projection, and the share of tokens recomputed per step."""
+    name: str = "spa"
+    cfg_id: int = 6
+    n_tok: int = 1024
+    d_model: int = 4096
+    rank: int = 128
+    n_steps: int = 4
+    ratio: float = 0.25
+
+    @property
+    def n_select(self):
+        return int(math.floor(self.ratio * self.n_tok + 0.5))
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+SPA = SpaConfig()
+
+
+def spectrum(n):
+    """Singular values of the synthetic value projection: (i + 1) ** -0.5."""
+    return (np.arange(n, dtype=np.float64) + 1.0) ** -0.5
+
+
+def _orthonormal(g, rows, cols):
+    q, r = np.linalg.qr(g.standard_normal((rows, cols)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def spa_factor(cfg, variant=0):
+    """The stored rank-r factor [D, r] (bf16 bits): U_r diag(sigma_1..r) of a
+    value projection W = U diag(sigma) V^T whose U has orthonormal columns
+    (QR of a seeded Gaussian matrix) and sigma = ``spectrum``."""
+    u = _orthonormal(rng(cfg.cfg_id, variant, 0, 0, TAG_FACTOR_U), cfg.d_model, cfg.rank)
+    f = u * spectrum(cfg.rank)[None, :]
+    return bf16_bits(f.astype(np.float32))
+
+
+def spa_projection(cfg, variant=0):
+    """A whole synthetic value projection for small D: (U [D, D], sigma [D],
+    V [D, D]) in float64, W = U diag(sigma) V^T, U and V orthonormal."""
+    d = cfg.d_model
+    u = _orthonormal(rng(cfg.cfg_id, variant, 0, 0, TAG_FACTOR_U), d, d)
+    v = _orthonormal(rng(cfg.cfg_id, variant, 0, 0, TAG_FACTOR_V), d, d)
+    return u, spectrum(d), v
+
+
+def spa_steps(cfg, variant=0):
+    """Hidden states [N, D] (bf16 bits) per denoising step: x^0 ~ N(0, 1), then
+    a random walk x^{s+1} = x^s + delta_t eps with one drift scale per token,
+    delta_t ~ LogUniform(1e-3, 1) (kept in float32, rounded per step)."""
+    n, d = cfg.n_tok, cfg.d_model
+    delta = np.exp(rng(cfg.cfg_id, variant, 0, 0, TAG_DRIFT).uniform(
+        math.log(1e-3), 0.0, n)).astype(np.float32)[:, None]
+    x = None
+    out = []
+    for s in range(cfg.n_steps):
+        eps = rng(cfg.cfg_id, variant, 0, s, TAG_HIDDEN).standard_normal((n, d), dtype=np.float32)
+        x = eps if s == 0 else x + delta * eps
+        out.append(bf16_bits(x))
+    return out
+
+
 __all__ = [
     "Config", "CONFIGS", "TINY", "TEXT", "LONG", "VIDEO", "SPARSE",
     "LONG_CONTEXTS", "LONG_BLOCKS", "SPARSE_DENSITIES", "bf16_bits",
     "bf16_to_f32", "values", "rng", "prefix_kv", "text_steps",
-    "video_sigmas", "video_steps", "sparse_steps",
+    "video_sigmas", "video_steps", "sparse_steps", "SpaConfig", "SPA", "spectrum",
+    "spa_factor", "spa_projection", "spa_steps",
 ]
