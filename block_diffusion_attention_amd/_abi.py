@@ -54,6 +54,15 @@ class fb_kv_cache(C.Structure):
                 ("n_tok", C.c_int64), ("stride_tok", C.c_int64), ("stride_head", C.c_int64)]
 
 
+class fb_proxy_args(C.Structure):
+    _fields_ = [("n_tok", C.c_int32), ("d_model", C.c_int32), ("rank", C.c_int32),
+                ("dtype", C.c_int), ("x", C.c_void_p), ("x_stride", C.c_int64),
+                ("factor", C.c_void_p), ("cache", C.c_void_p), ("n_select", C.c_int32),
+                ("init", C.c_int32), ("key", C.c_void_p), ("selected", C.c_void_p),
+                ("mask", C.c_void_p), ("proxy", C.c_void_p), ("ws", C.c_void_p),
+                ("ws_bytes", C.c_size_t)]
+
+
 class fb_step_state(C.Structure):
     _fields_ = [("shape", fb_attn_shape), ("mode", C.c_int), ("n_q", C.c_int32),
                 ("k_prefix", fb_tensor), ("v_prefix", fb_tensor),
@@ -101,6 +110,8 @@ _SIGS = [
     ("fb_page_select", C.c_int,
      [C.POINTER(fb_attn_shape), fb_tensor, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
       C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("fb_proxy_decide_workspace", C.c_size_t, [C.POINTER(fb_proxy_args)]),
+    ("fb_proxy_decide", C.c_int, [C.POINTER(fb_proxy_args), C.c_void_p]),
     ("fb_kv_append", C.c_int,
      [C.POINTER(fb_attn_shape), C.POINTER(fb_kv_cache), fb_tensor, fb_tensor, C.c_void_p]),
     ("fb_step_workspace", C.c_size_t, [C.POINTER(fb_step_state)]),
@@ -252,6 +263,31 @@ def fb_page_select(shape, q, kmin, kmax, n_pages, k_pages, pages, bound=None, ws
                                int(n_pages), int(page_cap), int(k_pages), ptr(pages), ptr(bound),
                                ptr(ws), ws_bytes, stream_of(stream))
     _check("fb_page_select", st)
+
+
+def fb_proxy_decide_workspace(args):
+    return load().fb_proxy_decide_workspace(C.byref(args))
+
+
+def fb_proxy_decide(args, stream=None):
+    _check("fb_proxy_decide", load().fb_proxy_decide(C.byref(args), stream_of(stream)))
+
+
+def proxy_args(x, factor, cache, mask, selected=None, n_select=0, init=False, key=None,
+               proxy=None, ws=None):
+    """fb_proxy_args of torch tensors: x [N, D], factor [D, r] (same dtype),
+    cache [N, r] float64, mask [N] uint8, selected [n_select] int32."""
+    if x.dim() != 2 or x.stride(1) != 1 or not factor.is_contiguous():
+        raise ValueError("x must be [N, D] with contiguous rows, factor contiguous")
+    a = fb_proxy_args()
+    a.n_tok, a.d_model, a.rank = x.shape[0], x.shape[1], factor.shape[1]
+    a.dtype = dtype_code(x.dtype)
+    a.x, a.x_stride, a.factor = x.data_ptr(), x.stride(0), factor.data_ptr()
+    a.cache, a.mask, a.selected = ptr(cache), ptr(mask), ptr(selected)
+    a.n_select, a.init = int(n_select), 1 if init else 0
+    a.key, a.proxy = ptr(key), ptr(proxy)
+    a.ws, a.ws_bytes = ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
+    return a
 
 
 def fb_kv_append(shape, cache, k_blk, v_blk, stream=None):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashblock.so")
-SOURCES = ["fb_host.hip", "k1_prefix.hip", "k2_block.hip", "k3_decide.hip", "k4_pages.hip", "k5_rows.hip", "k6_sparse.hip", "k7_cache.hip"]
+SOURCES = ["fb_host.hip", "k1_prefix.hip", "k2_block.hip", "k3_decide.hip", "k4_pages.hip", "k5_rows.hip", "k6_sparse.hip", "k7_cache.hip", "k8_proxy.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -623,6 +623,52 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
                                 pages, stream));
 }
 
+size_t fb_proxy_decide_workspace(const fb_proxy_args* a) {
+  if (!a || a->n_tok < 1 || a->d_model < 1 || !proxy_rank_ok(a->rank)) return 0;
+  const size_t n = static_cast<size_t>(a->n_tok), r = static_cast<size_t>(a->rank);
+  size_t ws = align_up(static_cast<size_t>(proxy_n_blocks(a->d_model)) * n * r * sizeof(double));
+  if (!a->proxy) ws += align_up(n * r * sizeof(double));
+  ws += align_up(n * sizeof(double));                 // negated keys (top-k input)
+  return ws;
+}
+
+fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
+  if (!a || a->n_tok < 1 || a->d_model < 1 || a->x_stride < a->d_model) return FB_ERR_INVALID_ARGUMENT;
+  if (a->dtype != FB_BF16 && a->dtype != FB_F32) return FB_ERR_INVALID_ARGUMENT;
+  if (!a->x || !a->factor || !a->cache || !a->mask) return FB_ERR_INVALID_ARGUMENT;
+  if (a->init != 0 && a->init != 1) return FB_ERR_INVALID_ARGUMENT;
+  if (!a->init && (a->n_select < 0 || a->n_select > a->n_tok)) return FB_ERR_INVALID_ARGUMENT;
+  if (!a->init && a->n_select > 0 && !a->selected) return FB_ERR_INVALID_ARGUMENT;
+  if (!proxy_rank_ok(a->rank)) return FB_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(a->n_tok) * a->rank > INT32_MAX) return FB_ERR_UNSUPPORTED;
+  const size_t need = fb_proxy_decide_workspace(a);
+  if (a->ws_bytes < need || !a->ws) return FB_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(a->ws)) return FB_ERR_INVALID_ARGUMENT;
+  const size_t n = static_cast<size_t>(a->n_tok), r = static_cast<size_t>(a->rank);
+  const int nb = proxy_n_blocks(a->d_model);
+  char* w = static_cast<char*>(a->ws);
+  double* part = reinterpret_cast<double*>(w);
+  w += align_up(static_cast<size_t>(nb) * n * r * sizeof(double));
+  double* proxy = a->proxy;
+  if (!proxy) {
+    proxy = reinterpret_cast<double*>(w);
+    w += align_up(n * r * sizeof(double));
+  }
+  double* neg_key = reinterpret_cast<double*>(w);
+  fb_status rc = dev(launch_proxy_partials(a->x, a->x_stride, a->factor, a->dtype, a->n_tok,
+                                           a->d_model, a->rank, part, stream));
+  if (rc != FB_OK) return rc;
+  if (!a->init && (rc = dev(launch_fill_u8(a->mask, a->n_tok, 0, stream))) != FB_OK) return rc;
+  rc = dev(launch_proxy_keys(part, nb, a->n_tok, a->rank, a->init, a->cache, proxy, a->key,
+                             neg_key, a->mask, stream));
+  if (rc != FB_OK || a->init) return rc;
+  // the lowest keys are the largest negated keys (ties: lower id)
+  rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, a->selected, stream));
+  if (rc != FB_OK) return rc;
+  return dev(launch_proxy_scatter(a->selected, a->n_select, a->n_tok, proxy, a->rank, a->cache,
+                                  a->mask, stream));
+}
+
 fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* c, fb_tensor k_blk,
                        fb_tensor v_blk, hipStream_t stream) {
   fb_status st = check_shape(shape);

@@ -209,6 +209,22 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                               const void* kmax, int n_q, int hq, int hkv, int d,
                               int64_t n_pages, int64_t page_cap, int k_pages, fb_dtype dt,
                               double* bound, int32_t* pages, hipStream_t s);
+// exact top-k of each row of keys [n_rows * hkv][n] (largest first, ties to
+// the lower index), the chosen indices listed ascending in out [.., k]
+hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
+                            int32_t* out, hipStream_t s);
+// singular-proxy identification: block partials of the proxies, then the
+// proxies, cache fill (init) or ranking keys (+ negated keys for the top-k)
+bool proxy_rank_ok(int rank);
+hipError_t launch_proxy_partials(const void* x, int64_t x_st, const void* factor, fb_dtype dt,
+                                 int n_tok, int d_model, int rank, double* part, hipStream_t s);
+int proxy_n_blocks(int d_model);
+hipError_t launch_proxy_keys(const double* part, int n_blocks, int n_tok, int rank, int init,
+                             double* cache, double* proxy, double* key, double* neg_key,
+                             uint8_t* mask, hipStream_t s);
+hipError_t launch_proxy_scatter(const int32_t* selected, int n_select, int n_tok,
+                                const double* proxy, int rank, double* cache, uint8_t* mask,
+                                hipStream_t s);
 // the finished block's K/V rows into cache tokens [tok0, tok0 + n_blk); byte
 // strides; rows are (d * elem_bytes) bytes, a multiple of 16
 hipError_t launch_kv_append(const void* k_src, int64_t ks_t, int64_t ks_h, const void* v_src,

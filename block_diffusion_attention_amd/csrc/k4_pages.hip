@@ -397,15 +397,20 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
 #undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;
-  if (n_pages <= 256 * 16)
-    hipLaunchKernelGGL(page_topk_reg_kernel<16>, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv,
-                       n_pages, k_pages, pages);
-  else if (n_pages <= 256 * 32)
-    hipLaunchKernelGGL(page_topk_reg_kernel<32>, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv,
-                       n_pages, k_pages, pages);
+  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, pages, s);
+}
+
+hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
+                            int32_t* out, hipStream_t s) {
+  if (k <= 0 || n_rows <= 0) return hipSuccess;
+  if (n <= 256 * 16)
+    hipLaunchKernelGGL(page_topk_reg_kernel<16>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
+                       k, out);
+  else if (n <= 256 * 32)
+    hipLaunchKernelGGL(page_topk_reg_kernel<32>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
+                       k, out);
   else
-    hipLaunchKernelGGL(page_topk_kernel, dim3(n_q, hkv), dim3(256), 0, s, bound, hkv, n_pages,
-                       k_pages, pages);
+    hipLaunchKernelGGL(page_topk_kernel, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n, k, out);
   return hipGetLastError();
 }
 

@@ -255,6 +255,55 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * fb_proxy_decide -- singular-proxy identification (SPA-Cache, "Proxy       *
+ * singolari per la caching adattiva nei modelli linguistici diffusivi",     *
+ * methodology s1): which tokens to recompute, found from rank-r proxies of  *
+ * their value states.                                                       *
+ *                                                                           *
+ * x [n_tok, d_model] input states (dtype; row stride x_stride elements);    *
+ * factor [d_model, rank] contiguous (dtype): U_r diag(sigma_r) of the value *
+ * projection's truncated SVD; cache [n_tok, rank] float64: the proxy kept   *
+ * per token from the step it was last recomputed (in/out).                  *
+ *   proxy p[t][i] = sum_c x[t][c] factor[c][i] in float64, in blocks of 512 *
+ *     consecutive c (each in c order, the block sums then in block order;   *
+ *     products of two bf16 or two fp32 values are exact in float64);       *
+ *   key[t] = sign(cos) cos^2 of p[t] against cache[t]: dot^2 / (|p|^2       *
+ *     |c|^2), dot and the squared norms summed over i in order from         *
+ *     separately rounded products, negated when dot < 0 and the quotient   *
+ *     is not 0; both norms 0 -> 1, one -> 0 (monotone in the cosine).       *
+ * init = 1: cache <- p for every token, mask all 1 (key, selected unused).  *
+ * init = 0: selected [n_select] = the n_select tokens of lowest key (ties:  *
+ *   lower id), ascending; mask[t] = 1 for them, 0 otherwise; their cache    *
+ *   rows <- p. key (nullable) receives every token's key, proxy (nullable) *
+ *   every current proxy.                                                    *
+ * Errors: INVALID_ARGUMENT for n_tok < 1, d_model < 1, x_stride < d_model, *
+ *   NULL x / factor / cache / mask (selected when n_select > 0), n_select   *
+ *   outside [0, n_tok], init not 0 or 1; UNSUPPORTED for rank not a        *
+ *   multiple of 32 in [32, 128]; WORKSPACE_TOO_SMALL.                       *
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_tok;           /* N                                                */
+  int32_t d_model;         /* D                                                */
+  int32_t rank;            /* r                                                */
+  fb_dtype dtype;          /* of x and factor                                  */
+  const void* x;           /* [n_tok, d_model]                                 */
+  int64_t x_stride;        /* elements between tokens                          */
+  const void* factor;      /* [d_model, rank]                                  */
+  double* cache;           /* [n_tok, rank] in/out                             */
+  int32_t n_select;        /* tokens to recompute (init = 0)                   */
+  int32_t init;            /* 1: first step, every token recomputed            */
+  double* key;             /* out [n_tok], nullable                            */
+  int32_t* selected;       /* out [n_select]                                   */
+  uint8_t* mask;           /* out [n_tok]                                      */
+  double* proxy;           /* out [n_tok, rank], nullable                      */
+  void* ws;                /* device workspace >= fb_proxy_decide_workspace() */
+  size_t ws_bytes;
+} fb_proxy_args;
+
+size_t fb_proxy_decide_workspace(const fb_proxy_args* args);
+fb_status fb_proxy_decide(const fb_proxy_args* args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Growing prefix cache (FlashBlock s1 problem statement: block-wise         *
  * decoding attends over a KV cache that grows as blocks finish).            *
  *                                                                           *

@@ -54,6 +54,7 @@ STRUCTS = {
     "fb_step_state": [f[0] for f in _abi.fb_step_state._fields_],
     "fb_step_args": [f[0] for f in _abi.fb_step_args._fields_],
     "fb_kv_cache": [f[0] for f in _abi.fb_kv_cache._fields_],
+    "fb_proxy_args": [f[0] for f in _abi.fb_proxy_args._fields_],
 }
 
 
@@ -299,3 +300,27 @@ def test_step_next_block_requires_the_state_to_view_the_cache(lib):
     st.mode, st.page_size, st.page_cap = fb.FB_STEP_SPARSE, 16, 2
     assert nb(C.byref(st), C.byref(c), blk, blk, None) == 1              # 3 pages > page_cap 2
     assert st.step == 3 and c.n_tok == 40 and st.k_prefix.n_tok == 40
+
+
+# ------------------------------------------------------ proxy identifier, no GPU
+
+def test_proxy_decide_rejects(lib):
+    a = fb.fb_proxy_args()
+    a.n_tok, a.d_model, a.rank, a.dtype = 1024, 4096, 128, fb.FB_BF16
+    a.x, a.x_stride, a.factor, a.cache, a.mask = FAKE, 4096, FAKE, FAKE, FAKE
+    a.n_select, a.selected = 256, FAKE
+    need = lib.fb_proxy_decide_workspace(C.byref(a))
+    # partials of 8 blocks + the proxies + the negated keys
+    assert need == 8 * 1024 * 128 * 8 + 1024 * 128 * 8 + 1024 * 8
+    assert lib.fb_proxy_decide(C.byref(a), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    a.ws, a.ws_bytes = FAKE, need
+    for field, bad, want in (("x_stride", 4095, 1), ("n_select", 1025, 1), ("n_select", -1, 1),
+                             ("init", 2, 1), ("rank", 48, 2), ("rank", 160, 2), ("dtype", 5, 1),
+                             ("n_tok", 0, 1), ("x", None, 1), ("selected", None, 1)):
+        old = getattr(a, field)
+        setattr(a, field, bad)
+        assert lib.fb_proxy_decide(C.byref(a), None) == want, field
+        setattr(a, field, old)
+    a.init, a.selected = 1, None              # init: the selection is not used
+    a.ws_bytes = need - 1
+    assert lib.fb_proxy_decide(C.byref(a), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
