@@ -89,7 +89,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
-    ap.add_argument("--only", choices=("video", "sparse", "growing", "losa"),
+    ap.add_argument("--only", choices=("video", "sparse", "growing", "losa", "spa"),
                     help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
@@ -119,7 +119,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.only:
         fn = {"video": video_extra, "sparse": sparse_extra, "growing": growing_extra,
-              "losa": losa_extra}[args.only]
+              "losa": losa_extra, "spa": spa_extra}[args.only]
         print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream(), args.kv_layout)}),
               flush=True)
         return
@@ -278,6 +278,7 @@ def main():
         extra["sparse"] = sparse_extra(fb, W, dev, stream, args.kv_layout)
         extra["growing"] = growing_extra(fb, W, dev, stream, args.kv_layout)
         extra["losa"] = losa_extra(fb, W, dev, stream, args.kv_layout)
+        extra["spa"] = spa_extra(fb, W, dev, stream, args.kv_layout)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
@@ -586,6 +587,41 @@ def losa_extra(fb, W, dev, stream, layout):
                         "B_times_k": B * k, "active_times_k": round(float(np.mean(n_act)) * k, 1),
                         "pages": P}})
     return res
+
+
+def spa_extra(fb, W, dev, stream, layout):
+    """The singular-proxy identifier (1024 tokens of width 4096, rank-128
+    factor of the value projection, a quarter of the tokens recomputed per
+    step): one identification step, and its block-partial contraction
+    (2 N D r float64 flops) against the float64 vector peak."""
+    import torch
+    del layout
+    cfg = W.SPA
+    n, d, r = cfg.n_tok, cfg.d_model, cfg.rank
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    f = bf(W.spa_factor(cfg))
+    xs = [bf(x) for x in W.spa_steps(cfg.with_(n_steps=2))]
+    cache = torch.empty(n, r, device=dev, dtype=torch.float64)
+    mask = torch.empty(n, device=dev, dtype=torch.uint8)
+    out = {"workload": "singular-proxy identification: %d tokens x %d, rank %d" % (n, d, r)}
+    for ratio in (0.25, 0.16):
+        k = int(np.floor(ratio * n + 0.5))
+        sel = torch.empty(k, device=dev, dtype=torch.int32)
+        a0 = fb.proxy_args(xs[0], f, cache, mask, sel, k, init=True)
+        ws = torch.empty(max(fb.fb_proxy_decide_workspace(a0), 16), dtype=torch.uint8, device=dev)
+        a0.ws, a0.ws_bytes = ws.data_ptr(), ws.numel()
+        a1 = fb.proxy_args(xs[1], f, cache, mask, sel, k, init=False, ws=ws)
+        fb.fb_proxy_decide(a0, stream)
+        ms = _timed(lambda: fb.fb_proxy_decide(a1, stream), stream, 50)
+        out["step_us_select_%d" % k] = round(ms * 1e3, 2)
+    flops = 2.0 * n * d * r
+    out["proxy_flop"] = flops
+    out["proxy_TFLOP_s_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6) / 1e12, 2)
+    out["frac_of_fp64_vector_peak_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6)
+                                                       / 1e12 / 78.6, 4)
+    return out
 
 
 def growing_extra(fb, W, dev, stream, layout):

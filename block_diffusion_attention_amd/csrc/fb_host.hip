@@ -635,7 +635,8 @@ size_t fb_proxy_decide_workspace(const fb_proxy_args* a) {
 fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
   if (!a || a->n_tok < 1 || a->d_model < 1 || a->x_stride < a->d_model) return FB_ERR_INVALID_ARGUMENT;
   if (a->dtype != FB_BF16 && a->dtype != FB_F32) return FB_ERR_INVALID_ARGUMENT;
-  if (!a->x || !a->factor || !a->cache || !a->mask) return FB_ERR_INVALID_ARGUMENT;
+  if (!a->x || !a->factor || !a->cache || !a->mask || !aligned16(a->factor))
+    return FB_ERR_INVALID_ARGUMENT;
   if (a->init != 0 && a->init != 1) return FB_ERR_INVALID_ARGUMENT;
   if (!a->init && (a->n_select < 0 || a->n_select > a->n_tok)) return FB_ERR_INVALID_ARGUMENT;
   if (!a->init && a->n_select > 0 && !a->selected) return FB_ERR_INVALID_ARGUMENT;

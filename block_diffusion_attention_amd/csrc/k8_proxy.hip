@@ -8,7 +8,7 @@
 // are recomputed.
 //
 // Arithmetic, fixed so that every bit is reproducible:
-//  * p[t][i] = sum_c x[t][c] F[c][i] in float64, in blocks of 512
+//  * p[t][i] = sum_c x[t][c] F[c][i] in float64, in blocks of 128
 //    consecutive c: each block summed in c order with fused multiply-add
 //    (a product of two bf16 or two fp32 values is exact in float64, so each
 //    step rounds once, as a multiply followed by an add would), the block
@@ -18,18 +18,20 @@
 //    order from separately rounded products; both norms 0 -> 1, one -> 0.
 //
 // The block partials are an fp64 FMA-bound contraction (N x D x r): each
-// workgroup takes 32 tokens x r dims of one 512-wide block, staged 64 c at a
-// time through LDS as float64; each thread keeps 4 tokens x r/32 dims of
-// accumulators and reads its operands with 16-byte LDS loads.
+// workgroup takes 32 tokens x r dims of one 128-wide block, staged 32 c at a
+// time through LDS as float64 (40 KB: four workgroups per CU) (16-byte global loads, the next stage in
+// flight while the current one is computed); each thread keeps 4 tokens x
+// r/32 dims of accumulators. The float64 FMA pipe needs several waves per
+// SIMD: blocks of 128 give 4 per SIMD at 1024 tokens x 4096, rank 128.
 #include "fb_internal.h"
 
 namespace fb {
 namespace {
 
-constexpr int kProxyBlock = 512;     // c per summation block
+constexpr int kProxyBlock = 128;     // c per summation block
 constexpr int kTokTile = 32;         // tokens per workgroup (partials)
-constexpr int kCStage = 64;          // c per LDS stage
-constexpr int kKeyTok = 32;          // tokens per workgroup (keys)
+constexpr int kCStage = 32;          // c per LDS stage
+constexpr int kKeyTok = 2;           // tokens per workgroup (keys)
 constexpr int kMaxRank = 128;
 
 template <typename T> __device__ __forceinline__ double ldd(const T* p);
@@ -40,13 +42,54 @@ template <> __device__ __forceinline__ double ldd<uint16_t>(const uint16_t* p) {
 
 typedef __attribute__((__vector_size__(2 * sizeof(double)))) double f64x2;
 
+// Element groups of 16 bytes (8 bf16 or 4 fp32) as float64, zeros at and
+// past `end`; `vec` = the group is 16-byte aligned (a single load).
+template <typename T> struct Grp { static constexpr int N = 16 / sizeof(T); };
+
+template <typename T>
+__device__ __forceinline__ u32x4v load_grp(const T* row, int c, int end, bool vec) {
+  constexpr int NE = Grp<T>::N;
+  if (vec && c + NE <= end) return *reinterpret_cast<const u32x4v*>(row + c);
+  u32x4v r = {0u, 0u, 0u, 0u};
+  T tmp[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) tmp[e] = c + e < end ? row[c + e] : T(0);
+  __builtin_memcpy(&r, tmp, 16);
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ double grp_elem(u32x4v g, int e);
+template <> __device__ __forceinline__ double grp_elem<uint16_t>(u32x4v g, int e) {
+  const uint32_t w = g[e >> 1];
+  return static_cast<double>(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)));
+}
+template <> __device__ __forceinline__ double grp_elem<float>(u32x4v g, int e) {
+  return static_cast<double>(__uint_as_float(g[e]));
+}
+
+// The dim held in accumulator slot j of lane ig: pairs 64 q + 2 ig,
+// 64 q + 2 ig + 1 (j = 2 q, 2 q + 1) and, for odd OI, 64 (OI / 2) + ig, so
+// the lanes of a wave read one contiguous run of LDS per load.
+template <int OI>
+__device__ __forceinline__ int dim_of(int j, int ig) {
+  return (j + 1 < OI || (OI % 2) == 0) ? 32 * (j & ~1) + 2 * ig + (j & 1) : 32 * j + ig;
+}
+
 // part[b][t][i] = sum over c in block b, in order, of x[t][c] F[c][i].
-// Thread (tg, ig): tokens 4 tg .. 4 tg + 3, dims OI ig .. OI ig + OI - 1.
+// Workgroup: 32 tokens x R dims (R = 32 OI) of one block, 256 threads;
+// thread (tg, ig): tokens 4 tg .. 4 tg + 3, the OI dims dim_of(j, ig).
+// Each 32-c stage is loaded into registers (16-byte groups) while the
+// previous one is computed, then converted into the LDS tiles.
 template <typename T, int OI>
 __global__ __launch_bounds__(256) void proxy_partials_kernel(const T* x, int64_t x_st,
                                                              const T* f, int n_tok, int d_model,
-                                                             double* part) {
+                                                             int x_vec, double* part) {
   constexpr int R = 32 * OI;
+  constexpr int NE = Grp<T>::N;
+  constexpr int XGN = kTokTile * kCStage / NE;        // x groups per stage
+  constexpr int FGN = kCStage * R / NE;               // F groups per stage
+  constexpr int XG = (XGN + 255) / 256;               // per thread
+  constexpr int FG = (FGN + 255) / 256;
   __shared__ __attribute__((aligned(16))) double xs[kCStage][kTokTile];   // [c][t]
   __shared__ __attribute__((aligned(16))) double fs[kCStage][R];          // [c][i]
   const int tid = threadIdx.x;
@@ -61,21 +104,53 @@ __global__ __launch_bounds__(256) void proxy_partials_kernel(const T* x, int64_t
 #pragma unroll
     for (int j = 0; j < OI; ++j) acc[a][j] = 0.0;
 
-  for (int c0 = c_begin; c0 < c_end; c0 += kCStage) {
-    // stage x[t0 .. t0 + 31][c0 .. c0 + 63] and F[c0 .. c0 + 63][0 .. R);
-    // positions past the block, the width or the tokens read as zero (a
-    // zero product leaves a sum that is not -0 unchanged)
-    for (int e = tid; e < kCStage * kTokTile; e += 256) {
-      const int t = e / kCStage, c = e % kCStage;          // consecutive threads: consecutive c
-      const int tt = t0 + t, cc = c0 + c;
-      xs[c][t] = (tt < n_tok && cc < c_end) ? ldd<T>(x + static_cast<int64_t>(tt) * x_st + cc) : 0.0;
+  u32x4v xr[XG], fr[FG];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < XG; ++k) {
+      const int v = tid + 256 * k;                 // group v: token v / (64 / NE), c-group v % ...
+      const int t = v / (kCStage / NE), c = c0 + (v % (kCStage / NE)) * NE;
+      const int tt = t0 + t;
+      xr[k] = (v < XGN && tt < n_tok)
+                  ? load_grp<T>(x + static_cast<int64_t>(tt) * x_st, c, c_end, x_vec != 0)
+                  : u32x4v{0u, 0u, 0u, 0u};
     }
-    for (int e = tid; e < kCStage * R; e += 256) {
-      const int c = e / R, i = e % R;
-      const int cc = c0 + c;
-      fs[c][i] = cc < c_end ? ldd<T>(f + static_cast<int64_t>(cc) * R + i) : 0.0;
+#pragma unroll
+    for (int k = 0; k < FG; ++k) {
+      const int v = tid + 256 * k;                 // group v: row v / (R / NE), i-group ...
+      const int c = c0 + v / (R / NE), i = (v % (R / NE)) * NE;
+      fr[k] = (v < FGN && c < c_end)
+                  ? *reinterpret_cast<const u32x4v*>(f + static_cast<int64_t>(c) * R + i)
+                  : u32x4v{0u, 0u, 0u, 0u};
+    }
+  };
+  fetch(c_begin);
+  for (int c0 = c_begin; c0 < c_end; c0 += kCStage) {
+    // the staged groups into LDS as float64 (zeros past the block end or the
+    // tokens: a zero product leaves a sum that is not -0 unchanged)
+#pragma unroll
+    for (int k = 0; k < XG; ++k) {
+      const int v = tid + 256 * k;
+      const int t = v / (kCStage / NE), c = (v % (kCStage / NE)) * NE;
+      if (v < XGN) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) xs[c + e][t] = grp_elem<T>(xr[k], e);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < FG; ++k) {
+      const int v = tid + 256 * k;
+      const int c = v / (R / NE), i = (v % (R / NE)) * NE;
+      if (v < FGN) {
+#pragma unroll
+        for (int e = 0; e < NE; e += 2) {
+          const f64x2 w = {grp_elem<T>(fr[k], e), grp_elem<T>(fr[k], e + 1)};
+          *reinterpret_cast<f64x2*>(&fs[c][i + e]) = w;
+        }
+      }
     }
     __syncthreads();
+    if (c0 + kCStage < c_end) fetch(c0 + kCStage);
 #pragma unroll 4
     for (int c = 0; c < kCStage; ++c) {
       const f64x2 xa = *reinterpret_cast<const f64x2*>(&xs[c][4 * tg]);
@@ -85,11 +160,11 @@ __global__ __launch_bounds__(256) void proxy_partials_kernel(const T* x, int64_t
 #pragma unroll
       for (int j = 0; j < OI; j += 2) {
         if (j + 1 < OI) {
-          const f64x2 fp = *reinterpret_cast<const f64x2*>(&fs[c][OI * ig + j]);
+          const f64x2 fp = *reinterpret_cast<const f64x2*>(&fs[c][32 * j + 2 * ig]);
           fv[j] = fp[0];
           fv[j + 1] = fp[1];
         } else {
-          fv[j] = fs[c][OI * ig + j];
+          fv[j] = fs[c][32 * j + ig];
         }
       }
 #pragma unroll
@@ -103,9 +178,9 @@ __global__ __launch_bounds__(256) void proxy_partials_kernel(const T* x, int64_t
   for (int a = 0; a < 4; ++a) {
     const int t = t0 + 4 * tg + a;
     if (t >= n_tok) continue;
-    double* o = part + (static_cast<int64_t>(b) * n_tok + t) * R + OI * ig;
+    double* o = part + (static_cast<int64_t>(b) * n_tok + t) * R;
 #pragma unroll
-    for (int j = 0; j < OI; ++j) o[j] = acc[a][j];
+    for (int j = 0; j < OI; ++j) o[dim_of<OI>(j, ig)] = acc[a][j];
   }
 }
 
@@ -188,10 +263,13 @@ int proxy_n_blocks(int d_model) { return (d_model + kProxyBlock - 1) / kProxyBlo
 hipError_t launch_proxy_partials(const void* x, int64_t x_st, const void* factor, fb_dtype dt,
                                  int n_tok, int d_model, int rank, double* part, hipStream_t s) {
   const dim3 grid((n_tok + kTokTile - 1) / kTokTile, proxy_n_blocks(d_model));
-#define FB_PROXY(TT, OI)                                                                         \
-  hipLaunchKernelGGL((proxy_partials_kernel<TT, OI>), grid, dim3(256), 0, s,                     \
-                     static_cast<const TT*>(x), x_st, static_cast<const TT*>(factor), n_tok,      \
-                     d_model, part)
+  // x rows load as 16-byte groups when every row starts 16-byte aligned
+  const int esz = dt == FB_BF16 ? 2 : 4;
+  const int x_vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0 && (x_st * esz) % 16 == 0) ? 1 : 0;
+#define FB_PROXY(TY, OI)                                                                         \
+  hipLaunchKernelGGL((proxy_partials_kernel<TY, OI>), grid, dim3(256), 0, s,                     \
+                     static_cast<const TY*>(x), x_st, static_cast<const TY*>(factor), n_tok,      \
+                     d_model, x_vec, part)
   const int oi = rank / 32;
   if (dt == FB_BF16) {
     if (oi == 1) FB_PROXY(uint16_t, 1);

@@ -261,10 +261,11 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
  * their value states.                                                       *
  *                                                                           *
  * x [n_tok, d_model] input states (dtype; row stride x_stride elements);    *
- * factor [d_model, rank] contiguous (dtype): U_r diag(sigma_r) of the value *
+ * factor [d_model, rank] contiguous, 16-byte aligned (dtype): U_r         *
+ * diag(sigma_r) of the value                                                *
  * projection's truncated SVD; cache [n_tok, rank] float64: the proxy kept   *
  * per token from the step it was last recomputed (in/out).                  *
- *   proxy p[t][i] = sum_c x[t][c] factor[c][i] in float64, in blocks of 512 *
+ *   proxy p[t][i] = sum_c x[t][c] factor[c][i] in float64, in blocks of 128 *
  *     consecutive c (each in c order, the block sums then in block order;   *
  *     products of two bf16 or two fp32 values are exact in float64);       *
  *   key[t] = sign(cos) cos^2 of p[t] against cache[t]: dot^2 / (|p|^2       *

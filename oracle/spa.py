@@ -32,7 +32,7 @@ Readings (the pages fix no precision, order or tie rule):
 
 import numpy as np
 
-PROXY_BLOCK = 512
+PROXY_BLOCK = 128
 
 
 def proxy(x, factor):

@@ -310,8 +310,8 @@ def test_proxy_decide_rejects(lib):
     a.x, a.x_stride, a.factor, a.cache, a.mask = FAKE, 4096, FAKE, FAKE, FAKE
     a.n_select, a.selected = 256, FAKE
     need = lib.fb_proxy_decide_workspace(C.byref(a))
-    # partials of 8 blocks + the proxies + the negated keys
-    assert need == 8 * 1024 * 128 * 8 + 1024 * 128 * 8 + 1024 * 8
+    # partials of 32 blocks + the proxies + the negated keys
+    assert need == 32 * 1024 * 128 * 8 + 1024 * 128 * 8 + 1024 * 8
     assert lib.fb_proxy_decide(C.byref(a), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
     a.ws, a.ws_bytes = FAKE, need
     for field, bad, want in (("x_stride", 4095, 1), ("n_select", 1025, 1), ("n_select", -1, 1),

@@ -79,13 +79,13 @@ def test_identifier_matches_oracle_bit_for_bit(fb, name, n, d, r, k, dt):
                 assert np.array_equal(cpu(idn.selected)[:k], rec["selected"]), tag
 
 
-def test_identifier_sums_in_blocks_of_512(fb):
-    # 2^53 at c = 0, ones at c = 512 and 513, a factor of ones: the blocked
+def test_identifier_sums_in_blocks_of_128(fb):
+    # 2^53 at c = 0, ones at c = 128 and 129, a factor of ones: the blocked
     # sum is 2^53 + 2 exactly; a single running sum would give 2^53
-    d, r = 1024, 32
+    d, r = 256, 32
     x = np.zeros((1, d), np.float32)
     x[0, 0] = 2.0 ** 53
-    x[0, 512] = x[0, 513] = 1.0
+    x[0, 128] = x[0, 129] = 1.0
     f = np.ones((d, r), np.float32)
     idn = Ident(fb, 1, d, r, 0)
     idn.step(_dev(W.bf16_bits(x), "bf16"), _dev(W.bf16_bits(f), "bf16"), init=True)

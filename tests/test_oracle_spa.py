@@ -61,8 +61,8 @@ def test_proxy_matches_matmul_and_is_exact_on_integers():
     np.testing.assert_array_equal(S.proxy(xi, fi), xi @ fi)
 
 
-def test_proxy_sums_in_blocks_of_512():
-    # x = 2^53 at c = 0 and 1 at c = 512, 513: block 0 sums to 2^53, block 1
+def test_proxy_sums_in_blocks_of_128():
+    # x = 2^53 at c = 0 and 1 at c = 128, 129: block 0 sums to 2^53, block 1
     # to 2, total 2^53 + 2 (exact); one running sum over c would round each
     # +1 away and give 2^53.
     d = 2 * S.PROXY_BLOCK
