@@ -16,7 +16,7 @@ from ._abi import (  # noqa: F401
     FB_REUSE_HEAD_COS, FB_SEL_DENSE, FB_SEL_GATHER, FB_SEL_SPLIT, FB_STEP_SPARSE,
     FB_STEP_TEXT, FB_STEP_VIDEO, LIB_PATH, SYMBOLS, FlashBlockError, dtype_code,
     fb_abi_version, fb_attn_shape, fb_block_attn_merge, fb_block_attn_merge_workspace,
-    fb_kv_append, fb_kv_cache, fb_proxy_args, fb_proxy_decide, fb_proxy_decide_workspace,
+    fb_kv_append, fb_kv_cache, fb_layer_budgets, fb_proxy_args, fb_proxy_decide, fb_proxy_decide_workspace,
     proxy_args, fb_page_meta, fb_page_meta_update, fb_page_sel, fb_page_select,
     fb_page_select_workspace, fb_prefix_attn, fb_prefix_attn_workspace, fb_reuse_args,
     fb_reuse_decide, fb_reuse_decide_workspace, fb_status_string, fb_step, fb_step_args,

@@ -112,6 +112,9 @@ _SIGS = [
       C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     ("fb_proxy_decide_workspace", C.c_size_t, [C.POINTER(fb_proxy_args)]),
     ("fb_proxy_decide", C.c_int, [C.POINTER(fb_proxy_args), C.c_void_p]),
+    ("fb_layer_budgets", C.c_int,
+     [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double,
+      C.c_void_p, C.c_void_p]),
     ("fb_kv_append", C.c_int,
      [C.POINTER(fb_attn_shape), C.POINTER(fb_kv_cache), fb_tensor, fb_tensor, C.c_void_p]),
     ("fb_step_workspace", C.c_size_t, [C.POINTER(fb_step_state)]),
@@ -288,6 +291,16 @@ def proxy_args(x, factor, cache, mask, selected=None, n_select=0, init=False, ke
     a.key, a.proxy = ptr(key), ptr(proxy)
     a.ws, a.ws_bytes = ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
     return a
+
+
+def fb_layer_budgets(n_layers, n_tok, mean_ratio, floor_ratio, mu, s_left, s_right):
+    """Host schedule: (ratios list, counts list) per layer."""
+    ratios = (C.c_double * int(n_layers))()
+    counts = (C.c_int32 * int(n_layers))()
+    _check("fb_layer_budgets", load().fb_layer_budgets(
+        int(n_layers), int(n_tok), float(mean_ratio), float(floor_ratio), float(mu),
+        float(s_left), float(s_right), ratios, counts))
+    return list(ratios), list(counts)
 
 
 def fb_kv_append(shape, cache, k_blk, v_blk, stream=None):

@@ -670,6 +670,38 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
                                   a->mask, stream));
 }
 
+fb_status fb_layer_budgets(int32_t n_layers, int32_t n_tok, double mean_ratio, double floor_ratio,
+                           double mu, double s_left, double s_right, double* ratios,
+                           int32_t* counts) {
+#pragma clang fp contract(off)
+  if (n_layers < 1 || n_tok < 0 || !counts) return FB_ERR_INVALID_ARGUMENT;
+  if (!isfinite(mean_ratio) || !isfinite(floor_ratio) || !isfinite(mu) || !isfinite(s_left) ||
+      !isfinite(s_right))
+    return FB_ERR_INVALID_ARGUMENT;
+  if (!(s_left > 0.0) || !(s_right > 0.0)) return FB_ERR_INVALID_ARGUMENT;
+  if (!(floor_ratio >= 0.0 && floor_ratio <= mean_ratio && mean_ratio <= 1.0))
+    return FB_ERR_INVALID_ARGUMENT;
+  // the same operations, in the same order, as the reference schedule
+  double mg = 0.0;
+  for (int l = 0; l < n_layers; ++l) {
+    const double s = l < mu ? s_left : s_right;
+    const double z = (l - mu) / s;
+    mg = mg + exp(-0.5 * z * z);
+  }
+  mg = mg / n_layers;
+  const double peak = floor_ratio + (mean_ratio - floor_ratio) / mg;
+  for (int l = 0; l < n_layers; ++l) {
+    const double s = l < mu ? s_left : s_right;
+    const double z = (l - mu) / s;
+    const double r = floor_ratio + (peak - floor_ratio) * exp(-0.5 * z * z);
+    if (ratios) ratios[l] = r;
+    double n = floor(r * n_tok + 0.5);
+    n = n < 0.0 ? 0.0 : (n > n_tok ? n_tok : n);
+    counts[l] = static_cast<int32_t>(n);
+  }
+  return FB_OK;
+}
+
 fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* c, fb_tensor k_blk,
                        fb_tensor v_blk, hipStream_t stream) {
   fb_status st = check_shape(shape);

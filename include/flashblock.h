@@ -305,6 +305,23 @@ size_t fb_proxy_decide_workspace(const fb_proxy_args* args);
 fb_status fb_proxy_decide(const fb_proxy_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * fb_layer_budgets -- per-layer update budgets over depth (SPA-Cache,       *
+ * methodology s2 "adaptive budget allocation": middle layers drift most,   *
+ * so they recompute more tokens; first and last layers cache more).        *
+ * HOST function (no device work, no stream).                                *
+ *   g(l) = exp(-(l - mu)^2 / (2 s^2)), s = s_left for l < mu, s_right     *
+ *   otherwise; ratio(l) = floor + (peak - floor) g(l) with peak chosen so  *
+ *   that the mean ratio over the n_layers layers is mean_ratio;            *
+ *   counts[l] = floor(ratio(l) n_tok + 1/2), clamped to [0, n_tok].         *
+ * ratios (host [n_layers], nullable), counts (host [n_layers]).             *
+ * Errors: INVALID_ARGUMENT for n_layers < 1, n_tok < 0, s_left or s_right  *
+ *   <= 0, a non-finite value, or not 0 <= floor <= mean_ratio <= 1.        *
+ * ------------------------------------------------------------------------ */
+fb_status fb_layer_budgets(int32_t n_layers, int32_t n_tok, double mean_ratio,
+                           double floor_ratio, double mu, double s_left,
+                           double s_right, double* ratios, int32_t* counts);
+
+/* ------------------------------------------------------------------------ *
  * Growing prefix cache (FlashBlock s1 problem statement: block-wise         *
  * decoding attends over a KV cache that grows as blocks finish).            *
  *                                                                           *

@@ -20,7 +20,8 @@ of the papers):
   diffusivi" (SPA-Cache), technical summary (gist.science/it/paper/2602.02544):
   methodology s1 identification by singular proxies (truncated SVD of the
   value projection, cosine against the cached proxy, lowest similarity
-  recomputed).
+  recomputed), s2 adaptive budget allocation (per-layer update ratio, a
+  piecewise Gaussian over depth).
 * [LoSA] "LoSA: Locality Aware Sparse Attention for Block-Wise Diffusion
   Language Models" (gist.science/it/paper/2604.12056): s1 KV inflation;
   s2 methodology -- token classification by query MSE, reuse for stable
@@ -40,6 +41,7 @@ Modules:
   and values join the prefix cache before the next block.
 * ``spa``        -- the singular-proxy identifier: rank-r proxies of the value
   states, their cosine against the cached proxies, the least similar tokens.
+* ``budget``     -- per-layer update budgets over depth (piecewise Gaussian).
 
 All arithmetic is float64 on the exact upcast of the bf16 (or fp32) input
 bits. Every function is pinned by the ``-m "not gpu"`` tests against closed
@@ -47,4 +49,4 @@ forms, invariants, library routines or brute force on tiny inputs; none is
 "parity unpinned".
 """
 
-from . import attention, controller, growing, quest, spa  # noqa: F401
+from . import attention, budget, controller, growing, quest, spa  # noqa: F401

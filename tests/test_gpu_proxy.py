@@ -122,3 +122,24 @@ def test_identifier_full_size_bit_exact(fb):
         assert np.array_equal(cpu(idn.cache), rec["cache"]), s
     assert np.array_equal(cpu(idn.key), recs[1]["key"])
     assert np.array_equal(cpu(idn.selected), recs[1]["selected"])
+
+
+def test_layer_stack_with_depth_budgets(fb):
+    """A stack of layers, each with its own value-projection factor and
+    hidden-state walk, recomputing the per-layer counts of fb_layer_budgets:
+    every layer's selection and cache bit for bit."""
+    from oracle import budget as OB
+    n_layers, n, d, r = 4, 96, 640, 32
+    ratios, counts = fb.fb_layer_budgets(n_layers, n, 0.16, 0.04, 1.5, 1.0, 0.75)
+    assert counts == OB.layer_counts(n, OB.layer_ratios(n_layers, 0.16, 0.04, 1.5, 1.0, 0.75)).tolist()
+    for layer in range(n_layers):
+        cfg = W.SPA.with_(n_tok=n, d_model=d, rank=r, n_steps=3)
+        f = W.spa_factor(cfg, variant=layer)
+        steps = W.spa_steps(cfg, variant=layer)
+        recs = OS.spa_run([W.values(x, "bf16") for x in steps], W.values(f, "bf16"), counts[layer])
+        idn = Ident(fb, n, d, r, counts[layer])
+        f_d = _dev(f, "bf16")
+        for s, (x, rec) in enumerate(zip(steps, recs)):
+            idn.step(_dev(x, "bf16"), f_d, init=(s == 0))
+            assert np.array_equal(cpu(idn.cache), rec["cache"]), (layer, s)
+            assert np.array_equal(cpu(idn.mask).astype(bool), rec["mask"]), (layer, s)
