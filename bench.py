@@ -89,7 +89,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
-    ap.add_argument("--only", choices=("video", "sparse", "growing", "losa", "spa"),
+    ap.add_argument("--only", choices=("video", "sparse", "growing", "losa", "spa", "stack"),
                     help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the prefix pass over 128k-800k contexts and B in {8, 16}")
@@ -119,7 +119,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.only:
         fn = {"video": video_extra, "sparse": sparse_extra, "growing": growing_extra,
-              "losa": losa_extra, "spa": spa_extra}[args.only]
+              "losa": losa_extra, "spa": spa_extra, "stack": stack_extra}[args.only]
         print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream(), args.kv_layout)}),
               flush=True)
         return
@@ -279,6 +279,7 @@ def main():
         extra["growing"] = growing_extra(fb, W, dev, stream, args.kv_layout)
         extra["losa"] = losa_extra(fb, W, dev, stream, args.kv_layout)
         extra["spa"] = spa_extra(fb, W, dev, stream, args.kv_layout)
+        extra["stack"] = stack_extra(fb, W, dev, stream, args.kv_layout)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
@@ -621,6 +622,53 @@ def spa_extra(fb, W, dev, stream, layout):
     out["proxy_TFLOP_s_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6) / 1e12, 2)
     out["frac_of_fp64_vector_peak_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6)
                                                        / 1e12 / 78.6, 4)
+    return out
+
+
+def stack_extra(fb, W, dev, stream, layout):
+    """A 32-layer stack (1024 tokens of width 4096, rank-128 factor per
+    layer): one denoising step identifies the tokens to recompute in every
+    layer, with the depth schedule of per-layer counts (mean ratio 16%,
+    floor 4%, peak at the middle layers) against a uniform 25%."""
+    import torch
+    del layout
+    n_layers = 32
+    cfg = W.SPA.with_(n_steps=2)
+    n, d, r = cfg.n_tok, cfg.d_model, cfg.rank
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    layers = []
+    for l in range(n_layers):
+        xs = [bf(x) for x in W.spa_steps(cfg, variant=l)]
+        layers.append((bf(W.spa_factor(cfg, variant=l)), xs,
+                       torch.empty(n, r, device=dev, dtype=torch.float64)))
+    mask = torch.empty(n, device=dev, dtype=torch.uint8)
+    sel = torch.empty(n, device=dev, dtype=torch.int32)
+    ws = None
+    _, adaptive = fb.fb_layer_budgets(n_layers, n, 0.16, 0.04, (n_layers - 1) / 2.0,
+                                      n_layers / 5.0, n_layers / 8.0)
+    uniform = [int(np.floor(0.25 * n + 0.5))] * n_layers
+    out = {"workload": "%d layers x singular-proxy identification (%d tokens x %d, rank %d)"
+                       % (n_layers, n, d, r),
+           "counts_adaptive": adaptive, "tokens_recomputed_adaptive": int(sum(adaptive)),
+           "tokens_recomputed_uniform_25pct": int(sum(uniform))}
+    for name, counts in (("adaptive", adaptive), ("uniform_25pct", uniform)):
+        args = []
+        for (f, xs, cache), k in zip(layers, counts):
+            a0 = fb.proxy_args(xs[0], f, cache, mask, sel, k, init=True)
+            if ws is None:
+                ws = torch.empty(max(fb.fb_proxy_decide_workspace(a0), 16), dtype=torch.uint8,
+                                 device=dev)
+            a0.ws, a0.ws_bytes = ws.data_ptr(), ws.numel()
+            fb.fb_proxy_decide(a0, stream)
+            args.append(fb.proxy_args(xs[1], f, cache, mask, sel, k, init=False, ws=ws))
+
+        def step():
+            for a in args:
+                fb.fb_proxy_decide(a, stream)
+        ms = _timed(step, stream, 5)
+        out["ms_step_%s" % name] = round(ms, 3)
     return out
 
 
