@@ -563,14 +563,20 @@ def losa_extra(fb, W, dev, stream, layout):
         ws_h = torch.empty(max(fb.fb_page_select_workspace(per_head, B, P), 16), dtype=torch.uint8,
                            device=dev)
         u_act, u_all, u_head, n_act = [], [], [], []
+        pages_all = torch.empty(B, G, k, device=dev, dtype=torch.int32)
+        ws_g = torch.empty(max(fb.fb_page_select_workspace(shape, B, P), 16), dtype=torch.uint8,
+                           device=dev)
         losa.new_block()
         for i, (q, kb, vb) in enumerate(steps):
             losa.step(q, kb, vb, af, lf)
             if i == 0:
                 continue
+            # every token's selection (LoSA selects for the active ones only)
+            fb.fb_page_select(shape, q, losa.kmin, losa.kmax, P, k, pages_all, ws=ws_g,
+                              stream=stream)
             fb.fb_page_select(per_head, q, kmin_h, kmax_h, P, k, pages_h, ws=ws_h, stream=stream)
             torch.cuda.synchronize()
-            pg, on, ph = losa.pages.cpu().numpy(), losa.active.cpu().numpy().astype(bool), pages_h.cpu().numpy()
+            pg, on, ph = pages_all.cpu().numpy(), losa.active.cpu().numpy().astype(bool), pages_h.cpu().numpy()
             grp = H // G
             u_act.append(np.mean([np.unique(pg[on, g]).size for g in range(G)]))
             u_all.append(np.mean([np.unique(pg[:, g]).size for g in range(G)]))

@@ -109,7 +109,7 @@ _SIGS = [
     ("fb_page_select_workspace", C.c_size_t, [C.POINTER(fb_attn_shape), C.c_int64, C.c_int64]),
     ("fb_page_select", C.c_int,
      [C.POINTER(fb_attn_shape), fb_tensor, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
-      C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+      C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     ("fb_proxy_decide_workspace", C.c_size_t, [C.POINTER(fb_proxy_args)]),
     ("fb_proxy_decide", C.c_int, [C.POINTER(fb_proxy_args), C.c_void_p]),
     ("fb_layer_budgets", C.c_int,
@@ -260,11 +260,11 @@ def fb_page_meta_update(shape, k, page_size, n_tok_old, page_cap, kmin, kmax, st
 
 
 def fb_page_select(shape, q, kmin, kmax, n_pages, k_pages, pages, bound=None, ws=None,
-                   stream=None, page_cap=0):
+                   stream=None, page_cap=0, active=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = load().fb_page_select(C.byref(shape), tensor_of(q), ptr(kmin), ptr(kmax),
-                               int(n_pages), int(page_cap), int(k_pages), ptr(pages), ptr(bound),
-                               ptr(ws), ws_bytes, stream_of(stream))
+                               int(n_pages), int(page_cap), int(k_pages), ptr(active), ptr(pages),
+                               ptr(bound), ptr(ws), ws_bytes, stream_of(stream))
     _check("fb_page_select", st)
 
 

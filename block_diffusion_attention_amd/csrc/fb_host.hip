@@ -594,8 +594,8 @@ size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t
 
 fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* kmin,
                          const void* kmax, int64_t n_pages, int64_t page_cap, int32_t k_pages,
-                         int32_t* pages, double* bound, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         const uint8_t* active, int32_t* pages, double* bound, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   if (q.n_tok < 1 || q.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
@@ -619,8 +619,8 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
   }
   return dev(launch_page_select(q.ptr, q.stride_tok, q.stride_head, kmin, kmax,
                                 static_cast<int>(q.n_tok), shape->n_q_heads, shape->n_kv_heads,
-                                shape->head_dim, n_pages, page_cap, k_pages, shape->dtype, bound,
-                                pages, stream));
+                                shape->head_dim, n_pages, page_cap, k_pages, shape->dtype, active,
+                                bound, pages, stream));
 }
 
 size_t fb_proxy_decide_workspace(const fb_proxy_args* a) {
@@ -664,7 +664,7 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
                              neg_key, a->mask, stream));
   if (rc != FB_OK || a->init) return rc;
   // the lowest keys are the largest negated keys (ties: lower id)
-  rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, a->selected, stream));
+  rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, nullptr, a->selected, stream));
   if (rc != FB_OK) return rc;
   return dev(launch_proxy_scatter(a->selected, a->n_select, a->n_tok, proxy, a->rank, a->cache,
                                   a->mask, stream));
@@ -886,7 +886,7 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
                               stream);
         } else {
           rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
-                              st->pages, nullptr, st->ws, st->ws_bytes, stream);
+                              nullptr, st->pages, nullptr, st->ws, st->ws_bytes, stream);
           if (rc != FB_OK) return rc;
           sel.mode = FB_SEL_SPLIT;
           rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
@@ -898,9 +898,9 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       } else if (a->decision != 1) {
         rc = token_step(a->decision == 0 ? 0 : 1, 1);
         if (rc != FB_OK) return rc;
-        if (reselect) {                            // the current queries choose the pages
+        if (reselect) {                            // the active tokens' queries choose pages
           rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
-                              st->pages, nullptr, st->ws, st->ws_bytes, stream);
+                              st->active, st->pages, nullptr, st->ws, st->ws_bytes, stream);
           if (rc != FB_OK) return rc;
         }
         sel.mode = FB_SEL_GATHER;

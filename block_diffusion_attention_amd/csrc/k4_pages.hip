@@ -64,7 +64,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_st, int64_t q_sh,
                                                          const T* kmin, const T* kmax, int n_q,
                                                          int hq, int hkv, int d, int64_t n_pages,
-                                                         int64_t page_cap, double* bound) {
+                                                         int64_t page_cap, const uint8_t* active,
+                                                         double* bound) {
 #pragma clang fp contract(off)
   extern __shared__ float sm[];
   const int G = hq / hkv;
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
   __syncthreads();
   for (int e = threadIdx.x; e < np * n_q; e += blockDim.x) {
     const int pi = e % np, t = e / np;
+    if (active && !active[t]) continue;
     double best = -__builtin_huge_val();
     for (int j = 0; j < G; ++j) {
       const float* qr = qs + (t * G + j) * d;
@@ -108,27 +110,43 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
 
 // Same bound, with the G query heads of the group as G independent chains
 // (the sum of each head still runs sequentially over d, so every bit equals
-// the one-head-at-a-time kernel's).
-// Workgroup = (32 pages, KV group g, TC tokens).
+// the one-head-at-a-time kernel's). Each term is one select and one fused
+// multiply-add: max(q a, q b) with a <= b is q b for q >= 0 and q a
+// otherwise, and the product of two bf16 (or fp32) values is exact in
+// float64, so acc + that product rounds once either way.
+// Workgroup = (32 pages, KV group g, TC tokens); with an active mask only
+// the workgroup's active tokens are staged and scored, packed onto the
+// first threads.
 template <typename T, int G, int TC>
 __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q_st, int64_t q_sh,
                                                            const T* kmin, const T* kmax, int n_q,
                                                            int hkv, int d, int64_t n_pages,
-                                                           int64_t page_cap, double* bound) {
-#pragma clang fp contract(off)
+                                                           int64_t page_cap, const uint8_t* active,
+                                                           double* bound) {
   extern __shared__ float sm[];
+  __shared__ int tok[TC];
+  __shared__ int n_tok_s;
   const int g = blockIdx.y;
   const int t0 = blockIdx.z * TC;
-  const int nt = n_q - t0 < TC ? n_q - t0 : TC;
+  const int nt_all = n_q - t0 < TC ? n_q - t0 : TC;
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPagesPerBlock;
   const int np = n_pages - p0 < kPagesPerBlock ? static_cast<int>(n_pages - p0) : kPagesPerBlock;
   const int ds = d + 1;
   float* qs = sm;                                    // [TC][d][G] (heads innermost)
   float* mn = qs + TC * G * d;                       // [kPagesPerBlock][d + 1]
   float* mx = mn + kPagesPerBlock * ds;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int t = 0; t < nt_all; ++t)
+      if (!active || active[t0 + t]) tok[n++] = t0 + t;
+    n_tok_s = n;
+  }
+  __syncthreads();
+  const int nt = n_tok_s;
+  if (nt == 0) return;
   for (int e = threadIdx.x; e < nt * G * d; e += blockDim.x) {
     const int t = e / (G * d), c = (e / G) % d, j = e % G;
-    qs[e] = ldf<T>(q + (t0 + t) * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
+    qs[e] = ldf<T>(q + static_cast<int64_t>(tok[t]) * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
   }
   for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
     const int64_t o = (static_cast<int64_t>(g) * page_cap + p0) * d + e;
@@ -150,15 +168,13 @@ __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const double qv = qr[c * G + j];
-        const double lo = qv * a;
-        const double hi = qv * b;
-        acc[j] = acc[j] + (lo > hi ? lo : hi);
+        acc[j] = __builtin_fma(qv, qv >= 0.0 ? b : a, acc[j]);
       }
     }
     double best = acc[0];
 #pragma unroll
     for (int j = 1; j < G; ++j) best = acc[j] > best ? acc[j] : best;
-    bound[(static_cast<int64_t>(t0 + t) * hkv + g) * n_pages + p0 + pi] = best;
+    bound[(static_cast<int64_t>(tok[t]) * hkv + g) * n_pages + p0 + pi] = best;
   }
 }
 
@@ -183,9 +199,11 @@ __device__ int block_sum(int v, int* red) {
 
 // One workgroup per (token, KV head): exact top-k of bound[t][g][:].
 __global__ __launch_bounds__(256) void page_topk_kernel(const double* bound, int hkv,
-                                                        int64_t n_pages, int k, int32_t* pages) {
+                                                        int64_t n_pages, int k,
+                                                        const uint8_t* active, int32_t* pages) {
   __shared__ int red[256];
   __shared__ int scan[256];
+  if (active && !active[blockIdx.x]) return;       // a row of an inactive token
   const int tid = threadIdx.x;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * hkv + blockIdx.y;
   const double* b = bound + row * n_pages;
@@ -282,11 +300,13 @@ __device__ __forceinline__ int block_inscan4(int v, int* red) {
 
 template <int KPT>
 __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound, int hkv,
-                                                            int64_t n_pages, int k, int32_t* pages) {
+                                                            int64_t n_pages, int k,
+                                                            const uint8_t* active, int32_t* pages) {
   __shared__ int hist[256];
   __shared__ int red[4];
   __shared__ unsigned long long sh_prefix;
   __shared__ int sh_kk;
+  if (active && !active[blockIdx.x]) return;       // a row of an inactive token
   const int tid = threadIdx.x;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * hkv + blockIdx.y;
   const double* b = bound + row * n_pages;
@@ -364,8 +384,8 @@ hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t
 
 hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const void* kmin,
                               const void* kmax, int n_q, int hq, int hkv, int d, int64_t n_pages,
-                              int64_t page_cap, int k_pages, fb_dtype dt, double* bound,
-                              int32_t* pages, hipStream_t s) {
+                              int64_t page_cap, int k_pages, fb_dtype dt, const uint8_t* active,
+                              double* bound, int32_t* pages, hipStream_t s) {
   if (n_pages == 0) return hipSuccess;
   const int G = hq / hkv;
   const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * (d + 1)) * sizeof(float);
@@ -376,7 +396,7 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                      dim3(grid.x, grid.y, (n_q + 8 / ((GG + 3) / 4) - 1) / (8 / ((GG + 3) / 4))), \
                      dim3(256), (8 / ((GG + 3) / 4) * GG * d + 2 * kPagesPerBlock * (d + 1)) * 4, s, \
                      static_cast<const TT*>(q), q_st, q_sh, static_cast<const TT*>(kmin),       \
-                     static_cast<const TT*>(kmax), n_q, hkv, d, n_pages, page_cap, bound)
+                     static_cast<const TT*>(kmax), n_q, hkv, d, n_pages, page_cap, active, bound)
   if (dt == FB_BF16 && G == 4) FB_BOUND_G(uint16_t, 4);
   else if (dt == FB_BF16 && G == 1) FB_BOUND_G(uint16_t, 1);
   else if (dt == FB_BF16 && G == 2) FB_BOUND_G(uint16_t, 2);
@@ -389,28 +409,30 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
     hipLaunchKernelGGL(page_bound_kernel<uint16_t>, grid, dim3(256), smem, s,
                        static_cast<const uint16_t*>(q), q_st, q_sh,
                        static_cast<const uint16_t*>(kmin), static_cast<const uint16_t*>(kmax), n_q,
-                       hq, hkv, d, n_pages, page_cap, bound);
+                       hq, hkv, d, n_pages, page_cap, active, bound);
   else
     hipLaunchKernelGGL(page_bound_kernel<float>, grid, dim3(256), smem, s,
                        static_cast<const float*>(q), q_st, q_sh, static_cast<const float*>(kmin),
-                       static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, page_cap, bound);
+                       static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, page_cap, active,
+                       bound);
 #undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;
-  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, pages, s);
+  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, active, pages, s);
 }
 
 hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
-                            int32_t* out, hipStream_t s) {
+                            const uint8_t* row_active, int32_t* out, hipStream_t s) {
   if (k <= 0 || n_rows <= 0) return hipSuccess;
   if (n <= 256 * 16)
     hipLaunchKernelGGL(page_topk_reg_kernel<16>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
-                       k, out);
+                       k, row_active, out);
   else if (n <= 256 * 32)
     hipLaunchKernelGGL(page_topk_reg_kernel<32>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
-                       k, out);
+                       k, row_active, out);
   else
-    hipLaunchKernelGGL(page_topk_kernel, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n, k, out);
+    hipLaunchKernelGGL(page_topk_kernel, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n, k,
+                       row_active, out);
   return hipGetLastError();
 }
 

@@ -234,9 +234,13 @@ fb_status fb_reuse_decide(const fb_reuse_args* args, hipStream_t stream);
  *   INVALID_ARGUMENT if n_tok_old > k.n_tok or ceil(k.n_tok / ps) > page_cap.*
  * fb_page_select: bound[t, g, p] = max over the query heads h of group g of *
  *   sum_{j = 0..d-1, in order} max(q[t,h,j]*kmin[g,p,j], q[t,h,j]*kmax[g,p,j])*
- *   in float64 without fused multiply-add; pages[t, g, :] = the k_pages     *
+ *   in float64 (each product of two bf16 or two fp32 values is exact, so a  *
+ *   fused multiply-add rounds as a multiply then an add would);             *
+ *   pages[t, g, :] = the k_pages                                            *
  *   pages of largest bound (ties: lower page id first), listed ascending.    *
  *   kmin/kmax hold page_cap pages per KV head (0: n_pages, packed).          *
+ *   active (nullable, device [n_q]): tokens whose byte is 0 are skipped;    *
+ *   their rows of bound and pages are left untouched.                       *
  *   bound may be NULL (then it lives in ws).                                  *
  * ------------------------------------------------------------------------ */
 fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k,
@@ -250,9 +254,9 @@ size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q,
                                 int64_t n_pages);
 fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
                          const void* kmin, const void* kmax, int64_t n_pages,
-                         int64_t page_cap, int32_t k_pages, int32_t* pages,
-                         double* bound, void* ws, size_t ws_bytes,
-                         hipStream_t stream);
+                         int64_t page_cap, int32_t k_pages,
+                         const uint8_t* active, int32_t* pages, double* bound,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * fb_proxy_decide -- singular-proxy identification (SPA-Cache, "Proxy       *
@@ -367,8 +371,9 @@ fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* cache,
  *        SPLIT pass (cache + residual); later steps classify tokens by      *
  *        query MSE and run the GATHER pass for active rows. With            *
  *        sparse_reselect = 1 (LoSA s2 workflow as it stands): step 0 is a    *
- *        dense pass; later steps select pages with the step's queries and   *
- *        run GATHER for active rows with no residual (a_res, l_res unused).  *
+ *        dense pass; later steps select pages with the step's queries for   *
+ *        the active tokens (pages rows of the others are left as they were) *
+ *        and run GATHER for them with no residual (a_res, l_res unused).    *
  *        Blocks with                                                        *
  *        n_q > 1024 or n_q * Hq > 4096 need a contiguous q_blk              *
  *        (UNSUPPORTED otherwise).                                           *

@@ -168,12 +168,12 @@ def test_reuse_decide_rejects(lib):
 def test_page_calls_reject(lib):
     sh = shape()
     assert lib.fb_page_meta(C.byref(sh), ten(100, 8), 0, FAKE, FAKE, None) == 1
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 0, 11, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 0, 11, None, FAKE, FAKE,
                               None, 0, None) == 1
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 0, 3, FAKE, None,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 0, 3, None, FAKE, None,
                               None, 0, None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
     # metadata storage smaller than the page count
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 9, 3, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 10, 9, 3, None, FAKE, FAKE,
                               None, 0, None) == 1
     up = lib.fb_page_meta_update
     assert up(C.byref(sh), ten(100, 8), 16, 0, 6, FAKE, FAKE, None) == 1      # 7 pages > 6
@@ -236,9 +236,9 @@ def test_many_rows_prefix_workspace_covers_masked_split(lib):
 
 def test_page_select_rejects_counts_beyond_int32(lib):
     sh = shape()
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 1 << 31, 0, 3, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, 1 << 31, 0, 3, None, FAKE, FAKE,
                               None, 0, None) == 1
-    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, -1, 0, 0, FAKE, FAKE,
+    assert lib.fb_page_select(C.byref(sh), ten(8, 32), FAKE, FAKE, -1, 0, 0, None, FAKE, FAKE,
                               None, 0, None) == 1
 
 

@@ -95,9 +95,10 @@ def test_losa_block_matches_oracle(fb, name, n_prefix, density, m_override):
                   dev_tensor(st["v"], "bf16"), a, l)
         torch.cuda.synchronize()
         tag = "%s step %d" % (name, s)
-        assert np.array_equal(cpu(step.active).astype(bool), rec["active"]), tag
-        if s > 0:
-            assert np.array_equal(cpu(step.pages), rec["sel"]), tag
+        act = rec["active"]
+        assert np.array_equal(cpu(step.active).astype(bool), act), tag
+        if s > 0:                                # pages are chosen for active tokens only
+            assert np.array_equal(cpu(step.pages)[act], rec["sel"][act]), tag
         check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 2e-3)
         check_l(tag + " L_out", cpu(step.l_out), rec["l_out"], 1e-3)
         check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)
@@ -131,3 +132,30 @@ def test_selection_per_query_head_bit_exact(fb):
     assert np.array_equal(got, ref)
     act = np.array([1, 0, 1, 1, 0, 1, 0, 0], dtype=bool)
     assert np.array_equal(OQ.union_size_heads(got, act, 8), OQ.union_size_heads(ref, act, 8))
+
+
+def test_selection_of_active_tokens_only(fb):
+    """fb_page_select with an active mask scores and selects the active
+    tokens' rows (bit for bit) and leaves the other rows untouched."""
+    cfg = W.SPARSE.with_(n_prefix=5003, n_steps=2)
+    kp, _ = W.prefix_kv(cfg, variant=9)
+    q = W.sparse_steps(cfg, variant=9)[1]["q"]
+    page, k = 16, 60
+    n_pages = -(-5003 // page)
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    kmin = torch.empty(8, n_pages, 128, device="cuda", dtype=torch.bfloat16)
+    kmax = torch.empty_like(kmin)
+    fb.fb_page_meta(shape, dev_tensor(kp, "bf16"), page, kmin, kmax)
+    act = np.array([0, 1, 1, 0, 0, 1, 0, 1], dtype=bool)
+    act_d = torch.from_numpy(act.astype(np.uint8)).cuda()
+    pages = torch.full((8, 8, k), -7, device="cuda", dtype=torch.int32)
+    bound = torch.full((8, 8, n_pages), 5.0, device="cuda", dtype=torch.float64)
+    fb.fb_page_select(shape, dev_tensor(q, "bf16"), kmin, kmax, n_pages, k, pages, bound=bound,
+                      active=act_d)
+    torch.cuda.synchronize()
+    rmin, rmax = OQ.page_meta(vals(kp, "bf16"), page)
+    rb = OQ.page_bound(vals(q, "bf16"), rmin, rmax)
+    got_b, got_p = cpu(bound), cpu(pages)
+    assert np.array_equal(got_b[act], rb[act])
+    assert np.array_equal(got_p[act], OQ.topk_pages(rb, k)[act])
+    assert (got_b[~act] == 5.0).all() and (got_p[~act] == -7).all()
