@@ -220,3 +220,48 @@ def test_count_since_refresh_hand_fixture(fb):
             assert int(m.item()) == g[mode]["m_count"][s], (mode, s)
             want = 1 if g[mode]["decision"][s] == "reuse" else 0
             assert (cpu(mask) == want).all(), (mode, s)
+
+
+def test_since_refresh_with_forced_decisions(fb):
+    """Forced reuse keeps the ids of the last recompute; forced recompute
+    takes the step's ids: M counted since the refresh follows both."""
+    cfg = W.LONG.with_(n_prefix=2000, n_block=16, n_steps=6, tau=3)
+    steps = W.text_steps(cfg, variant=2, m_override=[None, 2, 1, 1, 4, 1])
+    kp, vp = W.prefix_kv(cfg, variant=2)
+    force = [None, OC.REUSE, OC.RECOMPUTE, OC.REUSE, None, None]
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    step = fb.Step(fb.FB_STEP_TEXT, shape, 16, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
+                   tau=cfg.tau, since_refresh=True)
+    recs = OC.text_block(_step_inputs(cfg, steps), vals(kp, "bf16"), vals(vp, "bf16"), cfg.scale,
+                         cfg.tau, with_dense=False, force=force, since_refresh=True)
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        a = torch.empty(16, 32, 128, device="cuda")
+        l = torch.empty(16, 32, device="cuda")
+        dec = -1 if force[s] is None else (1 if force[s] == OC.REUSE else 0)
+        step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                  dev_tensor(st["v"], "bf16"), a, l, ids=torch.from_numpy(st["ids"]).cuda(),
+                  decision=dec)
+        torch.cuda.synchronize()
+        if s > 0:
+            assert int(step.m_count.item()) == rec["m_count"], s
+        assert np.all(cpu(step.mask) == (1 if rec["decision"] == OC.REUSE else 0)), s
+        check_a("forced since-refresh step %d" % s, cpu(a), rec["a_full"], 2e-3)
+
+
+def test_append_fills_the_cache_exactly(fb):
+    cfg = W.LONG
+    k_all, v_all = W.prefix_kv(cfg, n_tok=48, variant=5)
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    for layout in ("head", "token"):
+        cache = fb.KVCache(48, 8, 128, torch.bfloat16, "cuda", layout)
+        cache.append(shape, dev_tensor(k_all[:32], "bf16"), dev_tensor(v_all[:32], "bf16"))
+        # a head-major block as the source
+        cache.append(shape, dev_tensor(k_all[32:], "bf16", "head"),
+                     dev_tensor(v_all[32:], "bf16", "head"))
+        torch.cuda.synchronize()
+        assert cache.n_tok == 48
+        assert np.array_equal(_bits(cache.k_prefix), _bits(dev_tensor(k_all, "bf16")))
+        assert np.array_equal(_bits(cache.v_prefix), _bits(dev_tensor(v_all, "bf16")))
+        blk = dev_tensor(k_all[:1], "bf16")
+        with pytest.raises(fb.FlashBlockError):
+            cache.append(shape, blk, blk)
