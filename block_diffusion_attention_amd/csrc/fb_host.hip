@@ -602,7 +602,8 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
   if ((st = check_tensor(q, -1, shape->n_q_heads, shape->head_dim)) != FB_OK) return st;
   if (n_pages < 0 || n_pages > INT32_MAX || k_pages < 0 || k_pages > n_pages)
     return FB_ERR_INVALID_ARGUMENT;
-  if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
+  if (n_pages > 0 && (!kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)))
+    return FB_ERR_INVALID_ARGUMENT;
   if (k_pages > 0 && !pages) return FB_ERR_INVALID_ARGUMENT;
   if (page_cap == 0) page_cap = n_pages;
   if (page_cap < n_pages) return FB_ERR_INVALID_ARGUMENT;

@@ -56,6 +56,16 @@ __global__ __launch_bounds__(128) void page_meta_kernel(const T* k, int64_t kv_s
   kmax[o] = stf<T>(mx);
 }
 
+// Element e of a 16-byte group of bf16 (8) or fp32 (4) values, as float.
+template <typename T> __device__ __forceinline__ float grp_float(u32x4v w, int e);
+template <> __device__ __forceinline__ float grp_float<uint16_t>(u32x4v w, int e) {
+  const uint32_t x = w[e >> 1];
+  return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+template <> __device__ __forceinline__ float grp_float<float>(u32x4v w, int e) {
+  return __uint_as_float(w[e]);
+}
+
 // bound[t][g][p]: one thread per (page, token). The group's query rows and the
 // page block's metadata sit in LDS as float (exact copies of the inputs).
 constexpr int kPagesPerBlock = 32;
@@ -144,15 +154,28 @@ __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q
   __syncthreads();
   const int nt = n_tok_s;
   if (nt == 0) return;
-  for (int e = threadIdx.x; e < nt * G * d; e += blockDim.x) {
-    const int t = e / (G * d), c = (e / G) % d, j = e % G;
-    qs[e] = ldf<T>(q + static_cast<int64_t>(tok[t]) * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
+  // staging with 16-byte loads (rows of d elements, 16-byte aligned: the
+  // host checks the bases, strides are multiples of 8 elements)
+  constexpr int NE = 16 / sizeof(T);
+  const int gpr = d / NE;                            // 16-byte groups per row
+  for (int v = threadIdx.x; v < nt * G * gpr; v += blockDim.x) {
+    const int row = v / gpr, cg = (v % gpr) * NE;
+    const int t = row / G, j = row % G;
+    const u32x4v w = *reinterpret_cast<const u32x4v*>(
+        q + static_cast<int64_t>(tok[t]) * q_st + static_cast<int64_t>(g * G + j) * q_sh + cg);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) qs[(t * d + cg + e) * G + j] = grp_float<T>(w, e);
   }
-  for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
-    const int64_t o = (static_cast<int64_t>(g) * page_cap + p0) * d + e;
-    const int ls = (e / d) * ds + e % d;
-    mn[ls] = ldf<T>(kmin + o);
-    mx[ls] = ldf<T>(kmax + o);
+  for (int v = threadIdx.x; v < np * gpr; v += blockDim.x) {
+    const int pi = v / gpr, cg = (v % gpr) * NE;
+    const int64_t o = (static_cast<int64_t>(g) * page_cap + p0 + pi) * d + cg;
+    const u32x4v a = *reinterpret_cast<const u32x4v*>(kmin + o);
+    const u32x4v b = *reinterpret_cast<const u32x4v*>(kmax + o);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      mn[pi * ds + cg + e] = grp_float<T>(a, e);
+      mx[pi * ds + cg + e] = grp_float<T>(b, e);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < np * nt; e += blockDim.x) {

@@ -238,7 +238,8 @@ fb_status fb_reuse_decide(const fb_reuse_args* args, hipStream_t stream);
  *   fused multiply-add rounds as a multiply then an add would);             *
  *   pages[t, g, :] = the k_pages                                            *
  *   pages of largest bound (ties: lower page id first), listed ascending.    *
- *   kmin/kmax hold page_cap pages per KV head (0: n_pages, packed).          *
+ *   kmin/kmax (16-byte aligned) hold page_cap pages per KV head (0:         *
+ *   n_pages, packed).                                                       *
  *   active (nullable, device [n_q]): tokens whose byte is 0 are skipped;    *
  *   their rows of bound and pages are left untouched.                       *
  *   bound may be NULL (then it lives in ws).                                  *
