@@ -38,16 +38,26 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_pass_traffic.json")
+# What sets the prefix pass's traffic: its kernels, and in the host layer the
+# split-K planning and launch code (from the planning constants to the
+# argument validation that follows the launch function).
 KERNEL_SOURCES = ("block_diffusion_attention_amd/csrc/k1_prefix.hip",
-                  "block_diffusion_attention_amd/csrc/fb_host.hip")
+                  "block_diffusion_attention_amd/csrc/fb_host.hip"
+                  "#// Split-K planning..fb_status validate_prefix(")
 
 
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        path, _, region = rel.partition("#")
+        with open(os.path.join(ROOT, path), "rb") as f:
+            text = f.read()
+        if region:
+            begin, end = (x.encode() for x in region.split(".."))
+            i = text.index(begin)
+            text = text[i:text.index(end, i)]
+        h.update(text)
     return h.hexdigest()
 
 
