@@ -340,9 +340,38 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
   for (int i = 0; i < KPT; ++i) key[i] = p0 + i < n_pages ? okey(b[p0 + i]) : 0ull;
   // (okey of any bound is > 0; padding 0 is never in T's group, see below)
 
-  uint64_t prefix = 0, pmask = 0;
+  // Leading bytes every key shares (from the keys' min and max) need no
+  // histogram: they are T's bytes, and the group stays all keys.
+  __shared__ unsigned long long sh_lo[4], sh_hi[4];
+  uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (p0 + i < n_pages) {
+      lo = key[i] < lo ? key[i] : lo;
+      hi = key[i] > hi ? key[i] : hi;
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t l2 = __shfl_xor(lo, o, 64), h2 = __shfl_xor(hi, o, 64);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
+  }
+  if ((tid & 63) == 0) {
+    sh_lo[tid >> 6] = lo;
+    sh_hi[tid >> 6] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lo = sh_lo[w] < lo ? sh_lo[w] : lo;
+    hi = sh_hi[w] > hi ? sh_hi[w] : hi;
+  }
+  const uint64_t diff = lo ^ hi;
+  const int first = diff ? __clzll(diff) / 8 : 8;  // leading bytes in common
+  uint64_t pmask = first == 0 ? 0ull : (first == 8 ? ~0ull : ~0ull << (64 - 8 * first));
+  uint64_t prefix = lo & pmask;
   int kk = k;                                      // rank of T within the current group
-  for (int pass = 0; pass < 8; ++pass) {
+  for (int pass = first; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
     hist[tid] = 0;
     __syncthreads();
