@@ -561,7 +561,8 @@ fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k, int32_t page_siz
   if (st != FB_OK) return st;
   if ((st = check_tensor(k, -1, shape->n_kv_heads, shape->head_dim)) != FB_OK) return st;
   if (page_size < 1) return FB_ERR_INVALID_ARGUMENT;
-  if (k.n_tok > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
+  if (k.n_tok > 0 && (!kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)))
+    return FB_ERR_INVALID_ARGUMENT;
   const int64_t n_pages = (k.n_tok + page_size - 1) / page_size;
   if (n_pages > INT32_MAX) return FB_ERR_UNSUPPORTED;
   return dev(launch_page_meta(k.ptr, k.stride_tok, k.stride_head, k.n_tok, shape->n_kv_heads,
@@ -579,7 +580,8 @@ fb_status fb_page_meta_update(const fb_attn_shape* shape, fb_tensor k, int32_t p
   const int64_t n_pages = (k.n_tok + page_size - 1) / page_size;
   if (page_cap < n_pages) return FB_ERR_INVALID_ARGUMENT;
   if (n_pages > INT32_MAX) return FB_ERR_UNSUPPORTED;
-  if (n_pages > 0 && (!kmin || !kmax)) return FB_ERR_INVALID_ARGUMENT;
+  if (n_pages > 0 && (!kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)))
+    return FB_ERR_INVALID_ARGUMENT;
   // pages wholly below n_tok_old keep their metadata; the old partial page
   // and every new page are recomputed
   return dev(launch_page_meta(k.ptr, k.stride_tok, k.stride_head, k.n_tok, shape->n_kv_heads,

@@ -32,30 +32,6 @@ template <> __device__ __forceinline__ uint16_t stf<uint16_t>(float x) {
   return static_cast<uint16_t>(__float_as_uint(x) >> 16);   // exact: x is a bf16 value
 }
 
-// kmin/kmax[g][p][c] over the tokens of page p (the last page may be short),
-// for pages p0 .. p0 + gridDim.x - 1; page_cap pages per KV head in storage.
-template <typename T>
-__global__ __launch_bounds__(128) void page_meta_kernel(const T* k, int64_t kv_st, int64_t kv_sh,
-                                                        int64_t n_kv, int d, int page_size,
-                                                        int64_t p0, int64_t page_cap, T* kmin,
-                                                        T* kmax) {
-  const int64_t p = p0 + blockIdx.x;
-  const int g = blockIdx.y;
-  const int c = threadIdx.x;
-  if (c >= d) return;
-  const int64_t lo = p * page_size;
-  const int64_t hi = lo + page_size < n_kv ? lo + page_size : n_kv;
-  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-  for (int64_t t = lo; t < hi; ++t) {
-    const float x = ldf<T>(k + t * kv_st + g * kv_sh + c);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
-  }
-  const int64_t o = (static_cast<int64_t>(g) * page_cap + p) * d + c;
-  kmin[o] = stf<T>(mn);
-  kmax[o] = stf<T>(mx);
-}
-
 // Element e of a 16-byte group of bf16 (8) or fp32 (4) values, as float.
 template <typename T> __device__ __forceinline__ float grp_float(u32x4v w, int e);
 template <> __device__ __forceinline__ float grp_float<uint16_t>(u32x4v w, int e) {
@@ -64,6 +40,57 @@ template <> __device__ __forceinline__ float grp_float<uint16_t>(u32x4v w, int e
 }
 template <> __device__ __forceinline__ float grp_float<float>(u32x4v w, int e) {
   return __uint_as_float(w[e]);
+}
+
+// kmin/kmax[g][p][c] over the tokens of page p (the last page may be short),
+// for pages p0 .. p0 + n_pg - 1; page_cap pages per KV head in storage. One
+// thread per (page, 16-byte group of dims): it walks the page's tokens with
+// 16-byte loads and writes its groups of kmin and kmax with 16-byte stores
+// (the min and max of bf16 or fp32 values are themselves exact values).
+template <typename T>
+__global__ __launch_bounds__(256) void page_meta_kernel(const T* k, int64_t kv_st, int64_t kv_sh,
+                                                        int64_t n_kv, int d, int page_size,
+                                                        int64_t p0, int64_t n_pg, int64_t page_cap,
+                                                        T* kmin, T* kmax) {
+  constexpr int NE = 16 / sizeof(T);
+  const int gpr = d / NE;                          // groups per row
+  const int g = blockIdx.y;
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (v >= n_pg * gpr) return;
+  const int64_t p = p0 + v / gpr;
+  const int cg = static_cast<int>(v % gpr) * NE;
+  const int64_t lo = p * page_size;
+  const int64_t hi = lo + page_size < n_kv ? lo + page_size : n_kv;
+  float mn[NE], mx[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    mn[e] = __builtin_huge_valf();
+    mx[e] = -__builtin_huge_valf();
+  }
+  const T* base = k + static_cast<int64_t>(g) * kv_sh + cg;
+  for (int64_t t = lo; t < hi; ++t) {
+    const u32x4v w = *reinterpret_cast<const u32x4v*>(base + t * kv_st);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const float x = grp_float<T>(w, e);
+      mn[e] = fminf(mn[e], x);
+      mx[e] = fmaxf(mx[e], x);
+    }
+  }
+  u32x4v a, b;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (NE == 8) {                                 // bf16: the high halves of the floats
+      a[c] = (__float_as_uint(mn[2 * c]) >> 16) | (__float_as_uint(mn[2 * c + 1]) & 0xffff0000u);
+      b[c] = (__float_as_uint(mx[2 * c]) >> 16) | (__float_as_uint(mx[2 * c + 1]) & 0xffff0000u);
+    } else {
+      a[c] = __float_as_uint(mn[c]);
+      b[c] = __float_as_uint(mx[c]);
+    }
+  }
+  const int64_t o = (static_cast<int64_t>(g) * page_cap + p) * d + cg;
+  *reinterpret_cast<u32x4v*>(kmin + o) = a;
+  *reinterpret_cast<u32x4v*>(kmax + o) = b;
 }
 
 // bound[t][g][p]: one thread per (page, token). The group's query rows and the
@@ -422,15 +449,17 @@ hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t
                             int d, int page_size, fb_dtype dt, void* kmin, void* kmax,
                             int64_t p_begin, int64_t p_end, int64_t page_cap, hipStream_t s) {
   if (p_end <= p_begin) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(p_end - p_begin), hkv);
+  const int64_t n_pg = p_end - p_begin;
+  const int gpr = d * (dt == FB_BF16 ? 2 : 4) / 16;
+  dim3 grid(static_cast<unsigned>((n_pg * gpr + 255) / 256), hkv);
   if (dt == FB_BF16)
-    hipLaunchKernelGGL(page_meta_kernel<uint16_t>, grid, dim3(128), 0, s,
+    hipLaunchKernelGGL(page_meta_kernel<uint16_t>, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(k), kv_st, kv_sh, n_kv, d, page_size, p_begin,
-                       page_cap, static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax));
+                       n_pg, page_cap, static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax));
   else
-    hipLaunchKernelGGL(page_meta_kernel<float>, grid, dim3(128), 0, s,
+    hipLaunchKernelGGL(page_meta_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(k), kv_st, kv_sh, n_kv, d, page_size, p_begin,
-                       page_cap, static_cast<float*>(kmin), static_cast<float*>(kmax));
+                       n_pg, page_cap, static_cast<float*>(kmin), static_cast<float*>(kmax));
   return hipGetLastError();
 }
 

@@ -221,7 +221,8 @@ fb_status fb_reuse_decide(const fb_reuse_args* args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Page metadata and selection (optional sparse subsystem).                  *
- * fb_page_meta: kmin, kmax [Hkv, P, d] (dtype of k), P = ceil(n_kv / ps):   *
+ * fb_page_meta: kmin, kmax [Hkv, P, d] (dtype of k, 16-byte aligned),      *
+ *   P = ceil(n_kv / ps):                                                    *
  *   elementwise min / max of the page's keys (the last page may be short).  *
  * fb_page_meta_update: the same metadata kept in storage of page_cap pages  *
  *   per KV head ([Hkv, page_cap, d]) for a cache that grows: given storage  *
