@@ -662,12 +662,14 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
   fb_status rc = dev(launch_proxy_partials(a->x, a->x_stride, a->factor, a->dtype, a->n_tok,
                                            a->d_model, a->rank, part, stream));
   if (rc != FB_OK) return rc;
-  if (!a->init && (rc = dev(launch_fill_u8(a->mask, a->n_tok, 0, stream))) != FB_OK) return rc;
   rc = dev(launch_proxy_keys(part, nb, a->n_tok, a->rank, a->init, a->cache, proxy, a->key,
                              neg_key, a->mask, stream));
   if (rc != FB_OK || a->init) return rc;
-  // the lowest keys are the largest negated keys (ties: lower id)
-  rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, nullptr, a->selected, stream));
+  if (a->n_select == 0) return dev(launch_fill_u8(a->mask, a->n_tok, 0, stream));
+  // the lowest keys are the largest negated keys (ties: lower id); the
+  // top-k writes every token's mask byte
+  rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, nullptr, a->selected, a->mask,
+                            stream));
   if (rc != FB_OK) return rc;
   return dev(launch_proxy_scatter(a->selected, a->n_select, a->n_tok, proxy, a->rank, a->cache,
                                   a->mask, stream));

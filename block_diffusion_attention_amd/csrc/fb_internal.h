@@ -212,9 +212,11 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                               hipStream_t s);
 // exact top-k of each row of keys [n_rows * hkv][n] (largest first, ties to
 // the lower index), the chosen indices listed ascending in out [.., k];
-// row_active (nullable, [n_rows]): rows r * hkv + . with byte 0 are skipped
+// row_active (nullable, [n_rows]): rows r * hkv + . with byte 0 are skipped;
+// flags (nullable, [rows][n]): 1 for the chosen indices, 0 for the others
 hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
-                            const uint8_t* row_active, int32_t* out, hipStream_t s);
+                            const uint8_t* row_active, int32_t* out, uint8_t* flags,
+                            hipStream_t s);
 // singular-proxy identification: block partials of the proxies, then the
 // proxies, cache fill (init) or ranking keys (+ negated keys for the top-k)
 bool proxy_rank_ok(int rank);

@@ -250,7 +250,8 @@ __device__ int block_sum(int v, int* red) {
 // One workgroup per (token, KV head): exact top-k of bound[t][g][:].
 __global__ __launch_bounds__(256) void page_topk_kernel(const double* bound, int hkv,
                                                         int64_t n_pages, int k,
-                                                        const uint8_t* active, int32_t* pages) {
+                                                        const uint8_t* active, int32_t* pages,
+                                                        uint8_t* flags) {
   __shared__ int red[256];
   __shared__ int scan[256];
   if (active && !active[blockIdx.x]) return;       // a row of an inactive token
@@ -303,6 +304,7 @@ __global__ __launch_bounds__(256) void page_topk_kernel(const double* bound, int
       __syncthreads();
     }
     if (sel) out[written + scan[tid] - 1] = static_cast<int32_t>(p);
+    if (flags && p < n_pages) flags[row * n_pages + p] = sel ? 1 : 0;
     written += scan[255];
     eq_taken += tile_eq;
     __syncthreads();
@@ -351,7 +353,8 @@ __device__ __forceinline__ int block_inscan4(int v, int* red) {
 template <int KPT>
 __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound, int hkv,
                                                             int64_t n_pages, int k,
-                                                            const uint8_t* active, int32_t* pages) {
+                                                            const uint8_t* active, int32_t* pages,
+                                                            uint8_t* flags) {
   __shared__ int hist[256];
   __shared__ int red[4];
   __shared__ unsigned long long sh_prefix;
@@ -440,6 +443,7 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
     const bool sel = key[i] > T || (is_eq && eq_seen < take_eq);
     eq_seen += is_eq ? 1 : 0;
     if (sel) out[pos++] = static_cast<int32_t>(p0 + i);
+    if (flags && p0 + i < n_pages) flags[row * n_pages + p0 + i] = sel ? 1 : 0;
   }
 }
 
@@ -499,21 +503,22 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
 #undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;
-  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, active, pages, s);
+  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, active, pages, nullptr, s);
 }
 
 hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
-                            const uint8_t* row_active, int32_t* out, hipStream_t s) {
+                            const uint8_t* row_active, int32_t* out, uint8_t* flags,
+                            hipStream_t s) {
   if (k <= 0 || n_rows <= 0) return hipSuccess;
   if (n <= 256 * 16)
     hipLaunchKernelGGL(page_topk_reg_kernel<16>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
-                       k, row_active, out);
+                       k, row_active, out, flags);
   else if (n <= 256 * 32)
     hipLaunchKernelGGL(page_topk_reg_kernel<32>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
-                       k, row_active, out);
+                       k, row_active, out, flags);
   else
     hipLaunchKernelGGL(page_topk_kernel, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n, k,
-                       row_active, out);
+                       row_active, out, flags);
   return hipGetLastError();
 }
 

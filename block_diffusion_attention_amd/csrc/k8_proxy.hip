@@ -243,13 +243,13 @@ __global__ __launch_bounds__(256) void proxy_keys_kernel(const double* part, int
   }
 }
 
-// The selected tokens: mask 1 and the cache takes their current proxies.
+// The selected tokens' cache rows take their current proxies (the top-k
+// wrote the mask).
 __global__ __launch_bounds__(128) void proxy_scatter_kernel(const int32_t* selected, int n_tok,
                                                             const double* proxy, int rank,
                                                             double* cache, uint8_t* mask) {
   const int t = selected[blockIdx.x];
   if (t < 0 || t >= n_tok) return;                 // (the top-k emits ids in range)
-  if (threadIdx.x == 0) mask[t] = 1;
   const int64_t o = static_cast<int64_t>(t) * rank;
   for (int i = threadIdx.x; i < rank; i += 128) cache[o + i] = proxy[o + i];
 }
