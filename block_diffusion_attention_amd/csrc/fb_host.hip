@@ -672,7 +672,7 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
                             stream));
   if (rc != FB_OK) return rc;
   return dev(launch_proxy_scatter(a->selected, a->n_select, a->n_tok, proxy, a->rank, a->cache,
-                                  a->mask, stream));
+                                  stream));
 }
 
 fb_status fb_layer_budgets(int32_t n_layers, int32_t n_tok, double mean_ratio, double floor_ratio,

@@ -227,8 +227,7 @@ hipError_t launch_proxy_keys(const double* part, int n_blocks, int n_tok, int ra
                              double* cache, double* proxy, double* key, double* neg_key,
                              uint8_t* mask, hipStream_t s);
 hipError_t launch_proxy_scatter(const int32_t* selected, int n_select, int n_tok,
-                                const double* proxy, int rank, double* cache, uint8_t* mask,
-                                hipStream_t s);
+                                const double* proxy, int rank, double* cache, hipStream_t s);
 // the finished block's K/V rows into cache tokens [tok0, tok0 + n_blk); byte
 // strides; rows are (d * elem_bytes) bytes, a multiple of 16
 hipError_t launch_kv_append(const void* k_src, int64_t ks_t, int64_t ks_h, const void* v_src,

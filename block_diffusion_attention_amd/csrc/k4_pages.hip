@@ -26,11 +26,6 @@ template <> __device__ __forceinline__ float ldf<float>(const float* p) { return
 template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);
 }
-template <typename T> __device__ __forceinline__ T stf(float x);
-template <> __device__ __forceinline__ float stf<float>(float x) { return x; }
-template <> __device__ __forceinline__ uint16_t stf<uint16_t>(float x) {
-  return static_cast<uint16_t>(__float_as_uint(x) >> 16);   // exact: x is a bf16 value
-}
 
 // Element e of a 16-byte group of bf16 (8) or fp32 (4) values, as float.
 template <typename T> __device__ __forceinline__ float grp_float(u32x4v w, int e);

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void proxy_keys_kernel(const double* part, int
 // wrote the mask).
 __global__ __launch_bounds__(128) void proxy_scatter_kernel(const int32_t* selected, int n_tok,
                                                             const double* proxy, int rank,
-                                                            double* cache, uint8_t* mask) {
+                                                            double* cache) {
   const int t = selected[blockIdx.x];
   if (t < 0 || t >= n_tok) return;                 // (the top-k emits ids in range)
   const int64_t o = static_cast<int64_t>(t) * rank;
@@ -295,11 +295,10 @@ hipError_t launch_proxy_keys(const double* part, int n_blocks, int n_tok, int ra
 }
 
 hipError_t launch_proxy_scatter(const int32_t* selected, int n_select, int n_tok,
-                                const double* proxy, int rank, double* cache, uint8_t* mask,
-                                hipStream_t s) {
+                                const double* proxy, int rank, double* cache, hipStream_t s) {
   if (n_select <= 0) return hipSuccess;
   hipLaunchKernelGGL(proxy_scatter_kernel, dim3(n_select), dim3(128), 0, s, selected, n_tok, proxy,
-                     rank, cache, mask);
+                     rank, cache);
   return hipGetLastError();
 }
 
