@@ -166,7 +166,9 @@ class Step:
 
     @property
     def mask(self):
-        """The [Hq] reuse flags used by the latest step (1 = reused)."""
+        """The [Hq] reuse flags the state holds (1 = reuse): in TEXT mode those
+        the latest step used; in VIDEO mode, after a step, those the next step
+        will use (the step swaps the flag buffers)."""
         cur = self.state.mask
         return self._masks[0] if self._masks[0].data_ptr() == cur else self._masks[1]
 

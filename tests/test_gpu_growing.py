@@ -265,3 +265,50 @@ def test_append_fills_the_cache_exactly(fb):
         blk = dev_tensor(k_all[:1], "bf16")
         with pytest.raises(fb.FlashBlockError):
             cache.append(shape, blk, blk)
+
+
+def test_video_blocks_on_a_growing_cache(fb):
+    """Video mode (12 MHA heads, 256 block queries: the many-rows MFMA pass)
+    over a head-major cache of fixed capacity that takes each finished block:
+    per-head decisions and outputs against the oracle's growing run. The
+    per-head noise scales are redrawn until no head's similarity lies within
+    1e-3 of gamma, so both sides decide alike."""
+    cfg = W.VIDEO.with_(n_prefix=1500, n_block=256, n_steps=3)
+    n_blocks = 2
+    for variant in range(3, 20):
+        sig = W.video_sigmas(cfg, variant)
+        kp, vp = W.prefix_kv(cfg, variant=variant)
+        blocks = [W.video_steps(cfg, sig, variant=variant, block=j) for j in range(n_blocks)]
+        inputs = [[dict(q=vals(x["q"], "bf16"), k=vals(x["k"], "bf16"), v=vals(x["v"], "bf16"))
+                   for x in b] for b in blocks]
+        out, _ = OG.run_blocks(inputs, vals(kp, "bf16"), vals(vp, "bf16"), OC.video_block,
+                               scale=cfg.scale, gamma=cfg.gamma)
+        sims = np.concatenate([r["sim"] for b in out for r in b["recs"]])
+        sims = sims[~np.isnan(sims)]
+        if (np.abs(sims - cfg.gamma) > 1e-3).all():
+            break
+    shape = fb.shape_of(12, 12, 128, cfg.scale, torch.bfloat16)
+    cache = fb.KVCache(cfg.n_prefix + n_blocks * 256, 12, 128, torch.bfloat16, "cuda", "head")
+    cache.append(shape, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"))
+    step = fb.Step(fb.FB_STEP_VIDEO, shape, 256, cache=cache, gamma=cfg.gamma)
+    n_reused = 0
+    for j, (steps, blk) in enumerate(zip(blocks, out)):
+        for s, (st, rec) in enumerate(zip(steps, blk["recs"])):
+            # the state holds the flags the coming step uses; after a step,
+            # those of the next one
+            used = cpu(step.mask).astype(bool) if s > 0 else np.zeros(12, bool)
+            a = torch.empty(256, 12, 128, device="cuda")
+            l = torch.empty(256, 12, device="cuda")
+            step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                      dev_tensor(st["v"], "bf16"), a, l)
+            torch.cuda.synchronize()
+            tag = "block %d step %d" % (j, s)
+            assert np.array_equal(used, rec["reuse_used"]), tag
+            if s > 0:
+                assert np.array_equal(cpu(step.mask).astype(bool), rec["reuse_next"]), tag
+            n_reused += int(used.sum())
+            check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)
+            check_l(tag + " L_full", cpu(l), rec["l_full"], 1e-3)
+        step.next_block(dev_tensor(steps[-1]["k"], "bf16"), dev_tensor(steps[-1]["v"], "bf16"))
+    assert cache.n_tok == cfg.n_prefix + n_blocks * 256
+    assert n_reused > 0
