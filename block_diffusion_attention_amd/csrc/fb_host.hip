@@ -229,10 +229,19 @@ size_t prefix_ws_bytes(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
 
 fb_status dev(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_DEVICE; }
 
+// Extra work a sparse step folds into its GATHER pass: the token
+// classification inside the selection prep (am) and the q_prev <- q_cur copy
+// inside the reduce (q_src -> q_dst).
+struct PrefixHooks {
+  const ActiveFromMse* am;
+  const void* q_src; int64_t q_st, q_sh;
+  void* q_dst; int q_esize;
+};
+
 fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor& k,
                      const fb_tensor& v, const uint8_t* mask, const fb_page_sel* sel, float* a_out,
                      float* l_out, float* a_res, float* l_res, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+                     hipStream_t stream, const PrefixHooks* hooks = nullptr) {
   const int64_t n_q = q.n_tok, n_kv = k.n_tok;
   const int mode = sel ? sel->mode : FB_SEL_DENSE;
   const bool head_major = s.n_kv_heads == 1 ||
@@ -283,6 +292,7 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   if (v.stride_tok != k.stride_tok || v.stride_head != k.stride_head) return FB_ERR_UNSUPPORTED;
   if (pl.path != PATH_GENERIC && !offsets32(k)) return FB_ERR_UNSUPPORTED;
 
+  if (hooks && (pl.n_chunks == 0 || pl.direct)) return FB_ERR_UNSUPPORTED;   // they ride on both
   if (pl.n_chunks > 0) {
     hipError_t e;
     if (pl.path == PATH_SPARSE) {
@@ -291,7 +301,13 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
       int32_t* ul = gather ? reinterpret_cast<int32_t*>(w + pl.off_ul) : nullptr;
       int32_t* uc = gather ? reinterpret_cast<int32_t*>(w + pl.off_uc) : nullptr;
       // (k_pages = 0: all-zero bitmaps, no list is read)
-      if (sel_prep_fits(static_cast<int>(n_q), pl.words)) {
+      if (hooks && hooks->am) {
+        if (!gather || !sel_prep_mse_fits(static_cast<int>(n_q), s.n_q_heads, pl.words))
+          return FB_ERR_UNSUPPORTED;
+        e = launch_sel_prep_mse(sel->pages, static_cast<int>(n_q), s.n_kv_heads, sel->k_pages,
+                                pl.words, static_cast<int>(pl.n_pages), *hooks->am, bm, ul, uc,
+                                stream);
+      } else if (sel_prep_fits(static_cast<int>(n_q), pl.words)) {
         e = launch_sel_prep(sel->pages, static_cast<int>(n_q), s.n_kv_heads, sel->k_pages, pl.words,
                             static_cast<int>(pl.n_pages), sel->active, gather ? 1 : 0, bm, ul, uc,
                             stream);
@@ -359,6 +375,13 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   rp.mask = mask;
   rp.a_out = a_out;
   rp.l_out = l_out;
+  if (hooks && hooks->q_src) {
+    rp.q_src = hooks->q_src;
+    rp.q_st = hooks->q_st;
+    rp.q_sh = hooks->q_sh;
+    rp.q_dst = hooks->q_dst;
+    rp.q_esize = hooks->q_esize;
+  }
   if (mode == FB_SEL_SPLIT) {
     rp.part_ra = pp.out_res.a;
     rp.part_rl = pp.out_res.l;
@@ -877,6 +900,19 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         return dev(launch_copy_rows(a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head,
                                     st->q_prev, n_q, hq, d, s.dtype, stream));
       };
+      // a FlashBlock step the controller left open (decision -1) on the sparse
+      // kernel: the token classification rides on the selection prep
+      bool fuse_mse = false;
+      if (!first && a->decision == -1 && !reselect && st->k_prefix.n_tok > 0 &&
+          aligned16(a->q_blk.ptr) && aligned16(st->q_prev) && a->q_blk.stride_head % 8 == 0 &&
+          a->q_blk.stride_tok % 8 == 0) {
+        fb_page_sel g = sel;
+        g.mode = FB_SEL_GATHER;
+        g.active = st->active;
+        const PrefixPlan gp = plan_prefix(s, n_q, st->k_prefix.n_tok, &g, false);
+        fuse_mse = gp.path == PATH_SPARSE && gp.n_chunks > 0 &&
+                   sel_prep_mse_fits(static_cast<int>(n_q), hq, gp.words);
+      }
       if (first) {
         if (!st->meta_ready) {
           rc = fb_page_meta_update(&s, st->k_prefix, st->page_size, 0, page_cap, st->kmin,
@@ -899,6 +935,22 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         }
         if (rc != FB_OK) return rc;
         rc = token_step(0, 1);                     // every token active at the refresh step
+        if (rc != FB_OK) return rc;
+      } else if (fuse_mse) {
+        // one launch fewer: the selection prep classifies the tokens (query
+        // MSE, cutoff, active flags) and the reduce copies q_cur to q_prev
+        const ActiveFromMse am = {st->q_prev, a->q_blk.ptr, a->q_blk.stride_tok,
+                                  a->q_blk.stride_head, s.dtype, hq, d, st->pct, st->mse,
+                                  st->active};
+        const PrefixHooks hk = {&am, a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head,
+                                st->q_prev, s.dtype == FB_BF16 ? 2 : 4};
+        sel.mode = FB_SEL_GATHER;
+        sel.active = st->active;
+        rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, &sel, st->a_out, st->l_out,
+                             st->a_res, st->l_res);
+        if (rc != FB_OK) return rc;
+        rc = run_prefix(s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
+                        st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream, &hk);
         if (rc != FB_OK) return rc;
       } else if (a->decision != 1) {
         rc = token_step(a->decision == 0 ? 0 : 1, 1);

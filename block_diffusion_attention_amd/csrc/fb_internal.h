@@ -122,6 +122,22 @@ struct ReduceParams {
   float* a_out; float* l_out;   // merged (all partials [+ residual])
   float* a_res; float* l_res;   // SPLIT: residual-only merge
   RowsDyn dyn;                  // dyn.on: n_chunks = the many-rows pass's split from the mask
+  // optional: every row (t, h) copies its query q_src[t][h][:] (d elements of
+  // q_esize bytes, strides in elements) to q_dst[(t * hq + h) * d], before
+  // anything else (a sparse step's q_prev <- q_cur, after every read of it)
+  const void* q_src; int64_t q_st, q_sh; void* q_dst; int q_esize;
+};
+
+// A sparse GATHER step's token classification done inside the selection
+// prep: query MSE against q_prev, nearest-rank cutoff, active flags (the
+// same arithmetic as the active-step kernel), then the union over them.
+struct ActiveFromMse {
+  const void* q_prev;           // [n_q, hq, d] contiguous
+  const void* q_cur; int64_t q_st, q_sh;
+  fb_dtype dt;
+  int hq, d, pct;
+  double* mse;                  // out [n_q], nullable (written by workgroup 0)
+  uint8_t* active;              // out [n_q] (written by workgroup 0)
 };
 
 // ---- launchers (return hipError_t of the launch) -----------------------
@@ -140,6 +156,10 @@ bool sel_prep_fits(int n_q, int words);         // bitmaps of one KV group fit i
 hipError_t launch_sel_prep(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
                            int n_pages, const uint8_t* active, int do_union, uint32_t* bitmap,
                            int32_t* ulist, int32_t* ucnt, hipStream_t s);
+bool sel_prep_mse_fits(int n_q, int hq, int words);
+hipError_t launch_sel_prep_mse(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
+                               int n_pages, const ActiveFromMse& am, uint32_t* bitmap,
+                               int32_t* ulist, int32_t* ucnt, hipStream_t s);
 hipError_t launch_prefix_sparse(const PrefixParams& p, hipStream_t s);
 int sparse_max_tiles_per_chunk();               // 32-key tiles a GATHER chunk may span
 hipError_t launch_prefix_empty(float* a_out, float* l_out, int n_q, int hq, int d,

@@ -789,6 +789,17 @@ constexpr int64_t kReduceLeanRows = 4096;    // rows from which the lean reduce 
 // once, and the two halves meet in LDS; the chunk weights come from one
 // wave's max. The chunk order of every sum is fixed, so results are
 // run-to-run identical.
+// The row's query copy (ReduceParams.q_src), one 32-bit word per thread.
+__device__ __forceinline__ void copy_row_query(const ReduceParams& p, int t, int h) {
+  if (!p.q_src) return;
+  const int words = p.d * p.q_esize / 4;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(
+      static_cast<const char*>(p.q_src) + (t * p.q_st + h * p.q_sh) * p.q_esize);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(
+      static_cast<char*>(p.q_dst) + (static_cast<int64_t>(t) * p.hq + h) * p.d * p.q_esize);
+  for (int i = threadIdx.x; i < words; i += blockDim.x) dst[i] = src[i];
+}
+
 __global__ __launch_bounds__(256) void prefix_reduce_kernel(ReduceParams p) {
   __shared__ float wa[kMaxChunks];
   __shared__ float wr[kMaxChunks + 1];
@@ -797,6 +808,7 @@ __global__ __launch_bounds__(256) void prefix_reduce_kernel(ReduceParams p) {
   const int64_t row = blockIdx.x;
   const int h = static_cast<int>(row % p.hq);
   const int t = static_cast<int>(row / p.hq);
+  copy_row_query(p, t, h);
   if (p.mask && p.mask[h]) return;
   if (p.active && !p.active[t]) return;
   const int tid = threadIdx.x;
@@ -902,6 +914,7 @@ __global__ __launch_bounds__(128) void prefix_reduce_lean_kernel(ReduceParams p)
   const int64_t row = blockIdx.x;
   const int h = static_cast<int>(row % p.hq);
   const int t = static_cast<int>(row / p.hq);
+  copy_row_query(p, t, h);
   if (p.mask && p.mask[h]) return;
   if (p.active && !p.active[t]) return;
   const int tid = threadIdx.x;

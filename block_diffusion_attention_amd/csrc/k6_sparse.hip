@@ -110,6 +110,149 @@ __global__ __launch_bounds__(256) void sel_union_kernel(const uint32_t* bitmap, 
   if (tid == 0) ucnt[g] = base;
 }
 
+template <typename T> __device__ __forceinline__ double ldd(const T* p);
+template <> __device__ __forceinline__ double ldd<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ double ldd<uint16_t>(const uint16_t* p) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(*p) << 16));
+}
+
+// The selection prep of a sparse GATHER step with the step's token
+// classification folded in: every workgroup (one per KV group g) computes
+// the query MSE of every token against q_prev -- per (token, head) a float64
+// sum over d in order of (cur - prev)^2 (difference, square, add), the
+// heads' sums added in order, divided by Hq d -- the nearest-rank cutoff and
+// the active flags (MSE strictly above it), exactly as the active-step
+// kernel does; workgroup 0 writes them out. Then the bitmaps of group g and
+// their union over the active tokens, as in sel_prep_kernel. (q_prev is
+// only read here; the caller overwrites it later in the step.)
+template <typename T>
+__global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages, int n_q, int hkv,
+                                                           int k_pages, int words, int n_pages,
+                                                           ActiveFromMse am, uint32_t* bitmap,
+                                                           int32_t* ulist, int32_t* ucnt) {
+#pragma clang fp contract(off)
+  extern __shared__ uint32_t bm[];                 // [n_q][words], then the float64 sums
+  __shared__ int scan[256];
+  __shared__ double cutoff_s;
+  __shared__ uint8_t act_s[1024];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int hq = am.hq, d = am.d;
+  double* part = reinterpret_cast<double*>(bm + ((n_q * words + 1) & ~1));   // [n_q * hq]
+  double* mse_s = part + n_q * hq;                                            // [n_q]
+  const T* qp = static_cast<const T*>(am.q_prev);
+  const T* qc = static_cast<const T*>(am.q_cur);
+  const int chains = n_q * hq;
+  // rows load 32 dims at a time as 16-byte vectors (d is 128, strides are
+  // multiples of 8 elements, the base pointers 16-byte aligned)
+  constexpr int kV = 16 / sizeof(T);
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  for (int i = tid; i < chains; i += 1024) {
+    const int t = i / hq, h = i % hq;
+    const T* a = qp + static_cast<int64_t>(i) * d;
+    const T* b = qc + t * am.q_st + h * am.q_sh;
+    double acc = 0.0;
+    for (int j0 = 0; j0 < d; j0 += 32) {
+      u32x4v va[32 / kV], vb[32 / kV];
+#pragma unroll
+      for (int u = 0; u < 32 / kV; ++u) {
+        va[u] = *reinterpret_cast<const u32x4v*>(a + j0 + u * kV);
+        vb[u] = *reinterpret_cast<const u32x4v*>(b + j0 + u * kV);
+      }
+      const T* ea = reinterpret_cast<const T*>(va);
+      const T* eb = reinterpret_cast<const T*>(vb);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const double diff = ldd<T>(eb + j) - ldd<T>(ea + j);
+        const double sq = diff * diff;
+        acc = acc + sq;
+      }
+    }
+    part[i] = acc;
+  }
+  for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
+  __syncthreads();
+  for (int t = tid; t < n_q; t += 1024) {
+    double total = 0.0;
+    for (int h = 0; h < hq; ++h) total = total + part[t * hq + h];
+    const double v = total / static_cast<double>(hq * d);
+    mse_s[t] = v;
+    if (g == 0 && am.mse) am.mse[t] = v;
+  }
+  __syncthreads();
+  int rank = (am.pct * n_q + 99) / 100;
+  if (rank < 1) rank = 1;
+  for (int t = tid; t < n_q; t += 1024) {
+    const double v = mse_s[t];
+    int less = 0, leq = 0;
+    for (int u = 0; u < n_q; ++u) {
+      less += mse_s[u] < v ? 1 : 0;
+      leq += mse_s[u] <= v ? 1 : 0;
+    }
+    if (less < rank && rank <= leq) cutoff_s = v;  // every writer writes the same value
+  }
+  __syncthreads();
+  for (int t = tid; t < n_q; t += 1024) {
+    const uint8_t a = mse_s[t] > cutoff_s ? 1 : 0;
+    act_s[t] = a;
+    if (g == 0) am.active[t] = a;
+  }
+  // the selection bitmaps of group g (as sel_prep_kernel)
+  const int64_t n_ids = static_cast<int64_t>(n_q) * k_pages;
+  for (int64_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
+    int32_t pv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + tid;
+      pv[u] = -1;
+      if (i < n_ids) {
+        const int t = static_cast<int>(i / k_pages);
+        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + i % k_pages];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t pg = static_cast<uint32_t>(pv[u]);
+      if (i < n_ids && pg < static_cast<uint32_t>(n_pages))
+        atomicOr(&bm[static_cast<int>(i / k_pages) * words + (pg >> 5)], 1u << (pg & 31));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_q * words; i += 1024) {
+    const int t = i / words, w = i % words;
+    bitmap[(static_cast<int64_t>(t) * hkv + g) * words + w] = bm[i];
+  }
+  // the union over the active tokens, 256 words per pass
+  const bool scanner = tid < 256;
+  int base = 0;
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int w = w0 + tid;
+    uint32_t u = 0u;
+    if (scanner && w < words)
+      for (int t = 0; t < n_q; ++t)
+        if (act_s[t]) u |= bm[t * words + w];
+    const int c = __popc(u);
+    if (scanner) scan[tid] = c;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {            // inclusive scan
+      const int v = scanner && tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      if (scanner) scan[tid] += v;
+      __syncthreads();
+    }
+    int pos = base + (scanner ? scan[tid] : 0) - c;
+    while (u) {
+      const int b = __builtin_ctz(u);
+      ulist[static_cast<int64_t>(g) * n_pages + pos++] = w * 32 + b;
+      u &= u - 1;
+    }
+    base += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) ucnt[g] = base;
+}
+
 // Both of the above in one launch when a KV group's bitmaps fit in LDS: one
 // workgroup per g builds the rows (t, g) for every t, writes them, and (for
 // GATHER) compacts their union over the active tokens.
@@ -506,6 +649,28 @@ hipError_t launch_sel_prep(const int32_t* pages, int n_q, int hkv, int k_pages, 
   hipLaunchKernelGGL(sel_prep_kernel, dim3(hkv), dim3(1024), static_cast<size_t>(n_q) * words * 4, s,
                      pages, n_q, hkv, k_pages, words, n_pages, active, do_union, bitmap, ulist,
                      ucnt);
+  return hipGetLastError();
+}
+
+static size_t sel_prep_mse_lds(int n_q, int hq, int words) {
+  return (static_cast<size_t>((n_q * words + 1) & ~1) * 4) +
+         (static_cast<size_t>(n_q) * hq + n_q) * sizeof(double);
+}
+
+bool sel_prep_mse_fits(int n_q, int hq, int words) {
+  return n_q >= 1 && n_q <= 1024 && sel_prep_mse_lds(n_q, hq, words) <= 64 * 1024;
+}
+
+hipError_t launch_sel_prep_mse(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
+                               int n_pages, const ActiveFromMse& am, uint32_t* bitmap,
+                               int32_t* ulist, int32_t* ucnt, hipStream_t s) {
+  const size_t lds = sel_prep_mse_lds(n_q, am.hq, words);
+  if (am.dt == FB_BF16)
+    hipLaunchKernelGGL(sel_prep_mse_kernel<uint16_t>, dim3(hkv), dim3(1024), lds, s, pages, n_q,
+                       hkv, k_pages, words, n_pages, am, bitmap, ulist, ucnt);
+  else
+    hipLaunchKernelGGL(sel_prep_mse_kernel<float>, dim3(hkv), dim3(1024), lds, s, pages, n_q, hkv,
+                       k_pages, words, n_pages, am, bitmap, ulist, ucnt);
   return hipGetLastError();
 }
 
