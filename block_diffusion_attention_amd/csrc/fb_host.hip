@@ -816,6 +816,10 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
   if (!st->a_out || !st->l_out || !st->mask || !a->a_full) return FB_ERR_INVALID_ARGUMENT;
   if ((rc = check_tensor(st->k_prefix, -1, s.n_kv_heads, d)) != FB_OK) return rc;
   if ((rc = check_tensor(st->v_prefix, st->k_prefix.n_tok, s.n_kv_heads, d)) != FB_OK) return rc;
+  // the block's tensors too, before any launch of the step
+  if ((rc = check_tensor(a->q_blk, n_q, hq, d)) != FB_OK) return rc;
+  if ((rc = check_tensor(a->k_blk, n_q, s.n_kv_heads, d)) != FB_OK) return rc;
+  if ((rc = check_tensor(a->v_blk, n_q, s.n_kv_heads, d)) != FB_OK) return rc;
   if (fb_step_workspace(st) > st->ws_bytes) return FB_ERR_WORKSPACE_TOO_SMALL;
   const bool first = st->step == 0;
 
@@ -866,7 +870,7 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       if (st->sparse_reselect != 0 && st->sparse_reselect != 1) return FB_ERR_INVALID_ARGUMENT;
       const bool reselect = st->sparse_reselect == 1;
       if ((!reselect && (!st->a_res || !st->l_res)) || !st->pages || !st->kmin || !st->kmax ||
-          !st->q_prev || !st->active)
+          !st->q_prev || !aligned16(st->q_prev) || !st->active)
         return FB_ERR_INVALID_ARGUMENT;
       if (st->page_size < 1 || st->pct < 1 || st->pct > 100) return FB_ERR_INVALID_ARGUMENT;
       const int64_t n_pages = (st->k_prefix.n_tok + st->page_size - 1) / st->page_size;
@@ -903,9 +907,7 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       // a FlashBlock step the controller left open (decision -1) on the sparse
       // kernel: the token classification rides on the selection prep
       bool fuse_mse = false;
-      if (!first && a->decision == -1 && !reselect && st->k_prefix.n_tok > 0 &&
-          aligned16(a->q_blk.ptr) && aligned16(st->q_prev) && a->q_blk.stride_head % 8 == 0 &&
-          a->q_blk.stride_tok % 8 == 0) {
+      if (!first && a->decision == -1 && !reselect && st->k_prefix.n_tok > 0) {
         fb_page_sel g = sel;
         g.mode = FB_SEL_GATHER;
         g.active = st->active;

@@ -35,6 +35,49 @@ __device__ __forceinline__ bf16x8 bf16_lo_part(f32x8 w, bf16x8 hi) {
   return __builtin_bit_cast(bf16x8, lb);
 }
 
+// Sum over j = 0..d-1, in order, of (cur[j] - prev[j])^2 in float64
+// (difference, square, add: no contraction), for bf16 (T = uint16_t bits) or
+// fp32 rows; d a multiple of 64, both rows 16-byte aligned. Each 64-dim
+// round issues all of its 16-byte loads before the arithmetic, so a row
+// costs d / 64 memory round trips.
+template <typename T>
+__device__ __forceinline__ double sq_diff_sum(const T* prev, const T* cur, int d) {
+#pragma clang fp contract(off)
+  constexpr int kV = 16 / sizeof(T);               // elements per 16-byte vector
+  constexpr int kN = 64 / kV;                      // vectors per 64 dims
+  double acc = 0.0;
+  for (int j0 = 0; j0 < d; j0 += 64) {
+    u32x4v va[kN], vb[kN];
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+      va[u] = *reinterpret_cast<const u32x4v*>(prev + j0 + u * kV);
+      vb[u] = *reinterpret_cast<const u32x4v*>(cur + j0 + u * kV);
+    }
+#pragma unroll
+    for (int u = 0; u < kN; ++u) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (sizeof(T) == 2) {            // elements 2w (low half), 2w + 1
+          const double d0 = static_cast<double>(__uint_as_float(vb[u][w] << 16)) -
+                            static_cast<double>(__uint_as_float(va[u][w] << 16));
+          const double s0 = d0 * d0;
+          acc = acc + s0;
+          const double d1 = static_cast<double>(__uint_as_float(vb[u][w] & 0xffff0000u)) -
+                            static_cast<double>(__uint_as_float(va[u][w] & 0xffff0000u));
+          const double s1 = d1 * d1;
+          acc = acc + s1;
+        } else {
+          const double d0 = static_cast<double>(__uint_as_float(vb[u][w])) -
+                            static_cast<double>(__uint_as_float(va[u][w]));
+          const double s0 = d0 * d0;
+          acc = acc + s0;
+        }
+      }
+    }
+  }
+  return acc;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

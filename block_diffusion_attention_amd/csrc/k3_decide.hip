@@ -204,32 +204,10 @@ __global__ __launch_bounds__(1024) void active_step_kernel(T* q_prev, const T* q
   const int nt = blockDim.x;
   const int chains = n_q * hq;
   if (mode == 1) {
-    // each chain loads its rows 32 dims at a time as 16-byte vectors (rows are
-    // 16-byte aligned: d is a multiple of 32 and strides of 8 elements)
-    constexpr int kV = 16 / sizeof(T);             // elements per vector
-    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    // rows are 16-byte aligned: d is 64 or 128 and strides multiples of 8
     for (int i = tid; i < chains; i += nt) {
       const int t = i / hq, h = i % hq;
-      const T* a = q_prev + static_cast<int64_t>(i) * d;
-      const T* b = q_cur + t * q_st + h * q_sh;
-      double acc = 0.0;
-      for (int j0 = 0; j0 < d; j0 += 32) {
-        u32x4v va[32 / kV], vb[32 / kV];
-#pragma unroll
-        for (int u = 0; u < 32 / kV; ++u) {
-          va[u] = *reinterpret_cast<const u32x4v*>(a + j0 + u * kV);
-          vb[u] = *reinterpret_cast<const u32x4v*>(b + j0 + u * kV);
-        }
-        const T* ea = reinterpret_cast<const T*>(va);
-        const T* eb = reinterpret_cast<const T*>(vb);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const double diff = ldd<T>(eb + j) - ldd<T>(ea + j);
-          const double sq = diff * diff;
-          acc = acc + sq;
-        }
-      }
-      part[i] = acc;
+      part[i] = sq_diff_sum<T>(q_prev + static_cast<int64_t>(i) * d, q_cur + t * q_st + h * q_sh, d);
     }
     __syncthreads();
     for (int t = tid; t < n_q; t += nt) {

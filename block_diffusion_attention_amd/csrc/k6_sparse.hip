@@ -137,38 +137,17 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
   __shared__ uint8_t act_s[1024];
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
-  const int hq = am.hq, d = am.d;
+  const int hq = am.hq;
+  constexpr int d = 128;                           // the sparse kernels' head_dim
   double* part = reinterpret_cast<double*>(bm + ((n_q * words + 1) & ~1));   // [n_q * hq]
   double* mse_s = part + n_q * hq;                                            // [n_q]
   const T* qp = static_cast<const T*>(am.q_prev);
   const T* qc = static_cast<const T*>(am.q_cur);
   const int chains = n_q * hq;
-  // rows load 32 dims at a time as 16-byte vectors (d is 128, strides are
-  // multiples of 8 elements, the base pointers 16-byte aligned)
-  constexpr int kV = 16 / sizeof(T);
-  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  // (d is 128, strides are multiples of 8 elements, base pointers 16-byte aligned)
   for (int i = tid; i < chains; i += 1024) {
     const int t = i / hq, h = i % hq;
-    const T* a = qp + static_cast<int64_t>(i) * d;
-    const T* b = qc + t * am.q_st + h * am.q_sh;
-    double acc = 0.0;
-    for (int j0 = 0; j0 < d; j0 += 32) {
-      u32x4v va[32 / kV], vb[32 / kV];
-#pragma unroll
-      for (int u = 0; u < 32 / kV; ++u) {
-        va[u] = *reinterpret_cast<const u32x4v*>(a + j0 + u * kV);
-        vb[u] = *reinterpret_cast<const u32x4v*>(b + j0 + u * kV);
-      }
-      const T* ea = reinterpret_cast<const T*>(va);
-      const T* eb = reinterpret_cast<const T*>(vb);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const double diff = ldd<T>(eb + j) - ldd<T>(ea + j);
-        const double sq = diff * diff;
-        acc = acc + sq;
-      }
-    }
-    part[i] = acc;
+    part[i] = sq_diff_sum<T>(qp + static_cast<int64_t>(i) * d, qc + t * am.q_st + h * am.q_sh, d);
   }
   for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
   __syncthreads();
@@ -664,6 +643,7 @@ bool sel_prep_mse_fits(int n_q, int hq, int words) {
 hipError_t launch_sel_prep_mse(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
                                int n_pages, const ActiveFromMse& am, uint32_t* bitmap,
                                int32_t* ulist, int32_t* ucnt, hipStream_t s) {
+  if (am.d != 128) return hipErrorInvalidValue;
   const size_t lds = sel_prep_mse_lds(n_q, am.hq, words);
   if (am.dt == FB_BF16)
     hipLaunchKernelGGL(sel_prep_mse_kernel<uint16_t>, dim3(hkv), dim3(1024), lds, s, pages, n_q,

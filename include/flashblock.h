@@ -426,7 +426,7 @@ typedef struct {
   int32_t* pages;          /* SPARSE [n_q, Hkv, k_pages]                       */
   void* kmin;              /* SPARSE [Hkv, page_cap or P, d] (dtype)           */
   void* kmax;              /* SPARSE [Hkv, page_cap or P, d]                   */
-  void* q_prev;            /* SPARSE [n_q, Hq, d] contiguous (dtype)           */
+  void* q_prev;            /* SPARSE [n_q, Hq, d] contiguous (dtype), 16-B al. */
   double* mse;             /* SPARSE [n_q]                                     */
   uint8_t* active;         /* SPARSE [n_q]                                     */
   void* ws;                /* device workspace >= fb_step_workspace()          */

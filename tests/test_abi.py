@@ -200,6 +200,15 @@ def test_step_rejects(lib):
     assert lib.fb_step(C.byref(st), C.byref(args), None) == 1            # n_q mismatch
     args.q_blk = ten(4, 32)
     assert lib.fb_step(C.byref(st), C.byref(args), None) == 1            # ids missing
+    # the block's tensors are checked before any launch of the step
+    st.mode = fb.FB_STEP_VIDEO
+    for bad in (dict(q_blk=ten(4, 32, p=FAKE + 8)), dict(k_blk=ten(3, 8)),
+                dict(v_blk=ten(4, 8, st=8 * 128 + 4))):
+        for k, v in bad.items():
+            setattr(args, k, v)
+        assert lib.fb_step(C.byref(st), C.byref(args), None) == 1, bad
+        args.q_blk, args.k_blk, args.v_blk = ten(4, 32), ten(4, 8), ten(4, 8)
+    st.mode = fb.FB_STEP_TEXT
     st.mode = 7
     assert lib.fb_step(C.byref(st), C.byref(args), None) == 1
     st.mode = fb.FB_STEP_TEXT
