@@ -144,13 +144,41 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
   const T* qp = static_cast<const T*>(am.q_prev);
   const T* qc = static_cast<const T*>(am.q_cur);
   const int chains = n_q * hq;
+  for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
+  // page ids are loaded 8 at a time ahead of their LDS atomics; the first
+  // batch is in flight during the query loads below
+  const int64_t n_ids = static_cast<int64_t>(n_q) * k_pages;
+  int32_t pv[8];
+  auto load_ids = [&](int64_t i0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + tid;
+      pv[u] = -1;
+      if (i < n_ids) {
+        const int t = static_cast<int>(i / k_pages);
+        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + i % k_pages];
+      }
+    }
+  };
+  load_ids(0);
   // (d is 128, strides are multiples of 8 elements, base pointers 16-byte aligned)
   for (int i = tid; i < chains; i += 1024) {
     const int t = i / hq, h = i % hq;
     part[i] = sq_diff_sum<T>(qp + static_cast<int64_t>(i) * d, qc + t * am.q_st + h * am.q_sh, d);
   }
-  for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
   __syncthreads();
+  // the selection bitmaps of group g (as sel_prep_kernel)
+  for (int64_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
+    if (i0 > 0) load_ids(i0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t pg = static_cast<uint32_t>(pv[u]);
+      if (i < n_ids && pg < static_cast<uint32_t>(n_pages))
+        atomicOr(&bm[static_cast<int>(i / k_pages) * words + (pg >> 5)], 1u << (pg & 31));
+    }
+  }
+  // the token classification
   for (int t = tid; t < n_q; t += 1024) {
     double total = 0.0;
     for (int h = 0; h < hq; ++h) total = total + part[t * hq + h];
@@ -175,27 +203,6 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
     const uint8_t a = mse_s[t] > cutoff_s ? 1 : 0;
     act_s[t] = a;
     if (g == 0) am.active[t] = a;
-  }
-  // the selection bitmaps of group g (as sel_prep_kernel)
-  const int64_t n_ids = static_cast<int64_t>(n_q) * k_pages;
-  for (int64_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
-    int32_t pv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + tid;
-      pv[u] = -1;
-      if (i < n_ids) {
-        const int t = static_cast<int>(i / k_pages);
-        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + i % k_pages];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + tid;
-      const uint32_t pg = static_cast<uint32_t>(pv[u]);
-      if (i < n_ids && pg < static_cast<uint32_t>(n_pages))
-        atomicOr(&bm[static_cast<int>(i / k_pages) * words + (pg >> 5)], 1u << (pg & 31));
-    }
   }
   __syncthreads();
   for (int i = tid; i < n_q * words; i += 1024) {
