@@ -146,9 +146,16 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
 // multiply-add: max(q a, q b) with a <= b is q b for q >= 0 and q a
 // otherwise, and the product of two bf16 (or fp32) values is exact in
 // float64, so acc + that product rounds once either way.
-// Workgroup = (32 pages, KV group g, TC tokens); with an active mask only
-// the workgroup's active tokens are staged and scored, packed onto the
-// first threads.
+// Workgroup = (32 pages, KV group g, TC tokens). One round trip stages the
+// page rows (kept in their own dtype in LDS: bf16 rows are half the size,
+// so four workgroups fit on a CU), the TC tokens' query rows and their
+// active flags; with an active mask only the active tokens are scored,
+// packed onto the first threads.
+template <typename T>
+constexpr int bound_row_stride(int d) {            // LDS row of a page (elements)
+  return sizeof(T) == 2 ? d + 4 : d + 1;           // bf16: 2-word bank step; fp32: 1
+}
+
 template <typename T, int G, int TC>
 __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q_st, int64_t q_sh,
                                                            const T* kmin, const T* kmax, int n_q,
@@ -163,63 +170,89 @@ __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q
   const int nt_all = n_q - t0 < TC ? n_q - t0 : TC;
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPagesPerBlock;
   const int np = n_pages - p0 < kPagesPerBlock ? static_cast<int>(n_pages - p0) : kPagesPerBlock;
-  const int ds = d + 1;
+  const int rs = bound_row_stride<T>(d);
   float* qs = sm;                                    // [TC][d][G] (heads innermost)
-  float* mn = qs + TC * G * d;                       // [kPagesPerBlock][d + 1]
-  float* mx = mn + kPagesPerBlock * ds;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int t = 0; t < nt_all; ++t)
-      if (!active || active[t0 + t]) tok[n++] = t0 + t;
-    n_tok_s = n;
+  T* mn = reinterpret_cast<T*>(qs + TC * G * d);     // [kPagesPerBlock][rs]
+  T* mx = mn + kPagesPerBlock * rs;
+  // wave 0 compacts the active tokens (one flag load per lane, a ballot and
+  // a prefix count) while every thread stages rows
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const bool on = lane < nt_all && (!active || active[t0 + lane]);
+    const unsigned long long m = __ballot(on);
+    if (on) tok[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+    if (lane == 0) n_tok_s = __popcll(m);
   }
-  __syncthreads();
-  const int nt = n_tok_s;
-  if (nt == 0) return;
-  // staging with 16-byte loads (rows of d elements, 16-byte aligned: the
-  // host checks the bases, strides are multiples of 8 elements)
+  // 16-byte loads (rows of d elements, 16-byte aligned: the host checks the
+  // bases, strides are multiples of 8 elements)
   constexpr int NE = 16 / sizeof(T);
   const int gpr = d / NE;                            // 16-byte groups per row
-  for (int v = threadIdx.x; v < nt * G * gpr; v += blockDim.x) {
-    const int row = v / gpr, cg = (v % gpr) * NE;
-    const int t = row / G, j = row % G;
-    const u32x4v w = *reinterpret_cast<const u32x4v*>(
-        q + static_cast<int64_t>(tok[t]) * q_st + static_cast<int64_t>(g * G + j) * q_sh + cg);
-#pragma unroll
-    for (int e = 0; e < NE; ++e) qs[(t * d + cg + e) * G + j] = grp_float<T>(w, e);
-  }
   for (int v = threadIdx.x; v < np * gpr; v += blockDim.x) {
     const int pi = v / gpr, cg = (v % gpr) * NE;
     const int64_t o = (static_cast<int64_t>(g) * page_cap + p0 + pi) * d + cg;
     const u32x4v a = *reinterpret_cast<const u32x4v*>(kmin + o);
     const u32x4v b = *reinterpret_cast<const u32x4v*>(kmax + o);
+    uint32_t* wa = reinterpret_cast<uint32_t*>(mn + pi * rs + cg);
+    uint32_t* wb = reinterpret_cast<uint32_t*>(mx + pi * rs + cg);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      mn[pi * ds + cg + e] = grp_float<T>(a, e);
-      mx[pi * ds + cg + e] = grp_float<T>(b, e);
+    for (int e = 0; e < 4; ++e) {
+      wa[e] = a[e];
+      wb[e] = b[e];
     }
   }
+  for (int v = threadIdx.x; v < nt_all * G * gpr; v += blockDim.x) {
+    const int row = v / gpr, cg = (v % gpr) * NE;
+    const int t = row / G, j = row % G;
+    const u32x4v w = *reinterpret_cast<const u32x4v*>(
+        q + static_cast<int64_t>(t0 + t) * q_st + static_cast<int64_t>(g * G + j) * q_sh + cg);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) qs[(t * d + cg + e) * G + j] = grp_float<T>(w, e);
+  }
   __syncthreads();
+  const int nt = n_tok_s;
   for (int e = threadIdx.x; e < np * nt; e += blockDim.x) {
-    const int pi = e % np, t = e / np;
-    const float* qr = qs + t * G * d;
-    const float* mnr = mn + pi * ds;
-    const float* mxr = mx + pi * ds;
+    const int pi = e % np, tl = tok[e / np];
+    const float* qr = qs + tl * G * d;
     double acc[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.0;
-    for (int c = 0; c < d; ++c) {
-      const double a = mnr[c], b = mxr[c];
+    if constexpr (sizeof(T) == 2) {                  // two dims per LDS word
+      const uint32_t* mnw = reinterpret_cast<const uint32_t*>(mn + pi * rs);
+      const uint32_t* mxw = reinterpret_cast<const uint32_t*>(mx + pi * rs);
+      for (int c2 = 0; c2 < d / 2; ++c2) {
+        const uint32_t wa = mnw[c2], wb = mxw[c2];
+        const float a0 = __uint_as_float(wa << 16), a1 = __uint_as_float(wa & 0xffff0000u);
+        const float b0 = __uint_as_float(wb << 16), b1 = __uint_as_float(wb & 0xffff0000u);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const double qv = qr[c * G + j];
-        acc[j] = __builtin_fma(qv, qv >= 0.0 ? b : a, acc[j]);
+        for (int j = 0; j < G; ++j) {
+          const float qv = qr[2 * c2 * G + j];
+          acc[j] = __builtin_fma(static_cast<double>(qv), static_cast<double>(qv >= 0.f ? b0 : a0),
+                                 acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float qv = qr[(2 * c2 + 1) * G + j];
+          acc[j] = __builtin_fma(static_cast<double>(qv), static_cast<double>(qv >= 0.f ? b1 : a1),
+                                 acc[j]);
+        }
+      }
+    } else {
+      const float* mnr = reinterpret_cast<const float*>(mn) + pi * rs;
+      const float* mxr = reinterpret_cast<const float*>(mx) + pi * rs;
+      for (int c = 0; c < d; ++c) {
+        const float a = mnr[c], b = mxr[c];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float qv = qr[c * G + j];
+          acc[j] = __builtin_fma(static_cast<double>(qv), static_cast<double>(qv >= 0.f ? b : a),
+                                 acc[j]);
+        }
       }
     }
     double best = acc[0];
 #pragma unroll
     for (int j = 1; j < G; ++j) best = acc[j] > best ? acc[j] : best;
-    bound[(static_cast<int64_t>(tok[t]) * hkv + g) * n_pages + p0 + pi] = best;
+    bound[(static_cast<int64_t>(t0 + tl) * hkv + g) * n_pages + p0 + pi] = best;
   }
 }
 
@@ -474,7 +507,9 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
 #define FB_BOUND_G(TT, GG)                                                                      \
   hipLaunchKernelGGL((page_bound_g_kernel<TT, GG, 8 / ((GG + 3) / 4)>),                         \
                      dim3(grid.x, grid.y, (n_q + 8 / ((GG + 3) / 4) - 1) / (8 / ((GG + 3) / 4))), \
-                     dim3(256), (8 / ((GG + 3) / 4) * GG * d + 2 * kPagesPerBlock * (d + 1)) * 4, s, \
+                     dim3(256),                                                                 \
+                     8 / ((GG + 3) / 4) * GG * d * 4 +                                          \
+                         2 * kPagesPerBlock * bound_row_stride<TT>(d) * sizeof(TT), s,          \
                      static_cast<const TT*>(q), q_st, q_sh, static_cast<const TT*>(kmin),       \
                      static_cast<const TT*>(kmax), n_q, hkv, d, n_pages, page_cap, active, bound)
   if (dt == FB_BF16 && G == 4) FB_BOUND_G(uint16_t, 4);
