@@ -47,6 +47,9 @@ namespace {
 #ifndef FB_ROWS_MAX_DYN
 #define FB_ROWS_MAX_DYN 8         // key chunks a masked many-rows pass may take
 #endif
+#ifndef FB_TEXT_FUSE_REDUCE
+#define FB_TEXT_FUSE_REDUCE 1   // text steps: the in-block kernel merges the split-K partials
+#endif
 constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights in LDS
 constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
 constexpr int64_t kMinTilesMfma = FB_PREFIX_MIN_TILES;   // 32-token tiles per chunk (4 waves)
@@ -229,14 +232,21 @@ size_t prefix_ws_bytes(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
 
 fb_status dev(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_DEVICE; }
 
-// Extra work a sparse step folds into its GATHER pass: the token
-// classification inside the selection prep (am) and the q_prev <- q_cur copy
-// inside the reduce (q_src -> q_dst).
+// Extra work a step folds into a prefix pass: for a sparse GATHER step, the
+// token classification inside the selection prep (am) and the q_prev <- q_cur
+// copy inside the reduce (q_src -> q_dst); for a dense text step, the reduce
+// itself handed to the in-block kernel (defer).
 struct PrefixHooks {
   const ActiveFromMse* am;
   const void* q_src; int64_t q_st, q_sh;
   void* q_dst; int q_esize;
+  ReduceParams* defer;          // dense pass: fill this and leave the reduce to the caller
 };
+
+bool kv_head_major(const fb_attn_shape& s, const fb_tensor& k, const fb_tensor& v) {
+  return s.n_kv_heads == 1 || ((k.n_tok <= 1 || k.stride_head >= k.n_tok * k.stride_tok) &&
+                               (v.n_tok <= 1 || v.stride_head >= v.n_tok * v.stride_tok));
+}
 
 fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor& k,
                      const fb_tensor& v, const uint8_t* mask, const fb_page_sel* sel, float* a_out,
@@ -244,10 +254,7 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
                      hipStream_t stream, const PrefixHooks* hooks = nullptr) {
   const int64_t n_q = q.n_tok, n_kv = k.n_tok;
   const int mode = sel ? sel->mode : FB_SEL_DENSE;
-  const bool head_major = s.n_kv_heads == 1 ||
-                          ((k.n_tok <= 1 || k.stride_head >= k.n_tok * k.stride_tok) &&
-                           (v.n_tok <= 1 || v.stride_head >= v.n_tok * v.stride_tok));
-  const PrefixPlan pl = plan_prefix(s, n_q, n_kv, sel, head_major);
+  const PrefixPlan pl = plan_prefix(s, n_q, n_kv, sel, kv_head_major(s, k, v));
   if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;
   if (pl.ws_bytes > 0 && !aligned16(ws)) return FB_ERR_INVALID_ARGUMENT;
 
@@ -392,6 +399,11 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
     rp.res_a = a_res;
     rp.res_l = l_res;
   }
+  if (hooks && hooks->defer) {
+    if (mode != FB_SEL_DENSE || dyn) return FB_ERR_UNSUPPORTED;
+    *hooks->defer = rp;
+    return FB_OK;
+  }
   return dev(launch_prefix_reduce(rp, stream));
 }
 
@@ -417,52 +429,21 @@ fb_status validate_prefix(const fb_attn_shape* shape, const fb_tensor& q, const 
   return FB_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* fb_status_string(fb_status s) {
-  switch (s) {
-    case FB_OK: return "ok";
-    case FB_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case FB_ERR_UNSUPPORTED: return "unsupported configuration";
-    case FB_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-    case FB_ERR_DEVICE: return "device (HIP) error";
-  }
-  return "unknown status";
+// true when the in-block pass of n_q block queries takes the one-wave-per-row
+// kernel (which can also merge a dense pass's split-K partials)
+bool block_rows_path(const fb_attn_shape& s, int64_t n_q) {
+  const int G = s.n_q_heads / s.n_kv_heads;
+  return s.dtype == FB_BF16 && s.head_dim == 128 && n_q * G >= FB_ROWS_MIN_ROWS;
+}
+bool block_small_path(const fb_attn_shape& s, int64_t n_q) {
+  return !block_rows_path(s, n_q) && n_q <= 65535;
 }
 
-int fb_abi_version(void) { return FB_ABI_VERSION; }
-
-size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t n_kv,
-                                const fb_page_sel* sel) {
-  if (check_shape(shape) != FB_OK || n_q < 1 || n_kv < 0) return 0;
-  if (check_sel(sel, *shape, n_q, n_kv) != FB_OK) return 0;
-  return prefix_ws_bytes(*shape, n_q, n_kv, sel);
-}
-
-fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k, fb_tensor v,
-                         const uint8_t* head_reuse_mask, const fb_page_sel* sel, float* a_out,
-                         float* l_out, float* a_res, float* l_res, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
-  fb_status st = validate_prefix(shape, q, k, v, sel, a_out, l_out, a_res, l_res);
-  if (st != FB_OK) return st;
-  return run_prefix(*shape, q, k, v, head_reuse_mask, sel, a_out, l_out, a_res, l_res, ws,
-                    ws_bytes, stream);
-}
-
-size_t fb_block_attn_merge_workspace(const fb_attn_shape* shape, int64_t n_q) {
-  (void)shape;
-  (void)n_q;
-  return 0;
-}
-
-fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk, fb_tensor k_blk,
-                              fb_tensor v_blk, const float* a_out, const float* l_out,
-                              float* a_full, float* l_full, float* a_in, float* l_in, void* ws,
-                              size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const fb_tensor& k_blk,
+                      const fb_tensor& v_blk, const float* a_out, const float* l_out,
+                      float* a_full, float* l_full, float* a_in, float* l_in,
+                      const ReduceParams* fused, const uint8_t* fused_mask, float* cache_a,
+                      float* cache_l, hipStream_t stream) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   const int d = shape->head_dim;
@@ -473,7 +454,8 @@ fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk, fb_te
   if (!a_out || !l_out || !a_full) return FB_ERR_INVALID_ARGUMENT;
   if (q_blk.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
-  if (shape->dtype == FB_BF16 && d == 128 && q_blk.n_tok * G >= FB_ROWS_MIN_ROWS) {
+  if (fused && !block_small_path(*shape, q_blk.n_tok)) return FB_ERR_UNSUPPORTED;
+  if (block_rows_path(*shape, q_blk.n_tok)) {
     // many rows: MFMA pass with the merge in its epilogue (16-byte row access)
     if (!aligned16(a_out) || !aligned16(a_full) || (a_in && !aligned16(a_in)))
       return FB_ERR_INVALID_ARGUMENT;
@@ -530,7 +512,66 @@ fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk, fb_te
   bp.l_full = l_full;
   bp.a_in = a_in;
   bp.l_in = l_in;
+  if (fused) {
+    bp.part_a = fused->part_a;
+    bp.part_l = fused->part_l;
+    bp.n_chunks = fused->n_chunks;
+    bp.rows = fused->rows;
+    bp.mask = fused_mask;
+    bp.cache_a = cache_a;
+    bp.cache_l = cache_l;
+  }
   return dev(launch_block_small(bp, shape->dtype, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fb_status_string(fb_status s) {
+  switch (s) {
+    case FB_OK: return "ok";
+    case FB_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FB_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FB_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FB_ERR_DEVICE: return "device (HIP) error";
+  }
+  return "unknown status";
+}
+
+int fb_abi_version(void) { return FB_ABI_VERSION; }
+
+size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t n_kv,
+                                const fb_page_sel* sel) {
+  if (check_shape(shape) != FB_OK || n_q < 1 || n_kv < 0) return 0;
+  if (check_sel(sel, *shape, n_q, n_kv) != FB_OK) return 0;
+  return prefix_ws_bytes(*shape, n_q, n_kv, sel);
+}
+
+fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k, fb_tensor v,
+                         const uint8_t* head_reuse_mask, const fb_page_sel* sel, float* a_out,
+                         float* l_out, float* a_res, float* l_res, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  fb_status st = validate_prefix(shape, q, k, v, sel, a_out, l_out, a_res, l_res);
+  if (st != FB_OK) return st;
+  return run_prefix(*shape, q, k, v, head_reuse_mask, sel, a_out, l_out, a_res, l_res, ws,
+                    ws_bytes, stream);
+}
+
+size_t fb_block_attn_merge_workspace(const fb_attn_shape* shape, int64_t n_q) {
+  (void)shape;
+  (void)n_q;
+  return 0;
+}
+
+fb_status fb_block_attn_merge(const fb_attn_shape* shape, fb_tensor q_blk, fb_tensor k_blk,
+                              fb_tensor v_blk, const float* a_out, const float* l_out,
+                              float* a_full, float* l_full, float* a_in, float* l_in, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return block_merge(shape, q_blk, k_blk, v_blk, a_out, l_out, a_full, l_full, a_in, l_in,
+                     nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 size_t fb_reuse_decide_workspace(const fb_reuse_args* a) {
@@ -822,6 +863,8 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
   if ((rc = check_tensor(a->v_blk, n_q, s.n_kv_heads, d)) != FB_OK) return rc;
   if (fb_step_workspace(st) > st->ws_bytes) return FB_ERR_WORKSPACE_TOO_SMALL;
   const bool first = st->step == 0;
+  ReduceParams fused;                      // a dense pass's reduce left to the in-block kernel
+  bool has_fused = false;
 
   switch (st->mode) {
     case FB_STEP_TEXT: {
@@ -834,9 +877,27 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
                             stream));
       if (rc != FB_OK) return rc;
       if (force != 1) {
-        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, st->mask, nullptr, st->a_out,
-                            st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream);
-        if (rc != FB_OK) return rc;
+        // with split-K partials and the one-wave in-block kernel, that kernel
+        // merges the partials itself: the reduce launch is saved
+        const PrefixPlan pl = plan_prefix(s, n_q, st->k_prefix.n_tok, nullptr,
+                                          kv_head_major(s, st->k_prefix, st->v_prefix));
+        if (FB_TEXT_FUSE_REDUCE && (pl.path == PATH_MFMA || pl.path == PATH_GENERIC) &&
+            !pl.direct && pl.n_chunks > 0 && block_small_path(s, n_q)) {
+          rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, st->a_out,
+                               st->l_out, nullptr, nullptr);
+          if (rc != FB_OK) return rc;
+          PrefixHooks hk;
+          memset(&hk, 0, sizeof(hk));
+          hk.defer = &fused;
+          rc = run_prefix(s, a->q_blk, st->k_prefix, st->v_prefix, st->mask, nullptr, st->a_out,
+                          st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream, &hk);
+          if (rc != FB_OK) return rc;
+          has_fused = true;
+        } else {
+          rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, st->mask, nullptr,
+                              st->a_out, st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream);
+          if (rc != FB_OK) return rc;
+        }
       }
       break;
     }
@@ -977,8 +1038,9 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
     default:
       return FB_ERR_INVALID_ARGUMENT;
   }
-  rc = fb_block_attn_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full,
-                           a->l_full, nullptr, nullptr, nullptr, 0, stream);
+  rc = block_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full, a->l_full,
+                   nullptr, nullptr, has_fused ? &fused : nullptr, st->mask, st->a_out, st->l_out,
+                   stream);
   if (rc != FB_OK) return rc;
   st->step += 1;
   return FB_OK;

@@ -216,6 +216,13 @@ struct BlockParams {
   float scale_log2;
   const float* a_out; const float* l_out;
   float* a_full; float* l_full; float* a_in; float* l_in;
+  // optional (part_l != NULL): the split-K merge of a dense prefix pass done
+  // here instead of in its own reduce launch. Rows of heads with mask[h] = 0
+  // (or no mask) merge their n_chunks partials (chunk stride rows), use the
+  // result as the cached pair and store it to cache_a / cache_l; rows of
+  // heads with mask[h] = 1 read the cached pair as usual.
+  const float* part_a; const float* part_l; int n_chunks; int64_t rows;
+  const uint8_t* mask; float* cache_a; float* cache_l;
 };
 hipError_t launch_block_small(const BlockParams& p, fb_dtype dt, hipStream_t s);
 

@@ -26,6 +26,16 @@ template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);
 }
 
+// element e of a 16-byte group of T values, as float
+template <typename T> __device__ __forceinline__ float vec_elem(u32x4v w, int e);
+template <> __device__ __forceinline__ float vec_elem<float>(u32x4v w, int e) {
+  return __uint_as_float(w[e]);
+}
+template <> __device__ __forceinline__ float vec_elem<uint16_t>(u32x4v w, int e) {
+  const uint32_t x = w[e >> 1];
+  return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -37,6 +47,78 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+constexpr int kMaxMergeChunks = 1024;            // the host's split-K chunk limit
+
+// The split-K merge of one row (one wave; lane owns dims lane + 64 i): max of
+// the chunks' L, weights e^{L_c - M} (0 for empty chunks), S = their sum in
+// chunk order, and per dim the weighted sum of the normalised partials over
+// the first and the second half of the chunks, each in chunk order, then
+// added: A = (that sum) / S, L = M + ln S; A = 0, L = -inf if every chunk is
+// empty. The order of the operations is the reduce pass's.
+template <int NPL>
+__device__ __forceinline__ void merge_partials(const BlockParams& p, int64_t row, int lane,
+                                               float* wts, float (&a)[NPL], float& l) {
+  const int nc = p.n_chunks;
+  float m = kNegInf;
+  for (int ch = lane; ch < nc; ch += 64) m = fmaxf(m, p.part_l[ch * p.rows + row]);
+  m = wave_max(m);
+  for (int ch = lane; ch < nc; ch += 64) {
+    const float L = p.part_l[ch * p.rows + row];
+    wts[ch] = L == kNegInf ? 0.f : expf(L - m);
+  }
+  __syncthreads();
+  float S = 0.f;
+  for (int ch = 0; ch < nc; ++ch) S += wts[ch];
+  const int64_t cs = p.rows * NPL * 64;            // chunk stride
+  const int mid = (nc + 1) / 2;
+  const float* pa = p.part_a + row * NPL * 64 + lane;
+  // the two halves advance together, 16 chunks each per round, so a round
+  // has 2 x 16 x NPL loads in flight; each half still adds in chunk order
+  float acc[2][NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) acc[0][i] = acc[1][i] = 0.f;
+  auto batch = [&](int hf, int ch) {               // 16 chunks of one half
+    float v[16][NPL];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) v[u][i] = pa[(ch + u) * cs + 64 * i];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) acc[hf][i] += wts[ch + u] * v[u][i];
+  };
+  int ch0 = 0, ch1 = mid;
+  for (; ch0 + 16 <= mid && ch1 + 16 <= nc; ch0 += 16, ch1 += 16) {
+    float v0[16][NPL], v1[16][NPL];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        v0[u][i] = pa[(ch0 + u) * cs + 64 * i];
+        v1[u][i] = pa[(ch1 + u) * cs + 64 * i];
+      }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        acc[0][i] += wts[ch0 + u] * v0[u][i];
+        acc[1][i] += wts[ch1 + u] * v1[u][i];
+      }
+  }
+  for (; ch0 + 16 <= mid; ch0 += 16) batch(0, ch0);
+  for (; ch1 + 16 <= nc; ch1 += 16) batch(1, ch1);
+  for (; ch0 < mid; ++ch0)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) acc[0][i] += wts[ch0] * pa[ch0 * cs + 64 * i];
+  for (; ch1 < nc; ++ch1)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) acc[1][i] += wts[ch1] * pa[ch1 * cs + 64 * i];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) a[i] = m != kNegInf ? (acc[0][i] + acc[1][i]) / S : 0.f;
+  l = m != kNegInf ? m + logf(S) : kNegInf;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
   constexpr int NPL = D / 64;
@@ -46,10 +128,34 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
   const int g = h / p.group;
   __shared__ float qs[D];
   __shared__ float ps[64];
+  __shared__ float wts[kMaxMergeChunks];
 
   const T* qrow = static_cast<const T*>(p.q) + static_cast<int64_t>(t) * p.q_st +
                   static_cast<int64_t>(h) * p.q_sh;
-  for (int c = lane; c < D; c += 64) qs[c] = ld<T>(qrow + c);
+  const int64_t row = static_cast<int64_t>(t) * p.hq + h;
+  float a_out[NPL];
+  float l_out;
+  if (p.part_l && !(p.mask && p.mask[h])) {
+    // a fresh prefix pass: merge this row's split-K partials (the same
+    // operations in the same order as the reduce pass) into the pair
+    merge_partials<NPL>(p, row, lane, wts, a_out, l_out);
+    p.cache_l[row] = l_out;                        // (every lane writes the same value)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) p.cache_a[row * D + lane + 64 * i] = a_out[i];
+  } else {
+    // the cached pair, loaded now so its latency hides behind the pass
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) a_out[i] = p.a_out[row * D + lane + 64 * i];
+    l_out = p.l_out[row];
+  }
+  {
+    constexpr int kV = 16 / sizeof(T);             // the query row as 16-byte groups
+    if (lane < D / kV) {
+      const u32x4v w = *reinterpret_cast<const u32x4v*>(qrow + lane * kV);
+#pragma unroll
+      for (int e = 0; e < kV; ++e) qs[lane * kV + e] = vec_elem<T>(w, e);
+    }
+  }
   __syncthreads();
 
   const T* kb = static_cast<const T*>(p.k) + static_cast<int64_t>(g) * p.k_sh;
@@ -62,10 +168,23 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
     const int j = base + lane;
     float x = kNegInf;
     if (j < p.n_q) {
+      // the key row arrives as 16-byte loads issued together (256 bytes a
+      // round: one round for a bf16 row of 128), then the dot product runs
+      // from registers in dim order
       const T* kr = kb + static_cast<int64_t>(j) * p.k_st;
+      constexpr int kR = (256 / sizeof(T)) < D ? 256 / sizeof(T) : D;   // dims per round
+      constexpr int kV = 16 / sizeof(T);
       float acc = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < D; ++c) acc += qs[c] * ld<T>(kr + c);
+#pragma unroll
+      for (int c0 = 0; c0 < D; c0 += kR) {
+        u32x4v kv[kR / kV];
+#pragma unroll
+        for (int u = 0; u < kR / kV; ++u) kv[u] = *reinterpret_cast<const u32x4v*>(kr + c0 + u * kV);
+#pragma unroll
+        for (int u = 0; u < kR / kV; ++u)
+#pragma unroll
+          for (int e = 0; e < kV; ++e) acc += qs[c0 + u * kV + e] * vec_elem<T>(kv[u], e);
+      }
       x = acc * p.scale_log2;
     }
     const float mnew = fmaxf(m, wave_max(x));
@@ -87,10 +206,8 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
     __syncthreads();
   }
 
-  const int64_t row = static_cast<int64_t>(t) * p.hq + h;
   const float inv = 1.f / l;                       // n_q >= 1, so l >= 1
   const float l_in = (m + log2f(l)) * kLn2;
-  const float l_out = p.l_out[row];
   const float mm = fmaxf(l_out, l_in);
   const float w_out = l_out == kNegInf ? 0.f : expf(l_out - mm);
   const float w_in = expf(l_in - mm);
@@ -99,8 +216,7 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
   for (int i = 0; i < NPL; ++i) {
     const int c = lane + 64 * i;
     const float a_in = o[i] * inv;
-    const float a_out = p.a_out[row * D + c];
-    const float a_full = w_out == 0.f ? a_in : (w_out * a_out + w_in * a_in) / den;
+    const float a_full = w_out == 0.f ? a_in : (w_out * a_out[i] + w_in * a_in) / den;
     p.a_full[row * D + c] = a_full;
     if (p.a_in) p.a_in[row * D + c] = a_in;
   }
