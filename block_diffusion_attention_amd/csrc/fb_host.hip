@@ -48,7 +48,7 @@ namespace {
 #define FB_ROWS_MAX_DYN 8         // key chunks a masked many-rows pass may take
 #endif
 #ifndef FB_TEXT_FUSE_REDUCE
-#define FB_TEXT_FUSE_REDUCE 1   // text steps: the in-block kernel merges the split-K partials
+#define FB_TEXT_FUSE_REDUCE 1   // text and sparse steps: the in-block kernel merges the partials
 #endif
 constexpr int64_t kMaxChunks = 1024;      // the reduce keeps per-chunk weights in LDS
 constexpr int64_t kTargetWorkgroups = FB_PREFIX_TARGET_WGS;  // per resident round (x occupancy)
@@ -234,8 +234,8 @@ fb_status dev(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_DEVICE; }
 
 // Extra work a step folds into a prefix pass: for a sparse GATHER step, the
 // token classification inside the selection prep (am) and the q_prev <- q_cur
-// copy inside the reduce (q_src -> q_dst); for a dense text step, the reduce
-// itself handed to the in-block kernel (defer).
+// copy inside the reduce (q_src -> q_dst); for a dense text step or a sparse
+// GATHER step, the reduce itself handed to the in-block kernel (defer).
 struct PrefixHooks {
   const ActiveFromMse* am;
   const void* q_src; int64_t q_st, q_sh;
@@ -400,7 +400,7 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
     rp.res_l = l_res;
   }
   if (hooks && hooks->defer) {
-    if (mode != FB_SEL_DENSE || dyn) return FB_ERR_UNSUPPORTED;
+    if (mode == FB_SEL_SPLIT || dyn) return FB_ERR_UNSUPPORTED;
     *hooks->defer = rp;
     return FB_OK;
   }
@@ -442,8 +442,8 @@ bool block_small_path(const fb_attn_shape& s, int64_t n_q) {
 fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const fb_tensor& k_blk,
                       const fb_tensor& v_blk, const float* a_out, const float* l_out,
                       float* a_full, float* l_full, float* a_in, float* l_in,
-                      const ReduceParams* fused, const uint8_t* fused_mask, float* cache_a,
-                      float* cache_l, hipStream_t stream) {
+                      const ReduceParams* fused, float* cache_a, float* cache_l, void* q_dst,
+                      hipStream_t stream) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   const int d = shape->head_dim;
@@ -517,10 +517,14 @@ fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const 
     bp.part_l = fused->part_l;
     bp.n_chunks = fused->n_chunks;
     bp.rows = fused->rows;
-    bp.mask = fused_mask;
+    bp.mask = fused->mask;
+    bp.active = fused->active;
+    bp.res_a = fused->res_a;
+    bp.res_l = fused->res_l;
     bp.cache_a = cache_a;
     bp.cache_l = cache_l;
   }
+  bp.q_dst = q_dst;
   return dev(launch_block_small(bp, shape->dtype, stream));
 }
 
@@ -863,8 +867,9 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
   if ((rc = check_tensor(a->v_blk, n_q, s.n_kv_heads, d)) != FB_OK) return rc;
   if (fb_step_workspace(st) > st->ws_bytes) return FB_ERR_WORKSPACE_TOO_SMALL;
   const bool first = st->step == 0;
-  ReduceParams fused;                      // a dense pass's reduce left to the in-block kernel
+  ReduceParams fused;                      // a pass's reduce left to the in-block kernel
   bool has_fused = false;
+  void* q_dst = nullptr;                   // the in-block kernel's query copy (sparse steps)
 
   switch (st->mode) {
     case FB_STEP_TEXT: {
@@ -1005,8 +1010,17 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         const ActiveFromMse am = {st->q_prev, a->q_blk.ptr, a->q_blk.stride_tok,
                                   a->q_blk.stride_head, s.dtype, hq, d, st->pct, st->mse,
                                   st->active};
-        const PrefixHooks hk = {&am, a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head,
-                                st->q_prev, s.dtype == FB_BF16 ? 2 : 4};
+        // and, with the one-wave in-block kernel, that kernel merges the
+        // partials and copies the queries: no reduce launch
+        PrefixHooks hk = {&am, a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head,
+                          st->q_prev, s.dtype == FB_BF16 ? 2 : 4, nullptr};
+        if (FB_TEXT_FUSE_REDUCE && block_small_path(s, n_q)) {
+          hk.q_src = nullptr;
+          hk.q_dst = nullptr;
+          hk.defer = &fused;
+          has_fused = true;
+          q_dst = st->q_prev;
+        }
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
         rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, &sel, st->a_out, st->l_out,
@@ -1039,7 +1053,7 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       return FB_ERR_INVALID_ARGUMENT;
   }
   rc = block_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full, a->l_full,
-                   nullptr, nullptr, has_fused ? &fused : nullptr, st->mask, st->a_out, st->l_out,
+                   nullptr, nullptr, has_fused ? &fused : nullptr, st->a_out, st->l_out, q_dst,
                    stream);
   if (rc != FB_OK) return rc;
   st->step += 1;

@@ -223,6 +223,11 @@ struct BlockParams {
   // heads with mask[h] = 1 read the cached pair as usual.
   const float* part_a; const float* part_l; int n_chunks; int64_t rows;
   const uint8_t* mask; float* cache_a; float* cache_l;
+  // ... of a sparse GATHER pass: only rows of tokens with active[t] = 1 merge
+  // (the others keep the cached pair), with the cached residual (res_a,
+  // res_l; nullable) as one more weighted term
+  const uint8_t* active; const float* res_a; const float* res_l;
+  void* q_dst;                  // nullable: every row also stores its query to q_dst[t][h][:]
 };
 hipError_t launch_block_small(const BlockParams& p, fb_dtype dt, hipStream_t s);
 

@@ -49,12 +49,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 constexpr int kMaxMergeChunks = 1024;            // the host's split-K chunk limit
 
-// The split-K merge of one row (one wave; lane owns dims lane + 64 i): max of
-// the chunks' L, weights e^{L_c - M} (0 for empty chunks), S = their sum in
-// chunk order, and per dim the weighted sum of the normalised partials over
-// the first and the second half of the chunks, each in chunk order, then
-// added: A = (that sum) / S, L = M + ln S; A = 0, L = -inf if every chunk is
-// empty. The order of the operations is the reduce pass's.
+// The split-K merge of one row (one wave; lane owns dims lane + 64 i), with
+// the operations of the reduce pass in its order: M = the chunks' max L, Mr =
+// the cached residual's L (-inf without one), Mall = max(M, Mr); chunk
+// weights e^{L_c - Mall} (0 for empty chunks) summed in chunk order (S); per
+// dim the weighted partials summed over the first and the second half of
+// the chunks, each in chunk order, then added (acc); the residual enters
+// with weight e^{L_res - Mr} (Sr, accr) scaled by e^{Mr - Mall}:
+// A = (acc + accr w) / (S + Sr w), L = Mall + ln(S + Sr w); A = 0, L = -inf
+// when nothing is there.
 template <int NPL>
 __device__ __forceinline__ void merge_partials(const BlockParams& p, int64_t row, int lane,
                                                float* wts, float (&a)[NPL], float& l) {
@@ -62,13 +65,19 @@ __device__ __forceinline__ void merge_partials(const BlockParams& p, int64_t row
   float m = kNegInf;
   for (int ch = lane; ch < nc; ch += 64) m = fmaxf(m, p.part_l[ch * p.rows + row]);
   m = wave_max(m);
+  const float l_res = p.res_l ? p.res_l[row] : kNegInf;
+  const float mr = l_res;
+  const float mall = fmaxf(m, mr);
   for (int ch = lane; ch < nc; ch += 64) {
     const float L = p.part_l[ch * p.rows + row];
-    wts[ch] = L == kNegInf ? 0.f : expf(L - m);
+    wts[ch] = L == kNegInf ? 0.f : expf(L - mall);
   }
+  const float wr = l_res == kNegInf ? 0.f : expf(l_res - mr);
   __syncthreads();
   float S = 0.f;
   for (int ch = 0; ch < nc; ++ch) S += wts[ch];
+  const float Sr = p.res_l ? 0.f + wr : 0.f;
+  const float wrr = mr != kNegInf ? expf(mr - mall) : 0.f;
   const int64_t cs = p.rows * NPL * 64;            // chunk stride
   const int mid = (nc + 1) / 2;
   const float* pa = p.part_a + row * NPL * 64 + lane;
@@ -115,8 +124,12 @@ __device__ __forceinline__ void merge_partials(const BlockParams& p, int64_t row
 #pragma unroll
     for (int i = 0; i < NPL; ++i) acc[1][i] += wts[ch1] * pa[ch1 * cs + 64 * i];
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) a[i] = m != kNegInf ? (acc[0][i] + acc[1][i]) / S : 0.f;
-  l = m != kNegInf ? m + logf(S) : kNegInf;
+  for (int i = 0; i < NPL; ++i) {
+    float accr = 0.f;
+    if (p.res_l) accr += wr * p.res_a[row * NPL * 64 + lane + 64 * i];
+    a[i] = mall != kNegInf ? ((acc[0][i] + acc[1][i]) + accr * wrr) / (S + Sr * wrr) : 0.f;
+  }
+  l = mall != kNegInf ? mall + logf(S + Sr * wrr) : kNegInf;
 }
 
 template <typename T, int D>
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
   const int64_t row = static_cast<int64_t>(t) * p.hq + h;
   float a_out[NPL];
   float l_out;
-  if (p.part_l && !(p.mask && p.mask[h])) {
+  if (p.part_l && !(p.mask && p.mask[h]) && !(p.active && !p.active[t])) {
     // a fresh prefix pass: merge this row's split-K partials (the same
     // operations in the same order as the reduce pass) into the pair
     merge_partials<NPL>(p, row, lane, wts, a_out, l_out);
@@ -154,6 +167,8 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
       const u32x4v w = *reinterpret_cast<const u32x4v*>(qrow + lane * kV);
 #pragma unroll
       for (int e = 0; e < kV; ++e) qs[lane * kV + e] = vec_elem<T>(w, e);
+      if (p.q_dst)                                 // (after every read of q_dst this step)
+        *reinterpret_cast<u32x4v*>(static_cast<T*>(p.q_dst) + row * D + lane * kV) = w;
     }
   }
   __syncthreads();
