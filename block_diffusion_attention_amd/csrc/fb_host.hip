@@ -1039,10 +1039,27 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         }
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
-        rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
-                            st->l_out, reselect ? nullptr : st->a_res,
-                            reselect ? nullptr : st->l_res, st->ws, st->ws_bytes, stream);
-        if (rc != FB_OK) return rc;
+        float* ar = reselect ? nullptr : st->a_res;
+        float* lr = reselect ? nullptr : st->l_res;
+        const PrefixPlan gp = plan_prefix(s, n_q, st->k_prefix.n_tok, &sel,
+                                          kv_head_major(s, st->k_prefix, st->v_prefix));
+        if (FB_TEXT_FUSE_REDUCE && block_small_path(s, n_q) && gp.n_chunks > 0 && !gp.direct) {
+          // the in-block kernel merges the partials: no reduce launch
+          rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, &sel, st->a_out,
+                               st->l_out, ar, lr);
+          if (rc != FB_OK) return rc;
+          PrefixHooks hk;
+          memset(&hk, 0, sizeof(hk));
+          hk.defer = &fused;
+          rc = run_prefix(s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
+                          st->l_out, ar, lr, st->ws, st->ws_bytes, stream, &hk);
+          if (rc != FB_OK) return rc;
+          has_fused = true;
+        } else {
+          rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
+                              st->l_out, ar, lr, st->ws, st->ws_bytes, stream);
+          if (rc != FB_OK) return rc;
+        }
       } else {
         rc = token_step(0, 0);                     // forced reuse: no token active
         if (rc != FB_OK) return rc;
