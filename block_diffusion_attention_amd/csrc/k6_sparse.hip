@@ -74,12 +74,35 @@ __global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* pages, i
   for (int i = threadIdx.x; i < words; i += 256) bitmap[row * words + i] = wl[i];
 }
 
+// Inclusive prefix sum of c over threads 0..255 of the workgroup, by wave
+// shuffles and one exchange of the four wave totals in wsum (exact integer
+// sums); total = the sum over those threads. Every thread of the workgroup
+// calls it (threads from 256 on pass c = 0 and ignore the result); it holds
+// two barriers, the second before wsum can be written again.
+__device__ __forceinline__ int scan256(int c, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63 && wave < 4) wsum[wave] = x;
+  __syncthreads();
+  int pre = 0;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) pre += w < wave ? wsum[w] : 0;
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return x + pre;
+}
+
 // Union over the active tokens of their selected pages, per KV group g, as an
 // ascending page list and its length. One workgroup per g.
 __global__ __launch_bounds__(256) void sel_union_kernel(const uint32_t* bitmap, const uint8_t* active,
                                                         int n_q, int hkv, int words,
                                                         int32_t* ulist, int32_t* ucnt, int n_pages) {
-  __shared__ int scan[256];
+  __shared__ int scan[4];                          // wave totals of scan256
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   int base = 0;
@@ -90,22 +113,14 @@ __global__ __launch_bounds__(256) void sel_union_kernel(const uint32_t* bitmap, 
       for (int t = 0; t < n_q; ++t)
         if (!active || active[t]) u |= bitmap[(static_cast<int64_t>(t) * hkv + g) * words + w];
     const int c = __popc(u);
-    scan[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {            // inclusive scan
-      const int v = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    int pos = base + scan[tid] - c;
+    int total;
+    int pos = base + scan256(c, scan, total) - c;
     while (u) {
       const int b = __builtin_ctz(u);
       ulist[static_cast<int64_t>(g) * n_pages + pos++] = w * 32 + b;
       u &= u - 1;
     }
-    base += scan[255];
-    __syncthreads();
+    base += total;
   }
   if (tid == 0) ucnt[g] = base;
 }
@@ -132,7 +147,7 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
                                                            int32_t* ulist, int32_t* ucnt) {
 #pragma clang fp contract(off)
   extern __shared__ uint32_t bm[];                 // [n_q][words], then the float64 sums
-  __shared__ int scan[256];
+  __shared__ int scan[4];                          // wave totals of scan256
   __shared__ double cutoff_s;
   __shared__ uint8_t act_s[1024];
   const int g = blockIdx.x;
@@ -219,22 +234,15 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
       for (int t = 0; t < n_q; ++t)
         if (act_s[t]) u |= bm[t * words + w];
     const int c = __popc(u);
-    if (scanner) scan[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {            // inclusive scan
-      const int v = scanner && tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      if (scanner) scan[tid] += v;
-      __syncthreads();
-    }
-    int pos = base + (scanner ? scan[tid] : 0) - c;
+    int total;
+    const int incl = scan256(c, scan, total);
+    int pos = base + (scanner ? incl : 0) - c;
     while (u) {
       const int b = __builtin_ctz(u);
       ulist[static_cast<int64_t>(g) * n_pages + pos++] = w * 32 + b;
       u &= u - 1;
     }
-    base += scan[255];
-    __syncthreads();
+    base += total;
   }
   if (tid == 0) ucnt[g] = base;
 }
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(1024) void sel_prep_kernel(const int32_t* pages, in
                                                        uint32_t* bitmap, int32_t* ulist,
                                                        int32_t* ucnt) {
   extern __shared__ uint32_t bm[];                 // [n_q][words]
-  __shared__ int scan[256];
+  __shared__ int scan[4];                          // wave totals of scan256
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
@@ -292,22 +300,15 @@ __global__ __launch_bounds__(1024) void sel_prep_kernel(const int32_t* pages, in
       for (int t = 0; t < n_q; ++t)
         if (!active || active[t]) u |= bm[t * words + w];
     const int c = __popc(u);
-    if (scanner) scan[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {            // inclusive scan
-      const int v = scanner && tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      if (scanner) scan[tid] += v;
-      __syncthreads();
-    }
-    int pos = base + (scanner ? scan[tid] : 0) - c;
+    int total;
+    const int incl = scan256(c, scan, total);
+    int pos = base + (scanner ? incl : 0) - c;
     while (u) {
       const int b = __builtin_ctz(u);
       ulist[static_cast<int64_t>(g) * n_pages + pos++] = w * 32 + b;
       u &= u - 1;
     }
-    base += scan[255];
-    __syncthreads();
+    base += total;
   }
   if (tid == 0) ucnt[g] = base;
 }
