@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
   __shared__ int hist[256];
   __shared__ int red[4];
   __shared__ unsigned long long sh_prefix;
-  __shared__ int sh_kk;
+  __shared__ int sh_kk, sh_h;
   if (active && !active[blockIdx.x]) return;       // a row of an inactive token
   const int tid = threadIdx.x;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * hkv + blockIdx.y;
@@ -429,6 +429,7 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
   uint64_t pmask = first == 0 ? 0ull : (first == 8 ? ~0ull : ~0ull << (64 - 8 * first));
   uint64_t prefix = lo & pmask;
   int kk = k;                                      // rank of T within the current group
+  int early = 0;                                   // 1: T = the group's max, 2: its min
   for (int pass = first; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
     hist[tid] = 0;
@@ -445,14 +446,37 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
     if (S >= kk && S - h < kk) {                   // exactly one byte value
       sh_prefix = prefix | (static_cast<uint64_t>(bv) << shift);
       sh_kk = kk - (S - h);
+      sh_h = h;
     }
     __syncthreads();
     prefix = sh_prefix;
     kk = sh_kk;
     pmask |= 255ull << shift;
+    // T is the group's largest key when it takes rank 1 in it, its smallest
+    // when it takes the last rank: one reduction ends the search
+    if (kk == 1 || kk == sh_h) {
+      early = kk == 1 ? 1 : 2;
+      break;
+    }
   }
-  const uint64_t T = prefix;
-  const int need_eq = kk;                          // ties at T to take, lowest ids first
+  uint64_t T = prefix;
+  if (early) {
+    uint64_t v = early == 1 ? 0ull : ~0ull;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (p0 + i < n_pages && (key[i] & pmask) == prefix)
+        v = early == 1 ? (key[i] > v ? key[i] : v) : (key[i] < v ? key[i] : v);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t u = __shfl_xor(v, o, 64);
+      v = early == 1 ? (u > v ? u : v) : (u < v ? u : v);
+    }
+    if ((tid & 63) == 0) sh_lo[tid >> 6] = v;
+    __syncthreads();
+    T = sh_lo[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) T = early == 1 ? (sh_lo[w] > T ? sh_lo[w] : T) : (sh_lo[w] < T ? sh_lo[w] : T);
+  }
   int gt = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
@@ -460,6 +484,8 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
     eq += key[i] == T ? 1 : 0;
   }
   int tot;
+  (void)block_exscan4(gt, red, tot);
+  const int need_eq = k - tot;                     // ties at T to take, lowest ids first
   const int eq_before = block_exscan4(eq, red, tot);
   int take_eq = need_eq - eq_before;
   take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
