@@ -175,9 +175,12 @@ def test_page_meta_and_select_bit_exact(fb, n_kv, page, k):
         assert np.array_equal(cpu(pages), OQ.topk_pages(rb, k))
 
 
-def test_page_select_ties_take_lower_ids(fb):
+@pytest.mark.parametrize("n_take", [1, 7, 31, 32])
+def test_page_select_ties_take_lower_ids(fb, n_take):
     # pages 10..40 are copies of page 5: their bounds tie exactly, and k puts
-    # the selection boundary inside the tied group
+    # the selection boundary inside the tied group (taking the first, some,
+    # all but one, or all of the 32 tied pages: the radix select ends on the
+    # group's maximum, runs every pass, or ends on its minimum)
     n_kv, page = 4096, 16
     cfg = W.SPARSE.with_(n_prefix=n_kv, page=page)
     kp, _ = W.prefix_kv(cfg)
@@ -190,10 +193,10 @@ def test_page_select_ties_take_lower_ids(fb):
     t, g = 3, 2
     row = rb[t, g]
     above = int(np.sum(row > row[5]))
-    k = above + 7                                   # 7 of the 32 tied pages
+    k = above + n_take
     ref = OQ.topk_pages(rb, k)
     tied = set(range(10, 41)) | {5}
-    assert len(tied & set(ref[t, g].tolist())) == 7
+    assert len(tied & set(ref[t, g].tolist())) == n_take
     shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
     n_pages = n_kv // page
     kmin = torch.empty(8, n_pages, 128, dtype=torch.bfloat16, device="cuda")
