@@ -75,6 +75,7 @@ struct PrefixPlan {
   size_t off_bm = 0, off_ul = 0, off_uc = 0;   // PATH_SPARSE: bitmaps, union list, union sizes
   int words = 0;
   int64_t n_pages = 0;
+  bool fits = true;            // false: more split-K chunks than the reduce's LDS holds
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -186,6 +187,9 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
       const int64_t lo = (n_tiles + sparse_max_tiles_per_chunk() - 1) / sparse_max_tiles_per_chunk();
       chunks = chunks > lo ? chunks : lo;
     }
+    // the reduce (and the in-block kernel's merge) keep one weight per chunk
+    // in LDS arrays of kMaxChunks entries: a longer split is refused
+    if (chunks > kMaxChunks) pl.fits = false;
     pl.tiles_per_chunk = (n_tiles + chunks - 1) / chunks;
     pl.n_chunks = static_cast<int>((n_tiles + pl.tiles_per_chunk - 1) / pl.tiles_per_chunk);
     if (pl.path == PATH_ROWS) {
@@ -255,6 +259,7 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   const int64_t n_q = q.n_tok, n_kv = k.n_tok;
   const int mode = sel ? sel->mode : FB_SEL_DENSE;
   const PrefixPlan pl = plan_prefix(s, n_q, n_kv, sel, kv_head_major(s, k, v));
+  if (!pl.fits) return FB_ERR_UNSUPPORTED;
   if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;
   if (pl.ws_bytes > 0 && !aligned16(ws)) return FB_ERR_INVALID_ARGUMENT;
 
@@ -949,6 +954,14 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       sel.page_size = st->page_size;
       sel.k_pages = st->k_pages;
       sel.pages = st->pages;
+      // a split the reduce cannot merge is refused before any launch
+      for (fb_sel_mode m : {FB_SEL_SPLIT, FB_SEL_GATHER}) {
+        sel.mode = m;
+        if (!plan_prefix(s, n_q, st->k_prefix.n_tok, &sel, false).fits ||
+            !plan_prefix(s, n_q, st->k_prefix.n_tok, &sel, true).fits)
+          return FB_ERR_UNSUPPORTED;
+      }
+      sel.mode = FB_SEL_DENSE;
       // the step's token bookkeeping: active flags (query MSE, mode 1, or a
       // constant, mode 0), then q_prev <- q_cur; one kernel for text-sized
       // blocks, else separate kernels (whose MSE reads contiguous queries)

@@ -126,8 +126,11 @@ typedef struct {
  *   K partials); may be NULL when that size is 0.                            *
  * Errors: INVALID_ARGUMENT on bad shape/stride/alignment/NULL, n_q < 1,     *
  *   n_kv < 0, k/v token counts that differ; UNSUPPORTED for head_dim not   *
- *   in {64,128}; WORKSPACE_TOO_SMALL. Page ids are device data and are not  *
- *   validated (see fb_page_sel).                                             *
+ *   in {64,128}, and for a SPLIT/GATHER selection on the bf16, d = 128,     *
+ *   page-size-multiple-of-16 kernel over more than 8,355,840 keys (the      *
+ *   split-K reduce merges at most 1024 chunks of 8,160 keys); nothing is    *
+ *   launched then. WORKSPACE_TOO_SMALL. Page ids are device data and are    *
+ *   not validated (see fb_page_sel).                                         *
  * ------------------------------------------------------------------------ */
 size_t fb_prefix_attn_workspace(const fb_attn_shape* shape, int64_t n_q,
                                 int64_t n_kv, const fb_page_sel* sel);

@@ -261,6 +261,37 @@ def test_sparse_plan_workspace_includes_selection_buffers(lib):
     assert ns > bitmaps and ng > bitmaps + 8 * 4096 * 4           # GATHER adds the union list
 
 
+def test_sparse_split_beyond_the_reduce_is_refused(lib):
+    # 9,000,000 keys in 32-token pages: 281,250 pages fit the selection bitmap,
+    # but at most 8,160 keys per chunk would need 1,103 split-K chunks, more
+    # than the 1,024 the reduce merges: refused before any launch
+    sh = shape()
+    q = ten(8, 32)
+    for mode in (fb.FB_SEL_SPLIT, fb.FB_SEL_GATHER):
+        sel = fb.fb_page_sel(mode, 32, 64, FAKE, None)
+        big = ten(9000000, 8)
+        assert prefix(lib, sh, q, big, big, sel=sel, ar=FAKE, lr=FAKE, ws=FAKE,
+                      wsb=1 << 40) == fb.FB_ERR_UNSUPPORTED
+        # the largest prefix that fits (1,024 chunks of 8,160 keys) reaches the
+        # workspace check instead
+        edge = ten(1024 * 8160, 8)
+        assert prefix(lib, sh, q, edge, edge, sel=sel, ar=FAKE, lr=FAKE, ws=FAKE,
+                      wsb=0) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+    st = fb.fb_step_state()
+    st.shape = sh
+    st.mode, st.n_q = fb.FB_STEP_SPARSE, 8
+    st.k_prefix = st.v_prefix = ten(9000000, 8)
+    st.a_out = st.l_out = st.mask = st.a_res = st.l_res = FAKE
+    st.pages = st.kmin = st.kmax = st.q_prev = st.active = FAKE
+    st.page_size, st.k_pages, st.pct = 32, 64, 25
+    st.ws, st.ws_bytes = FAKE, 1 << 40
+    args = fb.fb_step_args()
+    args.q_blk, args.k_blk, args.v_blk = ten(8, 32), ten(8, 8), ten(8, 8)
+    args.a_full, args.decision = FAKE, -1
+    assert lib.fb_step(C.byref(st), C.byref(args), None) == fb.FB_ERR_UNSUPPORTED
+    assert st.step == 0 and st.meta_ready == 0
+
+
 # ------------------------------------------------------ growing cache, no GPU
 
 def cache(cap=64, n=60, st=8 * 128, sh=128, k=FAKE, v=FAKE + (1 << 24)):
