@@ -58,7 +58,7 @@ class fb_proxy_args(C.Structure):
     _fields_ = [("n_tok", C.c_int32), ("d_model", C.c_int32), ("rank", C.c_int32),
                 ("dtype", C.c_int), ("x", C.c_void_p), ("x_stride", C.c_int64),
                 ("factor", C.c_void_p), ("cache", C.c_void_p), ("n_select", C.c_int32),
-                ("init", C.c_int32), ("key", C.c_void_p), ("selected", C.c_void_p),
+                ("init", C.c_int32), ("sim", C.c_void_p), ("selected", C.c_void_p),
                 ("mask", C.c_void_p), ("proxy", C.c_void_p), ("ws", C.c_void_p),
                 ("ws_bytes", C.c_size_t)]
 
@@ -276,7 +276,7 @@ def fb_proxy_decide(args, stream=None):
     _check("fb_proxy_decide", load().fb_proxy_decide(C.byref(args), stream_of(stream)))
 
 
-def proxy_args(x, factor, cache, mask, selected=None, n_select=0, init=False, key=None,
+def proxy_args(x, factor, cache, mask, selected=None, n_select=0, init=False, sim=None,
                proxy=None, ws=None):
     """fb_proxy_args of torch tensors: x [N, D], factor [D, r] (same dtype),
     cache [N, r] float64, mask [N] uint8, selected [n_select] int32."""
@@ -288,7 +288,7 @@ def proxy_args(x, factor, cache, mask, selected=None, n_select=0, init=False, ke
     a.x, a.x_stride, a.factor = x.data_ptr(), x.stride(0), factor.data_ptr()
     a.cache, a.mask, a.selected = ptr(cache), ptr(mask), ptr(selected)
     a.n_select, a.init = int(n_select), 1 if init else 0
-    a.key, a.proxy = ptr(key), ptr(proxy)
+    a.sim, a.proxy = ptr(sim), ptr(proxy)
     a.ws, a.ws_bytes = ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
     return a
 

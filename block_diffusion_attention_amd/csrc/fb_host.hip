@@ -735,11 +735,11 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
   fb_status rc = dev(launch_proxy_partials(a->x, a->x_stride, a->factor, a->dtype, a->n_tok,
                                            a->d_model, a->rank, part, stream));
   if (rc != FB_OK) return rc;
-  rc = dev(launch_proxy_keys(part, nb, a->n_tok, a->rank, a->init, a->cache, proxy, a->key,
+  rc = dev(launch_proxy_keys(part, nb, a->n_tok, a->rank, a->init, a->cache, proxy, a->sim,
                              neg_key, a->mask, stream));
   if (rc != FB_OK || a->init) return rc;
   if (a->n_select == 0) return dev(launch_fill_u8(a->mask, a->n_tok, 0, stream));
-  // the lowest keys are the largest negated keys (ties: lower id); the
+  // the lowest similarities are the largest negated ones (ties: lower id); the
   // top-k writes every token's mask byte
   rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, nullptr, a->selected, a->mask,
                             stream));

@@ -299,7 +299,7 @@ hipError_t launch_proxy_partials(const void* x, int64_t x_st, const void* factor
                                  int n_tok, int d_model, int rank, double* part, hipStream_t s);
 int proxy_n_blocks(int d_model);
 hipError_t launch_proxy_keys(const double* part, int n_blocks, int n_tok, int rank, int init,
-                             double* cache, double* proxy, double* key, double* neg_key,
+                             double* cache, double* proxy, double* sim, double* neg_key,
                              uint8_t* mask, hipStream_t s);
 hipError_t launch_proxy_scatter(const int32_t* selected, int n_select, int n_tok,
                                 const double* proxy, int rank, double* cache, hipStream_t s);

@@ -7,15 +7,15 @@
 // cosine with the proxy cached for that token, and the least similar tokens
 // are recomputed.
 //
-// Arithmetic, fixed so that every bit is reproducible:
-//  * p[t][i] = sum_c x[t][c] F[c][i] in float64, in blocks of 128
-//    consecutive c: each block summed in c order with fused multiply-add
-//    (a product of two bf16 or two fp32 values is exact in float64, so each
-//    step rounds once, as a multiply followed by an add would), the block
+// Arithmetic (float64; run to run the bits repeat, the order is fixed):
+//  * p[t][i] = sum_c x[t][c] F[c][i]: blocks of 128 consecutive c, each
+//    summed in c order with fused multiply-add (a product of two bf16 or two
+//    fp32 values is exact in float64, so each step rounds once), the block
 //    sums then added in block order;
-//  * key = sign(cos) cos^2 = dot^2 / (|p|^2 |c|^2), negated when dot < 0
-//    (and the quotient is not 0), with dot, |p|^2 and |c|^2 summed over i in
-//    order from separately rounded products; both norms 0 -> 1, one -> 0.
+//  * sim = dot / sqrt(|p|^2 |c|^2), clamped to [-1, 1], with dot, |p|^2 and
+//    |c|^2 summed over i in order; both norms 0 -> 1, one -> 0. A proxy equal
+//    to its cache gives dot = |p|^2 = |c|^2 and sqrt(dot^2) = dot exactly in
+//    binary floating point, so it scores exactly 1.
 //
 // The block partials are an fp64 FMA-bound contraction (N x D x r): each
 // workgroup takes 32 tokens x r dims of one 128-wide block, staged 32 c at a
@@ -185,11 +185,11 @@ __global__ __launch_bounds__(256) void proxy_partials_kernel(const T* x, int64_t
 }
 
 // Proxies from the block partials (block order), then either the cache fill
-// (init) or the ranking keys against the cache.
+// (init) or the cosine similarities against the cache.
 __global__ __launch_bounds__(256) void proxy_keys_kernel(const double* part, int n_blocks,
                                                          int n_tok, int rank, int init,
                                                          double* cache, double* proxy,
-                                                         double* key, double* neg_key,
+                                                         double* sim, double* neg_key,
                                                          uint8_t* mask) {
 #pragma clang fp contract(off)
   __shared__ double ps[kKeyTok * (kMaxRank + 1)];  // [kKeyTok][rank + 1]
@@ -228,17 +228,16 @@ __global__ __launch_bounds__(256) void proxy_keys_kernel(const double* part, int
       pp = pp + m2;
       cc = cc + m3;
     }
-    const double den = pp * cc;
     double k;
-    if (den == 0.0) {
+    if (pp == 0.0 || cc == 0.0) {
       k = (pp == 0.0 && cc == 0.0) ? 1.0 : 0.0;
     } else {
-      const double d2 = dot * dot;
-      const double q = d2 / den;
-      k = (dot < 0.0 && q != 0.0) ? -q : q;
+      const double den = pp * cc;
+      k = dot / __builtin_sqrt(den);
+      k = k > 1.0 ? 1.0 : (k < -1.0 ? -1.0 : k);
     }
     const int t = t0 + tid;
-    if (key) key[t] = k;
+    if (sim) sim[t] = k;
     neg_key[t] = -k;
   }
 }
@@ -287,10 +286,10 @@ hipError_t launch_proxy_partials(const void* x, int64_t x_st, const void* factor
 }
 
 hipError_t launch_proxy_keys(const double* part, int n_blocks, int n_tok, int rank, int init,
-                             double* cache, double* proxy, double* key, double* neg_key,
+                             double* cache, double* proxy, double* sim, double* neg_key,
                              uint8_t* mask, hipStream_t s) {
   hipLaunchKernelGGL(proxy_keys_kernel, dim3((n_tok + kKeyTok - 1) / kKeyTok), dim3(256), 0, s,
-                     part, n_blocks, n_tok, rank, init, cache, proxy, key, neg_key, mask);
+                     part, n_blocks, n_tok, rank, init, cache, proxy, sim, neg_key, mask);
   return hipGetLastError();
 }
 

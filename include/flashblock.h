@@ -274,18 +274,17 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
  * diag(sigma_r) of the value                                                *
  * projection's truncated SVD; cache [n_tok, rank] float64: the proxy kept   *
  * per token from the step it was last recomputed (in/out).                  *
- *   proxy p[t][i] = sum_c x[t][c] factor[c][i] in float64, in blocks of 128 *
- *     consecutive c (each in c order, the block sums then in block order;   *
- *     products of two bf16 or two fp32 values are exact in float64);       *
- *   key[t] = sign(cos) cos^2 of p[t] against cache[t]: dot^2 / (|p|^2       *
- *     |c|^2), dot and the squared norms summed over i in order from         *
- *     separately rounded products, negated when dot < 0 and the quotient   *
- *     is not 0; both norms 0 -> 1, one -> 0 (monotone in the cosine).       *
- * init = 1: cache <- p for every token, mask all 1 (key, selected unused).  *
- * init = 0: selected [n_select] = the n_select tokens of lowest key (ties:  *
+ *   proxy p[t][i] = sum_c x[t][c] factor[c][i], float64 (products of two  *
+ *     bf16 or two fp32 values are exact in float64; the sums round in the   *
+ *     library's own order, within a few ulps of sum |x factor|);            *
+ *   sim[t] = the cosine of p[t] and cache[t]: dot / sqrt(|p|^2 |c|^2),      *
+ *     float64, clamped to [-1, 1]; both norms 0 -> 1, one -> 0 (a proxy    *
+ *     equal to its cache scores exactly 1).                                 *
+ * init = 1: cache <- p for every token, mask all 1 (sim, selected unused).  *
+ * init = 0: selected [n_select] = the n_select tokens of lowest sim (ties:  *
  *   lower id), ascending; mask[t] = 1 for them, 0 otherwise; their cache    *
- *   rows <- p. key (nullable) receives every token's key, proxy (nullable) *
- *   every current proxy.                                                    *
+ *   rows <- p. sim (nullable) receives every token's similarity, proxy    *
+ *   (nullable) every current proxy.                                         *
  * Errors: INVALID_ARGUMENT for n_tok < 1, d_model < 1, x_stride < d_model, *
  *   NULL x / factor / cache / mask (selected when n_select > 0), n_select   *
  *   outside [0, n_tok], init not 0 or 1; UNSUPPORTED for rank not a        *
@@ -302,7 +301,7 @@ typedef struct {
   double* cache;           /* [n_tok, rank] in/out                             */
   int32_t n_select;        /* tokens to recompute (init = 0)                   */
   int32_t init;            /* 1: first step, every token recomputed            */
-  double* key;             /* out [n_tok], nullable                            */
+  double* sim;             /* out [n_tok], nullable                            */
   int32_t* selected;       /* out [n_select]                                   */
   uint8_t* mask;           /* out [n_tok]                                      */
   double* proxy;           /* out [n_tok, rank], nullable                      */

@@ -1,13 +1,14 @@
 """Reuse controllers and the per-step FlashBlock paths (text, video, sparse).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring). Float64 throughout;
-the active-set MSE uses an explicit sequential loop so that its IEEE
-operations are fixed (difference, square, add, in (head, dim) order).
+the active-set MSE is the exact mean of the squared query changes, taken in
+rational arithmetic and rounded once, so no order of operations enters it.
 
 Citations are to the pages listed in ``oracle/__init__.py``.
 """
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -83,24 +84,24 @@ def active_mse(q_prev, q_cur):
 
     [LoSA s2 "token classification", "workflow"]: the score is the MSE
     between a token's query at step t and at step t-1, over all query heads
-    and dims. The pages fix no summation order; reading: float64, for each
-    head the squared differences are added in dim order (diff, square, add),
-    the per-head sums are added in head order, then one division by Hq*d.
+    and dims. The pages fix no precision or order; reading: the exact mean of
+    the squared differences of the float64 inputs (every difference, square
+    and the sum taken in rational arithmetic), rounded once to float64. The
+    result depends on no summation order.
 
     q_prev, q_cur [B, Hq, d]  ->  mse [B] float64.
     """
     a = np.asarray(q_prev, dtype=np.float64)
     b = np.asarray(q_cur, dtype=np.float64)
-    n_tok, hq, d = a.shape
-    total = np.zeros(n_tok)
-    for h in range(hq):
-        acc = np.zeros(n_tok)
-        for j in range(d):
-            diff = b[:, h, j] - a[:, h, j]
-            sq = diff * diff
-            acc = acc + sq
-        total = total + acc
-    return total / float(hq * d)
+    n_tok = a.shape[0]
+    a = a.reshape(n_tok, -1)
+    b = b.reshape(n_tok, -1)
+    n = a.shape[1]
+    out = np.empty(n_tok)
+    for t in range(n_tok):
+        total = sum((Fraction(y) - Fraction(x)) ** 2 for x, y in zip(a[t].tolist(), b[t].tolist()))
+        out[t] = float(total / n)          # one correctly rounded division
+    return out
 
 
 def percentile_cutoff(mse, pct=25):

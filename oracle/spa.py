@@ -14,69 +14,51 @@ rank-r value states x W_r: the stored factor is F = U_r diag(sigma_r) [D, r].
 
 Readings (the pages fix no precision, order or tie rule):
 
-* proxy p[t, i] = sum over c of x[t, c] * F[c, i] in float64, taken in fixed
-  blocks of ``PROXY_BLOCK`` consecutive c (each block summed in c order, the
-  block sums then added in block order). A product of two bf16 (or two fp32)
-  values is exact in float64, so each block sum rounds once per term.
-* the ranking key of token t is sign(cos) * cos^2 with cos the cosine of its
-  proxy and its cached proxy: dot, |p|^2 and |c|^2 summed over i in order
-  (multiply, then add), key = dot^2 / (|p|^2 |c|^2), negated when dot < 0 and
-  the quotient is not zero; both norms zero -> 1, one zero -> 0. The key is a
-  monotone function of the cosine, so the lowest keys are the lowest
-  similarities, with no square root.
-* the n_select tokens of lowest key are recomputed (ties: lower token id
-  first); their cached proxies become the current ones; the other tokens keep
-  the proxy cached at the step they were last recomputed.
+* proxy p = x F, one float64 matrix product (a library primitive; its
+  summation order is the library's -- the GPU's proxies are compared with it
+  to a rounding tolerance, not bit for bit);
+* similarity of token t: the cosine <p_t, c_t> / sqrt(|p_t|^2 |c_t|^2) of
+  its proxy and its cached proxy, clamped to [-1, 1]; both norms zero -> 1
+  (identical), one zero -> 0. (With the squared norms under one square root,
+  a proxy equal to its cache scores exactly 1: sqrt of a rounded square is
+  the value itself in binary floating point.)
+* the n_select tokens of lowest similarity are recomputed (ties: lower token
+  id first); their cached proxies become the current ones; the other tokens
+  keep the proxy cached at the step they were last recomputed;
 * the first step recomputes every token and caches every proxy.
 """
 
-import numpy as np
+import math
 
-PROXY_BLOCK = 128
+import numpy as np
 
 
 def proxy(x, factor):
-    """x [N, D], factor [D, r] -> p [N, r] (float64, the blocked order above)."""
-    x = np.asarray(x, dtype=np.float64)
-    f = np.asarray(factor, dtype=np.float64)
-    n, d = x.shape
-    total = np.zeros((n, f.shape[1]))
-    for b0 in range(0, d, PROXY_BLOCK):
-        acc = np.zeros_like(total)
-        for c in range(b0, min(d, b0 + PROXY_BLOCK)):
-            acc = acc + x[:, c:c + 1] * f[c:c + 1, :]
-        total = total + acc
-    return total
+    """x [N, D], factor [D, r] -> p = x F [N, r] (float64)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(factor, dtype=np.float64)
 
 
-def proxy_key(p, c):
-    """Ranking key sign(cos) cos^2 of proxies p against cached c, per row."""
+def proxy_cosine(p, c):
+    """Per row, the cosine of proxy p against cached proxy c (conventions above)."""
     p = np.asarray(p, dtype=np.float64)
     c = np.asarray(c, dtype=np.float64)
-    n, r = p.shape
-    dot = np.zeros(n)
-    pp = np.zeros(n)
-    cc = np.zeros(n)
-    for i in range(r):
-        dot = dot + p[:, i] * c[:, i]
-        pp = pp + p[:, i] * p[:, i]
-        cc = cc + c[:, i] * c[:, i]
-    den = pp * cc
-    key = np.empty(n)
-    for t in range(n):
-        if den[t] == 0.0:
-            key[t] = 1.0 if (pp[t] == 0.0 and cc[t] == 0.0) else 0.0
+    sim = np.empty(p.shape[0])
+    for t in range(p.shape[0]):
+        dot = float(np.dot(p[t], c[t]))
+        pp = float(np.dot(p[t], p[t]))
+        cc = float(np.dot(c[t], c[t]))
+        if pp == 0.0 or cc == 0.0:
+            sim[t] = 1.0 if (pp == 0.0 and cc == 0.0) else 0.0
         else:
-            q = (dot[t] * dot[t]) / den[t]
-            key[t] = -q if (dot[t] < 0.0 and q != 0.0) else q
-    return key
+            sim[t] = min(1.0, max(-1.0, dot / math.sqrt(pp * cc)))
+    return sim
 
 
-def select_lowest(key, n_select):
-    """Token ids of the n_select lowest keys (ties: lower id), ascending."""
-    key = np.asarray(key, dtype=np.float64)
-    ids = np.arange(key.size)
-    order = np.lexsort((ids, key))
+def select_lowest(sim, n_select):
+    """Token ids of the n_select lowest similarities (ties: lower id), ascending."""
+    sim = np.asarray(sim, dtype=np.float64)
+    ids = np.arange(sim.size)
+    order = np.lexsort((ids, sim))
     return np.sort(order[:int(n_select)]).astype(np.int32)
 
 
@@ -84,9 +66,9 @@ def spa_run(steps, factor, n_select):
     """The identifier over denoising steps of hidden states x^s [N, D].
 
     Per step: the proxies; at s = 0 every token is recomputed and cached; at
-    s >= 1 the keys against the cache, the n_select lowest recomputed and
-    their cache entries replaced. Records: proxy, key (None at s = 0),
-    selected, mask, cache after the step.
+    s >= 1 the similarities against the cache, the n_select lowest
+    recomputed and their cache entries replaced. Records: proxy, sim (None
+    at s = 0), selected, mask, cache after the step.
     """
     recs = []
     cache = None
@@ -94,17 +76,17 @@ def spa_run(steps, factor, n_select):
         p = proxy(x, factor)
         n = p.shape[0]
         if s == 0:
-            key, sel = None, np.arange(n, dtype=np.int32)
+            sim, sel = None, np.arange(n, dtype=np.int32)
             cache = p.copy()
         else:
-            key = proxy_key(p, cache)
-            sel = select_lowest(key, n_select)
+            sim = proxy_cosine(p, cache)
+            sel = select_lowest(sim, n_select)
             cache = cache.copy()
             cache[sel] = p[sel]
         mask = np.zeros(n, dtype=bool)
         mask[sel] = True
-        recs.append(dict(step=s, proxy=p, key=key, selected=sel, mask=mask, cache=cache))
+        recs.append(dict(step=s, proxy=p, sim=sim, selected=sel, mask=mask, cache=cache))
     return recs
 
 
-__all__ = ["PROXY_BLOCK", "proxy", "proxy_key", "select_lowest", "spa_run"]
+__all__ = ["proxy", "proxy_cosine", "select_lowest", "spa_run"]

@@ -91,3 +91,47 @@ def run_prefix(fb, cfg, n_q, n_kv, layout="tok", mask=None, q_gain=1.0, seed_var
     torch.cuda.synchronize()
     ra, rl = attn_gqa(vals(q, cfg.dtype), vals(kp, cfg.dtype), vals(vp, cfg.dtype), cfg.scale)
     return cpu(a), cpu(l), ra, rl, cfg
+
+
+# ---------------------------------------------------------------- margin guards
+#
+# Where a float64 value decides an integer result (the active set from the
+# query MSE, the recomputed tokens from the proxy similarity), the oracle
+# computes the plain definition (an exact mean; a library matrix product and
+# the plain cosine) and the GPU its own summation order. The values then
+# differ by rounding only, so they are compared to a tolerance, and the
+# integer results are compared bit for bit once the oracle's values leave a
+# margin around every decision that no rounding difference can cross.
+
+MSE_RTOL = 1e-12        # GPU float64 MSE (its own order) vs the exact mean
+MSE_MARGIN = 1e-9       # relative gap the guard requires between distinct MSEs
+SIM_ATOL = 1e-10        # GPU proxy cosine vs the oracle's
+SIM_MARGIN = 1e-8       # gap the guard requires at the selection boundary
+
+
+def check_mse(name, got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert np.array_equal(got == 0.0, want == 0.0), "%s: zero pattern differs" % name
+    err = np.abs(got - want)
+    assert np.all(err <= MSE_RTOL * np.abs(want)), "%s: MSE %s vs %s" % (name, got, want)
+
+
+def mse_margin_ok(mse):
+    """True when the distinct MSE values are more than MSE_MARGIN apart
+    (relative), so that any order of the GPU's sums ranks them alike and the
+    nearest-rank cutoff picks the same token; equal values (unchanged tokens
+    score exactly 0 on both sides) are allowed."""
+    u = np.unique(np.asarray(mse, dtype=np.float64))
+    if u.size < 2:
+        return True
+    return bool(np.all(np.diff(u) > MSE_MARGIN * u[1:]))
+
+
+def sim_margin_ok(sim, n_select):
+    """True when the n_select-th lowest and the next similarity are more than
+    SIM_MARGIN apart, so the selection cannot flip under rounding."""
+    s = np.sort(np.asarray(sim, dtype=np.float64))
+    if n_select <= 0 or n_select >= s.size:
+        return True
+    return bool(s[n_select] - s[n_select - 1] > SIM_MARGIN)

@@ -10,7 +10,7 @@ import workloads as W
 from oracle import controller as OC
 from oracle import quest as OQ
 from oracle.attention import attn_gqa, merge
-from _helpers import check_a, check_l, cpu, dev_tensor, tols, vals
+from _helpers import check_a, check_l, check_mse, cpu, dev_tensor, mse_margin_ok, tols, vals
 
 pytestmark = pytest.mark.gpu
 
@@ -129,7 +129,7 @@ def test_head_cos_bit_exact_decisions(fb):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_active_mse_bit_exact(fb, dtype):
+def test_active_mse_matches_oracle(fb, dtype):
     cfg = W.SPARSE.with_(dtype=dtype, n_steps=6)
     steps = W.sparse_steps(cfg, m_override=[None, 3, 0, 8, 1, 2])
     for s in range(1, len(steps)):
@@ -147,7 +147,8 @@ def test_active_mse_bit_exact(fb, dtype):
         fb.fb_reuse_decide(args)
         torch.cuda.synchronize()
         want = OC.active_mse(vals(qp, dtype), vals(qc, dtype))
-        assert np.array_equal(cpu(mse), want), (s, cpu(mse), want)
+        assert mse_margin_ok(want), (s, want)
+        check_mse("step %d" % s, cpu(mse), want)
         assert np.array_equal(cpu(act).astype(bool), OC.active_set(want, 25))
 
 

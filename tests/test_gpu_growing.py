@@ -17,7 +17,7 @@ import workloads as W
 from oracle import controller as OC
 from oracle import growing as OG
 from oracle import quest as OQ
-from _helpers import check_a, check_l, cpu, dev_tensor, tols, vals
+from _helpers import check_a, check_l, check_mse, cpu, dev_tensor, mse_margin_ok, tols, vals
 
 pytestmark = pytest.mark.gpu
 
@@ -185,6 +185,9 @@ def test_sparse_blocks_on_a_growing_cache(fb):
             torch.cuda.synchronize()
             tag = "block %d step %d" % (j, s)
             assert np.array_equal(cpu(step.pages), rec["sel"]), tag
+            if s > 0:
+                assert mse_margin_ok(rec["mse"]), tag
+                check_mse(tag, cpu(step.mse), rec["mse"])
             assert np.array_equal(cpu(step.active).astype(bool), rec["active"]), tag
             check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 2e-3)
             check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)

@@ -13,7 +13,7 @@ import torch
 import workloads as W
 from oracle import controller as OC
 from oracle import quest as OQ
-from _helpers import check_a, check_l, cpu, dev_tensor, vals
+from _helpers import check_a, check_l, check_mse, cpu, dev_tensor, mse_margin_ok, vals
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +96,9 @@ def test_losa_block_matches_oracle(fb, name, n_prefix, density, m_override):
         torch.cuda.synchronize()
         tag = "%s step %d" % (name, s)
         act = rec["active"]
+        if s > 0:
+            assert mse_margin_ok(rec["mse"]), tag
+            check_mse(tag, cpu(step.mse), rec["mse"])
         assert np.array_equal(cpu(step.active).astype(bool), act), tag
         if s > 0:                                # pages are chosen for active tokens only
             assert np.array_equal(cpu(step.pages)[act], rec["sel"][act]), tag

@@ -1,6 +1,8 @@
 """GPU parity of the singular-proxy identifier (fb_proxy_decide) against
-oracle.spa: proxies, keys and cache bit for bit (the float64 arithmetic is
-fixed operation by operation), selected token ids and masks exactly."""
+oracle.spa: proxies and cache within the rounding bound of a float64 dot
+product of d_model exact products, similarities within SIM_ATOL, and the
+selected token ids and masks exactly wherever the oracle's similarities leave
+a margin at the selection boundary (asserted per step)."""
 
 import numpy as np
 import pytest
@@ -8,9 +10,37 @@ import torch
 
 import workloads as W
 from oracle import spa as OS
-from _helpers import cpu
+from _helpers import SIM_ATOL, cpu, sim_margin_ok
 
 pytestmark = pytest.mark.gpu
+
+
+def check_proxy(name, got, x, f, want):
+    """|p_gpu - p_oracle| <= 2 d_model 2^-53 (|x| |F|) per entry: both sums of
+    the same exact products, each within d_model 2^-53 sum |x F| of the exact
+    value whatever its order."""
+    x = np.asarray(x, dtype=np.float64)
+    f = np.asarray(f, dtype=np.float64)
+    bound = 2 * x.shape[1] * 2.0 ** -53 * (np.abs(x) @ np.abs(f))
+    err = np.abs(np.asarray(got) - want)
+    assert np.all(err <= bound), "%s: proxy err %.3g (bound %.3g)" % (
+        name, float(err.max()), float(bound[err > bound].min()))
+
+
+def check_step(tag, idn, x, f, rec, k, cache_src):
+    """One step's outputs against the oracle record; cache_src: the GPU
+    cache rows are the GPU's own proxies of the steps they were taken at."""
+    if rec["sim"] is not None:
+        assert sim_margin_ok(rec["sim"], k), tag + ": similarities too close at the boundary"
+    check_proxy(tag + " proxy", cpu(idn.proxy), x, f, rec["proxy"])
+    assert np.array_equal(cpu(idn.mask).astype(bool), rec["mask"]), tag
+    if rec["sim"] is not None:
+        assert np.max(np.abs(cpu(idn.sim) - rec["sim"])) <= SIM_ATOL, tag
+        if k > 0:
+            assert np.array_equal(cpu(idn.selected)[:k], rec["selected"]), tag
+    cache = cpu(idn.cache)
+    for t in range(cache.shape[0]):
+        assert np.array_equal(cache[t], cache_src[t]), (tag, t)
 
 
 def _dev(x, dtype):
@@ -26,7 +56,7 @@ class Ident:
         self.fb, self.n, self.r, self.n_select = fb, n, r, n_select
         f64 = dict(device="cuda", dtype=torch.float64)
         self.cache = torch.full((n, r), 3.0, **f64)
-        self.key = torch.full((n,), 9.0, **f64)
+        self.sim = torch.full((n,), 9.0, **f64)
         self.proxy = torch.empty(n, r, **f64)
         self.mask = torch.full((n,), 7, device="cuda", dtype=torch.uint8)
         self.selected = torch.full((max(n_select, 1),), -1, device="cuda", dtype=torch.int32)
@@ -35,7 +65,7 @@ class Ident:
     def step(self, x, f, init, with_proxy=True):
         fb = self.fb
         a = fb.proxy_args(x, f, self.cache, self.mask, self.selected, self.n_select, init,
-                          key=self.key, proxy=self.proxy if with_proxy else None)
+                          sim=self.sim, proxy=self.proxy if with_proxy else None)
         ws = torch.empty(max(fb.fb_proxy_decide_workspace(a), 16), dtype=torch.uint8, device="cuda")
         a.ws, a.ws_bytes = ws.data_ptr(), ws.numel()
         fb.fb_proxy_decide(a)
@@ -55,7 +85,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("name,n,d,r,k,dt", CASES, ids=[c[0] for c in CASES])
-def test_identifier_matches_oracle_bit_for_bit(fb, name, n, d, r, k, dt):
+def test_identifier_matches_oracle(fb, name, n, d, r, k, dt):
     cfg = W.SPA.with_(n_tok=n, d_model=d, rank=r, n_steps=3, cfg_id=6 if dt == "bf16" else 16)
     fbits = W.spa_factor(cfg)
     steps = W.spa_steps(cfg)
@@ -67,34 +97,29 @@ def test_identifier_matches_oracle_bit_for_bit(fb, name, n, d, r, k, dt):
     recs = OS.spa_run(xs, fv, k)
     f_d = _dev(fbits, dt)
     idn = Ident(fb, n, d, r, k)
+    held = np.zeros((n, r))                  # the GPU's proxies at each token's last recompute
     for s, (x, rec) in enumerate(zip(steps, recs)):
         idn.step(_dev(x, dt), f_d, init=(s == 0))
-        tag = "%s step %d" % (name, s)
-        assert np.array_equal(cpu(idn.proxy), rec["proxy"]), tag
-        assert np.array_equal(cpu(idn.cache), rec["cache"]), tag
-        assert np.array_equal(cpu(idn.mask).astype(bool), rec["mask"]), tag
-        if s > 0:
-            assert np.array_equal(cpu(idn.key), rec["key"]), tag
-            if k > 0:
-                assert np.array_equal(cpu(idn.selected)[:k], rec["selected"]), tag
+        p = cpu(idn.proxy)
+        held[rec["mask"]] = p[rec["mask"]]
+        check_step("%s step %d" % (name, s), idn, xs[s], fv, rec, k, held)
 
 
-def test_identifier_sums_in_blocks_of_128(fb):
-    # 2^53 at c = 0, ones at c = 128 and 129, a factor of ones: the blocked
-    # sum is 2^53 + 2 exactly; a single running sum would give 2^53
-    d, r = 256, 32
-    x = np.zeros((1, d), np.float32)
-    x[0, 0] = 2.0 ** 53
-    x[0, 128] = x[0, 129] = 1.0
-    f = np.ones((d, r), np.float32)
-    idn = Ident(fb, 1, d, r, 0)
+def test_identifier_exact_on_small_integers(fb):
+    # integer states and factor: every partial sum is an exact integer, so
+    # the proxies equal the oracle's bit for bit in any order
+    n, d, r = 40, 700, 32
+    rng = np.random.default_rng(5)
+    x = rng.integers(-8, 9, size=(n, d)).astype(np.float32)
+    f = rng.integers(-8, 9, size=(d, r)).astype(np.float32)
+    idn = Ident(fb, n, d, r, 0)
     idn.step(_dev(W.bf16_bits(x), "bf16"), _dev(W.bf16_bits(f), "bf16"), init=True)
-    assert (cpu(idn.proxy) == 2.0 ** 53 + 2.0).all()
-    assert (cpu(idn.proxy) == OS.proxy(x, f)).all()
+    assert np.array_equal(cpu(idn.proxy), OS.proxy(x, f))
+    assert np.array_equal(cpu(idn.cache), OS.proxy(x, f))
 
 
 def test_identifier_ties_go_to_lower_ids(fb):
-    # every token identical and its cache identical: all keys are 1 exactly
+    # every token identical and its cache identical: every similarity is 1
     n, d, r, k = 50, 512, 32, 9
     rng = np.random.default_rng(0)
     row = W.bf16_bits(rng.standard_normal((1, d)).astype(np.float32))
@@ -103,25 +128,27 @@ def test_identifier_ties_go_to_lower_ids(fb):
     idn = Ident(fb, n, d, r, k)
     idn.step(_dev(x, "bf16"), _dev(f, "bf16"), init=True)
     idn.step(_dev(x, "bf16"), _dev(f, "bf16"), init=False, with_proxy=False)
-    assert (cpu(idn.key) == 1.0).all()
+    assert (cpu(idn.sim) == 1.0).all()
     assert cpu(idn.selected)[:k].tolist() == list(range(k))
 
 
-def test_identifier_full_size_bit_exact(fb):
+def test_identifier_full_size(fb):
     """1024 tokens of width 4096, rank 128, a quarter recomputed per step --
     the size the benchmark times."""
-    cfg = W.SPA.with_(n_steps=2)
+    cfg = W.SPA.with_(n_steps=3)
     f = W.spa_factor(cfg)
     steps = W.spa_steps(cfg)
-    recs = OS.spa_run([W.values(x, "bf16") for x in steps], W.values(f, "bf16"), cfg.n_select)
+    xs = [W.values(x, "bf16") for x in steps]
+    fv = W.values(f, "bf16")
+    recs = OS.spa_run(xs, fv, cfg.n_select)
     idn = Ident(fb, cfg.n_tok, cfg.d_model, cfg.rank, cfg.n_select)
     f_d = _dev(f, "bf16")
+    held = np.zeros((cfg.n_tok, cfg.rank))
     for s, (x, rec) in enumerate(zip(steps, recs)):
         idn.step(_dev(x, "bf16"), f_d, init=(s == 0))
-        assert np.array_equal(cpu(idn.proxy), rec["proxy"]), s
-        assert np.array_equal(cpu(idn.cache), rec["cache"]), s
-    assert np.array_equal(cpu(idn.key), recs[1]["key"])
-    assert np.array_equal(cpu(idn.selected), recs[1]["selected"])
+        p = cpu(idn.proxy)
+        held[rec["mask"]] = p[rec["mask"]]
+        check_step("full step %d" % s, idn, xs[s], fv, rec, cfg.n_select, held)
 
 
 def test_layer_stack_with_depth_budgets(fb):
@@ -136,10 +163,13 @@ def test_layer_stack_with_depth_budgets(fb):
         cfg = W.SPA.with_(n_tok=n, d_model=d, rank=r, n_steps=3)
         f = W.spa_factor(cfg, variant=layer)
         steps = W.spa_steps(cfg, variant=layer)
-        recs = OS.spa_run([W.values(x, "bf16") for x in steps], W.values(f, "bf16"), counts[layer])
+        xs, fv = [W.values(x, "bf16") for x in steps], W.values(f, "bf16")
+        recs = OS.spa_run(xs, fv, counts[layer])
         idn = Ident(fb, n, d, r, counts[layer])
         f_d = _dev(f, "bf16")
+        held = np.zeros((n, r))
         for s, (x, rec) in enumerate(zip(steps, recs)):
             idn.step(_dev(x, "bf16"), f_d, init=(s == 0))
-            assert np.array_equal(cpu(idn.cache), rec["cache"]), (layer, s)
-            assert np.array_equal(cpu(idn.mask).astype(bool), rec["mask"]), (layer, s)
+            p = cpu(idn.proxy)
+            held[rec["mask"]] = p[rec["mask"]]
+            check_step("layer %d step %d" % (layer, s), idn, xs[s], fv, rec, counts[layer], held)

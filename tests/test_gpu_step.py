@@ -8,7 +8,7 @@ import torch
 
 import workloads as W
 from oracle import controller as OC
-from _helpers import check_a, check_l, cpu, dev_tensor, tols, vals
+from _helpers import check_a, check_l, check_mse, cpu, dev_tensor, mse_margin_ok, tols, vals
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,8 @@ def run_text(fb, cfg, m_override=None, layout="tok", force=None):
         step.step(dev_tensor(st["q"], cfg.dtype), dev_tensor(st["k"], cfg.dtype),
                   dev_tensor(st["v"], cfg.dtype), a, l,
                   ids=torch.from_numpy(st["ids"]).cuda(), decision=dec)
-        got.append((cpu(a), cpu(l), int(step.m_count.item()), cpu(step.mask), cpu(step.a_out)))
+        got.append((cpu(a), cpu(l), int(step.m_count.item()), cpu(step.mask), cpu(step.a_out),
+                    cpu(step.l_out)))
     ksteps = [dict(q=vals(s["q"], cfg.dtype), k=vals(s["k"], cfg.dtype),
                    v=vals(s["v"], cfg.dtype), ids=s["ids"]) for s in steps]
     recs = OC.text_block(ksteps, vals(kp, cfg.dtype), vals(vp, cfg.dtype), cfg.scale, cfg.tau,
@@ -48,11 +49,12 @@ def run_text(fb, cfg, m_override=None, layout="tok", force=None):
 def test_text_block_matches_oracle(fb, name, cfg, m_override):
     got, recs = run_text(fb, cfg, m_override)
     atol, ltol = tols(cfg.dtype)
-    for s, (rec, (a, l, mc, mask, a_out)) in enumerate(zip(recs, got)):
+    for s, (rec, (a, l, mc, mask, a_out, l_out)) in enumerate(zip(recs, got)):
         if s > 0:
             assert mc == rec["m_count"], (s, mc, rec["m_count"])
         assert np.all(mask == (1 if rec["decision"] == OC.REUSE else 0)), (s, rec["decision"])
         check_a("%s step %d A_out" % (name, s), a_out, rec["a_out"], atol)
+        check_l("%s step %d L_out" % (name, s), l_out, rec["l_out"], ltol)
         check_a("%s step %d A_full" % (name, s), a, rec["a_full"], atol)
         check_l("%s step %d L_full" % (name, s), l, rec["l_full"], ltol)
 
@@ -61,7 +63,7 @@ def test_text_forced_reuse_and_recompute(fb):
     cfg = W.TEXT.with_(n_prefix=5000, n_steps=5)
     force = [None, OC.REUSE, OC.RECOMPUTE, OC.REUSE, OC.REUSE]
     got, recs = run_text(fb, cfg, m_override=[None, 4, 0, 4, 4], force=force)
-    for s, (rec, (a, l, mc, mask, a_out)) in enumerate(zip(recs, got)):
+    for s, (rec, (a, l, mc, mask, a_out, l_out)) in enumerate(zip(recs, got)):
         assert rec["decision"] == ([OC.INIT] + force[1:])[s]
         check_a("forced step %d" % s, a, rec["a_full"], 2e-3)
         check_l("forced step %d" % s, l, rec["l_full"], 1e-3)
@@ -131,6 +133,9 @@ def test_sparse_block_matches_oracle(fb, density):
                   dev_tensor(st["v"], "bf16"), a, l)
         torch.cuda.synchronize()
         assert np.array_equal(cpu(step.pages), rec["sel"]), s
+        if s > 0:
+            assert mse_margin_ok(rec["mse"]), s
+            check_mse("sparse step %d" % s, cpu(step.mse), rec["mse"])
         assert np.array_equal(cpu(step.active).astype(bool), rec["active"]), s
         if s == 0:
             check_a("sparse A_res", cpu(step.a_res), rec["a_res"], 2e-3)

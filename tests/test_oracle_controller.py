@@ -275,13 +275,32 @@ def test_sparse_stable_rows_keep_their_output():
             assert u[g] == want
 
 
-def test_mse_sums_each_head_in_dim_order_then_heads():
-    # Worked by hand (float64, round to nearest even). One token, 2 heads,
-    # d = 2; squared differences: head 0 = [2^54, 1], head 1 = [2.25, 2.25].
-    # Per head: 2^54 + 1 -> 2^54 (ulp 4); 2.25 + 2.25 = 4.5. Over heads:
-    # 2^54 + 4.5 -> 2^54 + 4. (One flat sequential sum would give 2^54 + 8:
-    # 2^54 + 1 -> 2^54, + 2.25 -> 2^54 + 4, + 2.25 -> 2^54 + 8.)
-    q_prev = np.zeros((1, 2, 2))
-    q_cur = np.array([[[2.0 ** 27, 1.0], [1.5, 1.5]]])
+def test_mse_is_the_exact_mean_rounded_once():
+    # Worked by hand. One token, one head, d = 4; q_prev = 0,
+    # q_cur = [2^27, 1, 1, 1]: squared differences 2^54, 1, 1, 1. Exact sum
+    # 2^54 + 3, mean 2^52 + 0.75, which rounds to 2^52 + 1 (ulp 1 at 2^52).
+    # Any float64 running or pairwise sum loses the ones: 2^54 + 1 and
+    # 2^54 + 2 both round to 2^54 (ulp 4, ties to even), giving 2^52.
+    q_prev = np.zeros((1, 1, 4))
+    q_cur = np.array([[[2.0 ** 27, 1.0, 1.0, 1.0]]])
     mse = C.active_mse(q_prev, q_cur)
-    assert mse[0] == (2.0 ** 54 + 4.0) / 4.0
+    assert mse[0] == 2.0 ** 52 + 1.0
+    run = 0.0
+    for v in (2.0 ** 54, 1.0, 1.0, 1.0):
+        run = run + v
+    assert run / 4 == 2.0 ** 52
+    # a constant shift c changes every value by c: MSE = c^2 exactly
+    a = np.round(rng.standard_normal((3, 2, 8)) * 64) / 64     # a + 0.25 exact
+    np.testing.assert_array_equal(C.active_mse(a, a + 0.25), np.full(3, 0.0625))
+
+
+def test_mse_does_not_depend_on_the_order_of_heads_and_dims():
+    a = rng.standard_normal((4, 8, 16))
+    b = a + rng.standard_normal((4, 8, 16)) * np.array([1.0, 1e-9, 1e7, 3.0])[:, None, None]
+    want = C.active_mse(a, b)
+    perm = rng.permutation(8 * 16)
+    pa = a.reshape(4, -1)[:, perm].reshape(4, 16, 8)
+    pb = b.reshape(4, -1)[:, perm].reshape(4, 16, 8)
+    np.testing.assert_array_equal(C.active_mse(pa, pb), want)
+
+

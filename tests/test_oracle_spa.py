@@ -1,6 +1,8 @@
 """Pins for the singular-proxy identifier (oracle.spa) and its synthetic
 value projection (workloads.spa_factor / spa_projection)."""
 
+import math
+
 import numpy as np
 
 import workloads as W
@@ -41,61 +43,63 @@ def test_proxy_cosine_is_the_rank_r_value_state_cosine():
     for r in (5, 40):
         f = u[:, :r] * sig[:r]
         w_r = f @ v[:, :r].T
-        kp = S.proxy_key(S.proxy(x, f), S.proxy(y, f))
-        c = _cos(x @ w_r, y @ w_r)
-        np.testing.assert_allclose(kp, np.sign(c) * c * c, rtol=1e-12, atol=1e-15)
+        got = S.proxy_cosine(S.proxy(x, f), S.proxy(y, f))
+        np.testing.assert_allclose(got, _cos(x @ w_r, y @ w_r), rtol=1e-12, atol=1e-15)
     w = u @ np.diag(sig) @ v.T
-    c = _cos(x @ w, y @ w)
-    kp = S.proxy_key(S.proxy(x, u * sig), S.proxy(y, u * sig))
-    np.testing.assert_allclose(kp, np.sign(c) * c * c, rtol=1e-12, atol=1e-15)
+    got = S.proxy_cosine(S.proxy(x, u * sig), S.proxy(y, u * sig))
+    np.testing.assert_allclose(got, _cos(x @ w, y @ w), rtol=1e-12, atol=1e-15)
 
 
-def test_proxy_matches_matmul_and_is_exact_on_integers():
+def test_proxy_brute_force_and_exact_on_integers():
+    # every entry against a pure-Python sum of the exact products, correctly
+    # rounded (math.fsum): the library product agrees to a few ulps
     rng = np.random.default_rng(2)
-    x = W.values(W.bf16_bits(rng.standard_normal((9, 1100)).astype(np.float32)), "bf16")
-    f = W.values(W.bf16_bits(rng.standard_normal((1100, 24)).astype(np.float32)), "bf16")
-    np.testing.assert_allclose(S.proxy(x, f), x.astype(np.float64) @ f.astype(np.float64),
-                               rtol=1e-12, atol=1e-12)
+    x = W.values(W.bf16_bits(rng.standard_normal((5, 300)).astype(np.float32)), "bf16")
+    f = W.values(W.bf16_bits(rng.standard_normal((300, 6)).astype(np.float32)), "bf16")
+    p = S.proxy(x, f)
+    for t in range(5):
+        for i in range(6):
+            terms = [float(x[t, c]) * float(f[c, i]) for c in range(300)]
+            exact = math.fsum(terms)
+            bound = 300 * 2.0 ** -53 * math.fsum(abs(v) for v in terms)
+            assert abs(p[t, i] - exact) <= bound
+    # small integers: every partial sum is exact, whatever the order
     xi = rng.integers(-50, 50, size=(5, 1300)).astype(np.float64)
     fi = rng.integers(-50, 50, size=(1300, 7)).astype(np.float64)
-    np.testing.assert_array_equal(S.proxy(xi, fi), xi @ fi)
+    brute = [[sum(int(xi[t, c]) * int(fi[c, i]) for c in range(1300)) for i in range(7)]
+             for t in range(5)]
+    np.testing.assert_array_equal(S.proxy(xi, fi), np.array(brute, dtype=np.float64))
 
 
-def test_proxy_sums_in_blocks_of_128():
-    # x = 2^53 at c = 0 and 1 at c = 128, 129: block 0 sums to 2^53, block 1
-    # to 2, total 2^53 + 2 (exact); one running sum over c would round each
-    # +1 away and give 2^53.
-    d = 2 * S.PROXY_BLOCK
-    x = np.zeros((1, d))
-    x[0, 0] = 2.0 ** 53
-    x[0, S.PROXY_BLOCK] = x[0, S.PROXY_BLOCK + 1] = 1.0
-    f = np.ones((d, 1))
-    assert S.proxy(x, f)[0, 0] == 2.0 ** 53 + 2.0
-    run = 0.0
-    for c in range(d):
-        run = run + x[0, c]
-    assert run == 2.0 ** 53
+def test_cosine_hand_values_and_conventions():
+    p = np.array([[1.0, 0.0], [1.0, 1.0], [2.0, 0.0], [0.0, 0.0], [0.0, 0.0], [3.0, 4.0],
+                  [0.3, -1.7]])
+    c = np.array([[1.0, 1.0], [1.0, 1.0], [-3.0, 0.0], [0.0, 0.0], [1.0, 0.0], [3.0, 4.0],
+                  [0.3, -1.7]])
+    k = S.proxy_cosine(p, c)
+    assert k[0] == 1.0 / math.sqrt(2.0)            # 1 / sqrt(1 * 2)
+    assert k[1] == 1.0 and k[5] == 1.0 and k[6] == 1.0    # identical proxies: exactly 1
+    assert k[2] == -1.0                            # opposite: -6 / sqrt(36)
+    assert k[3] == 1.0 and k[4] == 0.0             # both zero / one zero
+    z = S.proxy_cosine(np.array([[1.0, 0.0]]), np.array([[0.0, -1.0]]))
+    assert z[0] == 0.0                             # orthogonal
 
 
-def test_key_hand_values_and_conventions():
-    p = np.array([[1.0, 0.0], [1.0, 1.0], [2.0, 0.0], [0.0, 0.0], [0.0, 0.0], [3.0, 4.0]])
-    c = np.array([[1.0, 1.0], [1.0, 1.0], [-3.0, 0.0], [0.0, 0.0], [1.0, 0.0], [3.0, 4.0]])
-    k = S.proxy_key(p, c)
-    assert k[0] == 0.5                     # cos = 1/sqrt(2)
-    assert k[1] == 1.0 and k[5] == 1.0     # identical proxies: exactly 1
-    assert k[2] == -1.0                    # opposite
-    assert k[3] == 1.0 and k[4] == 0.0     # both zero / one zero
-    # orthogonal: 0 (not -0)
-    z = S.proxy_key(np.array([[1.0, 0.0]]), np.array([[0.0, -1.0]]))
-    assert z[0] == 0.0 and not np.signbit(z[0])
-
-
-def test_key_orders_like_the_cosine():
+def test_cosine_brute_force():
+    # pure-Python loops with correctly rounded sums, against the oracle
     rng = np.random.default_rng(3)
-    p, c = rng.standard_normal((300, 16)), rng.standard_normal((300, 16))
-    k = S.proxy_key(p, c)
-    cos = _cos(p, c)
-    np.testing.assert_array_equal(np.argsort(k, kind="stable"), np.argsort(cos, kind="stable"))
+    p, c = rng.standard_normal((40, 16)), rng.standard_normal((40, 16))
+    c[:5] = p[:5] * 2.5                            # parallel: cosine 1
+    c[5:8] = -p[5:8]                               # opposite: cosine -1
+    k = S.proxy_cosine(p, c)
+    for t in range(40):
+        dot = math.fsum(p[t, i] * c[t, i] for i in range(16))
+        npn = math.sqrt(math.fsum(p[t, i] ** 2 for i in range(16)))
+        ncn = math.sqrt(math.fsum(c[t, i] ** 2 for i in range(16)))
+        assert abs(k[t] - dot / (npn * ncn)) <= 1e-14
+    np.testing.assert_allclose(k[:5], 1.0, atol=1e-15)
+    np.testing.assert_allclose(k[5:8], -1.0, atol=1e-15)
+    assert np.all(np.abs(k) <= 1.0)
 
 
 def test_select_lowest_brute_force_and_ties():
@@ -116,7 +120,7 @@ def test_run_caches_at_recompute_and_still_tokens_are_exactly_similar():
     steps = [W.values(x, "bf16") for x in W.spa_steps(cfg)]
     steps[2] = steps[1].copy()                    # no token moves between steps 1 and 2
     recs = S.spa_run(steps, f, n_select=10)
-    assert recs[0]["mask"].all() and recs[0]["key"] is None
+    assert recs[0]["mask"].all() and recs[0]["sim"] is None
     np.testing.assert_array_equal(recs[0]["cache"], S.proxy(steps[0], f))
     for s in range(1, 4):
         r = recs[s]
@@ -125,9 +129,9 @@ def test_run_caches_at_recompute_and_still_tokens_are_exactly_similar():
         np.testing.assert_array_equal(r["cache"][r["mask"]], r["proxy"][r["mask"]])
         np.testing.assert_array_equal(r["cache"][~r["mask"]], prev[~r["mask"]])
         # every selected token is at most as similar as every other one
-        assert r["key"][r["mask"]].max() <= r["key"][~r["mask"]].min()
-    # tokens recomputed at step 1 have key exactly 1 at step 2 (same state)
-    assert (recs[2]["key"][recs[1]["mask"]] == 1.0).all()
+        assert r["sim"][r["mask"]].max() <= r["sim"][~r["mask"]].min()
+    # tokens recomputed at step 1 have similarity exactly 1 at step 2 (same state)
+    assert (recs[2]["sim"][recs[1]["mask"]] == 1.0).all()
 
 
 def test_drift_scales_order_the_selection():
