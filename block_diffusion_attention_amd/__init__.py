@@ -18,7 +18,8 @@ from ._abi import (  # noqa: F401
     fb_abi_version, fb_attn_shape, fb_block_attn_merge, fb_block_attn_merge_workspace,
     fb_kv_append, fb_kv_cache, fb_layer_budgets, fb_proxy_args, fb_proxy_decide, fb_proxy_decide_workspace,
     proxy_args, fb_page_meta, fb_page_meta_update, fb_page_sel, fb_page_select,
-    fb_page_select_workspace, fb_prefix_attn, fb_prefix_attn_workspace, fb_reuse_args,
+    fb_page_select_workspace, fb_prefix_attn, fb_prefix_attn_noalloc, fb_prefix_attn_workspace,
+    fb_reuse_args, NOALLOC_SCRATCH_BYTES,
     fb_reuse_decide, fb_reuse_decide_workspace, fb_status_string, fb_step, fb_step_args,
     fb_step_next_block, fb_step_state, fb_step_workspace, fb_tensor, load, page_sel, ptr,
     shape_of, stream_of, tensor_of)

@@ -95,6 +95,9 @@ _SIGS = [
      [C.POINTER(fb_attn_shape), fb_tensor, fb_tensor, fb_tensor, C.c_void_p,
       C.POINTER(fb_page_sel), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
       C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("fb_prefix_attn_noalloc", C.c_int,
+     [C.POINTER(fb_attn_shape), fb_tensor, fb_tensor, fb_tensor, C.c_void_p,
+      C.POINTER(fb_page_sel), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     ("fb_block_attn_merge_workspace", C.c_size_t, [C.POINTER(fb_attn_shape), C.c_int64]),
     ("fb_block_attn_merge", C.c_int,
      [C.POINTER(fb_attn_shape), fb_tensor, fb_tensor, fb_tensor, C.c_void_p, C.c_void_p,
@@ -220,6 +223,18 @@ def fb_prefix_attn(shape, q, k, v, a_out, l_out, mask=None, sel=None, a_res=None
                                ptr(a_out), ptr(l_out), ptr(a_res), ptr(l_res), ptr(ws),
                                ws_bytes, stream_of(stream))
     _check("fb_prefix_attn", st)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fb_prefix_attn_noalloc(shape, q, k, v, a_out, l_out, mask=None, sel=None, a_res=None,
+                           l_res=None, stream=None):
+    st = load().fb_prefix_attn_noalloc(C.byref(shape), tensor_of(q), tensor_of(k), tensor_of(v),
+                                       ptr(mask), C.byref(sel) if sel is not None else None,
+                                       ptr(a_out), ptr(l_out), ptr(a_res), ptr(l_res),
+                                       stream_of(stream))
+    _check("fb_prefix_attn_noalloc", st)
 
 
 def fb_block_attn_merge_workspace(shape, n_q):

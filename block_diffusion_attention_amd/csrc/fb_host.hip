@@ -8,6 +8,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fb_internal.h"
 
 namespace fb {
@@ -533,6 +535,33 @@ fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const 
   return dev(launch_block_small(bp, shape->dtype, stream));
 }
 
+// ---------------------------------------------------------------------------
+// Scratch for fb_prefix_attn_noalloc: the split-K partials (and, for sparse
+// selections, the bitmaps and the page union) live in this fixed device
+// array instead of a caller workspace. Each GPU the library runs on holds its
+// own copy until the process ends. Its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept; host code
+// never passes the array's name itself to a kernel or a copy.
+constexpr size_t kScratchBytes = size_t(16) << 20;     // FB_NOALLOC_SCRATCH_BYTES
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+fb_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FB_ERR_DEVICE;
+  if (dev >= kMaxDevices) return FB_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FB_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -565,6 +594,27 @@ fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k, f
   if (st != FB_OK) return st;
   return run_prefix(*shape, q, k, v, head_reuse_mask, sel, a_out, l_out, a_res, l_res, ws,
                     ws_bytes, stream);
+}
+
+fb_status fb_prefix_attn_noalloc(const fb_attn_shape* shape, fb_tensor q, fb_tensor k,
+                                 fb_tensor v, const uint8_t* head_reuse_mask,
+                                 const fb_page_sel* sel, float* a_out, float* l_out,
+                                 float* a_res, float* l_res, hipStream_t stream) {
+  fb_status st = validate_prefix(shape, q, k, v, sel, a_out, l_out, a_res, l_res);
+  if (st != FB_OK) return st;
+  const PrefixPlan pl = plan_prefix(*shape, q.n_tok, k.n_tok, sel, kv_head_major(*shape, k, v));
+  if (!pl.fits) return FB_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > kScratchBytes) return FB_ERR_WORKSPACE_TOO_SMALL;
+  // the stream must run on the current device (whose scratch copy is used)
+  int cur = -1;
+  hipDevice_t sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return FB_ERR_DEVICE;
+  if (stream && (hipStreamGetDevice(stream, &sdev) != hipSuccess)) return FB_ERR_DEVICE;
+  if (stream && sdev != cur) return FB_ERR_INVALID_ARGUMENT;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0 && (st = scratch_of_current_device(&ws)) != FB_OK) return st;
+  return run_prefix(*shape, q, k, v, head_reuse_mask, sel, a_out, l_out, a_res, l_res, ws,
+                    pl.ws_bytes > 0 ? kScratchBytes : 0, stream);
 }
 
 size_t fb_block_attn_merge_workspace(const fb_attn_shape* shape, int64_t n_q) {

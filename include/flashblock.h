@@ -23,8 +23,10 @@
  * ---------------------------------------
  *  - Every pointer argument is device memory owned by the caller, unless it
  *    is documented as host memory. The library allocates nothing, keeps no
- *    global state and is reentrant: calls on different streams may overlap
- *    as long as they do not share output buffers.
+ *    global state (except the per-device scratch array of
+ *    fb_prefix_attn_noalloc) and is reentrant: calls on different streams
+ *    may overlap as long as they do not share output buffers (calls of
+ *    fb_prefix_attn_noalloc on one GPU may not overlap at all).
  *  - Tensors of q, k, v are described by fb_tensor: element strides between
  *    tokens and between heads; the head dimension is contiguous (stride 1).
  *    Base pointers must be 16-byte aligned and token/head strides multiples
@@ -139,6 +141,37 @@ fb_status fb_prefix_attn(const fb_attn_shape* shape, fb_tensor q, fb_tensor k,
                          const fb_page_sel* sel, float* a_out, float* l_out,
                          float* a_res, float* l_res, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * fb_prefix_attn_noalloc -- fb_prefix_attn without a workspace argument,    *
+ * for callers that cannot allocate device memory (code under HIP graph      *
+ * capture, tight serving loops, harnesses that forbid allocation). The      *
+ * split-K partials (and a sparse selection's bitmaps and page union) live  *
+ * in a fixed 16 MiB device array inside the library, one copy per GPU the  *
+ * library runs on, held until the process ends; its address is looked up   *
+ * on the first call on each device. Arguments and results as               *
+ * fb_prefix_attn. The call allocates nothing (no hipMalloc, no library      *
+ * routine that allocates).                                                  *
+ * stream: must belong to the current device (NULL: the current device's     *
+ *   null stream).                                                           *
+ * Every call on one GPU shares that GPU's array: calls that overlap on one  *
+ * GPU (on different streams, or from different host threads) race and may  *
+ * return wrong results; calls in one stream's order are safe. No byte of    *
+ * the array needs to start at any value: a call reads only what it wrote    *
+ * earlier in the same call.                                                 *
+ * Errors: as fb_prefix_attn, and WORKSPACE_TOO_SMALL when the call needs    *
+ *   more than 16 MiB (fb_prefix_attn_workspace() > 16 MiB, e.g. many query  *
+ *   rows over a long prefix); INVALID_ARGUMENT for a stream of another      *
+ *   device; UNSUPPORTED for device ordinals >= 64. Nothing is launched on  *
+ *   an error.                                                               *
+ * ------------------------------------------------------------------------ */
+#define FB_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fb_status fb_prefix_attn_noalloc(const fb_attn_shape* shape, fb_tensor q,
+                                 fb_tensor k, fb_tensor v,
+                                 const uint8_t* head_reuse_mask,
+                                 const fb_page_sel* sel, float* a_out,
+                                 float* l_out, float* a_res, float* l_res,
+                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * fb_block_attn_merge -- the block-internal pass and the log-space merge.  *

@@ -292,6 +292,23 @@ def test_sparse_split_beyond_the_reduce_is_refused(lib):
     assert st.step == 0 and st.meta_ready == 0
 
 
+def test_noalloc_prefix_refuses_beyond_its_scratch(lib):
+    # checked before any HIP call: bad arguments, then the 16 MiB scratch limit
+    assert fb.NOALLOC_SCRATCH_BYTES == 16 << 20
+    sh = shape(hq=12, hkv=12)
+    q, k = ten(4680, 12), ten(12480, 12)
+    assert lib.fb_prefix_attn_workspace(C.byref(sh), 4680, 12480, None) > 16 << 20
+    f = lib.fb_prefix_attn_noalloc
+    assert f(C.byref(sh), q, k, k, None, None, FAKE, FAKE, None, None, None) == \
+        fb.FB_ERR_WORKSPACE_TOO_SMALL
+    assert f(C.byref(sh), q, k, k, None, None, None, FAKE, None, None, None) == \
+        fb.FB_ERR_INVALID_ARGUMENT
+    sel = fb.fb_page_sel(fb.FB_SEL_SPLIT, 32, 64, FAKE, None)
+    big = ten(9000000, 8)
+    assert f(C.byref(shape()), ten(8, 32), big, big, None, C.byref(sel), FAKE, FAKE, FAKE, FAKE,
+             None) == fb.FB_ERR_UNSUPPORTED
+
+
 # ------------------------------------------------------ growing cache, no GPU
 
 def cache(cap=64, n=60, st=8 * 128, sh=128, k=FAKE, v=FAKE + (1 << 24)):
