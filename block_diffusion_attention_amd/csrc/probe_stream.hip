@@ -1,0 +1,85 @@
+// probe_stream.hip -- the achievable HBM read rate on this part, for the
+// benchmark's roofline: a read-only streaming kernel over two buffers (the
+// prefix K and V the attention pass reads), with the same access style as
+// that pass (16-byte non-temporal loads, several in flight per lane) and no
+// arithmetic beyond an XOR that keeps the loads live. Not part of the
+// FlashBlock ABI: built as its own library, used by the benchmark only.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;           // 16-byte loads in flight per lane
+constexpr int64_t kChunk = int64_t(kThreads) * kUnroll * 16;   // bytes per round of a workgroup
+
+// Workgroup w reads rounds w, w + grid, w + 2 grid, ... of the concatenation
+// of a and b (each a multiple of 16 bytes); bytes past a's end come from b.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* a, int64_t a_vecs,
+                                                               const u32x4* b, int64_t b_vecs,
+                                                               uint32_t* out) {
+  const int64_t total = a_vecs + b_vecs;
+  const int64_t per_round = kChunk / 16;
+  uint32_t acc = 0;
+  for (int64_t r = blockIdx.x; r * per_round < total; r += gridDim.x) {
+    const int64_t base = r * per_round + threadIdx.x;
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = base + int64_t(u) * kThreads;
+      if (i < a_vecs) {
+        v[u] = __builtin_nontemporal_load(a + i);
+      } else if (i < total) {
+        v[u] = __builtin_nontemporal_load(b + (i - a_vecs));
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // one word per workgroup: thread 0's value (the XOR of the rest is folded
+  // through a shuffle so no load is dead)
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  __shared__ uint32_t wave_acc[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wave_acc[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t x = 0;
+    for (int w = 0; w < kThreads / 64; ++w) x ^= wave_acc[w];
+    out[blockIdx.x] = x;
+  }
+}
+
+__global__ void empty_kernel() {}
+
+}  // namespace
+
+extern "C" {
+
+// n back-to-back launches of an empty one-wave kernel on `stream`: the
+// launch floor a sequence of n dependent kernels cannot go below.
+int fb_probe_empty_launches(int n, hipStream_t stream) {
+  if (n < 0) return 1;
+  for (int i = 0; i < n; ++i) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Reads a_bytes at a and b_bytes at b (device, 16-byte aligned, sizes
+// multiples of 16) once; out: device [n_workgroups] uint32 (one word each).
+// Returns 0 on success, 1 on invalid arguments, 2 on a launch error.
+int fb_probe_stream_read(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes,
+                         uint32_t* out, int n_workgroups, hipStream_t stream) {
+  if (a_bytes < 0 || b_bytes < 0 || (a_bytes % 16) != 0 || (b_bytes % 16) != 0) return 1;
+  if ((a_bytes > 0 && !a) || (b_bytes > 0 && !b) || !out || n_workgroups < 1) return 1;
+  if ((reinterpret_cast<uintptr_t>(a) % 16) != 0 || (reinterpret_cast<uintptr_t>(b) % 16) != 0)
+    return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(n_workgroups), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(a), a_bytes / 16, static_cast<const u32x4*>(b),
+                     b_bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"
