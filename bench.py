@@ -181,7 +181,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the video and sparse workload measurements")
     ap.add_argument("--only", choices=("video", "sparse", "growing", "losa", "spa", "stack",
-                                       "sweep", "text32k"),
+                                       "stackid", "sweep", "text32k"),
                     help="profiling mode: measure only that workload and print its JSON")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 100k-800k x B in {8, 16} context sweep")
@@ -209,9 +209,10 @@ def main():
     fb.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.only in ("video", "sparse", "growing", "losa", "spa", "stack"):
+    if args.only in ("video", "sparse", "growing", "losa", "spa", "stack", "stackid"):
         fn = {"video": video_extra, "sparse": sparse_extra, "growing": growing_extra,
-              "losa": losa_extra, "spa": spa_extra, "stack": stack_extra}[args.only]
+              "losa": losa_extra, "spa": spa_extra, "stack": stack_extra,
+              "stackid": stack_identification_extra}[args.only]
         print(json.dumps({args.only: fn(fb, W, dev, torch.cuda.current_stream(), args.kv_layout)}),
               flush=True)
         return
@@ -379,6 +380,8 @@ def main():
         extra["losa"] = losa_extra(fb, W, dev, stream, args.kv_layout)
         extra["spa"] = spa_extra(fb, W, dev, stream, args.kv_layout)
         extra["stack"] = stack_extra(fb, W, dev, stream, args.kv_layout)
+        extra["stack_identification"] = stack_identification_extra(fb, W, dev, stream,
+                                                                   args.kv_layout)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
@@ -878,7 +881,7 @@ def spa_extra(fb, W, dev, stream, layout):
     return out
 
 
-def stack_extra(fb, W, dev, stream, layout):
+def stack_identification_extra(fb, W, dev, stream, layout):
     """A 32-layer stack (1024 tokens of width 4096, rank-128 factor per
     layer): one denoising step identifies the tokens to recompute in every
     layer, with the depth schedule of per-layer counts (mean ratio 16%,
@@ -922,6 +925,65 @@ def stack_extra(fb, W, dev, stream, layout):
                 fb.fb_proxy_decide(a, stream)
         ms = _timed(step, stream, 5)
         out["ms_step_%s" % name] = round(ms, 3)
+    return out
+
+
+def stack_extra(fb, W, dev, stream, layout):
+    """A 32-layer stack of FlashBlock text layers (32q/8kv, d = 128, B = 16,
+    8 denoising steps, a 131,072-token prefix per layer; every layer sees
+    the same token updates, M ~ Binomial(16, 0.3)): one block, every layer
+    through fb_step at every step, with the per-layer reuse thresholds of the
+    depth schedule (fb_layer_budgets: mean update ratio 16%, floor 4%, peak
+    at the middle layers; fb_layer_taus: tau_l = round(4 x 0.16 / ratio_l))
+    against a uniform tau = 4. Each layer holds its own prefix K/V in HBM (a
+    copy of one draw: the timing sees only the bytes), and its own block
+    Q/K/V per step."""
+    import torch
+    n_layers, n_prefix = 32, 131072
+    cfg = W.LONG.with_(n_prefix=n_prefix, n_block=16)
+    hq, hkv, d, B = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_block
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kp, vp = W.prefix_kv(cfg)
+    k0, v0 = prefix_cache(kp, dev, layout), prefix_cache(vp, dev, layout)
+    shape = fb.shape_of(hq, hkv, d, cfg.scale, torch.bfloat16)
+    mu = (n_layers - 1) / 2.0
+    ratios, _ = fb.fb_layer_budgets(n_layers, B, 0.16, 0.04, mu, n_layers / 5.0, n_layers / 8.0)
+    taus = fb.fb_layer_taus(B, cfg.tau, 0.16, ratios)
+    layers = []
+    for l in range(n_layers):
+        kl, vl = k0.clone(), v0.clone()            # the layer's own HBM copy, same layout
+        inputs = [(bf(x["q"]), bf(x["k"]), bf(x["v"]), torch.from_numpy(x["ids"]).to(dev))
+                  for x in W.text_steps(cfg, variant=100 + l, update_variant=0)]
+        layers.append((kl, vl, inputs))
+    del k0, v0
+    af = torch.empty(B, hq, d, device=dev)
+    lf = torch.empty(B, hq, device=dev)
+    ids_host = [x["ids"] for x in W.text_steps(cfg, variant=100, update_variant=0)]
+    ms_upd = [int(np.count_nonzero(ids_host[s] != ids_host[s - 1])) for s in range(1, len(ids_host))]
+    out = {"workload": "%d layers x text block (32q/8kv, d=128, B=16, 8 steps, prefix %d per layer)"
+                       % (n_layers, n_prefix),
+           "ratios": [round(r, 4) for r in ratios], "taus_depth": taus, "M_per_step": ms_upd}
+    for name, tl in (("depth", taus), ("uniform_tau4", [cfg.tau] * n_layers)):
+        steps = [fb.Step(fb.FB_STEP_TEXT, shape, B, kl, vl, tau=t) for (kl, vl, _), t in zip(layers, tl)]
+
+        def block():
+            for st in steps:
+                st.new_block()
+            for s in range(len(layers[0][2])):
+                for st, (_, _, inputs) in zip(steps, layers):
+                    q, k, v, ids = inputs[s]
+                    st.step(q, k, v, af, lf, ids=ids)
+        ms = _timed(block, stream, 3)
+        recompute = sum(1 for t in tl for m in ms_upd if m >= t)
+        out["ms_block_%s" % name] = round(ms, 3)
+        out["recompute_layer_steps_%s" % name] = recompute
+        out["query_tok_per_s_%s" % name] = round(len(ids_host) * B / (ms * 1e-3), 1)
+        del steps
+    out["speedup_depth_vs_uniform"] = round(out["ms_block_uniform_tau4"] / out["ms_block_depth"], 3)
+    del layers
+    torch.cuda.empty_cache()
     return out
 
 

@@ -118,6 +118,8 @@ _SIGS = [
     ("fb_layer_budgets", C.c_int,
      [C.c_int32, C.c_int32, C.c_double, C.c_double, C.c_double, C.c_double, C.c_double,
       C.c_void_p, C.c_void_p]),
+    ("fb_layer_taus", C.c_int,
+     [C.c_int32, C.c_int32, C.c_int32, C.c_double, C.c_void_p, C.c_void_p]),
     ("fb_kv_append", C.c_int,
      [C.POINTER(fb_attn_shape), C.POINTER(fb_kv_cache), fb_tensor, fb_tensor, C.c_void_p]),
     ("fb_step_workspace", C.c_size_t, [C.POINTER(fb_step_state)]),
@@ -306,6 +308,16 @@ def proxy_args(x, factor, cache, mask, selected=None, n_select=0, init=False, si
     a.sim, a.proxy = ptr(sim), ptr(proxy)
     a.ws, a.ws_bytes = ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
     return a
+
+
+def fb_layer_taus(block, base_tau, mean_ratio, ratios):
+    """Host schedule: per-layer reuse thresholds (list) from per-layer ratios."""
+    n = len(ratios)
+    r = (C.c_double * n)(*[float(x) for x in ratios])
+    taus = (C.c_int32 * n)()
+    _check("fb_layer_taus", load().fb_layer_taus(int(n), int(block), int(base_tau),
+                                                 float(mean_ratio), r, taus))
+    return list(taus)
 
 
 def fb_layer_budgets(n_layers, n_tok, mean_ratio, floor_ratio, mu, s_left, s_right):

@@ -830,6 +830,29 @@ fb_status fb_layer_budgets(int32_t n_layers, int32_t n_tok, double mean_ratio, d
   return FB_OK;
 }
 
+fb_status fb_layer_taus(int32_t n_layers, int32_t block, int32_t base_tau, double mean_ratio,
+                        const double* ratios, int32_t* taus) {
+#pragma clang fp contract(off)
+  if (n_layers < 1 || block < 1 || base_tau < 1 || !ratios || !taus) return FB_ERR_INVALID_ARGUMENT;
+  if (!isfinite(mean_ratio) || !(mean_ratio > 0.0 && mean_ratio <= 1.0))
+    return FB_ERR_INVALID_ARGUMENT;
+  for (int l = 0; l < n_layers; ++l)
+    if (!isfinite(ratios[l])) return FB_ERR_INVALID_ARGUMENT;
+  // tau_l = floor(base_tau mean_ratio / ratio_l + 1/2) in [1, block + 1];
+  // a layer with no budget (ratio <= 0) never recomputes after its first step
+  const double q = static_cast<double>(base_tau) * mean_ratio;
+  const double never = static_cast<double>(block) + 1.0;
+  for (int l = 0; l < n_layers; ++l) {
+    double t = never;
+    if (ratios[l] > 0.0) {
+      t = floor(q / ratios[l] + 0.5);
+      t = t < 1.0 ? 1.0 : (t > never ? never : t);
+    }
+    taus[l] = static_cast<int32_t>(t);
+  }
+  return FB_OK;
+}
+
 fb_status fb_kv_append(const fb_attn_shape* shape, fb_kv_cache* c, fb_tensor k_blk,
                        fb_tensor v_blk, hipStream_t stream) {
   fb_status st = check_shape(shape);

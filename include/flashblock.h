@@ -363,6 +363,25 @@ fb_status fb_layer_budgets(int32_t n_layers, int32_t n_tok, double mean_ratio,
                            double s_right, double* ratios, int32_t* counts);
 
 /* ------------------------------------------------------------------------ *
+ * fb_layer_taus -- per-layer reuse thresholds of a stack of FlashBlock       *
+ * layers from per-layer update budgets. HOST function.                      *
+ * FlashBlock s2 "adaptive reuse strategies" (a layer reuses its cached      *
+ * pair while fewer than tau block tokens changed) under SPA-Cache           *
+ * methodology s2 "adaptive budget allocation" (a layer whose states drift   *
+ * more gets a larger update budget): a layer's staleness tolerance is       *
+ * inversely proportional to its budget, scaled so that a layer at the mean  *
+ * budget keeps base_tau:                                                    *
+ *   taus[l] = floor(base_tau mean_ratio / ratios[l] + 1/2), clamped to      *
+ *   [1, block + 1]; ratios[l] <= 0 -> block + 1 (the layer never            *
+ *   recomputes after a block's first step).                                 *
+ * ratios (host [n_layers], e.g. from fb_layer_budgets), taus (host out).    *
+ * Errors: INVALID_ARGUMENT for n_layers, block or base_tau < 1, NULL        *
+ *   arrays, a non-finite ratio, or mean_ratio outside (0, 1].               *
+ * ------------------------------------------------------------------------ */
+fb_status fb_layer_taus(int32_t n_layers, int32_t block, int32_t base_tau,
+                        double mean_ratio, const double* ratios, int32_t* taus);
+
+/* ------------------------------------------------------------------------ *
  * Growing prefix cache (FlashBlock s1 problem statement: block-wise         *
  * decoding attends over a KV cache that grows as blocks finish).            *
  *                                                                           *

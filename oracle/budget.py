@@ -51,4 +51,27 @@ def layer_counts(n_tok, ratios):
     return out
 
 
-__all__ = ["layer_shape", "layer_ratios", "layer_counts"]
+def layer_taus(ratios, block, base_tau, mean_ratio):
+    """Per-layer reuse thresholds of a stack of FlashBlock layers.
+
+    [FB s2 "adaptive reuse strategies"]: a layer reuses its cached pair while
+    fewer than tau block tokens changed; [SPA methodology s2]: layers whose
+    states drift more get a larger update budget. Reading: a layer's
+    staleness tolerance is inversely proportional to its budget, scaled so
+    that a layer at the mean budget keeps base_tau:
+    tau(l) = floor(base_tau * mean_ratio / ratio(l) + 1/2), clamped to
+    [1, block + 1]; a layer with no budget (ratio <= 0) gets block + 1 and so
+    never recomputes after the first step of a block.
+    """
+    out = np.empty(len(ratios), dtype=np.int32)
+    never = block + 1
+    for l, r in enumerate(ratios):
+        if r <= 0:
+            out[l] = never
+        else:
+            t = math.floor(base_tau * mean_ratio / r + 0.5)
+            out[l] = min(max(t, 1), never)
+    return out
+
+
+__all__ = ["layer_shape", "layer_ratios", "layer_counts", "layer_taus"]

@@ -75,3 +75,45 @@ def test_host_entry_point_rejects():
         p[i] = bad
         assert lib.fb_layer_budgets(*p, None, counts) == 1, (i, bad)
     assert lib.fb_layer_budgets(*good, None, None) == 1
+
+
+def test_taus_hand_values():
+    # base 4 at the mean ratio 0.16, B = 16 (never = 17):
+    # 0.64 / r: 0.16 -> 4, 0.32 -> 2, 0.08 -> 8, 0.04 -> 16, 0 -> 17 (no
+    # budget), 0.64 -> 1, 0.01 -> 64 clamped to 17, 0.11 -> 5.82 rounds to 6
+    r = [0.16, 0.32, 0.08, 0.04, 0.0, 0.64, 0.01, 0.11]
+    assert B.layer_taus(r, 16, 4, 0.16).tolist() == [4, 2, 8, 16, 17, 1, 17, 6]
+    assert B.layer_taus([1.0, 0.5], 4, 3, 0.9).tolist() == [3, 5]       # 2.7 -> 3, 5.4 -> 5
+
+
+def test_taus_fall_as_the_budget_grows():
+    r = B.layer_ratios(32, 0.16, 0.04, 15.5, 6.4, 4.0)
+    t = B.layer_taus(r, 16, 4, 0.16)
+    order = np.argsort(r)
+    assert (np.diff(t[order]) <= 0).all()            # larger budget -> no larger tau
+    assert t[np.argmax(r)] < 4 < t[np.argmin(r)]
+    # a uniform schedule keeps the base threshold in every layer
+    assert (B.layer_taus(np.full(8, 0.16), 16, 4, 0.16) == 4).all()
+
+
+def test_taus_host_entry_point_matches_bit_for_bit():
+    import block_diffusion_attention_amd as fb
+    r = B.layer_ratios(32, 0.16, 0.04, 15.5, 6.4, 4.0)
+    for block, base in ((16, 4), (8, 2), (4, 2), (16, 1)):
+        assert fb.fb_layer_taus(block, base, 0.16, r) == B.layer_taus(r, block, base, 0.16).tolist()
+    odd = [0.16, 0.32, 0.08, 0.04, 0.0, 0.64, 0.01, 0.11, -0.5, 1e-300]
+    assert fb.fb_layer_taus(16, 4, 0.16, odd) == B.layer_taus(odd, 16, 4, 0.16).tolist()
+
+
+def test_taus_host_entry_point_rejects():
+    import block_diffusion_attention_amd as fb
+    lib = fb.load()
+    r = (C.c_double * 3)(0.1, 0.2, 0.3)
+    t = (C.c_int32 * 3)()
+    assert lib.fb_layer_taus(3, 16, 4, 0.16, r, t) == 0
+    for args in ((0, 16, 4, 0.16, r, t), (3, 0, 4, 0.16, r, t), (3, 16, 0, 0.16, r, t),
+                 (3, 16, 4, 0.0, r, t), (3, 16, 4, 1.5, r, t), (3, 16, 4, float("nan"), r, t),
+                 (3, 16, 4, 0.16, None, t), (3, 16, 4, 0.16, r, None)):
+        assert lib.fb_layer_taus(*args) == 1, args
+    bad = (C.c_double * 3)(0.1, float("inf"), 0.3)
+    assert lib.fb_layer_taus(3, 16, 4, 0.16, bad, t) == 1

@@ -192,11 +192,14 @@ def _draw_m(cfg, g):
     return 0
 
 
-def text_steps(cfg, variant=0, block=0, m_override=None):
+def text_steps(cfg, variant=0, block=0, m_override=None, update_variant=None):
     """Per-step block inputs: dicts with q [B,Hq,d], k, v [B,Hkv,d], ids [B].
 
     ``m_override`` (list, one entry per step >= 1, or None entries) fixes M
     for chosen steps; positions are still drawn from the step's seed.
+    ``update_variant``: draw M and the updated positions from that variant's
+    seeds instead of ``variant``'s (layers of one stack share the block's
+    token updates and differ in their Q/K/V).
     """
     b, hq, hkv, d = cfg.n_block, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     steps = []
@@ -216,7 +219,8 @@ def text_steps(cfg, variant=0, block=0, m_override=None):
             m = b
             pos = np.arange(b)
         else:
-            gu = rng(cfg.cfg_id, variant, block, s, TAG_UPDATE)
+            gu = rng(cfg.cfg_id, variant if update_variant is None else update_variant, block, s,
+                     TAG_UPDATE)
             m = _draw_m(cfg, gu)
             if m_override is not None and m_override[s] is not None:
                 m = int(m_override[s])
@@ -227,6 +231,19 @@ def text_steps(cfg, variant=0, block=0, m_override=None):
             next_id += m
         steps.append(dict(q=q, k=k, v=v, ids=ids, m_drawn=m, updated=pos))
     return steps
+
+
+def stack_layers(cfg, n_layers, block=0, n_prefix=None):
+    """A stack of n_layers synthetic layers of the text workload ``cfg``: per
+    layer its own prefix K/V (variant 100 + l) and block Q/K/V per step;
+    every layer sees the same token updates (M, positions and ids of
+    variant 0), as the layers of one model do. Returns a list of
+    (k_prefix, v_prefix, steps)."""
+    out = []
+    for l in range(n_layers):
+        kp, vp = prefix_kv(cfg, n_tok=n_prefix, variant=100 + l)
+        out.append((kp, vp, text_steps(cfg, variant=100 + l, block=block, update_variant=0)))
+    return out
 
 
 # --------------------------------------------------------------------------
