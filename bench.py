@@ -745,7 +745,7 @@ def sparse_extra(fb, W, dev, stream, layout):
         ms_block = _timed(block, stream, 5)
         # the gather pass alone, on the block's last selection and active set
         act = st.active.clone()
-        sel = fb.page_sel(fb.FB_SEL_GATHER, PS, st.pages, act)
+        sel = fb.page_sel(fb.FB_SEL_GATHER, PS, st.pages, act, st.sel_bitmap)
         ws = torch.empty(max(fb.fb_prefix_attn_workspace(shape, B, N, sel), 16), dtype=torch.uint8,
                          device=dev)
         a = st.a_out.clone()

@@ -17,7 +17,7 @@ from ._abi import (  # noqa: F401
     FB_STEP_TEXT, FB_STEP_VIDEO, LIB_PATH, SYMBOLS, FlashBlockError, dtype_code,
     fb_abi_version, fb_attn_shape, fb_block_attn_merge, fb_block_attn_merge_workspace,
     fb_kv_append, fb_kv_cache, fb_layer_budgets, fb_layer_taus, fb_proxy_args, fb_proxy_decide, fb_proxy_decide_workspace,
-    proxy_args, fb_page_meta, fb_page_meta_update, fb_page_sel, fb_page_select,
+    proxy_args, fb_page_bitmap, fb_page_meta, fb_page_meta_update, fb_page_sel, fb_page_select,
     fb_page_select_workspace, fb_prefix_attn, fb_prefix_attn_noalloc, fb_prefix_attn_workspace,
     fb_reuse_args, NOALLOC_SCRATCH_BYTES,
     fb_reuse_decide, fb_reuse_decide_workspace, fb_status_string, fb_step, fb_step_args,
@@ -82,12 +82,14 @@ class Step:
     prefix (the next call recomputes the cached pair). ``since_refresh``:
     TEXT counts the ids changed since the last recompute step. ``reselect``:
     SPARSE runs LoSA's own step (dense first step, pages chosen again at
-    every step, no residual).
+    every step, no residual). ``sel_bitmap``: SPARSE (residual mode) keeps the
+    refresh step's selection as bitmaps in a buffer of its own, so later
+    steps run no selection prep (False: rebuilt every step).
     """
 
     def __init__(self, mode, shape, n_q, k_prefix=None, v_prefix=None, tau=0, gamma=0.0,
                  page_size=16, k_pages=0, pct=25, device=None, cache=None,
-                 since_refresh=False, reselect=False):
+                 since_refresh=False, reselect=False, sel_bitmap=True):
         load()
         self.cache = cache
         if cache is not None:
@@ -143,6 +145,13 @@ class Step:
             self.active = torch.zeros(n_q, device=dev, dtype=torch.uint8)
             for name in ("a_res", "l_res", "pages", "kmin", "kmax", "q_prev", "mse", "active"):
                 setattr(st, name, ptr(getattr(self, name)))
+            # FlashBlock's residual mode keeps the refresh step's selection as
+            # bitmaps: later steps read them instead of rebuilding them
+            self.sel_bitmap = None
+            if not reselect and sel_bitmap:
+                words = (max(n_pages, 1) + 31) // 32
+                self.sel_bitmap = torch.zeros(n_q, hkv, words, device=dev, dtype=torch.int32)
+                st.sel_bitmap = ptr(self.sel_bitmap)
             st.page_cap = n_pages if cache is not None else 0
             st.sparse_reselect = 1 if reselect else 0
         st.count_since_refresh = 1 if since_refresh else 0

@@ -18,7 +18,7 @@ FB_BF16, FB_F32 = 0, 1
 FB_SEL_DENSE, FB_SEL_SPLIT, FB_SEL_GATHER = 0, 1, 2
 FB_REUSE_COUNT, FB_REUSE_HEAD_COS, FB_REUSE_ACTIVE_MSE = 0, 1, 2
 FB_STEP_TEXT, FB_STEP_VIDEO, FB_STEP_SPARSE = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class fb_attn_shape(C.Structure):
@@ -33,7 +33,7 @@ class fb_tensor(C.Structure):
 
 class fb_page_sel(C.Structure):
     _fields_ = [("mode", C.c_int), ("page_size", C.c_int32), ("k_pages", C.c_int32),
-                ("pages", C.c_void_p), ("active", C.c_void_p)]
+                ("pages", C.c_void_p), ("active", C.c_void_p), ("bitmap", C.c_void_p)]
 
 
 class fb_reuse_args(C.Structure):
@@ -78,7 +78,7 @@ class fb_step_state(C.Structure):
                 ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
                 ("step", C.c_int64), ("meta_ready", C.c_int32),
                 ("page_cap", C.c_int64), ("count_since_refresh", C.c_int32),
-                ("sparse_reselect", C.c_int32)]
+                ("sparse_reselect", C.c_int32), ("sel_bitmap", C.c_void_p)]
 
 
 class fb_step_args(C.Structure):
@@ -113,6 +113,9 @@ _SIGS = [
     ("fb_page_select", C.c_int,
      [C.POINTER(fb_attn_shape), fb_tensor, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
       C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    ("fb_page_bitmap", C.c_int,
+     [C.POINTER(fb_attn_shape), C.c_void_p, C.c_int64, C.c_int64, C.c_int32, C.c_void_p,
+      C.c_void_p]),
     ("fb_proxy_decide_workspace", C.c_size_t, [C.POINTER(fb_proxy_args)]),
     ("fb_proxy_decide", C.c_int, [C.POINTER(fb_proxy_args), C.c_void_p]),
     ("fb_layer_budgets", C.c_int,
@@ -205,9 +208,17 @@ def stream_of(stream=None):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
-def page_sel(mode, page_size=16, pages=None, active=None):
+def page_sel(mode, page_size=16, pages=None, active=None, bitmap=None):
     k = 0 if pages is None else int(pages.shape[-1])
-    return fb_page_sel(int(mode), int(page_size), k, ptr(pages), ptr(active))
+    return fb_page_sel(int(mode), int(page_size), k, ptr(pages), ptr(active), ptr(bitmap))
+
+
+def fb_page_bitmap(shape, pages, n_pages, bitmap, stream=None):
+    """Selection bitmaps [n_q, Hkv, ceil(n_pages / 32)] uint32 of page lists
+    pages [n_q, Hkv, k]."""
+    _check("fb_page_bitmap", load().fb_page_bitmap(
+        C.byref(shape), ptr(pages), int(pages.shape[0]), int(n_pages), int(pages.shape[-1]),
+        ptr(bitmap), stream_of(stream)))
 
 
 # ------------------------------------------------------------------- wrappers

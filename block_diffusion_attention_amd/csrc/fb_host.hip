@@ -49,6 +49,9 @@ namespace {
 #ifndef FB_ROWS_MAX_DYN
 #define FB_ROWS_MAX_DYN 8         // key chunks a masked many-rows pass may take
 #endif
+#ifndef FB_SPARSE_GATHER_OCC
+#define FB_SPARSE_GATHER_OCC 1    // GATHER pass: workgroups per CU the split-K plan aims at
+#endif
 #ifndef FB_TEXT_FUSE_REDUCE
 #define FB_TEXT_FUSE_REDUCE 1   // text and sparse steps: the in-block kernel merges the partials
 #endif
@@ -178,6 +181,7 @@ PrefixPlan plan_prefix(const fb_attn_shape& s, int64_t n_q, int64_t n_kv, const 
   if (n_tiles > 0) {
     const int64_t occ = pl.path == PATH_MFMA   ? prefix_mfma_occupancy(pl.row_blocks)
                         : pl.path == PATH_ROWS ? rows_occupancy()
+                        : (pl.path == PATH_SPARSE && mode == FB_SEL_GATHER) ? FB_SPARSE_GATHER_OCC
                                                : 1;
     int64_t want = kTargetWorkgroups * occ / wg_per_chunk;
     if (want < 1) want = 1;
@@ -315,7 +319,28 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
       int32_t* ul = gather ? reinterpret_cast<int32_t*>(w + pl.off_ul) : nullptr;
       int32_t* uc = gather ? reinterpret_cast<int32_t*>(w + pl.off_uc) : nullptr;
       // (k_pages = 0: all-zero bitmaps, no list is read)
-      if (hooks && hooks->am) {
+      if (sel->bitmap) {
+        // the caller's bitmaps: no selection prep; a GATHER pass takes the
+        // union (and, with a classification hook, the active set) itself
+        bm = const_cast<uint32_t*>(sel->bitmap);
+        e = hipSuccess;
+        if (gather) {
+          if (!gather_union_fits(static_cast<int>(n_q), pl.words)) {
+            if (hooks && hooks->am) return FB_ERR_UNSUPPORTED;
+            e = launch_sel_union(bm, sel->active, static_cast<int>(n_q), s.n_kv_heads, pl.words,
+                                 ul, uc, static_cast<int>(pl.n_pages), stream);
+          } else {
+            pp.union_from_bitmap = 1;
+            if (hooks && hooks->am) {
+              if (!gather_classify_fits(static_cast<int>(n_q), s.n_q_heads)) return FB_ERR_UNSUPPORTED;
+              pp.classify = 1;
+              pp.am = *hooks->am;
+            }
+          }
+        } else if (hooks && hooks->am) {
+          return FB_ERR_UNSUPPORTED;
+        }
+      } else if (hooks && hooks->am) {
         if (!gather || !sel_prep_mse_fits(static_cast<int>(n_q), s.n_q_heads, pl.words))
           return FB_ERR_UNSUPPORTED;
         e = launch_sel_prep_mse(sel->pages, static_cast<int>(n_q), s.n_kv_heads, sel->k_pages,
@@ -749,6 +774,20 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
                                 bound, pages, stream));
 }
 
+fb_status fb_page_bitmap(const fb_attn_shape* shape, const int32_t* pages, int64_t n_q,
+                         int64_t n_pages, int32_t k_pages, uint32_t* bitmap, hipStream_t stream) {
+  fb_status st = check_shape(shape);
+  if (st != FB_OK) return st;
+  if (n_q < 1 || n_pages < 1 || n_pages > INT32_MAX || k_pages < 0 || k_pages > n_pages)
+    return FB_ERR_INVALID_ARGUMENT;
+  if (!bitmap || (k_pages > 0 && !pages)) return FB_ERR_INVALID_ARGUMENT;
+  const int64_t words = (n_pages + 31) / 32;
+  if (words > kMaxBitmapWords) return FB_ERR_UNSUPPORTED;
+  if (n_q > INT32_MAX / shape->n_kv_heads) return FB_ERR_INVALID_ARGUMENT;
+  return dev(launch_sel_bitmap(pages, static_cast<int>(n_q) * shape->n_kv_heads, k_pages,
+                               static_cast<int>(words), static_cast<int>(n_pages), bitmap, stream));
+}
+
 size_t fb_proxy_decide_workspace(const fb_proxy_args* a) {
   if (!a || a->n_tok < 1 || a->d_model < 1 || !proxy_rank_ok(a->rank)) return 0;
   const size_t n = static_cast<size_t>(a->n_tok), r = static_cast<size_t>(a->rank);
@@ -1056,8 +1095,13 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         return dev(launch_copy_rows(a->q_blk.ptr, a->q_blk.stride_tok, a->q_blk.stride_head,
                                     st->q_prev, n_q, hq, d, s.dtype, stream));
       };
+      // FlashBlock's residual mode with a bitmap buffer: the refresh step
+      // writes the selection as bitmaps, later steps read them (no prep)
+      const bool prebuilt = st->sel_bitmap != nullptr && !reselect &&
+                            (n_pages + 31) / 32 <= kMaxBitmapWords;
       // a FlashBlock step the controller left open (decision -1) on the sparse
-      // kernel: the token classification rides on the selection prep
+      // kernel: the token classification rides on the selection prep, or on
+      // the GATHER pass itself when the bitmaps are prebuilt
       bool fuse_mse = false;
       if (!first && a->decision == -1 && !reselect && st->k_prefix.n_tok > 0) {
         fb_page_sel g = sel;
@@ -1065,7 +1109,9 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         g.active = st->active;
         const PrefixPlan gp = plan_prefix(s, n_q, st->k_prefix.n_tok, &g, false);
         fuse_mse = gp.path == PATH_SPARSE && gp.n_chunks > 0 &&
-                   sel_prep_mse_fits(static_cast<int>(n_q), hq, gp.words);
+                   (prebuilt ? gather_union_fits(static_cast<int>(n_q), gp.words) &&
+                                   gather_classify_fits(static_cast<int>(n_q), hq)
+                             : sel_prep_mse_fits(static_cast<int>(n_q), hq, gp.words));
       }
       if (first) {
         if (!st->meta_ready) {
@@ -1083,6 +1129,11 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
           rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
                               nullptr, st->pages, nullptr, st->ws, st->ws_bytes, stream);
           if (rc != FB_OK) return rc;
+          if (prebuilt && n_pages > 0) {
+            rc = fb_page_bitmap(&s, st->pages, n_q, n_pages, st->k_pages, st->sel_bitmap, stream);
+            if (rc != FB_OK) return rc;
+            sel.bitmap = st->sel_bitmap;
+          }
           sel.mode = FB_SEL_SPLIT;
           rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, &sel, st->a_out,
                               st->l_out, st->a_res, st->l_res, st->ws, st->ws_bytes, stream);
@@ -1109,6 +1160,7 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         }
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
+        if (prebuilt) sel.bitmap = st->sel_bitmap;
         rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, &sel, st->a_out, st->l_out,
                              st->a_res, st->l_res);
         if (rc != FB_OK) return rc;
@@ -1125,6 +1177,7 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         }
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
+        if (prebuilt) sel.bitmap = st->sel_bitmap;
         float* ar = reselect ? nullptr : st->a_res;
         float* lr = reselect ? nullptr : st->l_res;
         const PrefixPlan gp = plan_prefix(s, n_q, st->k_prefix.n_tok, &sel,

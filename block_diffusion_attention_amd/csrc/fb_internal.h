@@ -78,8 +78,59 @@ __device__ __forceinline__ double sq_diff_sum(const T* prev, const T* cur, int d
   return acc;
 }
 
+// Sum over j = 0..31, in order, of (cur[j] - prev[j])^2 in float64
+// (difference, square, add: no contraction); both rows 16-byte aligned. All
+// loads are issued before the arithmetic.
+template <typename T>
+__device__ __forceinline__ double sq_diff_sum32(const T* prev, const T* cur) {
+#pragma clang fp contract(off)
+  constexpr int kV = 16 / sizeof(T);               // elements per 16-byte vector
+  constexpr int kN = 32 / kV;
+  u32x4v va[kN], vb[kN];
+#pragma unroll
+  for (int u = 0; u < kN; ++u) {
+    va[u] = *reinterpret_cast<const u32x4v*>(prev + u * kV);
+    vb[u] = *reinterpret_cast<const u32x4v*>(cur + u * kV);
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int u = 0; u < kN; ++u) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if constexpr (sizeof(T) == 2) {
+        const double d0 = static_cast<double>(__uint_as_float(vb[u][w] << 16)) -
+                          static_cast<double>(__uint_as_float(va[u][w] << 16));
+        const double s0 = d0 * d0;
+        acc = acc + s0;
+        const double d1 = static_cast<double>(__uint_as_float(vb[u][w] & 0xffff0000u)) -
+                          static_cast<double>(__uint_as_float(va[u][w] & 0xffff0000u));
+        const double s1 = d1 * d1;
+        acc = acc + s1;
+      } else {
+        const double d0 = static_cast<double>(__uint_as_float(vb[u][w])) -
+                          static_cast<double>(__uint_as_float(va[u][w]));
+        const double s0 = d0 * d0;
+        acc = acc + s0;
+      }
+    }
+  }
+  return acc;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// A sparse GATHER step's token classification done inside the selection
+// prep or the GATHER pass itself: query MSE against q_prev, nearest-rank
+// cutoff, active flags (the same arithmetic as the active-step kernel).
+struct ActiveFromMse {
+  const void* q_prev;           // [n_q, hq, d] contiguous
+  const void* q_cur; int64_t q_st, q_sh;
+  fb_dtype dt;
+  int hq, d, pct;
+  double* mse;                  // out [n_q], nullable (written by workgroup 0)
+  uint8_t* active;              // out [n_q] (written by workgroup 0)
+};
 
 // Where a prefix pass writes its per-row result: either the final outputs
 // (chunk_stride 0, one chunk) or split-K partials (chunk-major).
@@ -112,6 +163,13 @@ struct PrefixParams {
   int64_t n_pages;
   const int32_t* ulist;         // GATHER: [Hkv, n_pages] union pages, ascending
   const int32_t* ucnt;          // GATHER: [Hkv] union sizes
+  // GATHER with caller-built bitmaps: each workgroup derives the union (and
+  // its slice of it) from the bitmaps and the active flags itself
+  int union_from_bitmap;
+  // ... and, with classify, the active flags too (query MSE against q_prev,
+  // nearest-rank cutoff; workgroup 0 writes mse / active out)
+  int classify;
+  ActiveFromMse am;
 };
 
 // Split-K of the many-rows pass sized on the device: when a head mask leaves
@@ -171,17 +229,6 @@ struct ReduceParams {
   const void* q_src; int64_t q_st, q_sh; void* q_dst; int q_esize;
 };
 
-// A sparse GATHER step's token classification done inside the selection
-// prep: query MSE against q_prev, nearest-rank cutoff, active flags (the
-// same arithmetic as the active-step kernel), then the union over them.
-struct ActiveFromMse {
-  const void* q_prev;           // [n_q, hq, d] contiguous
-  const void* q_cur; int64_t q_st, q_sh;
-  fb_dtype dt;
-  int hq, d, pct;
-  double* mse;                  // out [n_q], nullable (written by workgroup 0)
-  uint8_t* active;              // out [n_q] (written by workgroup 0)
-};
 
 // ---- launchers (return hipError_t of the launch) -----------------------
 // prefix pass
@@ -196,6 +243,8 @@ hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int 
 hipError_t launch_sel_union(const uint32_t* bitmap, const uint8_t* active, int n_q, int hkv,
                             int words, int32_t* ulist, int32_t* ucnt, int n_pages, hipStream_t s);
 bool sel_prep_fits(int n_q, int words);         // bitmaps of one KV group fit in LDS
+bool gather_union_fits(int n_q, int words);     // GATHER derives the union from bitmaps itself
+bool gather_classify_fits(int n_q, int hq);     // ... and classifies the tokens itself
 hipError_t launch_sel_prep(const int32_t* pages, int n_q, int hkv, int k_pages, int words,
                            int n_pages, const uint8_t* active, int do_union, uint32_t* bitmap,
                            int32_t* ulist, int32_t* ucnt, hipStream_t s);

@@ -30,7 +30,14 @@ namespace fb {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kWaves = 4;
+#ifndef FB_SPARSE_PREFETCH
+#define FB_SPARSE_PREFETCH 1      // GATHER: tiles each wave keeps in flight (1; 2 measured no faster)
+#endif
+#ifndef FB_SPARSE_GATHER_WAVES
+#define FB_SPARSE_GATHER_WAVES 4  // waves of a GATHER workgroup (SPLIT: 4, two softmax states)
+#endif
+constexpr int kSplitWaves = 4;
+constexpr int kGatherWaves = FB_SPARSE_GATHER_WAVES;
 constexpr int kTile = 32;
 constexpr int kD = 128;
 constexpr int kKRow = 272;                   // 17 x 16 B: 16 rows, 16 bank groups
@@ -162,16 +169,18 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
   for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
   // page ids are loaded 8 at a time ahead of their LDS atomics; the first
   // batch is in flight during the query loads below
-  const int64_t n_ids = static_cast<int64_t>(n_q) * k_pages;
+  // (n_q k_pages fits 32 bits: the bitmaps of a group fit in LDS)
+  const uint32_t n_ids = static_cast<uint32_t>(n_q) * static_cast<uint32_t>(k_pages);
+  const uint32_t kp32 = static_cast<uint32_t>(k_pages);
   int32_t pv[8];
-  auto load_ids = [&](int64_t i0) {
+  auto load_ids = [&](uint32_t i0) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t i = i0 + u * 1024 + tid;
       pv[u] = -1;
       if (i < n_ids) {
-        const int t = static_cast<int>(i / k_pages);
-        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + i % k_pages];
+        const uint32_t t = i / kp32;
+        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + (i - t * kp32)];
       }
     }
   };
@@ -183,14 +192,14 @@ __global__ __launch_bounds__(1024) void sel_prep_mse_kernel(const int32_t* pages
   }
   __syncthreads();
   // the selection bitmaps of group g (as sel_prep_kernel)
-  for (int64_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
+  for (uint32_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
     if (i0 > 0) load_ids(i0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t i = i0 + u * 1024 + tid;
       const uint32_t pg = static_cast<uint32_t>(pv[u]);
       if (i < n_ids && pg < static_cast<uint32_t>(n_pages))
-        atomicOr(&bm[static_cast<int>(i / k_pages) * words + (pg >> 5)], 1u << (pg & 31));
+        atomicOr(&bm[(i / kp32) * words + (pg >> 5)], 1u << (pg & 31));
     }
   }
   // the token classification
@@ -264,24 +273,26 @@ __global__ __launch_bounds__(1024) void sel_prep_kernel(const int32_t* pages, in
   for (int i = tid; i < n_q * words; i += 1024) bm[i] = 0u;
   __syncthreads();
   // page ids are loaded 8 at a time ahead of their LDS atomics
-  const int64_t n_ids = static_cast<int64_t>(n_q) * k_pages;
-  for (int64_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
+  // (n_q k_pages fits 32 bits: the bitmaps of a group fit in LDS)
+  const uint32_t n_ids = static_cast<uint32_t>(n_q) * static_cast<uint32_t>(k_pages);
+  const uint32_t kp32 = static_cast<uint32_t>(k_pages);
+  for (uint32_t i0 = 0; i0 < n_ids; i0 += 8 * 1024) {
     int32_t pv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t i = i0 + u * 1024 + tid;
       pv[u] = -1;
       if (i < n_ids) {
-        const int t = static_cast<int>(i / k_pages);
-        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + i % k_pages];
+        const uint32_t t = i / kp32;
+        pv[u] = pages[(static_cast<int64_t>(t) * hkv + g) * k_pages + (i - t * kp32)];
       }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t i = i0 + u * 1024 + tid;
+      const uint32_t i = i0 + u * 1024 + tid;
       const uint32_t pg = static_cast<uint32_t>(pv[u]);
       if (i < n_ids && pg < static_cast<uint32_t>(n_pages))
-        atomicOr(&bm[static_cast<int>(i / k_pages) * words + (pg >> 5)], 1u << (pg & 31));
+        atomicOr(&bm[(i / kp32) * words + (pg >> 5)], 1u << (pg & 31));
     }
   }
   __syncthreads();
@@ -312,6 +323,35 @@ __global__ __launch_bounds__(1024) void sel_prep_kernel(const int32_t* pages, in
   }
   if (tid == 0) ucnt[g] = base;
 }
+
+// Exclusive prefix sum of c over the NT threads of the workgroup (exact
+// integers), by wave shuffles and one exchange of the wave totals in wsum
+// (NT / 64 entries); total = the sum over all threads. Every thread calls it;
+// it holds two barriers.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int c, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    pre += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  total = tot;
+  __syncthreads();
+  return x - c + pre;
+}
+
+constexpr int kUnionWords = 1024;            // union bitmaps a GATHER workgroup builds itself
+constexpr int kClassifyTokens = 64;          // tokens it classifies itself
 
 // ---------------------------------------------------------------------------
 // The sparse MFMA pass.
@@ -357,10 +397,19 @@ __device__ __forceinline__ void softmax_set(const float (&x)[16], float c, float
   }
 }
 
-// SPLIT keeps two O states (occupancy 1, the register file holds both).
+// SPLIT keeps two O states (4 waves, one per SIMD: the register file holds
+// both); GATHER runs FB_SPARSE_GATHER_WAVES waves, each with its own tile in
+// flight (8 measured no faster than 4).
+// (GATHER is built for two workgroups per CU: a 256-register budget keeps
+// every value in VGPRs -- with a larger one the compiler parks state in
+// AGPRs and reads it back every tile.)
 template <bool SPLIT>
-__global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixParams p) {
+__global__ __launch_bounds__(64 * (SPLIT ? kSplitWaves : kGatherWaves),
+                             (SPLIT || kGatherWaves > 4) ? 1 : 2)
+void sparse_mfma_kernel(PrefixParams p) {
   constexpr int NSET = SPLIT ? 2 : 1;
+  constexpr int kWaves = SPLIT ? kSplitWaves : kGatherWaves;
+  constexpr int NT = 64 * kWaves;                  // threads
   constexpr int kStage = kWaves * kWaveLds;
   constexpr int kMerge = kWaves * 32 * kMergeStride * 4;
   constexpr int kLds = kMerge > kStage ? kMerge : kStage;
@@ -387,19 +436,136 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
   const int row = slab * 32 + r32;
   const bool row_ok = row < R;
   const int t_row = row_ok ? row / G : 0;
-  const bool row_on = row_ok && (SPLIT || !p.active || p.active[t_row] != 0);
+  const int hpp = p.page_size >> 4;                // 16-key halves per page
+
+  // GATHER with caller-built bitmaps: the token classification (optional)
+  // and the union over the active tokens, in this workgroup, before the
+  // tile LDS is first written (its space serves as scratch here)
+  __shared__ uint8_t act_s[kClassifyTokens];
+  __shared__ int wsum_s[kWaves];
+  __shared__ int utot_s;
+  uint32_t* ubits = reinterpret_cast<uint32_t*>(lds);               // [words]
+  int* upre = reinterpret_cast<int*>(lds) + kUnionWords;            // [words]
+  if (!SPLIT && p.union_from_bitmap) {
+    if (p.classify) {
+      // query MSE per token: per (token, head) four float64 sums of
+      // (cur - prev)^2 over 32 dims each, in dim order, combined in quarter
+      // order, the heads' sums in head order, / (Hq d) (no contraction);
+      // nearest-rank cutoff; active iff above it. Every workgroup computes
+      // the same bits; workgroup 0 writes them out.
+      double* part = reinterpret_cast<double*>(lds + 2 * kUnionWords * 4);   // [n_q hq][4]
+      double* mse_s = part + 4 * p.n_q * p.am.hq;                            // [n_q]
+      const int hq = p.am.hq;
+      const int items = 4 * p.n_q * hq;
+      for (int i = tid; i < items; i += NT) {
+        const int c = i >> 2, qd = i & 3;
+        const int t = c / hq, h = c % hq;
+        const int64_t po = static_cast<int64_t>(c) * kD + 32 * qd;
+        const int64_t co = t * p.am.q_st + h * p.am.q_sh + 32 * qd;
+        part[i] = p.am.dt == FB_BF16
+                      ? sq_diff_sum32<uint16_t>(static_cast<const uint16_t*>(p.am.q_prev) + po,
+                                                static_cast<const uint16_t*>(p.am.q_cur) + co)
+                      : sq_diff_sum32<float>(static_cast<const float*>(p.am.q_prev) + po,
+                                             static_cast<const float*>(p.am.q_cur) + co);
+      }
+      __syncthreads();
+      {
+#pragma clang fp contract(off)
+        for (int t = tid; t < p.n_q; t += NT) {
+          double total = 0.0;
+          for (int h = 0; h < hq; ++h) {
+            const double* q4 = part + 4 * (t * hq + h);
+            const double ch = ((q4[0] + q4[1]) + q4[2]) + q4[3];
+            total = total + ch;
+          }
+          mse_s[t] = total / static_cast<double>(hq * kD);
+        }
+      }
+      __syncthreads();
+      int rank = (p.am.pct * p.n_q + 99) / 100;
+      if (rank < 1) rank = 1;
+      double cut = 0.0;
+      for (int t = 0; t < p.n_q; ++t) {              // every thread finds the same cutoff
+        const double v = mse_s[t];
+        int less = 0, leq = 0;
+        for (int u = 0; u < p.n_q; ++u) {
+          less += mse_s[u] < v ? 1 : 0;
+          leq += mse_s[u] <= v ? 1 : 0;
+        }
+        if (less < rank && rank <= leq) cut = v;
+      }
+      for (int t = tid; t < p.n_q; t += NT) {
+        const uint8_t a = mse_s[t] > cut ? 1 : 0;
+        act_s[t] = a;
+        if (blockIdx.x == 0) {
+          p.am.active[t] = a;
+          if (p.am.mse) p.am.mse[t] = mse_s[t];
+        }
+      }
+    } else {
+      for (int t = tid; t < p.n_q; t += NT) act_s[t] = (!p.active || p.active[t]) ? 1 : 0;
+    }
+    const int words = p.words;
+    for (int wd = tid; wd < words; wd += NT) ubits[wd] = 0u;
+    __syncthreads();
+    // union words of group g over the active tokens: every (token, word)
+    // load in flight at once, folded into LDS
+    {
+      const int n_ld = p.n_q * words;
+      constexpr int kU = 8;
+      for (int i0 = 0; i0 < n_ld; i0 += kU * NT) {
+        uint32_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = i0 + u * NT + tid;
+          const int t = i < n_ld ? i / words : 0, wd = i - t * words;
+          v[u] = (i < n_ld && act_s[t])
+                     ? p.bitmap[(static_cast<int64_t>(t) * p.hkv + g) * words + wd] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = i0 + u * NT + tid;
+          if (i < n_ld && v[u]) atomicOr(&ubits[i % words], v[u]);
+        }
+      }
+    }
+    __syncthreads();
+    // popcounts' exclusive prefix over the words
+    const int per = (words + NT - 1) / NT;           // consecutive words per thread
+    int c = 0;
+    for (int k = 0; k < per; ++k) {
+      const int wd = tid * per + k;
+      if (wd < words) c += __popc(ubits[wd]);
+    }
+    int total;
+    int pre = block_excl_scan<NT>(c, wsum_s, total);
+    for (int k = 0; k < per; ++k) {
+      const int wd = tid * per + k;
+      if (wd < words) {
+        upre[wd] = pre;
+        pre += __popc(ubits[wd]);
+      }
+    }
+    if (tid == 0) utot_s = total;
+    __syncthreads();
+  }
+  auto tok_on = [&](int t) -> bool {
+    if (SPLIT) return true;
+    if (p.union_from_bitmap) return act_s[t] != 0;
+    return !p.active || p.active[t] != 0;
+  };
+  const bool row_on = row_ok && tok_on(t_row);
 
   // tiles of this group: all keys (SPLIT) or the union of selected pages
-  const int hpp = p.page_size >> 4;                // 16-key halves per page
   int64_t n_vt;
   const int32_t* ulist = nullptr;
   int64_t n_half = 0;
   if (SPLIT) {
     n_vt = (p.n_kv + kTile - 1) / kTile;
   } else {
-    n_half = static_cast<int64_t>(p.ucnt[g]) * hpp;
+    n_half = static_cast<int64_t>(p.union_from_bitmap ? utot_s : p.ucnt[g]) * hpp;
     n_vt = (n_half + 1) / 2;
-    ulist = p.ulist + static_cast<int64_t>(g) * p.n_pages;
+    if (!p.union_from_bitmap) ulist = p.ulist + static_cast<int64_t>(g) * p.n_pages;
   }
   // GATHER: the planned chunks share the actual union (no more tiles each
   // than planned for a union of every page)
@@ -414,15 +580,15 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
   };
   auto row_written = [&](int r) -> bool {
     if (r >= R) return false;
-    return SPLIT || !p.active || p.active[r / G] != 0;
+    return tok_on(r / G);
   };
 
   if (vt_begin >= vt_end) {                        // (GATHER) nothing to read: identity partial
-    for (int e = tid; e < 32 * kD; e += 256) {
+    for (int e = tid; e < 32 * kD; e += NT) {
       const int r = slab * 32 + e / kD;
       if (row_written(r)) p.out.a[out_row(r, 0) * kD + e % kD] = 0.f;
     }
-    for (int r0 = tid; r0 < 32; r0 += 256) {
+    for (int r0 = tid; r0 < 32; r0 += NT) {
       const int r = slab * 32 + r0;
       if (row_written(r)) p.out.l[out_row(r, 0)] = kNegInf;
     }
@@ -434,7 +600,23 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
   if (!SPLIT) {
     int64_t slice1 = (2 * vt_end - 1) / hpp;         // inclusive, within the union
     slice1 = slice1 < (n_half - 1) / hpp ? slice1 : (n_half - 1) / hpp;
-    for (int64_t i = tid; i <= slice1 - slice0; i += 256) upage[i] = ulist[slice0 + i];
+    if (p.union_from_bitmap) {
+      // the union pages of rank slice0 .. slice1, from the words that hold them
+      const int s0 = static_cast<int>(slice0), s1 = static_cast<int>(slice1);
+      for (int wd = tid; wd < p.words; wd += NT) {
+        int r = upre[wd];
+        uint32_t u = ubits[wd];
+        if (r > s1 || r + __popc(u) <= s0) continue;
+        while (u) {
+          const int b = __builtin_ctz(u);
+          if (r >= s0 && r <= s1) upage[r - s0] = wd * 32 + b;
+          ++r;
+          u &= u - 1;
+        }
+      }
+    } else {
+      for (int64_t i = tid; i <= slice1 - slice0; i += NT) upage[i] = ulist[slice0 + i];
+    }
     __syncthreads();
   }
 
@@ -463,9 +645,15 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
   const char* v_rd = vl + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
 
   const int64_t vt_last = vt_end - 1;
-  auto load_tile = [&](int64_t vt) -> SpTile {
+  // token and page arithmetic in 32 bits (prefixes on this path hold fewer
+  // than 2^31 keys), with no division for the usual 16-token pages
+  const uint32_t n_pages32 = static_cast<uint32_t>(p.n_pages);
+  const uint32_t ps32 = static_cast<uint32_t>(p.page_size);
+  const uint32_t hpp32 = static_cast<uint32_t>(hpp);
+  const uint32_t slice0_32 = static_cast<uint32_t>(slice0);
+  auto load_tile = [&](int64_t vt64) -> SpTile {
     SpTile r;
-    vt = vt < vt_last ? vt : vt_last;
+    const uint32_t vt = static_cast<uint32_t>(vt64 < vt_last ? vt64 : vt_last);
     int64_t tok0[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -473,16 +661,23 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
       int32_t page;
       bool exists;
       if (SPLIT) {
-        tok = vt * kTile + 16 * h;
-        const int64_t pg = tok / p.page_size;            // (past n_kv: no keys, any bit)
-        page = static_cast<int32_t>(pg < p.n_pages ? pg : p.n_pages - 1);
+        const uint32_t t32 = vt * kTile + 16 * h;
+        const uint32_t pg = hpp32 == 1 ? t32 >> 4 : t32 / ps32;   // (past n_kv: no keys, any bit)
+        page = static_cast<int32_t>(pg < n_pages32 ? pg : n_pages32 - 1);
+        tok = t32;
         exists = true;
       } else {
-        int64_t hx = 2 * vt + h;
-        exists = hx < n_half;
+        uint32_t hx = 2 * vt + h;
+        exists = hx < static_cast<uint64_t>(n_half);
         hx = exists ? hx : 2 * vt;
-        page = upage[hx / hpp - slice0];
-        tok = static_cast<int64_t>(page) * p.page_size + 16 * (hx % hpp);
+        if (hpp32 == 1) {
+          page = upage[hx - slice0_32];
+          tok = static_cast<int64_t>(static_cast<uint32_t>(page) * ps32);
+        } else {
+          const uint32_t q = hx / hpp32;
+          page = upage[q - slice0_32];
+          tok = static_cast<int64_t>(static_cast<uint32_t>(page) * ps32 + 16 * (hx - q * hpp32));
+        }
       }
       const int64_t rem = p.n_kv - tok;
       r.valid[h] = !exists || rem <= 0 ? 0 : (rem < 16 ? static_cast<int32_t>(rem) : 16);
@@ -552,17 +747,41 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
     asm volatile("" ::: "memory");
   };
 
-  SpTile cur = load_tile(vt_begin + w);
-  for (int64_t vt = vt_begin + w; vt < vt_end; vt += kWaves) {
+  auto stage = [&](const SpTile& tl) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(k_wr + 4 * i * kKRow) = cur.k[i];
-      *reinterpret_cast<u32x4*>(v_wr + 4 * i * kVRow) = cur.v[i];
+      *reinterpret_cast<u32x4*>(k_wr + 4 * i * kKRow) = tl.k[i];
+      *reinterpret_cast<u32x4*>(v_wr + 4 * i * kVRow) = tl.v[i];
     }
     asm volatile("" ::: "memory");
-    const SpTile nxt = load_tile(vt + kWaves);
-    process(cur);
-    cur = nxt;
+  };
+  if (SPLIT || FB_SPARSE_PREFETCH < 2) {
+    SpTile cur = load_tile(vt_begin + w);
+    for (int64_t vt = vt_begin + w; vt < vt_end; vt += kWaves) {
+      stage(cur);
+      const SpTile nxt = load_tile(vt + kWaves);
+      process(cur);
+      cur = nxt;
+    }
+  } else {
+    // two tiles in flight while one is processed: three register sets in
+    // rotation, the loop unrolled by three (loads past the chunk's last tile
+    // re-read it: load_tile clamps)
+    constexpr int K = kWaves;
+    SpTile ta = load_tile(vt_begin + w), tb = load_tile(vt_begin + w + K), tc;
+    for (int64_t vt = vt_begin + w; vt < vt_end; vt += 3 * K) {
+      stage(ta);
+      tc = load_tile(vt + 2 * K);
+      process(ta);
+      if (vt + K >= vt_end) break;
+      stage(tb);
+      ta = load_tile(vt + 3 * K);
+      process(tb);
+      if (vt + 2 * K >= vt_end) break;
+      stage(tc);
+      tb = load_tile(vt + 4 * K);
+      process(tc);
+    }
   }
 
   // ---- merge the four waves' states through LDS, write the chunk partial --
@@ -595,7 +814,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
     }
     __syncthreads();
     const RowOut& out = s == 0 ? p.out : p.out_res;
-    for (int e = tid; e < 32 * kD; e += 256) {
+    for (int e = tid; e < 32 * kD; e += NT) {
       const int r = e / kD, c = e % kD;
       if (!row_written(slab * 32 + r)) continue;
       float sum = 0.f;
@@ -603,7 +822,7 @@ __global__ __launch_bounds__(256, SPLIT ? 1 : 2) void sparse_mfma_kernel(PrefixP
       for (int ww = 0; ww < kWaves; ++ww) sum += mg[(ww * 32 + r) * kMergeStride + c];
       out.a[out_row(slab * 32 + r, s) * kD + c] = sum;
     }
-    for (int r = tid; r < 32; r += 256) {
+    for (int r = tid; r < 32; r += NT) {
       if (!row_written(slab * 32 + r)) continue;
       float M = kNegInf;
       for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, ml_s[ww][r][0]);
@@ -624,6 +843,15 @@ hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int 
   hipLaunchKernelGGL(sel_bitmap_kernel, dim3(n_rows), dim3(256), words * sizeof(uint32_t), s, pages,
                      k_pages, words, n_pages, bitmap);
   return hipGetLastError();
+}
+
+bool gather_union_fits(int n_q, int words) { return words >= 1 && words <= kUnionWords && n_q >= 1; }
+
+bool gather_classify_fits(int n_q, int hq) {
+  // the float64 sums of the classification (four per token and head, then
+  // one per token) in the tile LDS after the union words
+  const size_t need = 2 * kUnionWords * 4 + (4 * static_cast<size_t>(n_q) * hq + n_q) * sizeof(double);
+  return n_q >= 1 && n_q <= kClassifyTokens && need <= static_cast<size_t>(kGatherWaves) * kWaveLds;
 }
 
 bool sel_prep_fits(int n_q, int words) {
@@ -676,9 +904,9 @@ hipError_t launch_prefix_sparse(const PrefixParams& p, hipStream_t s) {
   const int n_cg = p.n_chunks * p.hkv;
   const dim3 grid(static_cast<unsigned>((n_cg + 7) / 8 * 8 * p.n_slabs));
   if (p.sel_mode == FB_SEL_SPLIT)
-    hipLaunchKernelGGL(sparse_mfma_kernel<true>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(sparse_mfma_kernel<true>, grid, dim3(64 * kSplitWaves), 0, s, p);
   else
-    hipLaunchKernelGGL(sparse_mfma_kernel<false>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(sparse_mfma_kernel<false>, grid, dim3(64 * kGatherWaves), 0, s, p);
   return hipGetLastError();
 }
 

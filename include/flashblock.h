@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FB_ABI_VERSION 2
+#define FB_ABI_VERSION 3
 
 typedef enum {
   FB_OK = 0,
@@ -101,6 +101,13 @@ typedef struct {
                              ids outside [0, ceil(n_kv / page_size)) select
                              nothing                                           */
   const uint8_t* active;  /* GATHER: [n_q] 1 = the row recomputes; NULL = all    */
+  const uint32_t* bitmap; /* NULL, or the same selection as bitmaps, written by
+                             fb_page_bitmap: [n_q, Hkv, ceil(n_pages / 32)]
+                             uint32, bit p of row (t, g) set iff page p is in
+                             S_{t,g}. Given, `pages` is not read and no
+                             selection prep runs: a GATHER pass then takes
+                             the union over the active rows in its own
+                             workgroups (one launch fewer)                    */
 } fb_page_sel;
 
 /* ------------------------------------------------------------------------ *
@@ -295,6 +302,22 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q,
                          int64_t page_cap, int32_t k_pages,
                          const uint8_t* active, int32_t* pages, double* bound,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * fb_page_bitmap -- a page selection as bitmaps (for fb_page_sel.bitmap and *
+ * fb_step_state.sel_bitmap): bitmap[(t Hkv + g) ceil(n_pages / 32) + w]     *
+ * bit b set iff page 32 w + b is in pages[t][g][0 .. k_pages). LoSA s2 /    *
+ * FlashBlock s2 sparse compatibility: the selection a GATHER pass masks     *
+ * its rows with, built once per selection instead of once per pass.        *
+ * pages [n_q, Hkv, k_pages] device int32 (ids outside [0, n_pages) set no  *
+ * bit); bitmap device out.                                                  *
+ * Errors: INVALID_ARGUMENT for a bad shape, n_q < 1, n_pages < 1 or beyond *
+ *   INT32_MAX, k_pages outside [0, n_pages], NULL pointers (pages when      *
+ *   k_pages > 0); UNSUPPORTED when a row exceeds 16,384 words.              *
+ * ------------------------------------------------------------------------ */
+fb_status fb_page_bitmap(const fb_attn_shape* shape, const int32_t* pages,
+                         int64_t n_q, int64_t n_pages, int32_t k_pages,
+                         uint32_t* bitmap, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * fb_proxy_decide -- singular-proxy identification (SPA-Cache, "Proxy       *
@@ -493,6 +516,12 @@ typedef struct {
                               recompute step instead of the previous step      */
   int32_t sparse_reselect; /* SPARSE: 1 = LoSA per step (dense first step, pages
                               re-selected each step, no residual)              */
+  uint32_t* sel_bitmap;    /* SPARSE (FlashBlock residual mode), nullable:
+                              [n_q, Hkv, ceil(page_cap or P / 32)] uint32. The
+                              refresh step writes its selection there as
+                              bitmaps; later steps read them instead of
+                              rebuilding them, and classify the tokens inside
+                              the GATHER pass (two launches a step)           */
 } fb_step_state;
 
 typedef struct {

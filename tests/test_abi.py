@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert fb.fb_abi_version() == 2
+    assert fb.fb_abi_version() == 3
     assert fb.fb_status_string(0) == "ok"
     assert fb.fb_status_string(3) == "workspace too small"
     assert fb.fb_status_string(99) == "unknown status"
@@ -49,7 +49,7 @@ def test_status_strings_and_version(lib):
 STRUCTS = {
     "fb_attn_shape": ["n_q_heads", "n_kv_heads", "head_dim", "scale", "dtype"],
     "fb_tensor": ["ptr", "n_tok", "stride_tok", "stride_head"],
-    "fb_page_sel": ["mode", "page_size", "k_pages", "pages", "active"],
+    "fb_page_sel": ["mode", "page_size", "k_pages", "pages", "active", "bitmap"],
     "fb_reuse_args": [f[0] for f in _abi.fb_reuse_args._fields_],
     "fb_step_state": [f[0] for f in _abi.fb_step_state._fields_],
     "fb_step_args": [f[0] for f in _abi.fb_step_args._fields_],
@@ -307,6 +307,17 @@ def test_noalloc_prefix_refuses_beyond_its_scratch(lib):
     big = ten(9000000, 8)
     assert f(C.byref(shape()), ten(8, 32), big, big, None, C.byref(sel), FAKE, FAKE, FAKE, FAKE,
              None) == fb.FB_ERR_UNSUPPORTED
+
+
+def test_page_bitmap_rejects(lib):
+    sh = shape()
+    f = lib.fb_page_bitmap
+    assert f(C.byref(sh), FAKE, 0, 4096, 819, FAKE, None) == 1        # n_q
+    assert f(C.byref(sh), FAKE, 8, 0, 0, FAKE, None) == 1             # no pages
+    assert f(C.byref(sh), FAKE, 8, 4096, 4097, FAKE, None) == 1       # k > pages
+    assert f(C.byref(sh), None, 8, 4096, 3, FAKE, None) == 1          # pages NULL
+    assert f(C.byref(sh), FAKE, 8, 4096, 3, None, None) == 1          # bitmap NULL
+    assert f(C.byref(sh), FAKE, 8, 1 << 20, 3, FAKE, None) == fb.FB_ERR_UNSUPPORTED  # 32,768 words
 
 
 # ------------------------------------------------------ growing cache, no GPU

@@ -32,12 +32,22 @@ def _inputs(n_q, n_kv, page, k, seed=0, hq=32, hkv=8):
     return cfg, q, kp, vp, sel
 
 
-def _run(fb, cfg, q, kp, vp, sel, page, mode, active=None, a_res=None, l_res=None, a0=None, l0=None):
+def _bitmaps(fb, shape, pages, n_pages):
+    bm = torch.full((pages.shape[0], pages.shape[1], -(-n_pages // 32)), -1, dtype=torch.int32,
+                    device="cuda")
+    fb.fb_page_bitmap(shape, pages, n_pages, bm)
+    torch.cuda.synchronize()
+    return bm
+
+
+def _run(fb, cfg, q, kp, vp, sel, page, mode, active=None, a_res=None, l_res=None, a0=None, l0=None,
+         prebuilt=False):
     n_q, hq, d = q.shape
     shape = fb.shape_of(hq, cfg.n_kv_heads, d, cfg.scale, torch.bfloat16)
     pages = torch.from_numpy(sel).cuda()
     act = None if active is None else torch.from_numpy(active.astype(np.uint8)).cuda()
-    s = fb.page_sel(mode, page, pages, act)
+    bm = _bitmaps(fb, shape, pages, -(-kp.shape[0] // page)) if prebuilt else None
+    s = fb.page_sel(mode, page, None if prebuilt else pages, act, bm)
     a = torch.from_numpy(a0).cuda() if a0 is not None else torch.full((n_q, hq, d), 7.0, device="cuda")
     l = torch.from_numpy(l0).cuda() if l0 is not None else torch.full((n_q, hq), 7.0, device="cuda")
     if a_res is None:
@@ -133,3 +143,46 @@ def test_out_of_range_page_ids_select_nothing(fb):
     (a_s, l_s), (a_r, l_r) = split_attn(qv, kv, vv, sel_ok, 16, cfg.scale)
     check_a("residual with ignored ids", ar, a_r, 2e-3)
     check_l("residual L with ignored ids", lr, l_r, 1e-3)
+
+
+def test_page_bitmap_encodes_the_page_lists(fb):
+    # every row's set bits are exactly its pages (ids outside [0, P) set none)
+    cfg, q, kp, vp, sel = _inputs(8, 20007, 16, 300, seed=5)
+    n_pages = -(-20007 // 16)
+    sel = sel.copy()
+    sel[0, 0, 0] = -2
+    sel[1, 3, -1] = n_pages + 5
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    bm = cpu(_bitmaps(fb, shape, torch.from_numpy(sel).cuda(), n_pages)).view(np.uint32)
+    for t in range(8):
+        for g in range(8):
+            bits = np.unpackbits(bm[t, g].view(np.uint8), bitorder="little")
+            got = np.nonzero(bits)[0]
+            want = np.array(sorted(p for p in sel[t, g] if 0 <= p < n_pages))
+            assert np.array_equal(got, want), (t, g)
+
+
+@pytest.mark.parametrize("name,n_q,n_kv,page,k,pattern", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_gather_with_prebuilt_bitmaps_is_bit_identical(fb, name, n_q, n_kv, page, k, pattern):
+    """The union taken inside the GATHER workgroups from caller bitmaps gives
+    the same slices, so the same partials and bit-identical outputs, as the
+    selection prep's compacted union."""
+    cfg, q, kp, vp, sel = _inputs(n_q, n_kv, page, k, seed=1)
+    active = {"all": np.ones(n_q, bool), "mostly": np.arange(n_q) % 4 != 0,
+              "one": np.arange(n_q) == 5, "none": np.zeros(n_q, bool)}[pattern]
+    qv, kv, vv = vals(q, "bf16"), vals(kp, "bf16"), vals(vp, "bf16")
+    (a_s, l_s), (a_r, l_r) = split_attn(qv, kv, vv, sel, page, cfg.scale)
+    a_r32, l_r32 = a_r.astype(np.float32), l_r.astype(np.float32)
+    a0 = np.full(a_s.shape, 7.0, np.float32)
+    l0 = np.full(l_s.shape, 7.0, np.float32)
+    outs = [_run(fb, cfg, q, kp, vp, sel, page, fb.FB_SEL_GATHER, active=active, a_res=a_r32,
+                 l_res=l_r32, a0=a0, l0=l0, prebuilt=pb) for pb in (False, True)]
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y), name
+
+
+def test_split_with_prebuilt_bitmaps_is_bit_identical(fb):
+    cfg, q, kp, vp, sel = _inputs(8, 20007, 16, 250, seed=3)
+    outs = [_run(fb, cfg, q, kp, vp, sel, 16, fb.FB_SEL_SPLIT, prebuilt=pb) for pb in (False, True)]
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)

@@ -116,13 +116,14 @@ def test_video_block_matches_oracle(fb, n_q, n_kv):
 
 
 @pytest.mark.parametrize("density", [0.2, 0.4])
-def test_sparse_block_matches_oracle(fb, density):
+@pytest.mark.parametrize("sel_bitmap", [True, False], ids=["bitmaps_kept", "prep_each_step"])
+def test_sparse_block_matches_oracle(fb, density, sel_bitmap):
     cfg = W.SPARSE.with_(n_prefix=4096, density=density, n_steps=5)
     steps = W.sparse_steps(cfg, m_override=[None, 2, 0, 5, 1])
     kp, vp = W.prefix_kv(cfg)
     shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
     step = fb.Step(fb.FB_STEP_SPARSE, shape, 8, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
-                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct)
+                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, sel_bitmap=sel_bitmap)
     ks = [dict(q=vals(s["q"], "bf16"), k=vals(s["k"], "bf16"), v=vals(s["v"], "bf16"))
           for s in steps]
     recs = OC.sparse_block(ks, vals(kp, "bf16"), vals(vp, "bf16"), cfg.scale, cfg.k_pages, cfg.page)
