@@ -8,8 +8,9 @@
 //   * the block-internal pass over J_in with the log-space composition of the
 //     cached pair and the fresh one in its epilogue (s2, the A_full equation).
 //
-// Workgroup = NW waves = (KV head g, key chunk, row tile of 32 NW rows), one
-// 32-row block per wave. Rows are (query token, query head of the group)
+// Workgroup = NW waves = (KV head g, key chunk, row tile of 32 NW RB rows),
+// RB 32-row blocks per wave (RB = 1 is the fastest measured: 2 blocks per
+// wave with 4 waves, O in accumulation registers, ran slower). Rows are (query token, query head of the group)
 // pairs r = t*G + j, so grouped heads share every K/V tile. The waves share
 // each 32-key K/V tile, staged global -> VGPR -> LDS with one barrier per
 // tile; each wave keeps the online-softmax state of its rows over the whole
@@ -22,6 +23,11 @@
 //       parts, V^T from LDS by the transposing read ds_read_b64_tr_b16)
 // The row max is taken on raw scores (scale > 0) and folded into one FMA per
 // weight; it is raised only when a tile's max exceeds it by more than 2^8.
+// The weights take the running max as it stands, so their exponentials do
+// not wait for the tile's max; the rare tile that raises the max recomputes
+// its weights (same values as computing them after the raise). The tile loop
+// runs two tiles per trip so S(t) and S(t+1) alternate between two register
+// sets instead of being copied.
 #include "fb_internal.h"
 
 #include <math.h>
@@ -44,6 +50,9 @@ constexpr float kRescaleLog2 = 8.f;
 #endif
 #ifndef FB_ROWS_WAVES
 #define FB_ROWS_WAVES 8           // waves (32 query rows each) per workgroup
+#endif
+#ifndef FB_ROWS_BLOCKS
+#define FB_ROWS_BLOCKS 1          // 32-row blocks per wave
 #endif
 #ifndef FB_ROWS_OCC
 #define FB_ROWS_OCC 1             // workgroups per CU the kernel is built for (register budget)
@@ -72,20 +81,28 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const char* lds_generic) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
 }
 
-// S^T[32 keys x 32 rows] = K . Q^T for one tile; k_rd = this lane's K row.
-__device__ __forceinline__ f32x16 qk_tile(const char* k_rd, const bf16x8 (&qop)[8]) {
-  f32x16 s = {};
+// S^T[32 keys x 32 rows] = K . Q^T for one tile and each of the wave's RB
+// row blocks; k_rd = this lane's K row. Each K operand is read once and
+// feeds the RB blocks' MFMAs.
+template <int RB>
+__device__ __forceinline__ void qk_tile(const char* k_rd, const bf16x8 (&qop)[RB][8],
+                                        f32x16 (&s)[RB]) {
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    s = mfma32(*reinterpret_cast<const bf16x8*>(k_rd + 32 * kk), qop[kk], s);
-  return s;
+  for (int b = 0; b < RB; ++b) s[b] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 k = *reinterpret_cast<const bf16x8*>(k_rd + 32 * kk);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) s[b] = mfma32(k, qop[b][kk], s[b]);
+  }
 }
 
-// O^T[128 x 32] += V^T . P^T for one tile; v_rd = this lane's transposing
-// read address. Consecutive MFMAs go to different accumulators.
-template <bool PSPLIT>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[4], const bf16x8 (&ph)[2],
-                                        const bf16x8 (&pl)[2], const char* v_rd) {
+// O^T[128 x 32] += V^T . P^T for one tile and each row block; v_rd = this
+// lane's transposing read address. Each V operand feeds every block's hi
+// (and lo) MFMA; consecutive MFMAs go to different accumulators.
+template <int RB, bool PSPLIT>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[RB][4], const bf16x8 (&ph)[RB][2],
+                                        const bf16x8 (&pl)[RB][2], const char* v_rd) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     bf16x8 va[4];
@@ -98,10 +115,14 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[4], const bf16x8 (&ph)[2],
       va[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = mfma32(va[db], ph[j], o[db]);
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[b][db] = mfma32(va[db], ph[b][j], o[b][db]);
     if (PSPLIT) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma32(va[db], pl[j], o[db]);
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[b][db] = mfma32(va[db], pl[b][j], o[b][db]);
     }
   }
 }
@@ -112,16 +133,9 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Online softmax of one tile's scores (lane = row, 16 of its 32 keys):
-// weights p = 2^(c*s - m) with the running max m raised lazily (only when
-// the tile's max exceeds it by more than 2^8), the row sum l adds the fp32
-// weights, and P^T leaves as bf16 (PSPLIT: hi + lo parts, ~2^-16 relative,
-// instead of bf16's 2^-8). Rescales O when m moves. `valid` = keys of the
-// tile that exist; c = scale * log2(e).
-template <bool PSPLIT, bool MASKED>
-__device__ __forceinline__ void softmax_tile(f32x16 s, int valid, int hl, float c, float& m_run,
-                                             float& l_run, float& alpha, bool& bump,
-                                             bf16x8 (&ph)[2], bf16x8 (&pl)[2]) {
+// Keys past `valid` in a partial tile get score -inf (weight 0).
+template <bool MASKED>
+__device__ __forceinline__ void mask_tile(f32x16& s, int valid, int hl) {
   if (MASKED) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -129,14 +143,21 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int valid, int hl, float 
       s[i] = tk < valid ? s[i] : kNegInf;
     }
   }
+}
+
+// The row's maximum raw score over the tile, times c (both lanes of the row).
+__device__ __forceinline__ float tile_max(const f32x16& s, float c) {
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = pair_max(mx) * c;
-  bump = mx > m_run + kRescaleLog2;
-  alpha = bump ? fast_exp2(m_run - mx) : 1.f;
-  m_run = bump ? mx : m_run;
-  const float nm = m_run == kNegInf ? 0.f : -m_run;
+  return pair_max(mx) * c;
+}
+
+// Weights p = 2^(c*s + nm) of one tile, P^T as bf16 (hi + lo with PSPLIT);
+// returns this lane's sum of the fp32 weights.
+template <bool PSPLIT>
+__device__ __forceinline__ float tile_weights(const f32x16& s, float c, float nm, bf16x8 (&ph)[2],
+                                              bf16x8 (&pl)[2]) {
   float psum = 0.f;
 #pragma unroll
   for (int hj = 0; hj < 2; ++hj) {
@@ -150,22 +171,22 @@ __device__ __forceinline__ void softmax_tile(f32x16 s, int valid, int hl, float 
     ph[hj] = hi;
     if (PSPLIT) pl[hj] = bf16_lo_part(pf, hi);
   }
-  l_run = l_run * alpha + psum;
+  return psum;
 }
 
 // Issue order for one pipelined tile (one scheduling region): the operand
 // reads first, then every MFMA followed by a few VALU instructions of the
 // softmax, so the matrix core and the VALU work side by side in one wave.
-template <bool PSPLIT>
+template <int RB, bool PSPLIT>
 __device__ __forceinline__ void tile_schedule() {
-  constexpr int kMfma = PSPLIT ? 24 : 16;
+  constexpr int kMfma = RB * (PSPLIT ? 24 : 16);
   constexpr int kValuPer = FB_ROWS_VALU_PER;
   __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);        // K operands, V operands (j = 0)
 #pragma unroll
   for (int i = 0; i < kMfma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
-    if (i == 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // V operands (j = 1)
+    if (i == 4 * RB) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // V operands (j = 1)
   }
 }
 
@@ -174,7 +195,7 @@ __device__ __forceinline__ void tile_schedule() {
 // O += P(t-1).V(t-1). LDS holds four tile stages: V(t-1) and K(t+1) being
 // read, tile t (its V is read next), and tile t+2 being written from the
 // registers that were loaded from global memory during the previous tile.
-template <int NW, int OCC, bool PSPLIT, bool MERGE>
+template <int NW, int RB, int OCC, bool PSPLIT, bool MERGE>
 __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   constexpr int RPT = 32 / (NW * 4);              // tile rows staged per thread
   constexpr int kStages = 4;
@@ -227,18 +248,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, r32 = lane & 31;
   const int R = p.n_q * G;
-  const int row = rt * (NW * 32) + w * 32 + r32;        // this lane's row
+  // this lane's row in block b: rows are (query token, query head of the group)
+  auto row_of = [&](int b) { return rt * (NW * 32 * RB) + w * (32 * RB) + b * 32 + r32; };
 
-  // Q^T operand: lane holds its row's dims 16 kk + 8 hl .. +8.
-  bf16x8 qop[8];
-  {
+  // Q^T operands: lane holds its row's dims 16 kk + 8 hl .. +8, per block.
+  bf16x8 qop[RB][8];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int row = row_of(b);
     const bool ok = row < R;
     const int t = ok ? row / G : 0, jh = ok ? row % G : 0;
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + static_cast<int64_t>(t) * p.q_st +
                          static_cast<int64_t>(g * G + jh) * p.q_sh;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      qop[kk] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl) : bf16x8{};
+      qop[b][kk] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * kk + 8 * hl) : bf16x8{};
   }
 
   const int64_t n_tiles = (p.n_kv + kTile - 1) / kTile;
@@ -301,11 +325,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   const int k_rd = r32 * kKRow + hl * 16;
   const int v_rd = kKBytes + (4 * (grp >> 1) + s4) * kVRow + 32 * (grp & 1) + 8 * q4;
 
-  f32x16 o[4];
+  f32x16 o[RB][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
-  bf16x8 ph[2] = {}, pl[2] = {};                   // P(t-1); zero before the first tile
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[b][db] = f32x16{};
+  float m_run[RB], l_run[RB];
+  bf16x8 ph[RB][2], pl[RB][2];                     // P(t-1); zero before the first tile
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    m_run[b] = kNegInf;
+    l_run[b] = 0.f;
+    ph[b][0] = ph[b][1] = pl[b][0] = pl[b][1] = bf16x8{};
+  }
 
   // prologue: tiles t_begin, t_begin + 1 staged, t_begin + 2 in registers,
   // the V part of stage (t_begin - 1) zeroed (the first PV adds P = 0 times it)
@@ -319,99 +351,142 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
     for (int i = tid; i < kVBytes / 16; i += 64 * NW) *reinterpret_cast<u32x4*>(vz + 16 * i) = u32x4{};
   }
   __syncthreads();
-  f32x16 s_cur = qk_tile(stage_of(t_begin) + k_rd, qop);
+  f32x16 s_cur[RB], s_nxt[RB];
+  qk_tile<RB>(stage_of(t_begin) + k_rd, qop, s_cur);
 
-  // one pipelined tile; MASKED only for a partial last tile of the keys
-  auto iter = [&](int64_t t, auto masked) {
+  // one pipelined tile; MASKED only for a partial last tile of the keys.
+  // s_in = S(t), computed by the previous tile; s_out receives S(t+1).
+  auto iter = [&](int64_t t, auto masked, const f32x16 (&s_in)[RB], f32x16 (&s_out)[RB]) {
     constexpr bool M = decltype(masked)::value;
-    const f32x16 s_nxt = qk_tile(stage_of(t + 1) + k_rd, qop);
-    pv_tile<PSPLIT>(o, ph, pl, stage_of(t - 1) + v_rd);
-    float alpha;
-    bool bump;
-    softmax_tile<PSPLIT, M>(s_cur, valid_of(t), hl, p.scale_log2, m_run, l_run, alpha, bump, ph, pl);
-    // keep the weights' computation in this region (else it sinks past the
-    // branch below, away from the MFMAs it should overlap)
-    asm volatile("" ::"v"(ph[0]), "v"(ph[1]), "v"(pl[0]), "v"(pl[1]), "v"(l_run));
-    tile_schedule<PSPLIT>();
-    if (__any(bump)) {                             // O (through tile t-1) to the new max
+    qk_tile<RB>(stage_of(t + 1) + k_rd, qop, s_out);
+    pv_tile<RB, PSPLIT>(o, ph, pl, stage_of(t - 1) + v_rd);
+    // The weights take the running max as it stands, so their exponentials
+    // do not wait for this tile's max; the max only decides whether the
+    // running max must rise (by more than 2^8), and the rare tile where it
+    // does recomputes its weights below with the raised max.
+    const float c = p.scale_log2;
+    f32x16 sm[RB];
+    float mx[RB], l_prev[RB];
+    bool bump[RB];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    for (int b = 0; b < RB; ++b) {
+      sm[b] = s_in[b];
+      mask_tile<M>(sm[b], valid_of(t), hl);
+      l_prev[b] = l_run[b];
+      l_run[b] = l_prev[b] + tile_weights<PSPLIT>(sm[b], c, m_run[b] == kNegInf ? 0.f : -m_run[b],
+                                                  ph[b], pl[b]);
+      mx[b] = tile_max(sm[b], c);
+      bump[b] = mx[b] > m_run[b] + kRescaleLog2;
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+      asm volatile("" ::"v"(ph[b][0]), "v"(ph[b][1]), "v"(pl[b][0]), "v"(pl[b][1]), "v"(l_run[b]),
+                   "v"(mx[b]));
+    tile_schedule<RB, PSPLIT>();
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if (__any(bump[b])) {
+        // raise the max: O (through tile t-1) and l rescaled, this tile's
+        // weights recomputed (lanes that keep their max get the same values)
+        const float alpha = bump[b] ? fast_exp2(m_run[b] - mx[b]) : 1.f;
+        m_run[b] = bump[b] ? mx[b] : m_run[b];
+        const float ps = tile_weights<PSPLIT>(sm[b], c, m_run[b] == kNegInf ? 0.f : -m_run[b], ph[b],
+                                              pl[b]);
+        l_run[b] = l_prev[b] * alpha + ps;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[b][db] *= alpha;
+      }
     }
     store(t + 2);
     load(t + 3);
     __syncthreads();
-    s_cur = s_nxt;
   };
-  for (int64_t t = t_begin; t < t_last; ++t) iter(t, Flag<false>{});
-  if (valid_of(t_last) < kTile) iter(t_last, Flag<true>{});
-  else iter(t_last, Flag<false>{});
-  pv_tile<PSPLIT>(o, ph, pl, stage_of(t_end - 1) + v_rd);
+  // two tiles per trip: S alternates between the two register sets
+  int64_t tt = t_begin;
+  for (; tt + 1 < t_last; tt += 2) {
+    iter(tt, Flag<false>{}, s_cur, s_nxt);
+    iter(tt + 1, Flag<false>{}, s_nxt, s_cur);
+  }
+  if (tt < t_last) {
+    iter(tt, Flag<false>{}, s_cur, s_nxt);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) s_cur[b] = s_nxt[b];
+  }
+  if (valid_of(t_last) < kTile) iter(t_last, Flag<true>{}, s_cur, s_nxt);
+  else iter(t_last, Flag<false>{}, s_cur, s_nxt);
+  pv_tile<RB, PSPLIT>(o, ph, pl, stage_of(t_end - 1) + v_rd);
 
-  // epilogue: lane (r32, hl) holds dims 32 db + 8 q + 4 hl + (0..3) of its row
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  if (row >= R) return;
-  const int t = row / G, h = g * G + row % G;
-  if (p.mask && p.mask[h]) return;
-  const int64_t orow_base = static_cast<int64_t>(t) * p.hq + h;
-  const bool any = l > 0.f;
-  const float inv = any ? 1.f / l : 0.f;
-  const float lz = any ? (m_run + __log2f(l)) * kLn2 : kNegInf;
-  if (!MERGE) {
-    const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows + orow_base;
-    float* a = p.out.a + orow * kD + 4 * hl;
+  // epilogue, per block: lane (r32, hl) holds dims 32 db + 8 q + 4 hl + (0..3) of its row
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int b = 0; b < RB; ++b) {
+    const float l = l_run[b] + __shfl_xor(l_run[b], 32, 64);
+    const int row = row_of(b);
+    if (row >= R) continue;
+    const int t = row / G, h = g * G + row % G;
+    if (p.mask && p.mask[h]) continue;
+    const int64_t orow_base = static_cast<int64_t>(t) * p.hq + h;
+    const bool any = l > 0.f;
+    const float inv = any ? 1.f / l : 0.f;
+    const float lz = any ? (m_run[b] + __log2f(l)) * kLn2 : kNegInf;
+    const f32x16* ob = o[b];
+    if (!MERGE) {
+      const int64_t orow = static_cast<int64_t>(chunk) * p.out.chunk_stride_rows + orow_base;
+      float* a = p.out.a + orow * kD + 4 * hl;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
-                         o[db][4 * q + 3] * inv};
-        *reinterpret_cast<f32x4*>(a + 32 * db + 8 * q) = v;
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {ob[db][4 * q] * inv, ob[db][4 * q + 1] * inv, ob[db][4 * q + 2] * inv,
+                           ob[db][4 * q + 3] * inv};
+          *reinterpret_cast<f32x4*>(a + 32 * db + 8 * q) = v;
+        }
+      if (hl == 0) p.out.l[orow] = lz;
+    } else {
+      // A_full = (w_out A_out + w_in A_in) / (w_out + w_in), m = max(L_out, L_in)
+      const int64_t r = orow_base;
+      const float l_prev = p.l_prev[r];
+      const float mm = fmaxf(l_prev, lz);
+      const float w_out = l_prev == kNegInf ? 0.f : expf(l_prev - mm);
+      const float w_in = expf(lz - mm);
+      const float den = w_out + w_in;
+      const float* ap = p.a_prev + r * kD + 4 * hl;
+      float* a = p.out.a + r * kD + 4 * hl;
+      float* ai = p.a_raw ? p.a_raw + r * kD + 4 * hl : nullptr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 vin = {ob[db][4 * q] * inv, ob[db][4 * q + 1] * inv, ob[db][4 * q + 2] * inv,
+                             ob[db][4 * q + 3] * inv};
+          const f32x4 vp = *reinterpret_cast<const f32x4*>(ap + 32 * db + 8 * q);
+          f32x4 vf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vf[e] = w_out == 0.f ? vin[e] : (w_out * vp[e] + w_in * vin[e]) / den;
+          *reinterpret_cast<f32x4*>(a + 32 * db + 8 * q) = vf;
+          if (ai) *reinterpret_cast<f32x4*>(ai + 32 * db + 8 * q) = vin;
+        }
+      if (hl == 0) {
+        if (p.out.l) p.out.l[r] = mm + logf(den);
+        if (p.l_raw) p.l_raw[r] = lz;
       }
-    if (hl == 0) p.out.l[orow] = lz;
-  } else {
-    // A_full = (w_out A_out + w_in A_in) / (w_out + w_in), m = max(L_out, L_in)
-    const int64_t r = orow_base;
-    const float l_prev = p.l_prev[r];
-    const float mm = fmaxf(l_prev, lz);
-    const float w_out = l_prev == kNegInf ? 0.f : expf(l_prev - mm);
-    const float w_in = expf(lz - mm);
-    const float den = w_out + w_in;
-    const float* ap = p.a_prev + r * kD + 4 * hl;
-    float* a = p.out.a + r * kD + 4 * hl;
-    float* ai = p.a_raw ? p.a_raw + r * kD + 4 * hl : nullptr;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 vin = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv,
-                           o[db][4 * q + 3] * inv};
-        const f32x4 vp = *reinterpret_cast<const f32x4*>(ap + 32 * db + 8 * q);
-        f32x4 vf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vf[e] = w_out == 0.f ? vin[e] : (w_out * vp[e] + w_in * vin[e]) / den;
-        *reinterpret_cast<f32x4*>(a + 32 * db + 8 * q) = vf;
-        if (ai) *reinterpret_cast<f32x4*>(ai + 32 * db + 8 * q) = vin;
-      }
-    if (hl == 0) {
-      if (p.out.l) p.out.l[r] = mm + logf(den);
-      if (p.l_raw) p.l_raw[r] = lz;
     }
   }
 }
 
 }  // namespace
 
-int rows_tile_rows() { return FB_ROWS_WAVES * 32; }
+int rows_tile_rows() { return FB_ROWS_WAVES * 32 * FB_ROWS_BLOCKS; }
 int rows_occupancy() { return FB_ROWS_OCC; }
 
 hipError_t launch_rows(const RowsParams& p, hipStream_t s) {
   const int per = (p.n_items + 7) / 8;
   const dim3 grid(per * 8);
   if (p.a_prev)
-    hipLaunchKernelGGL((rows_mfma_kernel<FB_ROWS_WAVES, FB_ROWS_OCC, FB_ROWS_PSPLIT != 0, true>),
+    hipLaunchKernelGGL((rows_mfma_kernel<FB_ROWS_WAVES, FB_ROWS_BLOCKS, FB_ROWS_OCC, FB_ROWS_PSPLIT != 0, true>),
                        grid, dim3(64 * FB_ROWS_WAVES), 0, s, p);
   else
-    hipLaunchKernelGGL((rows_mfma_kernel<FB_ROWS_WAVES, FB_ROWS_OCC, FB_ROWS_PSPLIT != 0, false>),
+    hipLaunchKernelGGL((rows_mfma_kernel<FB_ROWS_WAVES, FB_ROWS_BLOCKS, FB_ROWS_OCC, FB_ROWS_PSPLIT != 0, false>),
                        grid, dim3(64 * FB_ROWS_WAVES), 0, s, p);
   return hipGetLastError();
 }
