@@ -51,10 +51,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PROBE_LIB = os.path.join(ROOT, "block_diffusion_attention_amd", "libfbprobe.so")
-# kernels a device-decided text reuse step launches: the count/decision, the
-# prefix grid (which returns at once when the decision is reuse) and the
-# in-block pass with the merge
-TEXT_REUSE_STEP_LAUNCHES = 3
+# kernels a device-decided text reuse step launches: the prefix grid, whose
+# workgroups count the updated tokens and return at once when the decision is
+# reuse, and the in-block pass with the merge (which also updates the ids)
+TEXT_REUSE_STEP_LAUNCHES = 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefix_pass_traffic.json")
 # What sets the prefix pass's traffic: its kernels, and in the host layer the
 # split-K planning and launch code (from the planning constants to the
@@ -476,7 +476,7 @@ def reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N, hq, hkv, d, 
                 "speedup": round(t_dense / t_reuse, 2),
                 "required_min(traffic_ratio, t_dense/t_empty_step)": round(need, 2),
                 "met_within_5pct_timing_noise": bool(t_dense / t_reuse >= 0.95 * need)}
-    return {"decided_on": "device (count kernel: M = 0 reuses, M = B recomputes)",
+    return {"decided_on": "device (the prefix pass counts: M = 0 reuses, M = B recomputes)",
             "launches_per_reuse_step": n_launch,
             "empty_step": "device-decided reuse fb_step of a 1-token block, same heads and prefix",
             "eager": verdict(ms_reuse, ms_dense, ms_empty, ms_bare),
@@ -640,8 +640,9 @@ def text_short_extra(fb, W, dev, stream, probe, layout):
     ms_dense = _timed(lambda: block(0), stream, 20)
     ms_reuse = _timed(lambda: block(1), stream, 20)
     n_re = sum(1 for x in decisions if x == "reuse")
-    # a recompute step launches the count, the prefix kernel and the in-block
-    # kernel (which merges the split-K partials); a reuse step the same three
+    # a recompute step launches the prefix kernel (which takes the decision)
+    # and the in-block kernel (which merges the split-K partials); a reuse
+    # step the same two; a host-forced reuse step the count and the in-block
     floor3 = launch_floor_ms(probe, TEXT_REUSE_STEP_LAUNCHES, stream)
     g_block = graph_of(block)
     gms_block = _timed(g_block.replay, stream, 20)

@@ -40,6 +40,9 @@ namespace {
 #ifndef FB_PREFIX_PAIR_SMALL
 #define FB_PREFIX_PAIR_SMALL 1    // <= 32 rows per KV head on head-major K/V: pair kernel
 #endif
+#ifndef FB_TEXT_DECIDE_IN_PASS
+#define FB_TEXT_DECIDE_IN_PASS 1  // device-decided text steps: the pass counts, no count launch
+#endif
 #ifndef FB_ROWS_MIN_ROWS
 #define FB_ROWS_MIN_ROWS 128      // query rows per KV head from which the many-rows kernel runs
 #endif
@@ -251,6 +254,7 @@ struct PrefixHooks {
   const void* q_src; int64_t q_st, q_sh;
   void* q_dst; int q_esize;
   ReduceParams* defer;          // dense pass: fill this and leave the reduce to the caller
+  const TextDecide* decide;     // dense MFMA / generic pass: it takes the text decision
 };
 
 bool kv_head_major(const fb_attn_shape& s, const fb_tensor& k, const fb_tensor& v) {
@@ -311,6 +315,12 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   if (pl.path != PATH_GENERIC && !offsets32(k)) return FB_ERR_UNSUPPORTED;
 
   if (hooks && (pl.n_chunks == 0 || pl.direct)) return FB_ERR_UNSUPPORTED;   // they ride on both
+  if (hooks && hooks->decide) {
+    if (mode != FB_SEL_DENSE || mask || (pl.path != PATH_MFMA && pl.path != PATH_GENERIC))
+      return FB_ERR_UNSUPPORTED;
+    pp.decide_on = 1;
+    pp.decide = *hooks->decide;
+  }
   if (pl.n_chunks > 0) {
     hipError_t e;
     if (pl.path == PATH_SPARSE) {
@@ -411,7 +421,7 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   rp.rows = pl.rows;
   rp.hq = s.n_q_heads;
   rp.d = s.head_dim;
-  rp.mask = mask;
+  rp.mask = hooks && hooks->decide ? hooks->decide->mask : mask;
   rp.a_out = a_out;
   rp.l_out = l_out;
   if (hooks && hooks->q_src) {
@@ -471,11 +481,17 @@ bool block_small_path(const fb_attn_shape& s, int64_t n_q) {
   return !block_rows_path(s, n_q) && n_q <= 65535;
 }
 
+// The text step's reference-id update, when the prefix pass took the
+// decision (the in-block kernel runs after it and writes the ids).
+struct IdsUpdate {
+  const int32_t* cur; int32_t* store; int n; int keep_on_reuse;
+};
+
 fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const fb_tensor& k_blk,
                       const fb_tensor& v_blk, const float* a_out, const float* l_out,
                       float* a_full, float* l_full, float* a_in, float* l_in,
                       const ReduceParams* fused, float* cache_a, float* cache_l, void* q_dst,
-                      hipStream_t stream) {
+                      hipStream_t stream, const IdsUpdate* ids = nullptr) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   const int d = shape->head_dim;
@@ -486,7 +502,8 @@ fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const 
   if (!a_out || !l_out || !a_full) return FB_ERR_INVALID_ARGUMENT;
   if (q_blk.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
-  if (fused && !block_small_path(*shape, q_blk.n_tok)) return FB_ERR_UNSUPPORTED;
+  if ((fused || ids) && !block_small_path(*shape, q_blk.n_tok)) return FB_ERR_UNSUPPORTED;
+  if (ids && (!fused || !fused->mask)) return FB_ERR_UNSUPPORTED;
   if (block_rows_path(*shape, q_blk.n_tok)) {
     // many rows: MFMA pass with the merge in its epilogue (16-byte row access)
     if (!aligned16(a_out) || !aligned16(a_full) || (a_in && !aligned16(a_in)))
@@ -557,6 +574,12 @@ fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const 
     bp.cache_l = cache_l;
   }
   bp.q_dst = q_dst;
+  if (ids) {
+    bp.ids_cur = ids->cur;
+    bp.ids_store = ids->store;
+    bp.ids_n = ids->n;
+    bp.ids_keep_on_reuse = ids->keep_on_reuse;
+  }
   return dev(launch_block_small(bp, shape->dtype, stream));
 }
 
@@ -994,17 +1017,41 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       const int force = first ? 0 : a->decision;
       if (st->count_since_refresh != 0 && st->count_since_refresh != 1)
         return FB_ERR_INVALID_ARGUMENT;
+      // with split-K partials and the one-wave in-block kernel, that kernel
+      // merges the partials itself (no reduce launch); a step the device
+      // decides then also lets the pass take the decision (no count launch)
+      // and the in-block kernel update the reference ids
+      const PrefixPlan pl = plan_prefix(s, n_q, st->k_prefix.n_tok, nullptr,
+                                        kv_head_major(s, st->k_prefix, st->v_prefix));
+      const bool fuse = FB_TEXT_FUSE_REDUCE && (pl.path == PATH_MFMA || pl.path == PATH_GENERIC) &&
+                        !pl.direct && pl.n_chunks > 0 && block_small_path(s, n_q);
+      if (fuse && force != 1 && FB_TEXT_DECIDE_IN_PASS) {
+        rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, st->a_out,
+                             st->l_out, nullptr, nullptr);
+        if (rc != FB_OK) return rc;
+        const TextDecide td = {first ? nullptr : st->ids_prev, a->ids_cur, n_q, st->tau, force, hq,
+                               st->mask, st->m_count};
+        PrefixHooks hk;
+        memset(&hk, 0, sizeof(hk));
+        hk.defer = &fused;
+        hk.decide = &td;
+        rc = run_prefix(s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, nullptr, st->a_out,
+                        st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream, &hk);
+        if (rc != FB_OK) return rc;
+        const IdsUpdate ids = {a->ids_cur, st->ids_prev, n_q, st->count_since_refresh};
+        rc = block_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full,
+                         a->l_full, nullptr, nullptr, &fused, st->a_out, st->l_out, nullptr, stream,
+                         &ids);
+        if (rc != FB_OK) return rc;
+        st->step += 1;
+        return FB_OK;
+      }
       rc = dev(launch_count(first ? nullptr : st->ids_prev, a->ids_cur, n_q, st->tau, force, hq,
                             st->mask, st->m_count, st->ids_prev, st->count_since_refresh,
                             stream));
       if (rc != FB_OK) return rc;
       if (force != 1) {
-        // with split-K partials and the one-wave in-block kernel, that kernel
-        // merges the partials itself: the reduce launch is saved
-        const PrefixPlan pl = plan_prefix(s, n_q, st->k_prefix.n_tok, nullptr,
-                                          kv_head_major(s, st->k_prefix, st->v_prefix));
-        if (FB_TEXT_FUSE_REDUCE && (pl.path == PATH_MFMA || pl.path == PATH_GENERIC) &&
-            !pl.direct && pl.n_chunks > 0 && block_small_path(s, n_q)) {
+        if (fuse) {
           rc = validate_prefix(&s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, st->a_out,
                                st->l_out, nullptr, nullptr);
           if (rc != FB_OK) return rc;

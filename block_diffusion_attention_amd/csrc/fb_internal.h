@@ -140,6 +140,42 @@ struct RowOut {
   int64_t chunk_stride_rows;  // rows between chunks (n_q * Hq), 0 if final
 };
 
+// The text controller's decision taken inside the prefix pass (FlashBlock
+// technical summary, s2 "adaptive reuse strategies": reuse while fewer than
+// tau of the block's tokens changed). Every wave of every workgroup counts
+// the tokens whose id differs from the reference ids (a ballot per 64
+// tokens), so all of them take the same decision with no communication; on
+// reuse the workgroup exits before any K/V read. The writer (one wave of one
+// workgroup) publishes the decision as the head mask and the count. Nothing
+// in the pass writes the ids, so every wave reads the same ones.
+struct TextDecide {
+  const int32_t* ids_ref;       // [n] null: first step of a block (every token counts)
+  const int32_t* ids_cur;       // [n]
+  int n, tau, force;            // force: -1 the count decides, 0 recompute
+  int hq;
+  uint8_t* mask;                // [hq] out: 1 = reuse
+  int32_t* m_count;             // out, nullable
+};
+
+__device__ __forceinline__ bool text_step_reuse(const TextDecide& d, bool writer) {
+  const int lane = threadIdx.x & 63;
+  int m = d.n;
+  if (d.ids_ref) {
+    m = 0;
+    for (int i0 = 0; i0 < d.n; i0 += 64) {
+      const int i = i0 + lane;
+      const bool diff = i < d.n && d.ids_ref[i] != d.ids_cur[i];
+      m += __popcll(__ballot(diff));
+    }
+  }
+  const bool reuse = d.force == 0 ? false : m < d.tau;
+  if (writer) {
+    for (int h = lane; h < d.hq; h += 64) d.mask[h] = reuse ? 1 : 0;
+    if (lane == 0 && d.m_count) *d.m_count = m;
+  }
+  return reuse;
+}
+
 struct PrefixParams {
   const void* q; int64_t q_st, q_sh;
   const void* k; const void* v; int64_t kv_st, kv_sh;
@@ -170,6 +206,9 @@ struct PrefixParams {
   // nearest-rank cutoff; workgroup 0 writes mse / active out)
   int classify;
   ActiveFromMse am;
+  // dense text step: the pass decides reuse itself (mask must be null)
+  int decide_on;
+  TextDecide decide;
 };
 
 // Split-K of the many-rows pass sized on the device: when a head mask leaves
@@ -277,6 +316,10 @@ struct BlockParams {
   // res_l; nullable) as one more weighted term
   const uint8_t* active; const float* res_a; const float* res_l;
   void* q_dst;                  // nullable: every row also stores its query to q_dst[t][h][:]
+  // nullable: the text step's reference ids, updated after a pass that took
+  // the decision itself: ids_store := ids_cur unless ids_keep_on_reuse and
+  // the step reused (mask[0] = 1); done by workgroup (0, 0)
+  const int32_t* ids_cur; int32_t* ids_store; int ids_n; int ids_keep_on_reuse;
 };
 hipError_t launch_block_small(const BlockParams& p, fb_dtype dt, hipStream_t s);
 

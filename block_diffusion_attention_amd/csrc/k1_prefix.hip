@@ -72,6 +72,7 @@ __device__ __forceinline__ bool page_selected(const int32_t* pages, int k, int32
 template <typename T, int D>
 __global__ __launch_bounds__(64) void prefix_generic_kernel(PrefixParams p) {
   constexpr int NPL = D / 64;                 // dims per lane
+  if (p.decide_on && text_step_reuse(p.decide, blockIdx.x == 0 && blockIdx.y == 0)) return;
   const int chunk = blockIdx.x;
   const int64_t row = blockIdx.y;             // t * Hq + h
   const int t = static_cast<int>(row / p.hq);
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   __shared__ float ml_s[kWaves][RP][2];
 
+  if (p.decide_on && text_step_reuse(p.decide, blockIdx.x == 0 && threadIdx.x < 64)) return;
   // XCD-aware order: consecutive workgroup ids go to different XCDs (id mod 8),
   // so the row slabs of one (chunk, KV head) get ids congruent mod 8 and run
   // side by side on one XCD, where the second slab's K/V reads hit its L2.
@@ -581,6 +583,7 @@ __global__ __launch_bounds__(128 * NP, OCC) void prefix_pair_kernel(PrefixParams
   __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   __shared__ float ml_s[2 * NP][32][2];
 
+  if (p.decide_on && text_step_reuse(p.decide, blockIdx.x == 0 && threadIdx.x < 64)) return;
   int chunk, g, slab;
   {
     const int id = blockIdx.x;
