@@ -642,7 +642,7 @@ def text_short_extra(fb, W, dev, stream, probe, layout):
     n_re = sum(1 for x in decisions if x == "reuse")
     # a recompute step launches the prefix kernel (which takes the decision)
     # and the in-block kernel (which merges the split-K partials); a reuse
-    # step the same two; a host-forced reuse step the count and the in-block
+    # step the same two; a host-forced reuse step the in-block kernel alone
     floor3 = launch_floor_ms(probe, TEXT_REUSE_STEP_LAUNCHES, stream)
     g_block = graph_of(block)
     gms_block = _timed(g_block.replay, stream, 20)

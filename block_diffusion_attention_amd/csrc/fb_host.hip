@@ -485,6 +485,7 @@ bool block_small_path(const fb_attn_shape& s, int64_t n_q) {
 // decision (the in-block kernel runs after it and writes the ids).
 struct IdsUpdate {
   const int32_t* cur; int32_t* store; int n; int keep_on_reuse;
+  const TextDecide* decide;     // nullable: the decision is taken by the in-block kernel
 };
 
 fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const fb_tensor& k_blk,
@@ -503,7 +504,7 @@ fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const 
   if (q_blk.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
   if ((fused || ids) && !block_small_path(*shape, q_blk.n_tok)) return FB_ERR_UNSUPPORTED;
-  if (ids && (!fused || !fused->mask)) return FB_ERR_UNSUPPORTED;
+  if (ids && !ids->decide && (!fused || !fused->mask)) return FB_ERR_UNSUPPORTED;
   if (block_rows_path(*shape, q_blk.n_tok)) {
     // many rows: MFMA pass with the merge in its epilogue (16-byte row access)
     if (!aligned16(a_out) || !aligned16(a_full) || (a_in && !aligned16(a_in)))
@@ -579,6 +580,10 @@ fb_status block_merge(const fb_attn_shape* shape, const fb_tensor& q_blk, const 
     bp.ids_store = ids->store;
     bp.ids_n = ids->n;
     bp.ids_keep_on_reuse = ids->keep_on_reuse;
+    if (ids->decide) {
+      bp.decide_on = 1;
+      bp.decide = *ids->decide;
+    }
   }
   return dev(launch_block_small(bp, shape->dtype, stream));
 }
@@ -1038,9 +1043,21 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         rc = run_prefix(s, a->q_blk, st->k_prefix, st->v_prefix, nullptr, nullptr, st->a_out,
                         st->l_out, nullptr, nullptr, st->ws, st->ws_bytes, stream, &hk);
         if (rc != FB_OK) return rc;
-        const IdsUpdate ids = {a->ids_cur, st->ids_prev, n_q, st->count_since_refresh};
+        const IdsUpdate ids = {a->ids_cur, st->ids_prev, n_q, st->count_since_refresh, nullptr};
         rc = block_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full,
                          a->l_full, nullptr, nullptr, &fused, st->a_out, st->l_out, nullptr, stream,
+                         &ids);
+        if (rc != FB_OK) return rc;
+        st->step += 1;
+        return FB_OK;
+      }
+      if (force == 1 && block_small_path(s, n_q) && FB_TEXT_DECIDE_IN_PASS) {
+        // forced reuse: no pass; the in-block kernel counts and decides
+        const TextDecide td = {st->ids_prev, a->ids_cur, n_q, st->tau, 1, hq, st->mask,
+                               st->m_count};
+        const IdsUpdate ids = {a->ids_cur, st->ids_prev, n_q, st->count_since_refresh, &td};
+        rc = block_merge(&s, a->q_blk, a->k_blk, a->v_blk, st->a_out, st->l_out, a->a_full,
+                         a->l_full, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, stream,
                          &ids);
         if (rc != FB_OK) return rc;
         st->step += 1;

@@ -151,7 +151,7 @@ struct RowOut {
 struct TextDecide {
   const int32_t* ids_ref;       // [n] null: first step of a block (every token counts)
   const int32_t* ids_cur;       // [n]
-  int n, tau, force;            // force: -1 the count decides, 0 recompute
+  int n, tau, force;            // force: -1 the count decides, 0 recompute, 1 reuse
   int hq;
   uint8_t* mask;                // [hq] out: 1 = reuse
   int32_t* m_count;             // out, nullable
@@ -168,7 +168,7 @@ __device__ __forceinline__ bool text_step_reuse(const TextDecide& d, bool writer
       m += __popcll(__ballot(diff));
     }
   }
-  const bool reuse = d.force == 0 ? false : m < d.tau;
+  const bool reuse = d.force == 1 ? true : (d.force == 0 ? false : m < d.tau);
   if (writer) {
     for (int h = lane; h < d.hq; h += 64) d.mask[h] = reuse ? 1 : 0;
     if (lane == 0 && d.m_count) *d.m_count = m;
@@ -320,6 +320,11 @@ struct BlockParams {
   // the decision itself: ids_store := ids_cur unless ids_keep_on_reuse and
   // the step reused (mask[0] = 1); done by workgroup (0, 0)
   const int32_t* ids_cur; int32_t* ids_store; int ids_n; int ids_keep_on_reuse;
+  // a step with no prefix pass (host-forced reuse): workgroup (0, 0) also
+  // counts M and publishes the decision first (same wave, each id read
+  // before it is overwritten)
+  int decide_on;
+  TextDecide decide;
 };
 hipError_t launch_block_small(const BlockParams& p, fb_dtype dt, hipStream_t s);
 

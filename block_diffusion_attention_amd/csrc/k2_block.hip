@@ -144,9 +144,11 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
   __shared__ float wts[kMaxMergeChunks];
 
   if (p.ids_store && h == 0 && t == 0) {
-    // the step's decision is complete (previous launch): since-refresh
-    // counting keeps the ids of the last recompute step
-    if (!(p.ids_keep_on_reuse && p.mask[0]))
+    // the step's decision: taken here (no prefix pass) or by the pass (the
+    // previous launch); since-refresh counting keeps the ids of the last
+    // recompute step
+    const bool reuse = p.decide_on ? text_step_reuse(p.decide, true) : p.mask[0] != 0;
+    if (!(p.ids_keep_on_reuse && reuse))
       for (int i = lane; i < p.ids_n; i += 64) p.ids_store[i] = p.ids_cur[i];
   }
   const T* qrow = static_cast<const T*>(p.q) + static_cast<int64_t>(t) * p.q_st +

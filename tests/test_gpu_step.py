@@ -65,6 +65,13 @@ def test_text_forced_reuse_and_recompute(fb):
     got, recs = run_text(fb, cfg, m_override=[None, 4, 0, 4, 4], force=force)
     for s, (rec, (a, l, mc, mask, a_out, l_out)) in enumerate(zip(recs, got)):
         assert rec["decision"] == ([OC.INIT] + force[1:])[s]
+        # the count is reported on forced steps too (forced reuse: taken by
+        # the in-block kernel; forced recompute: by the prefix pass)
+        if s > 0:
+            assert mc == rec["m_count"], s
+        assert np.all(mask == (1 if rec["decision"] == OC.REUSE else 0)), s
+        check_a("forced step %d A_out" % s, a_out, rec["a_out"], 2e-3)
+        check_l("forced step %d L_out" % s, l_out, rec["l_out"], 1e-3)
         check_a("forced step %d" % s, a, rec["a_full"], 2e-3)
         check_l("forced step %d" % s, l, rec["l_full"], 1e-3)
 
