@@ -40,6 +40,9 @@ namespace {
 #ifndef FB_PREFIX_PAIR_SMALL
 #define FB_PREFIX_PAIR_SMALL 1    // <= 32 rows per KV head on head-major K/V: pair kernel
 #endif
+#ifndef FB_PREFIX_HEADS_INNER
+#define FB_PREFIX_HEADS_INNER 1   // token-major K/V: item order heads-inner (see run_prefix)
+#endif
 #ifndef FB_TEXT_DECIDE_IN_PASS
 #define FB_TEXT_DECIDE_IN_PASS 1  // device-decided text steps: the pass counts, no count launch
 #endif
@@ -293,6 +296,10 @@ fb_status run_prefix(const fb_attn_shape& s, const fb_tensor& q, const fb_tensor
   pp.tiles_per_chunk = pl.tiles_per_chunk;
   pp.n_chunks = pl.n_chunks;
   pp.n_slabs = pl.n_slabs;
+  // token-major K/V ([N, Hkv, d]): the KV heads of one key range run side by
+  // side (on the XCDs in turn), so the reads in flight cover whole token
+  // rows rather than one head's 256-byte slice of each
+  pp.heads_inner = FB_PREFIX_HEADS_INNER && !kv_head_major(s, k, v);
   pp.sel_mode = mode;
   if (mode != FB_SEL_DENSE) {
     pp.page_size = sel->page_size;

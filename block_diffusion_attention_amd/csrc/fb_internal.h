@@ -186,6 +186,7 @@ struct PrefixParams {
   int64_t tiles_per_chunk;      // in units of the kernel's tile
   int n_chunks;
   int n_slabs;                  // MFMA path: row slabs per (chunk, KV head)
+  int heads_inner;              // MFMA path: consecutive items = the KV heads of one chunk
   RowOut out;
   // sparse modes
   int sel_mode;                 // FB_SEL_*

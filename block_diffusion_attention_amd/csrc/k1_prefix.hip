@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256, OCC) void prefix_mfma_kernel(PrefixParams p) {
     slab = tq % p.n_slabs;
     const int idx = (tq / p.n_slabs) * 8 + (id & 7);
     if (idx >= p.n_chunks * p.hkv) return;
-    chunk = idx % p.n_chunks;
-    g = idx / p.n_chunks;
+    chunk = p.heads_inner ? idx / p.hkv : idx % p.n_chunks;
+    g = p.heads_inner ? idx % p.hkv : idx / p.n_chunks;
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -591,8 +591,8 @@ __global__ __launch_bounds__(128 * NP, OCC) void prefix_pair_kernel(PrefixParams
     slab = tq % p.n_slabs;
     const int idx = (tq / p.n_slabs) * 8 + (id & 7);
     if (idx >= p.n_chunks * p.hkv) return;
-    chunk = idx % p.n_chunks;
-    g = idx / p.n_chunks;
+    chunk = p.heads_inner ? idx / p.hkv : idx % p.n_chunks;
+    g = p.heads_inner ? idx % p.hkv : idx / p.n_chunks;
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
