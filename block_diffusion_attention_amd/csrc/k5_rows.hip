@@ -10,10 +10,10 @@
 //
 // Workgroup = NW waves = (KV head g, key chunk, row tile of 32 NW RB rows),
 // RB 32-row blocks per wave (RB = 1 is the fastest measured: 2 blocks per
-// wave with 4 waves, O in accumulation registers, ran slower). Rows are (query token, query head of the group)
-// pairs r = t*G + j, so grouped heads share every K/V tile. The waves share
-// each 32-key K/V tile, staged global -> VGPR -> LDS with one barrier per
-// tile; each wave keeps the online-softmax state of its rows over the whole
+// wave with 4 waves, O in accumulation registers, ran slower). Rows are
+// (query token, query head of the group) pairs r = t*G + j, so grouped heads
+// share every K/V tile. The waves share each 32-key K/V tile, staged global
+// -> VGPR -> LDS (eight stages, one barrier per two tiles); each wave keeps the online-softmax state of its rows over the whole
 // key range of its chunk, and runs a software pipeline over the tiles: the
 // softmax of tile t (VALU) is interleaved with S(t+1) = QK(t+1) and
 // O += P(t-1).V(t-1) (matrix core). Per tile and wave:
@@ -66,6 +66,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <bool B> struct Flag { static constexpr bool value = B; };
+template <int I> struct Int { static constexpr int value = I; };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -192,13 +193,15 @@ __device__ __forceinline__ void tile_schedule() {
 
 // Software pipeline over the key tiles of a chunk, per wave: while the
 // VALU runs the softmax of tile t, the matrix core runs S(t+1) = QK(t+1) and
-// O += P(t-1).V(t-1). LDS holds four tile stages: V(t-1) and K(t+1) being
-// read, tile t (its V is read next), and tile t+2 being written from the
-// registers that were loaded from global memory during the previous tile.
+// O += P(t-1).V(t-1). LDS holds eight tile stages (t-1 .. t+5): V(t-1) and
+// K(t+1) being read, and tile t+4 being written from the registers loaded
+// from global memory two tiles earlier (two register sets, by the parity of
+// the tile's position in the chunk).
 template <int NW, int RB, int OCC, bool PSPLIT, bool MERGE>
 __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   constexpr int RPT = 32 / (NW * 4);              // tile rows staged per thread
-  constexpr int kStages = 4;
+  constexpr int kStages = 8;
+  constexpr int kSets = 2;                         // register sets: tiles t+4 and t+5
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStage];
 
   // Work items are (KV group with an unmasked head, chunk, row tile), the
@@ -281,8 +284,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
   // Every step refills the registers unconditionally (tiles past the chunk's
   // last are clamped to it; keys past n_kv to the last key, masked in the
   // scores), so each path through the loop issues the same loads.
-  u32x4 kr[RPT], vr[RPT];
-  auto load = [&](int64_t tile) {
+  u32x4 kr[kSets][RPT], vr[kSets][RPT];
+  auto load = [&](auto set, int64_t tile) {
+    constexpr int S = decltype(set)::value;
     tile = tile < t_last ? tile : t_last;
     const int64_t tok0 = tile * kTile;
     if (tok0 + kTile <= p.n_kv) {
@@ -290,29 +294,30 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
       const char* vb = vg + tok0 * vst;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        kr[i] = *reinterpret_cast<const u32x4*>(kb + (4 * NW * i) * kst + koff);
-        vr[i] = *reinterpret_cast<const u32x4*>(vb + (4 * NW * i) * vst + voff);
+        kr[S][i] = *reinterpret_cast<const u32x4*>(kb + (4 * NW * i) * kst + koff);
+        vr[S][i] = *reinterpret_cast<const u32x4*>(vb + (4 * NW * i) * vst + voff);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         int64_t tok = tok0 + lr + 4 * NW * i;
         tok = tok < p.n_kv ? tok : p.n_kv - 1;
-        kr[i] = *reinterpret_cast<const u32x4*>(kg + tok * kst + lp * 16);
-        vr[i] = *reinterpret_cast<const u32x4*>(vg + tok * vst + lp * 16);
+        kr[S][i] = *reinterpret_cast<const u32x4*>(kg + tok * kst + lp * 16);
+        vr[S][i] = *reinterpret_cast<const u32x4*>(vg + tok * vst + lp * 16);
       }
     }
   };
   auto stage_of = [&](int64_t tile) -> char* {
     return lds + (static_cast<int>(tile - t_begin) & (kStages - 1)) * kStage;
   };
-  auto store = [&](int64_t tile) {
+  auto store = [&](auto set, int64_t tile) {
+    constexpr int S = decltype(set)::value;
     char* kl = stage_of(tile);
     char* vl = kl + kKBytes;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      *reinterpret_cast<u32x4*>(kl + (lr + 4 * NW * i) * kKRow + lp * 16) = kr[i];
-      *reinterpret_cast<u32x4*>(vl + (lr + 4 * NW * i) * kVRow + lp * 16) = vr[i];
+      *reinterpret_cast<u32x4*>(kl + (lr + 4 * NW * i) * kKRow + lp * 16) = kr[S][i];
+      *reinterpret_cast<u32x4*>(vl + (lr + 4 * NW * i) * kVRow + lp * 16) = vr[S][i];
     }
   };
   auto valid_of = [&](int64_t tile) -> int {
@@ -341,11 +346,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
 
   // prologue: tiles t_begin, t_begin + 1 staged, t_begin + 2 in registers,
   // the V part of stage (t_begin - 1) zeroed (the first PV adds P = 0 times it)
-  load(t_begin);
-  store(t_begin);
-  load(t_begin + 1);
-  store(t_begin + 1);
-  load(t_begin + 2);
+  // prologue: tiles t_begin .. t_begin + 3 staged, t_begin + 4 and + 5 in
+  // the two register sets
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    load(Int<0>{}, t_begin + i);
+    store(Int<0>{}, t_begin + i);
+  }
+  load(Int<0>{}, t_begin + 4);
+  load(Int<1>{}, t_begin + 5);
   {
     char* vz = stage_of(t_begin - 1) + kKBytes;
     for (int i = tid; i < kVBytes / 16; i += 64 * NW) *reinterpret_cast<u32x4*>(vz + 16 * i) = u32x4{};
@@ -356,7 +365,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
 
   // one pipelined tile; MASKED only for a partial last tile of the keys.
   // s_in = S(t), computed by the previous tile; s_out receives S(t+1).
-  auto iter = [&](int64_t t, auto masked, const f32x16 (&s_in)[RB], f32x16 (&s_out)[RB]) {
+  // set: the register set of this tile's position parity; sync: end with
+  // the workgroup barrier
+  auto iter = [&](int64_t t, auto masked, const f32x16 (&s_in)[RB], f32x16 (&s_out)[RB],
+                  auto set, auto sync) {
     constexpr bool M = decltype(masked)::value;
     qk_tile<RB>(stage_of(t + 1) + k_rd, qop, s_out);
     pv_tile<RB, PSPLIT>(o, ph, pl, stage_of(t - 1) + v_rd);
@@ -397,23 +409,32 @@ __global__ __launch_bounds__(64 * NW, OCC) void rows_mfma_kernel(RowsParams p) {
         for (int db = 0; db < 4; ++db) o[b][db] *= alpha;
       }
     }
-    store(t + 2);
-    load(t + 3);
-    __syncthreads();
+    // eight stages, stores four tiles ahead: a stage read at tile j was
+    // written at tile j - 3 (K) or j - 5 (V) and is overwritten at tile
+    // j + 5 (K) or j + 3 (V), so one barrier in any three consecutive tiles
+    // orders both; the loop syncs after every second tile
+    store(set, t + 4);
+    load(set, t + 6);
+    if (decltype(sync)::value) __syncthreads();
   };
   // two tiles per trip: S alternates between the two register sets
   int64_t tt = t_begin;
   for (; tt + 1 < t_last; tt += 2) {
-    iter(tt, Flag<false>{}, s_cur, s_nxt);
-    iter(tt + 1, Flag<false>{}, s_nxt, s_cur);
+    iter(tt, Flag<false>{}, s_cur, s_nxt, Int<0>{}, Flag<false>{});
+    iter(tt + 1, Flag<false>{}, s_nxt, s_cur, Int<kSets - 1>{}, Flag<true>{});
   }
   if (tt < t_last) {
-    iter(tt, Flag<false>{}, s_cur, s_nxt);
+    iter(tt, Flag<false>{}, s_cur, s_nxt, Int<0>{}, Flag<true>{});
 #pragma unroll
     for (int b = 0; b < RB; ++b) s_cur[b] = s_nxt[b];
   }
-  if (valid_of(t_last) < kTile) iter(t_last, Flag<true>{}, s_cur, s_nxt);
-  else iter(t_last, Flag<false>{}, s_cur, s_nxt);
+  // the last tile (position parity picks its register set)
+  auto last = [&](auto set) {
+    if (valid_of(t_last) < kTile) iter(t_last, Flag<true>{}, s_cur, s_nxt, set, Flag<true>{});
+    else iter(t_last, Flag<false>{}, s_cur, s_nxt, set, Flag<true>{});
+  };
+  if (((t_last - t_begin) & 1) == 0) last(Int<0>{});
+  else last(Int<kSets - 1>{});
   pv_tile<RB, PSPLIT>(o, ph, pl, stage_of(t_end - 1) + v_rd);
 
   // epilogue, per block: lane (r32, hl) holds dims 32 db + 8 q + 4 hl + (0..3) of its row
