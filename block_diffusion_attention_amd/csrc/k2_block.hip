@@ -154,8 +154,40 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
   const T* qrow = static_cast<const T*>(p.q) + static_cast<int64_t>(t) * p.q_st +
                   static_cast<int64_t>(h) * p.q_sh;
   const int64_t row = static_cast<int64_t>(t) * p.hq + h;
+  const T* kb = static_cast<const T*>(p.k) + static_cast<int64_t>(g) * p.k_sh;
+  const T* vb = static_cast<const T*>(p.v) + static_cast<int64_t>(g) * p.v_sh;
+  // bf16: the K row of this lane's key among the first 64 and this lane's
+  // dims of the first kPreV V rows are loaded before anything else, so a
+  // block of up to kPreV tokens needs one memory round trip (with the cached
+  // pair and the query row) instead of three
+  constexpr bool kPre = sizeof(T) == 2;
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kPreV = 16;
+  u32x4v k0[kPre ? D / kVec : 1];
+  T v0[kPre ? kPreV : 1][NPL];                     // raw bits, converted where used
+  if (kPre) {
+    // rows past the block clamp to its last (loaded, never used)
+    const int kj = lane < p.n_q ? lane : p.n_q - 1;
+    const T* kr = kb + static_cast<int64_t>(kj) * p.k_st;
+#pragma unroll
+    for (int u = 0; u < D / kVec; ++u) k0[u] = *reinterpret_cast<const u32x4v*>(kr + u * kVec);
+#pragma unroll
+    for (int jj = 0; jj < kPreV; ++jj) {
+      const T* vr = vb + static_cast<int64_t>(jj < p.n_q ? jj : p.n_q - 1) * p.v_st;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) v0[jj][i] = vr[lane + 64 * i];
+    }
+  }
+  // the query row (16-byte groups), issued with the prefetch above
+  constexpr int kQV = 16 / sizeof(T);
+  u32x4v qw = {0u, 0u, 0u, 0u};
+  if (lane < D / kQV) qw = *reinterpret_cast<const u32x4v*>(qrow + lane * kQV);
+  // the cached pair, loaded with the rest (on a fresh pass it is replaced
+  // by the merge of the partials below, and these values go unused)
   float a_out[NPL];
-  float l_out;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) a_out[i] = p.a_out[row * D + lane + 64 * i];
+  float l_out = p.l_out[row];
   if (p.part_l && !(p.mask && p.mask[h]) && !(p.active && !p.active[t])) {
     // a fresh prefix pass: merge this row's split-K partials (the same
     // operations in the same order as the reduce pass) into the pair
@@ -163,26 +195,15 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
     p.cache_l[row] = l_out;                        // (every lane writes the same value)
 #pragma unroll
     for (int i = 0; i < NPL; ++i) p.cache_a[row * D + lane + 64 * i] = a_out[i];
-  } else {
-    // the cached pair, loaded now so its latency hides behind the pass
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) a_out[i] = p.a_out[row * D + lane + 64 * i];
-    l_out = p.l_out[row];
   }
-  {
-    constexpr int kV = 16 / sizeof(T);             // the query row as 16-byte groups
-    if (lane < D / kV) {
-      const u32x4v w = *reinterpret_cast<const u32x4v*>(qrow + lane * kV);
+  if (lane < D / kQV) {
 #pragma unroll
-      for (int e = 0; e < kV; ++e) qs[lane * kV + e] = vec_elem<T>(w, e);
-      if (p.q_dst)                                 // (after every read of q_dst this step)
-        *reinterpret_cast<u32x4v*>(static_cast<T*>(p.q_dst) + row * D + lane * kV) = w;
-    }
+    for (int e = 0; e < kQV; ++e) qs[lane * kQV + e] = vec_elem<T>(qw, e);
+    if (p.q_dst)                                   // (after every read of q_dst this step)
+      *reinterpret_cast<u32x4v*>(static_cast<T*>(p.q_dst) + row * D + lane * kQV) = qw;
   }
   __syncthreads();
 
-  const T* kb = static_cast<const T*>(p.k) + static_cast<int64_t>(g) * p.k_sh;
-  const T* vb = static_cast<const T*>(p.v) + static_cast<int64_t>(g) * p.v_sh;
   float m = kNegInf, l = 0.f, o[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) o[i] = 0.f;
@@ -201,8 +222,13 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
 #pragma unroll
       for (int c0 = 0; c0 < D; c0 += kR) {
         u32x4v kv[kR / kV];
+        if (kPre && base == 0) {
 #pragma unroll
-        for (int u = 0; u < kR / kV; ++u) kv[u] = *reinterpret_cast<const u32x4v*>(kr + c0 + u * kV);
+          for (int u = 0; u < kR / kV; ++u) kv[u] = k0[(c0 / kV + u) % (kPre ? D / kVec : 1)];
+        } else {
+#pragma unroll
+          for (int u = 0; u < kR / kV; ++u) kv[u] = *reinterpret_cast<const u32x4v*>(kr + c0 + u * kV);
+        }
 #pragma unroll
         for (int u = 0; u < kR / kV; ++u)
 #pragma unroll
@@ -220,7 +246,18 @@ __global__ __launch_bounds__(64) void block_small_kernel(BlockParams p) {
     ps[lane] = pr;
     __syncthreads();
     const int nb = p.n_q - base < 64 ? p.n_q - base : 64;
-    for (int jj = 0; jj < nb; ++jj) {
+    int jj = 0;
+    if (kPre && base == 0) {
+#pragma unroll
+      for (int u = 0; u < kPreV; ++u)
+        if (u < nb) {
+          const float pj = ps[u];
+#pragma unroll
+          for (int i = 0; i < NPL; ++i) o[i] += pj * ld<T>(&v0[u % (kPre ? kPreV : 1)][i]);
+        }
+      jj = nb < kPreV ? nb : kPreV;
+    }
+    for (; jj < nb; ++jj) {
       const float pj = ps[jj];
       const T* vr = vb + static_cast<int64_t>(base + jj) * p.v_st;
 #pragma unroll
