@@ -718,7 +718,9 @@ def video_extra(fb, W, dev, stream, layout):
 def sparse_extra(fb, W, dev, stream, layout):
     """Sparse + residual reuse (32q/8kv, d=128, 65536-token prefix in 16-token
     pages, B=8, 8 steps): per density, the block through fb_step and the gather
-    pass's HBM rate over the union of the active tokens' selected pages."""
+    pass's HBM rate over the union of the active tokens' selected pages, back
+    to back and with the last-level cache filled with dirty lines before each
+    call."""
     import torch
     res = []
     base = W.SPARSE
@@ -729,6 +731,7 @@ def sparse_extra(fb, W, dev, stream, layout):
     kd, vd = prefix_cache(kp, dev, layout), prefix_cache(vp, dev, layout)
     H, G, d, B, N, PS = base.n_q_heads, base.n_kv_heads, base.head_dim, base.n_block, base.n_prefix, base.page
     shape = fb.shape_of(H, G, d, base.scale, torch.bfloat16)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for dens in W.SPARSE_DENSITIES:
         cfg = base.with_(density=dens)
         steps = [tuple(bf(s[n]) for n in ("q", "k", "v")) for s in W.sparse_steps(cfg)]
@@ -751,9 +754,23 @@ def sparse_extra(fb, W, dev, stream, layout):
                          device=dev)
         a = st.a_out.clone()
         l = st.l_out.clone()
-        ms_g = _timed(lambda: fb.fb_prefix_attn(shape, steps[-1][0], kd, vd, a, l, sel=sel,
-                                                a_res=st.a_res, l_res=st.l_res, ws=ws,
-                                                stream=stream), stream, 20)
+        call = lambda: fb.fb_prefix_attn(shape, steps[-1][0], kd, vd, a, l, sel=sel,
+                                         a_res=st.a_res, l_res=st.l_res, ws=ws, stream=stream)
+        # back to back: the union (112-186 MB) stays in the 256 MB last-level
+        # cache between calls, so this rate is partly a cache rate
+        ms_g = _timed(call, stream, 20)
+        # cold: the last-level cache filled with 1 GiB of freshly written
+        # (dirty) lines before every call, median of single calls
+        ts = []
+        for _ in range(15):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms_cold = float(np.median(ts))
         pg, on = st.pages.cpu().numpy(), act.cpu().numpy().astype(bool)
         u = np.array([np.unique(pg[on, g]).size for g in range(G)])   # pages the gather reads
         g_bytes = int(u.sum()) * PS * d * 2 * 2
@@ -763,7 +780,11 @@ def sparse_extra(fb, W, dev, stream, layout):
                     "union_pages_per_kv_head": [int(x) for x in u],
                     "gather_GB_s": round(g_bytes / (ms_g * 1e-3) / 1e9, 1),
                     "gather_frac_of_hbm_peak": round(g_bytes / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "gather_cold_pass_us": round(ms_cold * 1e3, 1),
+                    "gather_cold_frac_of_hbm_peak": round(g_bytes / (ms_cold * 1e-3) / 1e9 /
+                                                          PEAK_HBM_GBS, 4),
                     "active_tokens_last_step": int(act.sum().item())})
+    del flush
     return res
 
 

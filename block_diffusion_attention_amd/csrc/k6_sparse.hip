@@ -690,8 +690,10 @@ void sparse_mfma_kernel(PrefixParams p) {
       int64_t tok = tok0[i >> 2] + 4 * (i & 3) + lrow;
       tok = tok < p.n_kv ? tok : p.n_kv - 1;
       const int64_t off = tok * kvst_b + lpiece * 16;
-      r.k[i] = *reinterpret_cast<const u32x4*>(kg + off);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vg + off);
+      // streamed once: non-temporal, so the reads do not allocate in the
+      // last-level cache (and evict the dirty lines other work left there)
+      r.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + off));
+      r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + off));
     }
     return r;
   };
