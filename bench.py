@@ -90,7 +90,29 @@ def load_probe():
                                          C.c_void_p, C.c_int, C.c_void_p]
     lib.fb_probe_empty_launches.restype = C.c_int
     lib.fb_probe_empty_launches.argtypes = [C.c_int, C.c_void_p]
+    lib.fb_probe_f64_mfma.restype = C.c_int
+    lib.fb_probe_f64_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     return lib
+
+
+def f64_mfma_rate(probe, stream, dev):
+    """TFLOP/s of independent float64 MFMA chains (v_mfma_f64_16x16x4f64, 4
+    per wave) with 1, 2 and 4 waves per SIMD (256, 512, 1024 workgroups of 4
+    waves), after half a second of the same work: the rate the float64
+    contraction can reach on this part, the best of the three."""
+    import torch
+    iters = 1024
+    best = {}
+    for wgs in (256, 512, 1024):
+        out = torch.empty(wgs * 256, dtype=torch.float64, device=dev)
+
+        def run():
+            rc = probe.fb_probe_f64_mfma(wgs, iters, out.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("fb_probe_f64_mfma failed (%d)" % rc)
+        ms = _timed_settled(run, stream, 5, batches=3)
+        best[wgs // 256] = 8192.0 * iters * wgs * 4 / (ms * 1e-3) / 1e12
+    return best
 
 
 def stream_read_rate(probe, a_ptr, b_ptr, nbytes, stream, dev, reps=20):
@@ -402,6 +424,20 @@ def _timed(fn, stream, reps):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def _timed_settled(fn, stream, reps, warm_s=0.5, batches=5):
+    """Median over `batches` of the average ms of `reps` calls of fn (HIP
+    events on `stream`), after `warm_s` seconds of untimed calls: short
+    launches on an idle GPU otherwise time its clock ramp."""
+    import time
+    import torch
+    t_end = time.time() + warm_s
+    while time.time() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    return float(np.median([_timed(fn, stream, reps) for _ in range(batches)]))
 
 
 def reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N, hq, hkv, d, stream, probe):
@@ -871,8 +907,10 @@ def losa_extra(fb, W, dev, stream, layout):
 def spa_extra(fb, W, dev, stream, layout):
     """The singular-proxy identifier (1024 tokens of width 4096, rank-128
     factor of the value projection, a quarter of the tokens recomputed per
-    step): one identification step, and its block-partial contraction
-    (2 N D r float64 flops) against the float64 vector peak."""
+    step): one identification step (four launches), its block-partial
+    contraction's 2 N D r float64 flops over the whole step's time against
+    the float64 peak (78.6 TFLOP/s, matrix and vector alike) and against the
+    rate a probe of bare float64 MFMA chains reaches on the part."""
     import torch
     del layout
     cfg = W.SPA
@@ -893,13 +931,17 @@ def spa_extra(fb, W, dev, stream, layout):
         a0.ws, a0.ws_bytes = ws.data_ptr(), ws.numel()
         a1 = fb.proxy_args(xs[1], f, cache, mask, sel, k, init=False, ws=ws)
         fb.fb_proxy_decide(a0, stream)
-        ms = _timed(lambda: fb.fb_proxy_decide(a1, stream), stream, 50)
+        ms = _timed_settled(lambda: fb.fb_proxy_decide(a1, stream), stream, 50)
         out["step_us_select_%d" % k] = round(ms * 1e3, 2)
     flops = 2.0 * n * d * r
+    rates = f64_mfma_rate(load_probe(), stream, dev)
+    out["fp64_mfma_probe_TFLOP_s"] = {"%d_waves_per_simd" % w: round(v, 1) for w, v in rates.items()}
     out["proxy_flop"] = flops
     out["proxy_TFLOP_s_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6) / 1e12, 2)
-    out["frac_of_fp64_vector_peak_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6)
-                                                       / 1e12 / 78.6, 4)
+    out["frac_of_fp64_peak_whole_step"] = round(flops / (out["step_us_select_256"] * 1e-6)
+                                                / 1e12 / 78.6, 4)
+    out["frac_of_fp64_mfma_probe_whole_step"] = round(
+        flops / (out["step_us_select_256"] * 1e-6) / 1e12 / max(rates.values()), 4)
     return out
 
 
@@ -945,7 +987,7 @@ def stack_identification_extra(fb, W, dev, stream, layout):
         def step():
             for a in args:
                 fb.fb_proxy_decide(a, stream)
-        ms = _timed(step, stream, 5)
+        ms = _timed_settled(step, stream, 5, batches=3)
         out["ms_step_%s" % name] = round(ms, 3)
     return out
 

@@ -828,7 +828,8 @@ size_t fb_proxy_decide_workspace(const fb_proxy_args* a) {
   const size_t n = static_cast<size_t>(a->n_tok), r = static_cast<size_t>(a->rank);
   size_t ws = align_up(static_cast<size_t>(proxy_n_blocks(a->d_model)) * n * r * sizeof(double));
   if (!a->proxy) ws += align_up(n * r * sizeof(double));
-  ws += align_up(n * sizeof(double));                 // negated keys (top-k input)
+  ws += align_up(n * sizeof(double));                 // negated keys (selection input)
+  ws += align_up((n + 63) / 64 * sizeof(uint64_t));   // selection words, 64 tokens each
   return ws;
 }
 
@@ -856,6 +857,8 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
     w += align_up(n * r * sizeof(double));
   }
   double* neg_key = reinterpret_cast<double*>(w);
+  w += align_up(n * sizeof(double));
+  uint64_t* words = reinterpret_cast<uint64_t*>(w);
   fb_status rc = dev(launch_proxy_partials(a->x, a->x_stride, a->factor, a->dtype, a->n_tok,
                                            a->d_model, a->rank, part, stream));
   if (rc != FB_OK) return rc;
@@ -863,6 +866,11 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
                              neg_key, a->mask, stream));
   if (rc != FB_OK || a->init) return rc;
   if (a->n_select == 0) return dev(launch_fill_u8(a->mask, a->n_tok, 0, stream));
+  // up to a few thousand tokens: rank counting (mask, cache rows, selection
+  // words), then the ascending ids; beyond, the radix top-k and a scatter
+  if (a->n_tok <= proxy_select_max_tok())
+    return dev(launch_proxy_select(neg_key, a->n_tok, a->n_select, proxy, a->rank, a->cache,
+                                   a->mask, words, a->selected, stream));
   // the lowest similarities are the largest negated ones (ties: lower id); the
   // top-k writes every token's mask byte
   rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, nullptr, a->selected, a->mask,

@@ -399,6 +399,10 @@ int proxy_n_blocks(int d_model);
 hipError_t launch_proxy_keys(const double* part, int n_blocks, int n_tok, int rank, int init,
                              double* cache, double* proxy, double* sim, double* neg_key,
                              uint8_t* mask, hipStream_t s);
+int proxy_select_max_tok();
+hipError_t launch_proxy_select(const double* neg_key, int n_tok, int n_select,
+                               const double* proxy, int rank, double* cache, uint8_t* mask,
+                               uint64_t* words, int32_t* selected, hipStream_t s);
 hipError_t launch_proxy_scatter(const int32_t* selected, int n_select, int n_tok,
                                 const double* proxy, int rank, double* cache, hipStream_t s);
 // the finished block's K/V rows into cache tokens [tok0, tok0 + n_blk); byte

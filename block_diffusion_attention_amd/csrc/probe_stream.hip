@@ -1,9 +1,11 @@
-// probe_stream.hip -- the achievable HBM read rate on this part, for the
-// benchmark's roofline: a read-only streaming kernel over two buffers (the
-// prefix K and V the attention pass reads), with the same access style as
-// that pass (16-byte non-temporal loads, several in flight per lane) and no
-// arithmetic beyond an XOR that keeps the loads live. Not part of the
-// FlashBlock ABI: built as its own library, used by the benchmark only.
+// probe_stream.hip -- probes for the benchmark's rooflines: the achievable
+// HBM read rate on this part, from a read-only streaming kernel over two
+// buffers (the prefix K and V the attention pass reads) with the same access
+// style as that pass (16-byte non-temporal loads, several in flight per
+// lane) and no arithmetic beyond an XOR that keeps the loads live; the
+// float64 matrix-core rate (independent MFMA chains, nothing else); the
+// launch floor. Not part of the FlashBlock ABI: built as its own library,
+// used by the benchmark only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,9 +57,45 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* a, i
 
 __global__ void empty_kernel() {}
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// The float64 matrix-core rate: each wave runs 4 independent accumulator
+// chains of v_mfma_f64_16x16x4f64 (2048 flops each) for `iters` rounds; the
+// lane's sum goes to out so that nothing is dead.
+__global__ __launch_bounds__(256) void f64_mfma_kernel(double* out, int iters) {
+  const int l = threadIdx.x & 63;
+  const double a = 1.0 + l * 1e-3, b = 1.0 - l * 1e-3;
+  f64x4 c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c[q], 0, 0, 0);
+  }
+  // explicit wait before vector reads of the accumulators (128 cycles)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile(
+      "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\t"
+      "s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s += c[q][0] + c[q][1] + c[q][2] + c[q][3];
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
+
+// n_workgroups workgroups of 256 threads (4 waves) of the float64 MFMA rate
+// kernel, 4 MFMAs per wave per round for `iters` rounds: 8192 * iters flops
+// per wave. out: device [n_workgroups * 256] float64. Returns 0 on
+// success, 1 on invalid arguments, 2 on a launch error.
+int fb_probe_f64_mfma(int n_workgroups, int iters, double* out, hipStream_t stream) {
+  if (n_workgroups < 1 || iters < 1 || !out) return 1;
+  hipLaunchKernelGGL(f64_mfma_kernel, dim3(n_workgroups), dim3(256), 0, stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // n back-to-back launches of an empty one-wave kernel on `stream`: the
 // launch floor a sequence of n dependent kernels cannot go below.

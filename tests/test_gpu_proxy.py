@@ -81,6 +81,10 @@ CASES = [
     ("f32_r64", 50, 600, 64, 13, "f32"),
     ("select_none", 40, 512, 32, 0, "bf16"),
     ("select_all", 40, 512, 32, 40, "bf16"),
+    # the rank-counting selection at its largest size (128 workgroups), and
+    # the radix top-k + scatter just beyond it
+    ("select_rank_8192", 8192, 256, 32, 2000, "bf16"),
+    ("select_radix_8200", 8200, 256, 32, 2050, "bf16"),
 ]
 
 
@@ -118,9 +122,11 @@ def test_identifier_exact_on_small_integers(fb):
     assert np.array_equal(cpu(idn.cache), OS.proxy(x, f))
 
 
-def test_identifier_ties_go_to_lower_ids(fb):
+@pytest.mark.parametrize("n,k", [(50, 9), (300, 130), (8200, 3000)])
+def test_identifier_ties_go_to_lower_ids(fb, n, k):
     # every token identical and its cache identical: every similarity is 1
-    n, d, r, k = 50, 512, 32, 9
+    # (one workgroup, ties across several, and the radix top-k)
+    d, r = 512, 32
     rng = np.random.default_rng(0)
     row = W.bf16_bits(rng.standard_normal((1, d)).astype(np.float32))
     x = np.repeat(row, n, axis=0)
@@ -130,6 +136,7 @@ def test_identifier_ties_go_to_lower_ids(fb):
     idn.step(_dev(x, "bf16"), _dev(f, "bf16"), init=False, with_proxy=False)
     assert (cpu(idn.sim) == 1.0).all()
     assert cpu(idn.selected)[:k].tolist() == list(range(k))
+    assert cpu(idn.mask).astype(bool).tolist() == [t < k for t in range(n)]
 
 
 def test_identifier_full_size(fb):
