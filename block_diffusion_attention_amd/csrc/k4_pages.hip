@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q
                                                            int hkv, int d, int64_t n_pages,
                                                            int64_t page_cap, const uint8_t* active,
                                                            double* bound) {
-  extern __shared__ float sm[];
+  extern __shared__ __attribute__((aligned(16))) float sm[];
   __shared__ int tok[TC];
   __shared__ int n_tok_s;
   const int g = blockIdx.y;
@@ -217,24 +217,48 @@ __global__ __launch_bounds__(256) void page_bound_g_kernel(const T* q, int64_t q
 #pragma unroll
     for (int j = 0; j < G; ++j) acc[j] = 0.0;
     if constexpr (sizeof(T) == 2) {                  // two dims per LDS word
+      // 8 dims per step: the page's kmin / kmax words (two 8-byte reads
+      // each) and the token's 8 x G query values (2 G 16-byte reads) are
+      // read before the step's multiply-adds, and the next step's reads are
+      // issued before them (the LDS latency is otherwise paid per read)
       const uint32_t* mnw = reinterpret_cast<const uint32_t*>(mn + pi * rs);
       const uint32_t* mxw = reinterpret_cast<const uint32_t*>(mx + pi * rs);
-      for (int c2 = 0; c2 < d / 2; ++c2) {
-        const uint32_t wa = mnw[c2], wb = mxw[c2];
-        const float a0 = __uint_as_float(wa << 16), a1 = __uint_as_float(wa & 0xffff0000u);
-        const float b0 = __uint_as_float(wb << 16), b1 = __uint_as_float(wb & 0xffff0000u);
+      struct Chunk {
+        uint2 a0, a1, b0, b1;
+        float4 qv[2 * G];                            // [8 dims][G]
+      };
+      auto load = [&](int c8, Chunk& k) __attribute__((always_inline)) {
+        k.a0 = *reinterpret_cast<const uint2*>(mnw + c8 / 2);
+        k.a1 = *reinterpret_cast<const uint2*>(mnw + c8 / 2 + 2);
+        k.b0 = *reinterpret_cast<const uint2*>(mxw + c8 / 2);
+        k.b1 = *reinterpret_cast<const uint2*>(mxw + c8 / 2 + 2);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float qv = qr[2 * c2 * G + j];
-          acc[j] = __builtin_fma(static_cast<double>(qv), static_cast<double>(qv >= 0.f ? b0 : a0),
-                                 acc[j]);
-        }
+        for (int i = 0; i < 2 * G; ++i) k.qv[i] = *reinterpret_cast<const float4*>(qr + c8 * G + 4 * i);
+      };
+      auto step = [&](const Chunk& k) __attribute__((always_inline)) {
+        const uint32_t wa[4] = {k.a0.x, k.a0.y, k.a1.x, k.a1.y};
+        const uint32_t wb[4] = {k.b0.x, k.b0.y, k.b1.x, k.b1.y};
+        const float* qf = reinterpret_cast<const float*>(k.qv);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float qv = qr[(2 * c2 + 1) * G + j];
-          acc[j] = __builtin_fma(static_cast<double>(qv), static_cast<double>(qv >= 0.f ? b1 : a1),
-                                 acc[j]);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t ua = wa[e >> 1], ub = wb[e >> 1];
+          const float av = __uint_as_float((e & 1) ? (ua & 0xffff0000u) : (ua << 16));
+          const float bv = __uint_as_float((e & 1) ? (ub & 0xffff0000u) : (ub << 16));
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const float qv = qf[e * G + j];
+            acc[j] = __builtin_fma(static_cast<double>(qv),
+                                   static_cast<double>(qv >= 0.f ? bv : av), acc[j]);
+          }
         }
+      };
+      Chunk k0, k1;
+      load(0, k0);
+      for (int c8 = 0; c8 < d; c8 += 16) {           // (d is a multiple of 16)
+        load(c8 + 8, k1);
+        step(k0);
+        if (c8 + 16 < d) load(c8 + 16, k0);
+        step(k1);
       }
     } else {
       const float* mnr = reinterpret_cast<const float*>(mn) + pi * rs;
