@@ -82,9 +82,10 @@ class Step:
     prefix (the next call recomputes the cached pair). ``since_refresh``:
     TEXT counts the ids changed since the last recompute step. ``reselect``:
     SPARSE runs LoSA's own step (dense first step, pages chosen again at
-    every step, no residual). ``sel_bitmap``: SPARSE (residual mode) keeps the
-    refresh step's selection as bitmaps in a buffer of its own, so later
-    steps run no selection prep (False: rebuilt every step).
+    every step, no residual). ``sel_bitmap``: SPARSE keeps a selection as
+    bitmaps in a buffer of its own: in residual mode the refresh step's, so
+    later steps run no selection prep; with ``reselect`` each step's top-k
+    writes its fresh selection there (False: a selection prep every step).
     """
 
     def __init__(self, mode, shape, n_q, k_prefix=None, v_prefix=None, tau=0, gamma=0.0,
@@ -145,10 +146,10 @@ class Step:
             self.active = torch.zeros(n_q, device=dev, dtype=torch.uint8)
             for name in ("a_res", "l_res", "pages", "kmin", "kmax", "q_prev", "mse", "active"):
                 setattr(st, name, ptr(getattr(self, name)))
-            # FlashBlock's residual mode keeps the refresh step's selection as
-            # bitmaps: later steps read them instead of rebuilding them
+            # the selection as bitmaps: the refresh step's (residual mode) or
+            # each step's own (reselect), read by the GATHER workgroups
             self.sel_bitmap = None
-            if not reselect and sel_bitmap:
+            if sel_bitmap:
                 words = (max(n_pages, 1) + 31) // 32
                 self.sel_bitmap = torch.zeros(n_q, hkv, words, device=dev, dtype=torch.int32)
                 st.sel_bitmap = ptr(self.sel_bitmap)

@@ -777,10 +777,14 @@ size_t fb_page_select_workspace(const fb_attn_shape* shape, int64_t n_q, int64_t
   return align_up(static_cast<size_t>(n_q) * shape->n_kv_heads * n_pages * sizeof(double));
 }
 
-fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* kmin,
-                         const void* kmax, int64_t n_pages, int64_t page_cap, int32_t k_pages,
-                         const uint8_t* active, int32_t* pages, double* bound, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+// fb_page_select, and (bitmap non-null, n_pages <= topk_bitmap_max()) the
+// selection also written as bitmap words [n_q, Hkv, ceil(n_pages / 32)]
+// for the active tokens' rows
+static fb_status page_select_impl(const fb_attn_shape* shape, fb_tensor q, const void* kmin,
+                                  const void* kmax, int64_t n_pages, int64_t page_cap,
+                                  int32_t k_pages, const uint8_t* active, int32_t* pages,
+                                  double* bound, uint32_t* bitmap, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   if (q.n_tok < 1 || q.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
@@ -803,10 +807,19 @@ fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* km
     if (ws_bytes < need || (need > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;
     bound = static_cast<double*>(ws);
   }
+  if (bitmap && n_pages > topk_bitmap_max()) return FB_ERR_UNSUPPORTED;
   return dev(launch_page_select(q.ptr, q.stride_tok, q.stride_head, kmin, kmax,
                                 static_cast<int>(q.n_tok), shape->n_q_heads, shape->n_kv_heads,
                                 shape->head_dim, n_pages, page_cap, k_pages, shape->dtype, active,
-                                bound, pages, stream));
+                                bound, pages, bitmap, stream));
+}
+
+fb_status fb_page_select(const fb_attn_shape* shape, fb_tensor q, const void* kmin,
+                         const void* kmax, int64_t n_pages, int64_t page_cap, int32_t k_pages,
+                         const uint8_t* active, int32_t* pages, double* bound, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return page_select_impl(shape, q, kmin, kmax, n_pages, page_cap, k_pages, active, pages, bound,
+                          nullptr, ws, ws_bytes, stream);
 }
 
 fb_status fb_page_bitmap(const fb_attn_shape* shape, const int32_t* pages, int64_t n_q,
@@ -874,7 +887,7 @@ fb_status fb_proxy_decide(const fb_proxy_args* a, hipStream_t stream) {
   // the lowest similarities are the largest negated ones (ties: lower id); the
   // top-k writes every token's mask byte
   rc = dev(launch_topk_rows(neg_key, 1, 1, a->n_tok, a->n_select, nullptr, a->selected, a->mask,
-                            stream));
+                            nullptr, stream));
   if (rc != FB_OK) return rc;
   return dev(launch_proxy_scatter(a->selected, a->n_select, a->n_tok, proxy, a->rank, a->cache,
                                   stream));
@@ -1249,14 +1262,22 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
       } else if (a->decision != 1) {
         rc = token_step(a->decision == 0 ? 0 : 1, 1);
         if (rc != FB_OK) return rc;
-        if (reselect) {                            // the active tokens' queries choose pages
-          rc = fb_page_select(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
-                              st->active, st->pages, nullptr, st->ws, st->ws_bytes, stream);
+        // the active tokens' queries choose pages; with a bitmap buffer the
+        // top-k also writes them as bitmaps and the GATHER workgroups take
+        // their union themselves (no selection-prep launch)
+        const bool sel_bits = reselect && st->sel_bitmap && st->k_pages > 0 &&
+                              n_pages <= topk_bitmap_max() &&
+                              gather_union_fits(static_cast<int>(n_q),
+                                                static_cast<int>((n_pages + 31) / 32));
+        if (reselect) {
+          rc = page_select_impl(&s, a->q_blk, st->kmin, st->kmax, n_pages, page_cap, st->k_pages,
+                                st->active, st->pages, nullptr, sel_bits ? st->sel_bitmap : nullptr,
+                                st->ws, st->ws_bytes, stream);
           if (rc != FB_OK) return rc;
         }
         sel.mode = FB_SEL_GATHER;
         sel.active = st->active;
-        if (prebuilt) sel.bitmap = st->sel_bitmap;
+        if (prebuilt || sel_bits) sel.bitmap = st->sel_bitmap;
         float* ar = reselect ? nullptr : st->a_res;
         float* lr = reselect ? nullptr : st->l_res;
         const PrefixPlan gp = plan_prefix(s, n_q, st->k_prefix.n_tok, &sel,

@@ -382,14 +382,17 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                               const void* kmax, int n_q, int hq, int hkv, int d,
                               int64_t n_pages, int64_t page_cap, int k_pages, fb_dtype dt,
                               const uint8_t* active, double* bound, int32_t* pages,
-                              hipStream_t s);
+                              uint32_t* bitmap, hipStream_t s);
 // exact top-k of each row of keys [n_rows * hkv][n] (largest first, ties to
 // the lower index), the chosen indices listed ascending in out [.., k];
 // row_active (nullable, [n_rows]): rows r * hkv + . with byte 0 are skipped;
-// flags (nullable, [rows][n]): 1 for the chosen indices, 0 for the others
+// flags (nullable, [rows][n]): 1 for the chosen indices, 0 for the others;
+// bitmap (nullable, [rows][ceil(n / 32)], n <= topk_bitmap_max()): the
+// chosen indices as bits (rows skipped by row_active are not written)
+int topk_bitmap_max();
 hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
                             const uint8_t* row_active, int32_t* out, uint8_t* flags,
-                            hipStream_t s);
+                            uint32_t* bitmap, hipStream_t s);
 // singular-proxy identification: block partials of the proxies, then the
 // proxies, cache fill (init) or ranking keys (+ negated keys for the top-k)
 bool proxy_rank_ok(int rank);

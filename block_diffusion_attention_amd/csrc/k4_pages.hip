@@ -406,7 +406,7 @@ template <int KPT>
 __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound, int hkv,
                                                             int64_t n_pages, int k,
                                                             const uint8_t* active, int32_t* pages,
-                                                            uint8_t* flags) {
+                                                            uint8_t* flags, uint32_t* bitmap) {
   __shared__ int hist[256];
   __shared__ int red[4];
   __shared__ unsigned long long sh_prefix;
@@ -515,6 +515,7 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
   take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
   int pos = block_exscan4(gt + take_eq, red, tot);
   int eq_seen = 0;
+  uint32_t bits = 0;                               // bit i: page p0 + i chosen
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const bool is_eq = key[i] == T;
@@ -522,6 +523,21 @@ __global__ __launch_bounds__(256) void page_topk_reg_kernel(const double* bound,
     eq_seen += is_eq ? 1 : 0;
     if (sel) out[pos++] = static_cast<int32_t>(p0 + i);
     if (flags && p0 + i < n_pages) flags[row * n_pages + p0 + i] = sel ? 1 : 0;
+    bits |= sel ? (1u << i) : 0u;
+  }
+  if (bitmap) {
+    // the selection as bitmap words (bit b of word w: page 32 w + b); with
+    // 16 pages a thread, word w is the even thread 2 w's bits and its
+    // neighbour's
+    static_assert(KPT == 16 || KPT == 32, "one or two threads per bitmap word");
+    const int64_t words = (n_pages + 31) / 32;
+    int64_t wd = tid;
+    if constexpr (KPT == 16) {
+      const uint32_t hi = __shfl_xor(bits, 1, 64);
+      bits |= hi << 16;
+      wd = tid >> 1;
+    }
+    if ((KPT == 32 || (tid & 1) == 0) && wd < words) bitmap[row * words + wd] = bits;
   }
 }
 
@@ -548,7 +564,7 @@ hipError_t launch_page_meta(const void* k, int64_t kv_st, int64_t kv_sh, int64_t
 hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const void* kmin,
                               const void* kmax, int n_q, int hq, int hkv, int d, int64_t n_pages,
                               int64_t page_cap, int k_pages, fb_dtype dt, const uint8_t* active,
-                              double* bound, int32_t* pages, hipStream_t s) {
+                              double* bound, int32_t* pages, uint32_t* bitmap, hipStream_t s) {
   if (n_pages == 0) return hipSuccess;
   const int G = hq / hkv;
   const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * (d + 1)) * sizeof(float);
@@ -583,19 +599,22 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
 #undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;
-  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, active, pages, nullptr, s);
+  return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, active, pages, nullptr, bitmap, s);
 }
+
+int topk_bitmap_max() { return 256 * 32; }
 
 hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
                             const uint8_t* row_active, int32_t* out, uint8_t* flags,
-                            hipStream_t s) {
+                            uint32_t* bitmap, hipStream_t s) {
   if (k <= 0 || n_rows <= 0) return hipSuccess;
+  if (bitmap && n > topk_bitmap_max()) return hipErrorInvalidValue;
   if (n <= 256 * 16)
     hipLaunchKernelGGL(page_topk_reg_kernel<16>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
-                       k, row_active, out, flags);
+                       k, row_active, out, flags, bitmap);
   else if (n <= 256 * 32)
     hipLaunchKernelGGL(page_topk_reg_kernel<32>, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n,
-                       k, row_active, out, flags);
+                       k, row_active, out, flags, bitmap);
   else
     hipLaunchKernelGGL(page_topk_kernel, dim3(n_rows, hkv), dim3(256), 0, s, keys, hkv, n, k,
                        row_active, out, flags);

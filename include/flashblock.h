@@ -516,12 +516,15 @@ typedef struct {
                               recompute step instead of the previous step      */
   int32_t sparse_reselect; /* SPARSE: 1 = LoSA per step (dense first step, pages
                               re-selected each step, no residual)              */
-  uint32_t* sel_bitmap;    /* SPARSE (FlashBlock residual mode), nullable:
-                              [n_q, Hkv, ceil(page_cap or P / 32)] uint32. The
-                              refresh step writes its selection there as
-                              bitmaps; later steps read them instead of
-                              rebuilding them, and classify the tokens inside
-                              the GATHER pass (two launches a step)           */
+  uint32_t* sel_bitmap;    /* SPARSE, nullable: [n_q, Hkv, ceil(page_cap or P
+                              / 32)] uint32. Residual mode: the refresh step
+                              writes its selection there as bitmaps; later
+                              steps read them instead of rebuilding them, and
+                              classify the tokens inside the GATHER pass (two
+                              launches a step). sparse_reselect: each step's
+                              top-k writes the active tokens' fresh selection
+                              there (P <= 8192) and the GATHER pass takes
+                              their union itself (no selection prep)          */
 } fb_step_state;
 
 typedef struct {

@@ -75,15 +75,20 @@ LOSA_CASES = [
 ]
 
 
+@pytest.mark.parametrize("sel_bitmap", [True, False], ids=["topk_bitmaps", "prep_each_step"])
 @pytest.mark.parametrize("name,n_prefix,density,m_override", LOSA_CASES,
                          ids=[c[0] for c in LOSA_CASES])
-def test_losa_block_matches_oracle(fb, name, n_prefix, density, m_override):
+def test_losa_block_matches_oracle(fb, name, n_prefix, density, m_override, sel_bitmap):
+    # sel_bitmap: each step's top-k writes its selection as bitmaps and the
+    # GATHER workgroups take the union (True), or a selection prep builds
+    # them (False)
     cfg = W.SPARSE.with_(n_prefix=n_prefix, density=density, n_steps=len(m_override))
     steps = W.sparse_steps(cfg, variant=7, m_override=m_override)
     kp, vp = W.prefix_kv(cfg, variant=7)
     shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
     step = fb.Step(fb.FB_STEP_SPARSE, shape, 8, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
-                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, reselect=True)
+                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, reselect=True,
+                   sel_bitmap=sel_bitmap)
     ks = [dict(q=vals(s["q"], "bf16"), k=vals(s["k"], "bf16"), v=vals(s["v"], "bf16"))
           for s in steps]
     recs = OC.losa_block(ks, vals(kp, "bf16"), vals(vp, "bf16"), cfg.scale, cfg.k_pages,
@@ -102,6 +107,14 @@ def test_losa_block_matches_oracle(fb, name, n_prefix, density, m_override):
         assert np.array_equal(cpu(step.active).astype(bool), act), tag
         if s > 0:                                # pages are chosen for active tokens only
             assert np.array_equal(cpu(step.pages)[act], rec["sel"][act]), tag
+        if s > 0 and sel_bitmap:                 # the top-k's bitmaps of the same pages
+            bm = cpu(step.sel_bitmap).view(np.uint32)
+            want = np.zeros_like(bm)
+            for t in np.nonzero(act)[0]:
+                for g in range(8):
+                    for pg in rec["sel"][t][g]:
+                        want[t, g, pg // 32] |= np.uint32(1) << np.uint32(pg % 32)
+            assert np.array_equal(bm[act], want[act]), tag
         check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 2e-3)
         check_l(tag + " L_out", cpu(step.l_out), rec["l_out"], 1e-3)
         check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)
