@@ -81,6 +81,12 @@ CASES = [
     ("f32_r64", 50, 600, 64, 13, "f32"),
     ("select_none", 40, 512, 32, 0, "bf16"),
     ("select_all", 40, 512, 32, 40, "bf16"),
+    # one token (recomputed or not); 65 tokens (a second selection
+    # workgroup holding one token) over a width shorter than one block
+    ("one_token", 1, 256, 32, 1, "bf16"),
+    ("one_token_none", 1, 256, 32, 0, "bf16"),
+    ("t65_d100", 65, 100, 64, 30, "bf16"),
+    ("t65_f32_r96", 65, 100, 96, 64, "f32"),
     # the rank-counting selection at its largest size (128 workgroups), and
     # the radix top-k + scatter just beyond it
     ("select_rank_8192", 8192, 256, 32, 2000, "bf16"),
