@@ -722,7 +722,8 @@ fb_status fb_reuse_decide(const fb_reuse_args* a, hipStream_t stream) {
       if (a->ws_bytes < need || !a->ws) return FB_ERR_WORKSPACE_TOO_SMALL;
       return dev(launch_head_cos(a->a_cached, a->a_probe, a->n_q, a->n_heads, a->head_dim,
                                  a->mask_in, a->gamma, a->sim, a->mask,
-                                 static_cast<double*>(a->ws), head_cos_chunks(a->n_q), stream));
+                                 static_cast<double*>(a->ws), head_cos_chunks(a->n_q), nullptr,
+                                 nullptr, nullptr, stream));
     }
     case FB_REUSE_ACTIVE_MSE: {
       if (a->n_q < 1 || !a->q_prev || !a->q_cur || !a->active) return FB_ERR_INVALID_ARGUMENT;
@@ -1128,12 +1129,11 @@ fb_status fb_step(fb_step_state* st, const fb_step_args* a, hipStream_t stream) 
         rc = fb_prefix_attn(&s, a->q_blk, st->k_prefix, st->v_prefix, used, nullptr, st->a_probe,
                             st->l_probe, nullptr, nullptr, st->ws, st->ws_bytes, stream);
         if (rc != FB_OK) return rc;
+        // the cosine against the cache, and the cache taking the probe's
+        // pair for the heads recomputed, in one pass over both
         rc = dev(launch_head_cos(st->a_out, st->a_probe, n_q, hq, d, used, st->gamma, st->sim,
                                  st->mask_next, static_cast<double*>(st->ws), head_cos_chunks(n_q),
-                                 stream));
-        if (rc != FB_OK) return rc;
-        rc = dev(launch_copy_heads(st->a_probe, st->l_probe, st->a_out, st->l_out, n_q, hq, d, used,
-                                   stream));
+                                 st->a_out, st->l_probe, st->l_out, stream));
         if (rc != FB_OK) return rc;
         uint8_t* tmp = st->mask;
         st->mask = st->mask_next;

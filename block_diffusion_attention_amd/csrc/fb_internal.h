@@ -355,9 +355,12 @@ hipError_t launch_rows(const RowsParams& p, hipStream_t s);
 hipError_t launch_count(const int32_t* ids_prev, const int32_t* ids_cur, int n_q,
                         int tau, int force, int hq, uint8_t* mask, int32_t* m_count,
                         int32_t* ids_store, int store_on_recompute, hipStream_t s);
+// a_copy, l_src, l_copy (nullable): the probe pair is also copied into the
+// cache for the heads mask_in leaves (read before it is overwritten)
 hipError_t launch_head_cos(const float* a_cached, const float* a_probe, int n_q, int hq,
                            int d, const uint8_t* mask_in, double gamma, double* sim,
-                           uint8_t* mask, double* ws, int n_chunks, hipStream_t s);
+                           uint8_t* mask, double* ws, int n_chunks, float* a_copy,
+                           const float* l_src, float* l_copy, hipStream_t s);
 int head_cos_chunks(int n_q);
 hipError_t launch_active_mse(const void* q_prev, const void* q_cur, fb_dtype dt, int n_q,
                              int hq, int d, int pct, double* mse, uint8_t* active,
@@ -367,9 +370,6 @@ bool active_step_fits(int n_q, int hq);
 hipError_t launch_active_step(void* q_prev, const void* q_cur, int64_t q_st, int64_t q_sh,
                               fb_dtype dt, int n_q, int hq, int d, int mode, uint8_t fill, int pct,
                               double* mse, uint8_t* active, hipStream_t s);
-hipError_t launch_copy_heads(const float* a_src, const float* l_src, float* a_dst,
-                             float* l_dst, int n_q, int hq, int d, const uint8_t* mask,
-                             hipStream_t s);
 
 // pages
 // metadata of pages [p_begin, p_end) of the first n_kv tokens; storage holds

@@ -7,12 +7,12 @@
 //              of the last step that recomputed, which are the ones kept.
 //  * head_cos  (same section, per-head selection): cosine of a head's fresh
 //              block-external output against its cached one, float64, fixed
-//              reduction order; reuse iff sim > gamma.
+//              reduction order; reuse iff sim > gamma. The same pass can copy
+//              the fresh pair into the cache for the heads recomputed.
 //  * active_mse (LoSA s2, token classification): per-token mean squared
 //              query change in float64 with the operations in a fixed order
 //              and no fused multiply-add; active iff above the nearest-rank
 //              percentile cutoff.
-//  * copy_heads: the probe replaces the cache for recomputed heads.
 #include "fb_internal.h"
 
 #include <math.h>
@@ -47,25 +47,65 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* prev, const i
 // Partial sums of <a, b>, |a|^2, |b|^2 for head h over a chunk of rows.
 // Every product of two floats is exact in float64; the chunk sum uses a
 // fixed tree, the chunk partials are summed in order by the finaliser.
-__global__ __launch_bounds__(256) void head_cos_partial_kernel(const float* a_cached,
-                                                               const float* a_probe, int n_q,
-                                                               int hq, int d,
-                                                               const uint8_t* mask_in,
-                                                               int rows_per_chunk, double* ws) {
+// Per (chunk of rows, head): float64 dot, |x|^2, |y|^2 of the head's rows
+// lo .. hi, each thread summing its elements in order, then a fixed tree over
+// the threads. vec: 16-byte loads (bases 16-byte aligned, d % 4 == 0), eight
+// per array in flight per thread. a_copy (nullable): the probe is also
+// written there after it was read (the cache takes the fresh output of a head
+// that was recomputed), with l_src -> l_copy for the chunk's rows.
+__global__ __launch_bounds__(256) void head_cos_partial_kernel(
+    const float* a_cached, const float* a_probe, int n_q, int hq, int d, const uint8_t* mask_in,
+    int rows_per_chunk, int vec, double* ws, float* a_copy, const float* l_src, float* l_copy) {
   const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   if (mask_in && mask_in[h]) return;
   const int lo = chunk * rows_per_chunk;
   const int hi = lo + rows_per_chunk < n_q ? lo + rows_per_chunk : n_q;
   double dot = 0.0, nx = 0.0, ny = 0.0;
-  const int64_t n_el = static_cast<int64_t>(hi - lo) * d;
-  for (int64_t e = tid; e < n_el; e += 256) {
-    const int64_t t = lo + e / d, c = e % d;
-    const int64_t idx = (t * hq + h) * d + c;
-    const double x = a_probe[idx], y = a_cached[idx];
-    dot += x * y;
-    nx += x * x;
-    ny += y * y;
+  if (vec) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kU = 8;
+    const int vpr = d / 4;                           // 16-byte groups per row
+    const int n_vec = (hi - lo) * vpr;
+    for (int v0 = 0; v0 < n_vec; v0 += kU * 256) {
+      f32x4 xv[kU], yv[kU];
+      int64_t at[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v = v0 + u * 256 + tid;
+        const int t = lo + (v < n_vec ? v / vpr : 0), g = v < n_vec ? v % vpr : 0;
+        at[u] = (static_cast<int64_t>(t) * hq + h) * d + 4 * g;
+        if (v < n_vec) {
+          xv[u] = *reinterpret_cast<const f32x4*>(a_probe + at[u]);
+          yv[u] = *reinterpret_cast<const f32x4*>(a_cached + at[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (v0 + u * 256 + tid >= n_vec) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double x = xv[u][e], y = yv[u][e];
+          dot += x * y;
+          nx += x * x;
+          ny += y * y;
+        }
+        if (a_copy) *reinterpret_cast<f32x4*>(a_copy + at[u]) = xv[u];
+      }
+    }
+  } else {
+    const int64_t n_el = static_cast<int64_t>(hi - lo) * d;
+    for (int64_t e = tid; e < n_el; e += 256) {
+      const int64_t t = lo + e / d, c = e % d;
+      const int64_t idx = (t * hq + h) * d + c;
+      const double x = a_probe[idx], y = a_cached[idx];
+      dot += x * y;
+      nx += x * x;
+      ny += y * y;
+      if (a_copy) a_copy[idx] = a_probe[idx];
+    }
   }
+  if (l_copy)
+    for (int t = lo + tid; t < hi; t += 256) l_copy[t * hq + h] = l_src[t * hq + h];
   __shared__ double red[3][256];
   red[0][tid] = dot;
   red[1][tid] = nx;
@@ -87,31 +127,62 @@ __global__ __launch_bounds__(256) void head_cos_partial_kernel(const float* a_ca
   }
 }
 
-__global__ void head_cos_final_kernel(int hq, int n_chunks, const uint8_t* mask_in, double gamma,
-                                      const double* ws, double* sim, uint8_t* mask) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= hq) return;
-  if (mask_in && mask_in[h]) {
-    mask[h] = 1;
-    return;
+// One workgroup: every chunk's (dot, |x|^2, |y|^2) is read into LDS at once
+// (one round trip instead of one per chunk), then thread h adds its head's
+// in chunk order. sim = dot / sqrt(|x|^2 |y|^2) (a probe equal to its cache
+// then scores exactly 1: sqrt(dot^2) = dot), clamped to [-1, 1]; both sides
+// zero -> 1, one side zero -> 0.
+constexpr int kCosStage = 4096;                  // staged doubles (chunks x heads x 3)
+
+__global__ __launch_bounds__(256) void head_cos_final_kernel(int hq, int n_chunks,
+                                                             const uint8_t* mask_in, double gamma,
+                                                             const double* ws, double* sim,
+                                                             uint8_t* mask) {
+  __shared__ double st[kCosStage];
+  const int n = n_chunks * hq * 3;
+  const bool staged = n <= kCosStage;
+  if (staged) {
+    for (int i0 = 0; i0 < n; i0 += 8 * 256) {     // eight loads in flight per thread
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + static_cast<int>(threadIdx.x);
+        v[u] = i < n ? ws[i] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + static_cast<int>(threadIdx.x);
+        if (i < n) st[i] = v[u];
+      }
+    }
   }
-  double dot = 0.0, nx = 0.0, ny = 0.0;
-  for (int c = 0; c < n_chunks; ++c) {
-    const double* o = ws + (static_cast<int64_t>(c) * hq + h) * 3;
-    dot += o[0];
-    nx += o[1];
-    ny += o[2];
+  __syncthreads();
+  const double* src = staged ? st : ws;
+  for (int h = threadIdx.x; h < hq; h += 256) {
+    if (mask_in && mask_in[h]) {
+      mask[h] = 1;
+      continue;
+    }
+    double dot = 0.0, nx = 0.0, ny = 0.0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const double* o = src + (static_cast<int64_t>(c) * hq + h) * 3;
+      dot += o[0];
+      nx += o[1];
+      ny += o[2];
+    }
+    double s;
+    if (nx == 0.0 || ny == 0.0) {
+      s = (nx == 0.0 && ny == 0.0) ? 1.0 : 0.0;
+    } else {
+      const double den = nx * ny;
+      // (a product past the double range falls back to the two roots)
+      s = (den > 0.0 && den < __builtin_huge_val()) ? dot / sqrt(den)
+                                                     : dot / (sqrt(nx) * sqrt(ny));
+      s = s > 1.0 ? 1.0 : (s < -1.0 ? -1.0 : s);
+    }
+    sim[h] = s;
+    mask[h] = s > gamma ? 1 : 0;
   }
-  const double ax = sqrt(nx), ay = sqrt(ny);
-  double s;
-  if (ax * ay == 0.0) {
-    s = (ax == 0.0 && ay == 0.0) ? 1.0 : 0.0;
-  } else {
-    s = dot / (ax * ay);
-    s = s > 1.0 ? 1.0 : (s < -1.0 ? -1.0 : s);
-  }
-  sim[h] = s;
-  mask[h] = s > gamma ? 1 : 0;
 }
 
 template <typename T> __device__ __forceinline__ double ldd(const T* p);
@@ -259,21 +330,6 @@ __global__ __launch_bounds__(1024) void active_step_kernel(T* q_prev, const T* q
   }
 }
 
-__global__ __launch_bounds__(256) void copy_heads_kernel(const float* a_src, const float* l_src,
-                                                         float* a_dst, float* l_dst, int n_q,
-                                                         int hq, int d, const uint8_t* mask) {
-  const int h = blockIdx.y;
-  if (mask && mask[h]) return;
-  const int64_t n_el = static_cast<int64_t>(n_q) * d;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n_el;
-       e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t t = e / d, c = e % d;
-    const int64_t idx = (t * hq + h) * d + c;
-    a_dst[idx] = a_src[idx];
-    if (c == 0) l_dst[t * hq + h] = l_src[t * hq + h];
-  }
-}
-
 __global__ __launch_bounds__(256) void fill_u8_kernel(uint8_t* p, int n, uint8_t v) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
@@ -328,14 +384,18 @@ int head_cos_chunks(int n_q) {
 
 hipError_t launch_head_cos(const float* a_cached, const float* a_probe, int n_q, int hq, int d,
                            const uint8_t* mask_in, double gamma, double* sim, uint8_t* mask,
-                           double* ws, int n_chunks, hipStream_t s) {
+                           double* ws, int n_chunks, float* a_copy, const float* l_src,
+                           float* l_copy, hipStream_t s) {
   const int rows_per_chunk = 64;
+  const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const int vec = (d % 4 == 0 && al16(a_cached) && al16(a_probe) && (!a_copy || al16(a_copy)))
+                      ? 1 : 0;
   hipLaunchKernelGGL(head_cos_partial_kernel, dim3(n_chunks, hq), dim3(256), 0, s, a_cached,
-                     a_probe, n_q, hq, d, mask_in, rows_per_chunk, ws);
+                     a_probe, n_q, hq, d, mask_in, rows_per_chunk, vec, ws, a_copy, l_src, l_copy);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(head_cos_final_kernel, dim3((hq + 63) / 64), dim3(64), 0, s, hq, n_chunks,
-                     mask_in, gamma, ws, sim, mask);
+  hipLaunchKernelGGL(head_cos_final_kernel, dim3(1), dim3(256), 0, s, hq, n_chunks, mask_in, gamma,
+                     ws, sim, mask);
   return hipGetLastError();
 }
 
@@ -375,14 +435,5 @@ hipError_t launch_active_step(void* q_prev, const void* q_cur, int64_t q_st, int
   return hipGetLastError();
 }
 
-hipError_t launch_copy_heads(const float* a_src, const float* l_src, float* a_dst, float* l_dst,
-                             int n_q, int hq, int d, const uint8_t* mask, hipStream_t s) {
-  const int64_t n_el = static_cast<int64_t>(n_q) * d;
-  int nb = static_cast<int>((n_el + 255) / 256);
-  if (nb > 1024) nb = 1024;
-  hipLaunchKernelGGL(copy_heads_kernel, dim3(nb, hq), dim3(256), 0, s, a_src, l_src, a_dst, l_dst,
-                     n_q, hq, d, mask);
-  return hipGetLastError();
-}
 
 }  // namespace fb
