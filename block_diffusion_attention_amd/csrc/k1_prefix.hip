@@ -984,6 +984,87 @@ __global__ __launch_bounds__(128) void prefix_reduce_lean_kernel(ReduceParams p)
   }
 }
 
+// Many-row variant with up to 64 chunks: one wave per row (lane c holds
+// chunk c's log-normaliser and weight, lane l dims l, l + 64), 4 waves a
+// workgroup, kWaveRows rows a wave. The weights are read back lane by lane in
+// chunk order, so every sum has the operations and the order of the
+// 128-thread form (the same bits) without its barriers; a workgroup per row
+// made the 56,160-row video reduce a dispatch-bound launch.
+constexpr int kWaveRows = 2;
+constexpr int kWaveMaxChunks = 64;
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__global__ __launch_bounds__(256) void prefix_reduce_wave_kernel(ReduceParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kWaveRows;
+  const int nc = p.dyn.on ? rows_dyn_split(groups_on(p.mask, p.dyn.hkv, p.dyn.group), p.dyn).chunks
+                          : p.n_chunks;
+  const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
+  const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
+  const int64_t cs = p.rows * p.d;                 // chunk stride
+  for (int r = 0; r < kWaveRows; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= p.rows) return;                     // (uniform in the wave)
+    const int h = static_cast<int>(row % p.hq);
+    const int t = static_cast<int>(row / p.hq);
+    if (p.q_src) {                                 // the row's query copy
+      const int words = p.d * p.q_esize / 4;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          static_cast<const char*>(p.q_src) + (t * p.q_st + h * p.q_sh) * p.q_esize);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<char*>(p.q_dst) + row * p.d * p.q_esize);
+      for (int i = lane; i < words; i += 64) dst[i] = src[i];
+    }
+    if (p.mask && p.mask[h]) continue;
+    if (p.active && !p.active[t]) continue;
+    const float L = lane < nc ? p.part_l[lane * p.rows + row] : kNegInf;
+    const float Lr = lane < nr ? p.part_rl[lane * p.rows + row] : kNegInf;
+    const float Lc = cached ? p.res_l[row] : kNegInf;
+    float mr = Lr;
+    if (cached && lane == 0) mr = fmaxf(mr, Lc);
+    const float M = wave_max(L);
+    const float Mr = wave_max(mr);
+    const float Mall = fmaxf(M, Mr);
+    const float wa = lane < nc ? (L == kNegInf ? 0.f : expf(L - Mall)) : 0.f;
+    const float wr = lane < nr ? (Lr == kNegInf ? 0.f : expf(Lr - Mr)) : 0.f;
+    const float wc = cached ? (Lc == kNegInf ? 0.f : expf(Lc - Mr)) : 0.f;
+    float S = 0.f, Sr = 0.f;                       // chunk order, as in every thread there
+    for (int ch = 0; ch < nc; ++ch) S += lane_f(wa, ch);
+    for (int ch = 0; ch < nr; ++ch) Sr += lane_f(wr, ch);
+    if (cached) Sr += wc;
+    for (int c = lane; c < p.d; c += 64) {
+      float acc = 0.f, accr = 0.f;
+      const float* pa = p.part_a + row * p.d + c;
+      int ch = 0;
+      for (; ch + 8 <= nc; ch += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pa[(ch + u) * cs];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += lane_f(wa, ch + u) * v[u];
+      }
+      for (; ch < nc; ++ch) acc += lane_f(wa, ch) * pa[ch * cs];
+      if (nr) {
+        const float* pr = p.part_ra + row * p.d + c;
+        for (ch = 0; ch < nr; ++ch) accr += lane_f(wr, ch) * pr[ch * cs];
+      }
+      if (cached) accr += wc * p.res_a[row * p.d + c];
+      if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
+      // fold the residual pair into the full pair (same composition)
+      const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+      const float Stot = S + Sr * wrr;
+      p.a_out[row * p.d + c] = Mall != kNegInf ? (acc + accr * wrr) / Stot : 0.f;
+    }
+    if (lane == 0) {
+      if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+      const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+      p.l_out[row] = Mall != kNegInf ? Mall + logf(S + Sr * wrr) : kNegInf;
+    }
+  }
+}
+
 __global__ __launch_bounds__(128) void prefix_empty_kernel(float* a, float* l, int hq, int d,
                                                            const uint8_t* mask) {
   const int64_t row = blockIdx.x;
@@ -1028,7 +1109,11 @@ hipError_t launch_prefix_mfma(const PrefixParams& p, int row_blocks, hipStream_t
 }
 
 hipError_t launch_prefix_reduce(const ReduceParams& p, hipStream_t s) {
-  if (p.rows >= kReduceLeanRows)
+  if (p.rows >= kReduceLeanRows && p.n_chunks <= kWaveMaxChunks && p.d <= 128)
+    hipLaunchKernelGGL(prefix_reduce_wave_kernel,
+                       dim3(static_cast<unsigned>((p.rows + 4 * kWaveRows - 1) / (4 * kWaveRows))),
+                       dim3(256), 0, s, p);
+  else if (p.rows >= kReduceLeanRows)
     hipLaunchKernelGGL(prefix_reduce_lean_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(128), 0,
                        s, p);
   else
