@@ -992,6 +992,7 @@ __global__ __launch_bounds__(128) void prefix_reduce_lean_kernel(ReduceParams p)
 // made the 56,160-row video reduce a dispatch-bound launch.
 constexpr int kWaveRows = 2;
 constexpr int kWaveMaxChunks = 64;
+constexpr int kWavePreChunks = 8;                // chunks whose partials are loaded up front
 
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -1005,6 +1006,70 @@ __global__ __launch_bounds__(256) void prefix_reduce_wave_kernel(ReduceParams p)
   const int nr = p.part_rl ? nc : 0;               // residual partials (SPLIT)
   const bool cached = p.res_l != nullptr;          // cached residual (GATHER)
   const int64_t cs = p.rows * p.d;                 // chunk stride
+  if (nc <= kWavePreChunks && nr == 0 && p.d <= 128 && !p.q_src) {
+    // the usual masked pass (a few chunks): every load of the wave's rows is
+    // issued first (nothing for rows past the end or rows the mask or the
+    // active flags leave), then each row is formed as below
+    float Lv[kWaveRows], Lcv[kWaveRows], rav[kWaveRows][2], av[kWaveRows][kWavePreChunks][2];
+    bool on[kWaveRows];
+#pragma unroll
+    for (int r = 0; r < kWaveRows; ++r) {
+      const int64_t row = row0 + r;
+      on[r] = row < p.rows && !(p.mask && p.mask[row % p.hq]) &&
+              !(p.active && !p.active[row / p.hq]);
+    }
+#pragma unroll
+    for (int r = 0; r < kWaveRows; ++r) {
+      const int64_t row = row0 + r;
+      if (!on[r]) continue;                        // (uniform in the wave)
+      Lv[r] = lane < nc ? p.part_l[lane * p.rows + row] : kNegInf;
+      Lcv[r] = cached ? p.res_l[row] : kNegInf;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = lane + 64 * j < p.d ? lane + 64 * j : 0;
+        rav[r][j] = cached ? p.res_a[row * p.d + c] : 0.f;
+#pragma unroll
+        for (int ch = 0; ch < kWavePreChunks; ++ch)
+          av[r][ch][j] = ch < nc ? p.part_a[row * p.d + c + ch * cs] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kWaveRows; ++r) {
+      const int64_t row = row0 + r;
+      if (!on[r]) continue;                        // (uniform in the wave)
+      const float L = Lv[r], Lc = Lcv[r];
+      float mr = kNegInf;
+      if (cached && lane == 0) mr = fmaxf(mr, Lc);
+      const float M = wave_max(L);
+      const float Mr = wave_max(mr);
+      const float Mall = fmaxf(M, Mr);
+      const float wa = lane < nc ? (L == kNegInf ? 0.f : expf(L - Mall)) : 0.f;
+      const float wc = cached ? (Lc == kNegInf ? 0.f : expf(Lc - Mr)) : 0.f;
+      float S = 0.f, Sr = 0.f;
+      for (int ch = 0; ch < nc; ++ch) S += lane_f(wa, ch);
+      if (cached) Sr += wc;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = lane + 64 * j;
+        if (c >= p.d) continue;
+        float acc = 0.f, accr = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < kWavePreChunks; ++ch)
+          if (ch < nc) acc += lane_f(wa, ch) * av[r][ch][j];
+        if (cached) accr += wc * rav[r][j];
+        if (p.a_res) p.a_res[row * p.d + c] = Mr != kNegInf ? accr / Sr : 0.f;
+        const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+        const float Stot = S + Sr * wrr;
+        p.a_out[row * p.d + c] = Mall != kNegInf ? (acc + accr * wrr) / Stot : 0.f;
+      }
+      if (lane == 0) {
+        if (p.a_res) p.l_res[row] = Mr != kNegInf ? Mr + logf(Sr) : kNegInf;
+        const float wrr = Mr != kNegInf ? expf(Mr - Mall) : 0.f;
+        p.l_out[row] = Mall != kNegInf ? Mall + logf(S + Sr * wrr) : kNegInf;
+      }
+    }
+    return;
+  }
   for (int r = 0; r < kWaveRows; ++r) {
     const int64_t row = row0 + r;
     if (row >= p.rows) return;                     // (uniform in the wave)
