@@ -847,7 +847,10 @@ hipError_t launch_sel_bitmap(const int32_t* pages, int n_rows, int k_pages, int 
   return hipGetLastError();
 }
 
-bool gather_union_fits(int n_q, int words) { return words >= 1 && words <= kUnionWords && n_q >= 1; }
+// the workgroup keeps the union words and every token's active flag in LDS
+bool gather_union_fits(int n_q, int words) {
+  return words >= 1 && words <= kUnionWords && n_q >= 1 && n_q <= kClassifyTokens;
+}
 
 bool gather_classify_fits(int n_q, int hq) {
   // the float64 sums of the classification (four per token and head, then

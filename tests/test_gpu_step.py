@@ -151,3 +151,34 @@ def test_sparse_block_matches_oracle(fb, density, sel_bitmap):
         check_a("sparse step %d A_out" % s, cpu(step.a_out), rec["a_out"], 2e-3)
         check_a("sparse step %d A_full" % s, cpu(a), rec["a_full"], 2e-3)
         check_l("sparse step %d L_full" % s, cpu(l), rec["l_full"], 1e-3)
+
+
+@pytest.mark.parametrize("sel_bitmap", [True, False], ids=["bitmaps_kept", "prep_each_step"])
+def test_sparse_block_more_than_64_tokens(fb, sel_bitmap):
+    """72 block tokens: more than a GATHER workgroup takes the union of (and
+    classifies) itself, so the union of the kept bitmaps and the active set
+    come from launches of their own."""
+    B = 72
+    cfg = W.SPARSE.with_(n_prefix=2048, n_block=B, n_steps=3)
+    steps = W.sparse_steps(cfg, m_override=[None, 30, 4])
+    kp, vp = W.prefix_kv(cfg)
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    step = fb.Step(fb.FB_STEP_SPARSE, shape, B, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
+                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, sel_bitmap=sel_bitmap)
+    ks = [dict(q=vals(s["q"], "bf16"), k=vals(s["k"], "bf16"), v=vals(s["v"], "bf16"))
+          for s in steps]
+    recs = OC.sparse_block(ks, vals(kp, "bf16"), vals(vp, "bf16"), cfg.scale, cfg.k_pages, cfg.page)
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        a = torch.empty(B, 32, 128, device="cuda")
+        l = torch.empty(B, 32, device="cuda")
+        step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                  dev_tensor(st["v"], "bf16"), a, l)
+        torch.cuda.synchronize()
+        assert np.array_equal(cpu(step.pages), rec["sel"]), s
+        if s > 0:
+            assert mse_margin_ok(rec["mse"]), s
+            check_mse("B72 step %d" % s, cpu(step.mse), rec["mse"])
+        assert np.array_equal(cpu(step.active).astype(bool), rec["active"]), s
+        check_a("B72 step %d A_out" % s, cpu(step.a_out), rec["a_out"], 2e-3)
+        check_a("B72 step %d A_full" % s, cpu(a), rec["a_full"], 2e-3)
+        check_l("B72 step %d L_full" % s, cpu(l), rec["l_full"], 1e-3)
