@@ -59,6 +59,26 @@ def test_text_block_matches_oracle(fb, name, cfg, m_override):
         check_l("%s step %d L_full" % (name, s), l, rec["l_full"], ltol)
 
 
+@pytest.mark.parametrize("B", [24, 40, 128])
+def test_text_larger_blocks(fb, B):
+    """Blocks past 64 rows per KV head: two row slabs of the decode kernel
+    (24 tokens), the many-rows kernel for both passes under the device-set
+    head mask (40), and 4,096 rows whose split-K partials go through the
+    many-row reduce (128); reuse and recompute steps alternate."""
+    cfg = W.LONG.with_(n_prefix=6000, n_block=B, n_steps=6)
+    got, recs = run_text(fb, cfg, m_override=[None, 0, B // 2, 1, B, 3])
+    assert [r["decision"] for r in recs[1:]] == [OC.REUSE, OC.RECOMPUTE, OC.REUSE,
+                                                 OC.RECOMPUTE, OC.REUSE]
+    for s, (rec, (a, l, mc, mask, a_out, l_out)) in enumerate(zip(recs, got)):
+        if s > 0:
+            assert mc == rec["m_count"], (s, mc, rec["m_count"])
+        assert np.all(mask == (1 if rec["decision"] == OC.REUSE else 0)), (s, rec["decision"])
+        check_a("B%d step %d A_out" % (B, s), a_out, rec["a_out"], 2e-3)
+        check_l("B%d step %d L_out" % (B, s), l_out, rec["l_out"], 1e-3)
+        check_a("B%d step %d A_full" % (B, s), a, rec["a_full"], 2e-3)
+        check_l("B%d step %d L_full" % (B, s), l, rec["l_full"], 1e-3)
+
+
 def test_text_forced_reuse_and_recompute(fb):
     cfg = W.TEXT.with_(n_prefix=5000, n_steps=5)
     force = [None, OC.REUSE, OC.RECOMPUTE, OC.REUSE, OC.REUSE]
