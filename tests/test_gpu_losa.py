@@ -175,3 +175,40 @@ def test_selection_of_active_tokens_only(fb):
     assert np.array_equal(got_b[act], rb[act])
     assert np.array_equal(got_p[act], OQ.topk_pages(rb, k)[act])
     assert (got_b[~act] == 5.0).all() and (got_p[~act] == -7).all()
+
+
+@pytest.mark.parametrize("sel_bitmap", [True, False], ids=["bitmap_buffer", "no_bitmap_buffer"])
+def test_losa_block_more_than_64_tokens(fb, sel_bitmap):
+    """72 block tokens: more than a GATHER workgroup takes the union of, so
+    the top-k writes page lists only and a selection prep builds the union,
+    with or without a bitmap buffer in the step."""
+    B = 72
+    cfg = W.SPARSE.with_(n_prefix=2048, density=0.3, n_block=B, n_steps=3)
+    steps = W.sparse_steps(cfg, variant=7, m_override=[None, 30, 4])
+    kp, vp = W.prefix_kv(cfg, variant=7)
+    shape = fb.shape_of(32, 8, 128, cfg.scale, torch.bfloat16)
+    step = fb.Step(fb.FB_STEP_SPARSE, shape, B, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
+                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, reselect=True,
+                   sel_bitmap=sel_bitmap)
+    ks = [dict(q=vals(s["q"], "bf16"), k=vals(s["k"], "bf16"), v=vals(s["v"], "bf16"))
+          for s in steps]
+    recs = OC.losa_block(ks, vals(kp, "bf16"), vals(vp, "bf16"), cfg.scale, cfg.k_pages,
+                         cfg.page, cfg.pct)
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        a = torch.empty(B, 32, 128, device="cuda")
+        l = torch.empty(B, 32, device="cuda")
+        step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                  dev_tensor(st["v"], "bf16"), a, l)
+        torch.cuda.synchronize()
+        tag = "B72 step %d" % s
+        act = rec["active"]
+        if s > 0:
+            assert mse_margin_ok(rec["mse"]), tag
+            check_mse(tag, cpu(step.mse), rec["mse"])
+        assert np.array_equal(cpu(step.active).astype(bool), act), tag
+        if s > 0:
+            assert np.array_equal(cpu(step.pages)[act], rec["sel"][act]), tag
+        check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 2e-3)
+        check_l(tag + " L_out", cpu(step.l_out), rec["l_out"], 1e-3)
+        check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)
+        check_l(tag + " L_full", cpu(l), rec["l_full"], 1e-3)
