@@ -789,6 +789,7 @@ static fb_status page_select_impl(const fb_attn_shape* shape, fb_tensor q, const
   fb_status st = check_shape(shape);
   if (st != FB_OK) return st;
   if (q.n_tok < 1 || q.n_tok > INT32_MAX / shape->n_q_heads) return FB_ERR_INVALID_ARGUMENT;
+  if (q.n_tok > 65535) return FB_ERR_UNSUPPORTED;   // token tiles of the bound grid (<= 65,535)
   if ((st = check_tensor(q, -1, shape->n_q_heads, shape->head_dim)) != FB_OK) return st;
   if (n_pages < 0 || n_pages > INT32_MAX || k_pages < 0 || k_pages > n_pages)
     return FB_ERR_INVALID_ARGUMENT;
@@ -798,11 +799,11 @@ static fb_status page_select_impl(const fb_attn_shape* shape, fb_tensor q, const
   if (page_cap == 0) page_cap = n_pages;
   if (page_cap < n_pages) return FB_ERR_INVALID_ARGUMENT;
   const int G = shape->n_q_heads / shape->n_kv_heads;
-  // LDS of the generic bound kernel (group sizes other than 1, 2, 4, 8)
+  // the generic bound kernel (group sizes other than 1, 2, 4, 8) needs one
+  // token's query rows and a page block's rows in 64 KB of LDS
   const bool g_kernel = G == 1 || G == 2 || G == 4 || G == 8;
-  const size_t smem = (static_cast<size_t>(q.n_tok) * G * shape->head_dim + 2 * 32 * (shape->head_dim + 1)) *
-                      sizeof(float);
-  if (!g_kernel && smem > 64 * 1024) return FB_ERR_UNSUPPORTED;
+  if (!g_kernel && page_bound_tokens(static_cast<int>(q.n_tok), G, shape->head_dim) < 1)
+    return FB_ERR_UNSUPPORTED;
   if (!bound) {
     const size_t need = fb_page_select_workspace(shape, q.n_tok, n_pages);
     if (ws_bytes < need || (need > 0 && !ws)) return FB_ERR_WORKSPACE_TOO_SMALL;

@@ -390,6 +390,7 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
 // bitmap (nullable, [rows][ceil(n / 32)], n <= topk_bitmap_max()): the
 // chosen indices as bits (rows skipped by row_active are not written)
 int topk_bitmap_max();
+int page_bound_tokens(int n_q, int G, int d);   // tokens per workgroup of the generic bound kernel
 hipError_t launch_topk_rows(const double* keys, int n_rows, int hkv, int64_t n, int k,
                             const uint8_t* row_active, int32_t* out, uint8_t* flags,
                             uint32_t* bitmap, hipStream_t s);

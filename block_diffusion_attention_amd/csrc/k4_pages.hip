@@ -88,31 +88,34 @@ __global__ __launch_bounds__(256) void page_meta_kernel(const T* k, int64_t kv_s
   *reinterpret_cast<u32x4v*>(kmax + o) = b;
 }
 
-// bound[t][g][p]: one thread per (page, token). The group's query rows and the
-// page block's metadata sit in LDS as float (exact copies of the inputs).
+// bound[t][g][p]: one thread per (page, token). The query rows of the
+// workgroup's tokens (tc of them, from blockIdx.z * tc) and the page block's
+// metadata sit in LDS as float (exact copies of the inputs).
 constexpr int kPagesPerBlock = 32;
 
 template <typename T>
 __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_st, int64_t q_sh,
                                                          const T* kmin, const T* kmax, int n_q,
-                                                         int hq, int hkv, int d, int64_t n_pages,
-                                                         int64_t page_cap, const uint8_t* active,
-                                                         double* bound) {
+                                                         int tc, int hq, int hkv, int d,
+                                                         int64_t n_pages, int64_t page_cap,
+                                                         const uint8_t* active, double* bound) {
 #pragma clang fp contract(off)
   extern __shared__ float sm[];
   const int G = hq / hkv;
   const int g = blockIdx.y;
+  const int t0 = blockIdx.z * tc;
+  const int nt = n_q - t0 < tc ? n_q - t0 : tc;
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPagesPerBlock;
   const int np = n_pages - p0 < kPagesPerBlock ? static_cast<int>(n_pages - p0) : kPagesPerBlock;
   // page rows padded to d + 1 floats: the 32 pages a wave reads at once fall
   // in distinct LDS banks
   const int ds = d + 1;
-  float* qs = sm;                                    // [n_q][G][d]
-  float* mn = qs + n_q * G * d;                      // [kPagesPerBlock][d + 1]
+  float* qs = sm;                                    // [tc][G][d]
+  float* mn = qs + tc * G * d;                       // [kPagesPerBlock][d + 1]
   float* mx = mn + kPagesPerBlock * ds;
-  for (int e = threadIdx.x; e < n_q * G * d; e += blockDim.x) {
+  for (int e = threadIdx.x; e < nt * G * d; e += blockDim.x) {
     const int t = e / (G * d), j = (e / d) % G, c = e % d;
-    qs[e] = ldf<T>(q + t * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
+    qs[e] = ldf<T>(q + static_cast<int64_t>(t0 + t) * q_st + static_cast<int64_t>(g * G + j) * q_sh + c);
   }
   for (int e = threadIdx.x; e < np * d; e += blockDim.x) {
     const int64_t o = (static_cast<int64_t>(g) * page_cap + p0) * d + e;
@@ -121,12 +124,12 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const T* q, int64_t q_s
     mx[ls] = ldf<T>(kmax + o);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < np * n_q; e += blockDim.x) {
-    const int pi = e % np, t = e / np;
+  for (int e = threadIdx.x; e < np * nt; e += blockDim.x) {
+    const int pi = e % np, tl = e / np, t = t0 + tl;
     if (active && !active[t]) continue;
     double best = -__builtin_huge_val();
     for (int j = 0; j < G; ++j) {
-      const float* qr = qs + (t * G + j) * d;
+      const float* qr = qs + (tl * G + j) * d;
       double acc = 0.0;
       for (int c = 0; c < d; ++c) {
         const double qv = qr[c];
@@ -567,7 +570,6 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
                               double* bound, int32_t* pages, uint32_t* bitmap, hipStream_t s) {
   if (n_pages == 0) return hipSuccess;
   const int G = hq / hkv;
-  const size_t smem = (static_cast<size_t>(n_q) * G * d + 2 * kPagesPerBlock * (d + 1)) * sizeof(float);
   dim3 grid(static_cast<unsigned>((n_pages + kPagesPerBlock - 1) / kPagesPerBlock), hkv);
   // G-chain kernel: 32 pages x TC tokens per workgroup, TC = 8 (G <= 4) or 4 (G = 8)
 #define FB_BOUND_G(TT, GG)                                                                      \
@@ -586,20 +588,36 @@ hipError_t launch_page_select(const void* q, int64_t q_st, int64_t q_sh, const v
   else if (dt == FB_F32 && G == 2) FB_BOUND_G(float, 2);
   else if (dt == FB_F32 && G == 4) FB_BOUND_G(float, 4);
   else if (dt == FB_F32 && G == 8) FB_BOUND_G(float, 8);
-  else if (dt == FB_BF16)
-    hipLaunchKernelGGL(page_bound_kernel<uint16_t>, grid, dim3(256), smem, s,
-                       static_cast<const uint16_t*>(q), q_st, q_sh,
-                       static_cast<const uint16_t*>(kmin), static_cast<const uint16_t*>(kmax), n_q,
-                       hq, hkv, d, n_pages, page_cap, active, bound);
-  else
-    hipLaunchKernelGGL(page_bound_kernel<float>, grid, dim3(256), smem, s,
-                       static_cast<const float*>(q), q_st, q_sh, static_cast<const float*>(kmin),
-                       static_cast<const float*>(kmax), n_q, hq, hkv, d, n_pages, page_cap, active,
-                       bound);
+  else {
+    const int tc = page_bound_tokens(n_q, G, d);
+    if (tc < 1) return hipErrorInvalidValue;
+    const size_t smem = (static_cast<size_t>(tc) * G * d + 2 * kPagesPerBlock * (d + 1)) * sizeof(float);
+    const dim3 gz(grid.x, grid.y, static_cast<unsigned>((n_q + tc - 1) / tc));
+    if (dt == FB_BF16)
+      hipLaunchKernelGGL(page_bound_kernel<uint16_t>, gz, dim3(256), smem, s,
+                         static_cast<const uint16_t*>(q), q_st, q_sh,
+                         static_cast<const uint16_t*>(kmin), static_cast<const uint16_t*>(kmax),
+                         n_q, tc, hq, hkv, d, n_pages, page_cap, active, bound);
+    else
+      hipLaunchKernelGGL(page_bound_kernel<float>, gz, dim3(256), smem, s,
+                         static_cast<const float*>(q), q_st, q_sh, static_cast<const float*>(kmin),
+                         static_cast<const float*>(kmax), n_q, tc, hq, hkv, d, n_pages, page_cap,
+                         active, bound);
+  }
 #undef FB_BOUND_G
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k_pages <= 0) return e;
   return launch_topk_rows(bound, n_q, hkv, n_pages, k_pages, active, pages, nullptr, bitmap, s);
+}
+
+// Tokens per workgroup of the generic bound kernel: as many as keep their
+// query rows and the page block's rows within 64 KB of LDS (0: not even one).
+int page_bound_tokens(int n_q, int G, int d) {
+  const int64_t room = 64 * 1024 / static_cast<int64_t>(sizeof(float)) - 2 * kPagesPerBlock * (d + 1);
+  const int64_t per = static_cast<int64_t>(G) * d;
+  int64_t tc = room > 0 ? room / per : 0;
+  if (tc > n_q) tc = n_q;
+  return static_cast<int>(tc);
 }
 
 int topk_bitmap_max() { return 256 * 32; }

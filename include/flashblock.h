@@ -287,6 +287,9 @@ fb_status fb_reuse_decide(const fb_reuse_args* args, hipStream_t stream);
  *   active (nullable, device [n_q]): tokens whose byte is 0 are skipped;    *
  *   their rows of bound and pages are left untouched.                       *
  *   bound may be NULL (then it lives in ws).                                  *
+ *   UNSUPPORTED for more than 65,535 block tokens, or when one token's      *
+ *   G * d query values and 64 page rows of d + 1 floats exceed 64 KB (group *
+ *   sizes other than 1, 2, 4, 8: e.g. G > 63 at d = 128).                   *
  * ------------------------------------------------------------------------ */
 fb_status fb_page_meta(const fb_attn_shape* shape, fb_tensor k,
                        int32_t page_size, void* kmin, void* kmax,

@@ -208,3 +208,33 @@ def test_page_select_ties_take_lower_ids(fb, n_take):
     fb.fb_page_select(shape, dev_tensor(q, "bf16"), kmin, kmax, n_pages, k, pages, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(cpu(pages), ref)
+
+
+@pytest.mark.parametrize("hq,hkv,dt,d", [(16, 8, "bf16", 128), (64, 8, "bf16", 128),
+                                         (32, 2, "bf16", 128), (32, 8, "f32", 64),
+                                         (24, 3, "f32", 128)],
+                         ids=["G2", "G8", "G16_generic", "f32_G4_d64", "f32_G8_three_groups"])
+def test_page_select_group_sizes(fb, hq, hkv, dt, d):
+    """The bound kernel is built per group size (1, 2, 4, 8 query heads per KV
+    head, bf16 and float32) with a generic form for the rest: every form gives
+    the oracle's bounds and pages bit for bit."""
+    n_kv, page, k = 5000, 16, 60
+    cfg = W.SPARSE.with_(n_prefix=n_kv, page=page, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                         dtype=dt)
+    kp, _ = W.prefix_kv(cfg)
+    q = W.sparse_steps(cfg.with_(n_steps=1))[0]["q"]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    shape = fb.shape_of(hq, hkv, d, cfg.scale, tdt)
+    n_pages = (n_kv + page - 1) // page
+    kmin = torch.empty(hkv, n_pages, d, dtype=tdt, device="cuda")
+    kmax = torch.empty_like(kmin)
+    fb.fb_page_meta(shape, dev_tensor(kp, dt), page, kmin, kmax)
+    bound = torch.empty(8, hkv, n_pages, dtype=torch.float64, device="cuda")
+    pages = torch.full((8, hkv, k), -1, dtype=torch.int32, device="cuda")
+    fb.fb_page_select(shape, dev_tensor(q, dt), kmin, kmax, n_pages, k, pages, bound=bound)
+    torch.cuda.synchronize()
+    rmin, rmax = OQ.page_meta(vals(kp, dt), page)
+    assert np.array_equal(cpu(kmin.float()), rmin) and np.array_equal(cpu(kmax.float()), rmax)
+    rb = OQ.page_bound(vals(q, dt), rmin, rmax)
+    assert np.array_equal(cpu(bound), rb)
+    assert np.array_equal(cpu(pages), OQ.topk_pages(rb, k))
