@@ -44,6 +44,28 @@ def test_prefix_matches_oracle(fb, name, cfg, n_q, n_kv, layout):
     check_l(name + " L_out", l, rl, ltol)
 
 
+HEAD_SHAPES = [
+    # name, query heads, KV heads, block tokens, layout
+    ("q64_kv8_b16", 64, 8, 16, "tok"),       # 128 rows per KV head: the many-rows kernel
+    ("q64_kv8_b6", 64, 8, 6, "head"),        # 48 rows: the pair kernel
+    ("q28_kv4_b16", 28, 4, 16, "tok"),       # 7 query heads per KV head, two row slabs
+    ("q28_kv4_b3_head", 28, 4, 3, "head"),
+    ("q32_kv1_b16", 32, 1, 16, "tok"),       # one KV head: 512 rows, many-rows kernel
+    ("q32_kv1_b2", 32, 1, 2, "head"),
+    ("q40_kv5_b8", 40, 5, 8, "tok"),         # KV heads not a multiple of the 8 XCDs
+    ("q16_kv2_b4_head", 16, 2, 4, "head"),
+    ("q8_kv8_b30", 8, 8, 30, "tok"),         # one query head per KV head, 30 rows
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,n_q,layout", HEAD_SHAPES, ids=[c[0] for c in HEAD_SHAPES])
+def test_prefix_head_shapes(fb, name, hq, hkv, n_q, layout):
+    cfg = W.LONG.with_(n_q_heads=hq, n_kv_heads=hkv)
+    a, l, ra, rl, cfg = run_prefix(fb, cfg, n_q, 10007, layout)
+    check_a(name + " A_out", a, ra, 2e-3)
+    check_l(name + " L_out", l, rl, 1e-3)
+
+
 @pytest.mark.parametrize("gain", [4.0, 8.0])
 def test_prefix_peaked_scores(fb, gain):
     # Q scaled up: O(1) outputs dominated by few keys, exercising the running
