@@ -79,6 +79,20 @@ def test_text_larger_blocks(fb, B):
         check_l("B%d step %d L_full" % (B, s), l, rec["l_full"], 1e-3)
 
 
+@pytest.mark.parametrize("hq,hkv,B", [(28, 4, 8), (64, 8, 16), (32, 1, 4)],
+                         ids=["q28_kv4_b8", "q64_kv8_b16", "q32_kv1_b4"])
+def test_text_block_head_shapes(fb, hq, hkv, B):
+    cfg = W.LONG.with_(n_prefix=7000, n_block=B, n_steps=5, n_q_heads=hq, n_kv_heads=hkv)
+    got, recs = run_text(fb, cfg, m_override=[None, 1, B, 0, min(B, 5)])
+    for s, (rec, (a, l, mc, mask, a_out, l_out)) in enumerate(zip(recs, got)):
+        if s > 0:
+            assert mc == rec["m_count"], (s, mc, rec["m_count"])
+        assert np.all(mask == (1 if rec["decision"] == OC.REUSE else 0)), (s, rec["decision"])
+        check_a("q%d/kv%d step %d A_out" % (hq, hkv, s), a_out, rec["a_out"], 2e-3)
+        check_a("q%d/kv%d step %d A_full" % (hq, hkv, s), a, rec["a_full"], 2e-3)
+        check_l("q%d/kv%d step %d L_full" % (hq, hkv, s), l, rec["l_full"], 1e-3)
+
+
 def test_text_forced_reuse_and_recompute(fb):
     cfg = W.TEXT.with_(n_prefix=5000, n_steps=5)
     force = [None, OC.REUSE, OC.RECOMPUTE, OC.REUSE, OC.REUSE]
@@ -202,3 +216,34 @@ def test_sparse_block_more_than_64_tokens(fb, sel_bitmap):
         check_a("B72 step %d A_out" % s, cpu(step.a_out), rec["a_out"], 2e-3)
         check_a("B72 step %d A_full" % s, cpu(a), rec["a_full"], 2e-3)
         check_l("B72 step %d L_full" % s, cpu(l), rec["l_full"], 1e-3)
+
+
+@pytest.mark.parametrize("hq,hkv", [(28, 4), (64, 8)], ids=["q28_kv4", "q64_kv8"])
+@pytest.mark.parametrize("sel_bitmap", [True, False], ids=["bitmaps_kept", "prep_each_step"])
+def test_sparse_block_head_shapes(fb, hq, hkv, sel_bitmap):
+    """7 query heads per KV head (the selector's generic bound kernel) and 8
+    (two row slabs in the sparse pass for 8 tokens)."""
+    cfg = W.SPARSE.with_(n_prefix=3000, n_steps=4, n_q_heads=hq, n_kv_heads=hkv)
+    steps = W.sparse_steps(cfg, m_override=[None, 2, 0, 5])
+    kp, vp = W.prefix_kv(cfg)
+    shape = fb.shape_of(hq, hkv, 128, cfg.scale, torch.bfloat16)
+    step = fb.Step(fb.FB_STEP_SPARSE, shape, 8, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
+                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, sel_bitmap=sel_bitmap)
+    ks = [dict(q=vals(s["q"], "bf16"), k=vals(s["k"], "bf16"), v=vals(s["v"], "bf16"))
+          for s in steps]
+    recs = OC.sparse_block(ks, vals(kp, "bf16"), vals(vp, "bf16"), cfg.scale, cfg.k_pages, cfg.page)
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        a = torch.empty(8, hq, 128, device="cuda")
+        l = torch.empty(8, hq, device="cuda")
+        step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                  dev_tensor(st["v"], "bf16"), a, l)
+        torch.cuda.synchronize()
+        tag = "q%d/kv%d step %d" % (hq, hkv, s)
+        assert np.array_equal(cpu(step.pages), rec["sel"]), tag
+        if s > 0:
+            assert mse_margin_ok(rec["mse"]), tag
+            check_mse(tag, cpu(step.mse), rec["mse"])
+        assert np.array_equal(cpu(step.active).astype(bool), rec["active"]), tag
+        check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 2e-3)
+        check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)
+        check_l(tag + " L_full", cpu(l), rec["l_full"], 1e-3)
