@@ -156,6 +156,36 @@ def test_video_block_matches_oracle(fb, n_q, n_kv):
         check_l("video step %d L_full" % s, cpu(l), rec["l_full"], 1e-3)
 
 
+@pytest.mark.parametrize("hq,hkv,n_q,n_kv", [(24, 8, 150, 500), (16, 2, 40, 700)],
+                         ids=["q24_kv8", "q16_kv2"])
+def test_video_block_grouped_heads(fb, hq, hkv, n_q, n_kv):
+    """Query heads sharing KV heads: the per-head reuse mask leaves groups
+    partly on, so the masked passes compute a group for its open heads and
+    must leave the reused heads' cached pair alone."""
+    cfg = W.VIDEO.with_(n_block=n_q, n_prefix=n_kv, n_steps=4, n_q_heads=hq, n_kv_heads=hkv)
+    sig, steps, kp, vp, recs = _video_sigmas(cfg, 0, cfg.gamma)
+    shape = fb.shape_of(hq, hkv, 128, cfg.scale, torch.bfloat16)
+    step = fb.Step(fb.FB_STEP_VIDEO, shape, n_q, dev_tensor(kp, "bf16"), dev_tensor(vp, "bf16"),
+                   gamma=cfg.gamma)
+    partly = False
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        used = cpu(step.mask).copy() if s > 0 else np.zeros(hq, np.uint8)
+        a = torch.empty(n_q, hq, 128, device="cuda")
+        l = torch.empty(n_q, hq, device="cuda")
+        step.step(dev_tensor(st["q"], "bf16"), dev_tensor(st["k"], "bf16"),
+                  dev_tensor(st["v"], "bf16"), a, l)
+        torch.cuda.synchronize()
+        if s > 0:
+            assert np.array_equal(used.astype(bool), rec["reuse_used"]), (s, used, rec["reuse_used"])
+            assert np.array_equal(cpu(step.mask).astype(bool), rec["reuse_next"])
+            grp = rec["reuse_used"].reshape(hkv, hq // hkv)
+            partly = partly or bool(np.any(grp.any(1) & ~grp.all(1)))
+        check_a("video step %d A_out" % s, cpu(step.a_out), rec["a_out"], 2e-3)
+        check_a("video step %d A_full" % s, cpu(a), rec["a_full"], 2e-3)
+        check_l("video step %d L_full" % s, cpu(l), rec["l_full"], 1e-3)
+    assert partly                              # some group was partly reused
+
+
 @pytest.mark.parametrize("density", [0.2, 0.4])
 @pytest.mark.parametrize("sel_bitmap", [True, False], ids=["bitmaps_kept", "prep_each_step"])
 def test_sparse_block_matches_oracle(fb, density, sel_bitmap):

@@ -257,17 +257,24 @@ def video_sigmas(cfg, variant=0):
 
 
 def video_steps(cfg, sigmas, variant=0, block=0):
-    """Per-step block Q/K/V [Nq, H, d] following X^{s+1} = X^s + sigma_h eps.
+    """Per-step block Q [Nq, Hq, d] and K/V [Nq, Hkv, d] following
+    X^{s+1} = X^s + sigma_h eps, sigma_h per query head; a KV head takes the
+    sigma of its group's first query head (with one query head per KV head,
+    every head its own).
 
     The walk is kept in float32; each step's inputs are its bf16 rounding.
     """
-    nq, h, d = cfg.n_block, cfg.n_q_heads, cfg.head_dim
-    sig = np.asarray(sigmas, dtype=np.float32)[None, :, None]
+    nq, hq, hkv, d = cfg.n_block, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    sig_q = np.asarray(sigmas, dtype=np.float32)
+    sigs = {"q": sig_q[None, :, None], "k": sig_q[::hq // hkv][None, :, None]}
+    sigs["v"] = sigs["k"]
     state = {}
     steps = []
     for s in range(cfg.n_steps):
         cur = {}
         for name, tag in (("q", TAG_Q), ("k", TAG_K), ("v", TAG_V)):
+            h = hq if name == "q" else hkv
+            sig = sigs[name]
             g = rng(cfg.cfg_id, variant, block, s, tag)
             eps = g.standard_normal((nq, h, d), dtype=np.float32)
             if s == 0:
