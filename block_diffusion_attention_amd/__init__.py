@@ -22,7 +22,7 @@ from ._abi import (  # noqa: F401
     fb_reuse_args, NOALLOC_SCRATCH_BYTES,
     fb_reuse_decide, fb_reuse_decide_workspace, fb_status_string, fb_step, fb_step_args,
     fb_step_next_block, fb_step_state, fb_step_workspace, fb_tensor, load, page_sel, ptr,
-    shape_of, stream_of, tensor_of)
+    shape_of, stream_of, tensor_of, tensors_of)
 
 
 class KVCache:
@@ -116,8 +116,7 @@ class Step:
             st.k_prefix = fb_tensor(c.k, c.n_tok, c.stride_tok, c.stride_head)
             st.v_prefix = fb_tensor(c.v, c.n_tok, c.stride_tok, c.stride_head)
         else:
-            st.k_prefix = tensor_of(k_prefix)
-            st.v_prefix = tensor_of(v_prefix)
+            _, st.k_prefix, st.v_prefix = tensors_of(shape, None, k_prefix, v_prefix)
         st.tau = int(tau)
         st.gamma = float(gamma)
         st.page_size = int(page_size)
@@ -193,7 +192,7 @@ class Step:
 
     def step(self, q, k, v, a_full, l_full=None, ids=None, decision=-1, stream=None):
         args = fb_step_args()
-        args.q_blk, args.k_blk, args.v_blk = tensor_of(q), tensor_of(k), tensor_of(v)
+        args.q_blk, args.k_blk, args.v_blk = tensors_of(self.shape, q, k, v)
         args.ids_cur = ptr(ids)
         args.decision = int(decision)
         args.a_full, args.l_full = ptr(a_full), ptr(l_full)

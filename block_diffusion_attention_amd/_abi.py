@@ -198,6 +198,18 @@ def tensor_of(t):
     return fb_tensor(ptr, t.shape[0], t.stride(0), t.stride(1))
 
 
+def tensors_of(shape, q, k, v):
+    """fb_tensors of q [n, Hq, d] and k, v [n_kv, Hkv, d], their head counts and
+    widths checked against the shape first (the C calls see strides only, so a
+    tensor of the wrong head count would be read as if it had the right one)."""
+    for name, t, heads in (("q", q, shape.n_q_heads), ("k", k, shape.n_kv_heads),
+                           ("v", v, shape.n_kv_heads)):
+        if t is not None and t.dim() == 3 and (t.shape[1] != heads or t.shape[2] != shape.head_dim):
+            raise ValueError("%s: expected [n, %d, %d], got %s"
+                             % (name, heads, shape.head_dim, tuple(t.shape)))
+    return tensor_of(q), tensor_of(k), tensor_of(v)
+
+
 def ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -231,7 +243,8 @@ def fb_prefix_attn_workspace(shape, n_q, n_kv, sel=None):
 def fb_prefix_attn(shape, q, k, v, a_out, l_out, mask=None, sel=None, a_res=None,
                    l_res=None, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    st = load().fb_prefix_attn(C.byref(shape), tensor_of(q), tensor_of(k), tensor_of(v),
+    tq, tk, tv = tensors_of(shape, q, k, v)
+    st = load().fb_prefix_attn(C.byref(shape), tq, tk, tv,
                                ptr(mask), C.byref(sel) if sel is not None else None,
                                ptr(a_out), ptr(l_out), ptr(a_res), ptr(l_res), ptr(ws),
                                ws_bytes, stream_of(stream))
@@ -243,7 +256,8 @@ NOALLOC_SCRATCH_BYTES = 16 << 20
 
 def fb_prefix_attn_noalloc(shape, q, k, v, a_out, l_out, mask=None, sel=None, a_res=None,
                            l_res=None, stream=None):
-    st = load().fb_prefix_attn_noalloc(C.byref(shape), tensor_of(q), tensor_of(k), tensor_of(v),
+    tq, tk, tv = tensors_of(shape, q, k, v)
+    st = load().fb_prefix_attn_noalloc(C.byref(shape), tq, tk, tv,
                                        ptr(mask), C.byref(sel) if sel is not None else None,
                                        ptr(a_out), ptr(l_out), ptr(a_res), ptr(l_res),
                                        stream_of(stream))
@@ -257,7 +271,8 @@ def fb_block_attn_merge_workspace(shape, n_q):
 def fb_block_attn_merge(shape, q, k, v, a_out, l_out, a_full, l_full=None, a_in=None,
                         l_in=None, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    st = load().fb_block_attn_merge(C.byref(shape), tensor_of(q), tensor_of(k), tensor_of(v),
+    tq, tk, tv = tensors_of(shape, q, k, v)
+    st = load().fb_block_attn_merge(C.byref(shape), tq, tk, tv,
                                     ptr(a_out), ptr(l_out), ptr(a_full), ptr(l_full),
                                     ptr(a_in), ptr(l_in), ptr(ws), ws_bytes, stream_of(stream))
     _check("fb_block_attn_merge", st)

@@ -393,3 +393,38 @@ def test_proxy_decide_rejects(lib):
     a.init, a.selected = 1, None              # init: the selection is not used
     a.ws_bytes = need - 1
     assert lib.fb_proxy_decide(C.byref(a), None) == fb.FB_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_page_select_refuses_beyond_its_grid_and_lds(lib):
+    sh = shape()
+    # more block tokens than the bound grid's token tiles cover
+    assert lib.fb_page_select(C.byref(sh), ten(70000, 32), FAKE, FAKE, 100, 0, 3, None, FAKE,
+                              FAKE, None, 0, None) == 2
+    # 64 query heads on one KV head at d = 128: one token's rows do not fit the
+    # generic bound kernel's 64 KB with the page rows
+    assert lib.fb_page_select(C.byref(shape(64, 1)), ten(4, 64), FAKE, FAKE, 100, 0, 3, None,
+                              FAKE, FAKE, None, 0, None) == 2
+
+
+def test_binding_checks_head_counts():
+    """The C calls see strides only; the binding refuses tensors whose head
+    count or width disagrees with the shape before calling them."""
+    import torch
+    sh = shape()
+    q = torch.zeros(4, 32, 128, dtype=torch.bfloat16)
+    k_ok = torch.zeros(100, 8, 128, dtype=torch.bfloat16)
+    k_bad = torch.zeros(100, 32, 128, dtype=torch.bfloat16)
+    a = torch.zeros(4, 32, 128)
+    l = torch.zeros(4, 32)
+    with pytest.raises(ValueError, match="k: expected"):
+        fb.fb_prefix_attn(sh, q, k_bad, k_ok, a, l)
+    with pytest.raises(ValueError, match="v: expected"):
+        fb.fb_prefix_attn(sh, q, k_ok, k_bad, a, l)
+    with pytest.raises(ValueError, match="q: expected"):
+        fb.fb_prefix_attn(sh, torch.zeros(4, 8, 128, dtype=torch.bfloat16), k_ok, k_ok, a, l)
+    with pytest.raises(ValueError, match="k: expected"):
+        fb.fb_block_attn_merge(sh, q, torch.zeros(4, 32, 128, dtype=torch.bfloat16),
+                               torch.zeros(4, 8, 128, dtype=torch.bfloat16), a, l, a)
+    with pytest.raises(ValueError, match="q: expected"):
+        fb.fb_prefix_attn_noalloc(sh, torch.zeros(4, 32, 64, dtype=torch.bfloat16), k_ok, k_ok,
+                                  a, l)
