@@ -93,6 +93,20 @@ def test_text_block_head_shapes(fb, hq, hkv, B):
         check_l("q%d/kv%d step %d L_full" % (hq, hkv, s), l, rec["l_full"], 1e-3)
 
 
+def test_text_block_d64_bf16(fb):
+    """bf16 with 64-dim heads: the generic pass and the in-block kernel's
+    64-dim form."""
+    cfg = W.LONG.with_(n_prefix=5000, n_block=8, n_steps=5, head_dim=64)
+    got, recs = run_text(fb, cfg, m_override=[None, 1, 8, 0, 5])
+    for s, (rec, (a, l, mc, mask, a_out, l_out)) in enumerate(zip(recs, got)):
+        if s > 0:
+            assert mc == rec["m_count"], (s, mc, rec["m_count"])
+        assert np.all(mask == (1 if rec["decision"] == OC.REUSE else 0)), (s, rec["decision"])
+        check_a("d64 step %d A_out" % s, a_out, rec["a_out"], 2e-3)
+        check_a("d64 step %d A_full" % s, a, rec["a_full"], 2e-3)
+        check_l("d64 step %d L_full" % s, l, rec["l_full"], 1e-3)
+
+
 def test_text_forced_reuse_and_recompute(fb):
     cfg = W.TEXT.with_(n_prefix=5000, n_steps=5)
     force = [None, OC.REUSE, OC.RECOMPUTE, OC.REUSE, OC.REUSE]
@@ -154,6 +168,42 @@ def test_video_block_matches_oracle(fb, n_q, n_kv):
         check_a("video step %d A_out" % s, cpu(step.a_out), rec["a_out"], 2e-3)
         check_a("video step %d A_full" % s, cpu(a), rec["a_full"], 2e-3)
         check_l("video step %d L_full" % s, cpu(l), rec["l_full"], 1e-3)
+
+
+def test_video_block_f32(fb):
+    """float32 video block (4 heads of 64 dims): the generic passes and the
+    float32 cosine decision."""
+    cfg = W.VIDEO.with_(n_block=50, n_prefix=300, n_steps=4, n_q_heads=4, n_kv_heads=4,
+                        head_dim=64, dtype="f32")
+    kp, vp = W.prefix_kv(cfg)
+    for var in range(20):
+        sig = W.video_sigmas(cfg, var)
+        steps = W.video_steps(cfg, sig)
+        ks = [dict(q=vals(s["q"], "f32"), k=vals(s["k"], "f32"), v=vals(s["v"], "f32"))
+              for s in steps]
+        recs = OC.video_block(ks, vals(kp, "f32"), vals(vp, "f32"), cfg.scale, cfg.gamma)
+        sims = np.concatenate([r["sim"][~np.isnan(r["sim"])] for r in recs[1:]])
+        nxt = recs[1]["reuse_next"]             # margin-clean, some heads reused and some not
+        if np.all(np.abs(sims - cfg.gamma) >= 1e-3) and nxt.any() and not nxt.all():
+            break
+    else:
+        raise RuntimeError("no margin-clean draw with mixed reuse")
+    shape = fb.shape_of(4, 4, 64, cfg.scale, torch.float32)
+    step = fb.Step(fb.FB_STEP_VIDEO, shape, 50, dev_tensor(kp, "f32"), dev_tensor(vp, "f32"),
+                   gamma=cfg.gamma)
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        used = cpu(step.mask).copy() if s > 0 else np.zeros(4, np.uint8)
+        a = torch.empty(50, 4, 64, device="cuda")
+        l = torch.empty(50, 4, device="cuda")
+        step.step(dev_tensor(st["q"], "f32"), dev_tensor(st["k"], "f32"),
+                  dev_tensor(st["v"], "f32"), a, l)
+        torch.cuda.synchronize()
+        if s > 0:
+            assert np.array_equal(used.astype(bool), rec["reuse_used"]), s
+            assert np.array_equal(cpu(step.mask).astype(bool), rec["reuse_next"]), s
+        check_a("f32 video step %d A_out" % s, cpu(step.a_out), rec["a_out"], 1e-5)
+        check_a("f32 video step %d A_full" % s, cpu(a), rec["a_full"], 1e-5)
+        check_l("f32 video step %d L_full" % s, cpu(l), rec["l_full"], 1e-5)
 
 
 @pytest.mark.parametrize("hq,hkv,n_q,n_kv", [(24, 8, 150, 500), (16, 2, 40, 700)],

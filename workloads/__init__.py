@@ -262,7 +262,8 @@ def video_steps(cfg, sigmas, variant=0, block=0):
     sigma of its group's first query head (with one query head per KV head,
     every head its own).
 
-    The walk is kept in float32; each step's inputs are its bf16 rounding.
+    The walk is kept in float32; each step's inputs are its bf16 rounding
+    (the float32 workload: the walk itself).
     """
     nq, hq, hkv, d = cfg.n_block, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     sig_q = np.asarray(sigmas, dtype=np.float32)
@@ -282,7 +283,7 @@ def video_steps(cfg, sigmas, variant=0, block=0):
             else:
                 x = state[name] + sig * eps
             state[name] = x
-            cur[name] = bf16_bits(x)
+            cur[name] = bf16_bits(x) if cfg.dtype == "bf16" else x.copy()
         steps.append(cur)
     return steps
 
