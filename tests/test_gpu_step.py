@@ -327,3 +327,36 @@ def test_sparse_block_head_shapes(fb, hq, hkv, sel_bitmap):
         check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 2e-3)
         check_a(tag + " A_full", cpu(a), rec["a_full"], 2e-3)
         check_l(tag + " L_full", cpu(l), rec["l_full"], 1e-3)
+
+
+@pytest.mark.parametrize("sel_bitmap", [True, False], ids=["bitmaps_kept", "prep_each_step"])
+def test_sparse_block_f32_d64(fb, sel_bitmap):
+    """float32, 64-dim heads: the page lists through the generic SPLIT and
+    GATHER passes, bounds from float32 metadata, the active set from float32
+    queries."""
+    cfg = W.SPARSE.with_(n_prefix=3000, n_steps=4, dtype="f32", head_dim=64)
+    steps = W.sparse_steps(cfg, m_override=[None, 2, 0, 5])
+    kp, vp = W.prefix_kv(cfg)
+    shape = fb.shape_of(32, 8, 64, cfg.scale, torch.float32)
+    step = fb.Step(fb.FB_STEP_SPARSE, shape, 8, dev_tensor(kp, "f32"), dev_tensor(vp, "f32"),
+                   page_size=cfg.page, k_pages=cfg.k_pages, pct=cfg.pct, sel_bitmap=sel_bitmap)
+    ks = [dict(q=vals(s["q"], "f32"), k=vals(s["k"], "f32"), v=vals(s["v"], "f32"))
+          for s in steps]
+    recs = OC.sparse_block(ks, vals(kp, "f32"), vals(vp, "f32"), cfg.scale, cfg.k_pages, cfg.page)
+    for s, (st, rec) in enumerate(zip(steps, recs)):
+        a = torch.empty(8, 32, 64, device="cuda")
+        l = torch.empty(8, 32, device="cuda")
+        step.step(dev_tensor(st["q"], "f32"), dev_tensor(st["k"], "f32"),
+                  dev_tensor(st["v"], "f32"), a, l)
+        torch.cuda.synchronize()
+        tag = "f32 sparse step %d" % s
+        assert np.array_equal(cpu(step.pages), rec["sel"]), tag
+        if s > 0:
+            assert mse_margin_ok(rec["mse"]), tag
+            check_mse(tag, cpu(step.mse), rec["mse"])
+        assert np.array_equal(cpu(step.active).astype(bool), rec["active"]), tag
+        if s == 0:
+            check_a(tag + " A_res", cpu(step.a_res), rec["a_res"], 1e-5)
+        check_a(tag + " A_out", cpu(step.a_out), rec["a_out"], 1e-5)
+        check_a(tag + " A_full", cpu(a), rec["a_full"], 1e-5)
+        check_l(tag + " L_full", cpu(l), rec["l_full"], 1e-5)
