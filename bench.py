@@ -92,6 +92,8 @@ def load_probe():
     lib.fb_probe_empty_launches.argtypes = [C.c_int, C.c_void_p]
     lib.fb_probe_f64_mfma.restype = C.c_int
     lib.fb_probe_f64_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    lib.fb_probe_bf16_mfma.restype = C.c_int
+    lib.fb_probe_bf16_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     return lib
 
 
@@ -112,6 +114,26 @@ def f64_mfma_rate(probe, stream, dev):
                 raise RuntimeError("fb_probe_f64_mfma failed (%d)" % rc)
         ms = _timed_settled(run, stream, 5, batches=3)
         best[wgs // 256] = 8192.0 * iters * wgs * 4 / (ms * 1e-3) / 1e12
+    return best
+
+
+def bf16_mfma_rate(probe, stream, dev):
+    """TFLOP/s of independent bf16 MFMA chains (v_mfma_f32_32x32x16_bf16, 4
+    accumulators per wave) with 1 and 2 waves per SIMD (256 and 512
+    workgroups of 4 waves), after half a second of the same work: the rate
+    the matrix core reaches on this part at the clock it holds under load."""
+    import torch
+    iters = 2048
+    best = {}
+    for wgs in (256, 512):
+        out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+
+        def run():
+            rc = probe.fb_probe_bf16_mfma(wgs, iters, out.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("fb_probe_bf16_mfma failed (%d)" % rc)
+        ms = _timed_settled(run, stream, 3, batches=3)
+        best[wgs // 256] = 524288.0 * iters * wgs * 4 / (ms * 1e-3) / 1e12
     return best
 
 
@@ -706,7 +728,8 @@ def text_short_extra(fb, W, dev, stream, probe, layout):
 def video_extra(fb, W, dev, stream, layout):
     """Video block diffusion (12 MHA heads, d=128, 4680 block queries, 12480-token
     prefix, 4 steps, gamma = 0.95): the block through fb_step, and the two
-    MFMA-bound passes alone against the bf16 MFMA peak."""
+    MFMA-bound passes alone against the bf16 MFMA peak and against the rate
+    bare bf16 MFMA chains reach in the same run."""
     import torch
     cfg = W.VIDEO
     H, d, NQ, NK = cfg.n_q_heads, cfg.head_dim, cfg.n_block, cfg.n_prefix
@@ -740,15 +763,20 @@ def video_extra(fb, W, dev, stream, layout):
                                                   stream=stream), stream, 20)
     f_pre = 4.0 * NQ * H * NK * d
     f_in = 4.0 * NQ * H * NQ * d
+    rates = bf16_mfma_rate(load_probe(), stream, dev)
+    top = max(rates.values())
     return {"workload": "video: 12 MHA heads, d=128, 4680 block queries, prefix 12480, 4 steps, "
                         "gamma=0.95, sigma_h ~ LogU(1e-3, 1)",
             "ms_block": round(ms_block, 3), "ms_block_all_heads_recompute": round(ms_dense, 3),
             "query_tok_per_s": round(4 * NQ / (ms_block * 1e-3), 1),
             "heads_reused_last_step": reused,
+            "bf16_mfma_probe_TFLOP_s": {"%d_waves_per_simd" % w: round(r, 1) for w, r in rates.items()},
             "prefix_pass": {"us": round(ms_pre * 1e3, 1), "TFLOP_s": round(f_pre / ms_pre / 1e9, 1),
-                            "frac_of_bf16_mfma_peak": round(f_pre / ms_pre / 1e9 / 2500.0, 4)},
+                            "frac_of_bf16_mfma_peak": round(f_pre / ms_pre / 1e9 / 2500.0, 4),
+                            "frac_of_bf16_mfma_probe": round(f_pre / ms_pre / 1e9 / top, 4)},
             "in_block_merge_pass": {"us": round(ms_in * 1e3, 1), "TFLOP_s": round(f_in / ms_in / 1e9, 1),
-                                    "frac_of_bf16_mfma_peak": round(f_in / ms_in / 1e9 / 2500.0, 4)}}
+                                    "frac_of_bf16_mfma_peak": round(f_in / ms_in / 1e9 / 2500.0, 4),
+                                    "frac_of_bf16_mfma_probe": round(f_in / ms_in / 1e9 / top, 4)}}
 
 
 def sparse_extra(fb, W, dev, stream, layout):

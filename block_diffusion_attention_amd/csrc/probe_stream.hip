@@ -3,8 +3,8 @@
 // buffers (the prefix K and V the attention pass reads) with the same access
 // style as that pass (16-byte non-temporal loads, several in flight per
 // lane) and no arithmetic beyond an XOR that keeps the loads live; the
-// float64 matrix-core rate (independent MFMA chains, nothing else); the
-// launch floor. Not part of the FlashBlock ABI: built as its own library,
+// float64 and bf16 matrix-core rates (independent MFMA chains, nothing
+// else); the launch floor. Not part of the FlashBlock ABI: built as its own library,
 // used by the benchmark only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -83,9 +83,52 @@ __global__ __launch_bounds__(256) void f64_mfma_kernel(double* out, int iters) {
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The bf16 matrix-core rate: each wave runs 4 independent accumulator chains
+// of v_mfma_f32_32x32x16_bf16 (32,768 flops each), consecutive MFMAs going to
+// different accumulators, for `iters` rounds; the lane's sum goes to out.
+__global__ __launch_bounds__(256) void bf16_mfma_kernel(float* out, int iters) {
+  const int l = threadIdx.x & 63;
+  bf16x8 a, b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = static_cast<__bf16>(1.0f + 1e-3f * (l + i));
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[q][i] = static_cast<__bf16>(1.0f - 1e-3f * (l + i + q));
+  f32x16 c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[q] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[kk], c[q], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += c[q][i];
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
+
+// n_workgroups workgroups of 256 threads (4 waves) of the bf16 MFMA rate
+// kernel, 16 MFMAs per wave per round for `iters` rounds: 524,288 * iters
+// flops per wave. out: device [n_workgroups * 256] float32. Returns 0 on
+// success, 1 on invalid arguments, 2 on a launch error.
+int fb_probe_bf16_mfma(int n_workgroups, int iters, float* out, hipStream_t stream) {
+  if (n_workgroups < 1 || iters < 1 || !out) return 1;
+  hipLaunchKernelGGL(bf16_mfma_kernel, dim3(n_workgroups), dim3(256), 0, stream, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // n_workgroups workgroups of 256 threads (4 waves) of the float64 MFMA rate
 // kernel, 4 MFMAs per wave per round for `iters` rounds: 8192 * iters flops
