@@ -377,9 +377,19 @@ def main():
     extra["stream_read_GB_s"] = read_gbs
     extra["prefix_frac_of_stream_read"] = round(achieved / read_gbs, 4)
 
+    def section(name, fn):
+        # a section that raises records its error and the line is still printed
+        # (the headline above does not depend on any section)
+        try:
+            extra[name] = fn()
+        except Exception as e:  # noqa: BLE001
+            torch.cuda.synchronize()
+            extra[name] = {"error": "%s: %s" % (type(e).__name__, e)}
+            print("bench section %s failed: %s" % (name, e), file=sys.stderr, flush=True)
+
     if not args.no_sweep:
-        extra["context_sweep"] = context_sweep(fb, W, W.LONG, k_dev, v_dev, stream, dev, probe,
-                                               args.kv_layout)
+        section("context_sweep", lambda: context_sweep(fb, W, W.LONG, k_dev, v_dev, stream, dev,
+                                                       probe, args.kv_layout))
 
     out = {
         "metric": "block-step attention query-tok/s (+ prefix-pass HBM GB/s vs peak)",
@@ -414,18 +424,19 @@ def main():
         "extra": extra,
     }
 
-    extra["reuse_step_check"] = reuse_step_check(fb, shape, step, inputs, a_full, l_full, B, N,
-                                                 hq, hkv, d, stream, probe)
+    section("reuse_step_check", lambda: reuse_step_check(fb, shape, step, inputs, a_full, l_full,
+                                                         B, N, hq, hkv, d, stream, probe))
     if not args.no_extras:
-        extra["text_32k_b4"] = text_short_extra(fb, W, dev, stream, probe, args.kv_layout)
-        extra["video"] = video_extra(fb, W, dev, stream, args.kv_layout)
-        extra["sparse"] = sparse_extra(fb, W, dev, stream, args.kv_layout)
-        extra["growing"] = growing_extra(fb, W, dev, stream, args.kv_layout)
-        extra["losa"] = losa_extra(fb, W, dev, stream, args.kv_layout)
-        extra["spa"] = spa_extra(fb, W, dev, stream, args.kv_layout)
-        extra["stack"] = stack_extra(fb, W, dev, stream, args.kv_layout)
-        extra["stack_identification"] = stack_identification_extra(fb, W, dev, stream,
-                                                                   args.kv_layout)
+        lay = args.kv_layout
+        section("text_32k_b4", lambda: text_short_extra(fb, W, dev, stream, probe, lay))
+        section("video", lambda: video_extra(fb, W, dev, stream, lay))
+        section("sparse", lambda: sparse_extra(fb, W, dev, stream, lay))
+        section("growing", lambda: growing_extra(fb, W, dev, stream, lay))
+        section("losa", lambda: losa_extra(fb, W, dev, stream, lay))
+        section("spa", lambda: spa_extra(fb, W, dev, stream, lay))
+        section("stack", lambda: stack_extra(fb, W, dev, stream, lay))
+        section("stack_identification",
+                lambda: stack_identification_extra(fb, W, dev, stream, lay))
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, kp, vp, steps, decisions)
