@@ -527,7 +527,11 @@ typedef struct {
                               launches a step). sparse_reselect: each step's
                               top-k writes the active tokens' fresh selection
                               there (P <= 8192) and the GATHER pass takes
-                              their union itself (no selection prep)          */
+                              their union itself (no selection prep). Inside
+                              the GATHER pass: blocks of up to 64 tokens and
+                              unions of up to 1,024 words; beyond, the union
+                              (and the classification) take launches of
+                              their own (results unchanged)                   */
 } fb_step_state;
 
 typedef struct {
